@@ -1,0 +1,255 @@
+/*
+ * dg.h -- C-ABI of the MI355X (gfx950) denoise step, entropy-bounded commit and
+ * structured slot read of a DiffusionGemma-style decoder.
+ *
+ * What the calls compute (pages cited by title and section):
+ *   dg_denoise_step  one decoder-mode denoise forward over every canvas position
+ *                    (24-ai.news "vLLM integrates DiffusionGemma", section "How is
+ *                    diffusion text generation different?": canvas refined in
+ *                    parallel, bidirectional attention with a +-W window; thakicloud
+ *                    "DiffusionGemma-as-Jev", section "What is DiffusionGemma":
+ *                    decoder mode reads the encoder KV), followed by the LM head, the
+ *                    vocabulary softmax giving confidence and entropy, and the
+ *                    self-conditioning vector (24-ai.news, section "Mechanism for
+ *                    deciding completed tokens").
+ *   dg_commit        the commit stage (24-ai.news, sections "Mechanism for deciding
+ *                    completed tokens" and "Integration into vLLM": denoise and
+ *                    commit are separate sampler stages): accept masked positions in
+ *                    confidence order until the cumulative entropy exceeds a
+ *                    threshold.
+ *   dg_slot_read     a read-only denoise forward on a caller-prefilled canvas that
+ *                    reports, at each decision slot, the logprobs of the allowed
+ *                    single-token labels, their renormalised distribution and its
+ *                    entropy (tau-home "DiffusionGemma like Jev", section "Refusing
+ *                    JSON token generation"); at most 26 labels (sotaaz "DiffusionGemma
+ *                    vLLM example server", section "The server takes at most 26
+ *                    alternatives"); a slot whose first-read entropy exceeds a
+ *                    threshold (0.1 on that page) is re-read with noise draws (4)
+ *                    whose distributions are averaged, n_draws = 1 being "samples: 1".
+ *
+ * The model is one attention block standing in for the backbone:
+ *   x = E[ids] + sc_in;  q,k,v = x Wq^T, x Wk^T, x Wv^T;
+ *   o = softmax(q k^T / sqrt(hd)) v over {all prompt keys} U {canvas j : |i-j| <= W},
+ *       query head h reading KV head h / (Hq/Hkv);
+ *   h = x + o Wo^T;  l = s_i * (h . LM_v);  p = softmax(l);
+ *   conf = max p;  entropy = -sum p ln p (nats);  argmax = lowest id of max l;
+ *   sc_out = sum_v p_v E_v.
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers unless stated otherwise; the caller
+ *     owns every buffer (inputs, outputs and the workspace) and keeps it alive
+ *     until the work queued on `stream` has finished.
+ *   - Row-major layouts; "T" is the storage type named by dg_dims.dtype (float or
+ *     bfloat16).  Accumulation is always fp32.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ *     and never synchronise the host.  They are safe to call concurrently from
+ *     several threads when each uses its own stream and workspace.
+ *   - The library never allocates device memory.  Scratch memory is the
+ *     caller-provided workspace, sized by the *_workspace queries.
+ *   - Host-visible arguments are checked before anything is launched; a failed
+ *     check returns a non-zero dg_status, launches nothing and leaves a message
+ *     for dg_last_error().  Index data that lives in device memory (token ids,
+ *     prompt offsets, slot positions, label ids) is checked inside the kernels,
+ *     which never read out of bounds; problems are reported through the
+ *     device-side flag / status outputs described below.
+ *   - A HIP launch failure returns DG_ERR_HIP.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_MAX_LABELS 26   /* labels A..Z, one token each */
+#define DG_MAX_CANVAS 1024 /* canvas positions per sequence handled by dg_commit */
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_INVALID_ARG = 1,
+    DG_ERR_TOO_MANY_LABELS = 2,
+    DG_ERR_UNSUPPORTED = 3,
+    DG_ERR_WORKSPACE = 4,
+    DG_ERR_HIP = 5
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* Model and canvas dimensions.
+ *   d_model    multiple of 32
+ *   head_dim   64 or 512
+ *   n_q_heads  multiple of n_kv_heads (GQA group G = n_q_heads / n_kv_heads)
+ *   vocab      multiple of 256
+ *   canvas     1 .. DG_MAX_CANVAS positions per sequence
+ *   window     W >= 0: canvas query i sees canvas keys j with |i - j| <= W
+ *   mask_id    token id of an undecided position, in [0, vocab)
+ *   dtype      a dg_dtype: storage type T of weights, prompt KV, sc vectors */
+typedef struct {
+    int32_t d_model, n_q_heads, n_kv_heads, head_dim, vocab, canvas, window, mask_id;
+    int32_t dtype;
+} dg_dims;
+
+/* Weights, all T, row-major, device.
+ *   embed    [vocab, d_model]  token embedding; also the LM head when lm_head is NULL
+ *   embed_t  [d_model, vocab]  the same matrix transposed (see dg_prepare_embed_t);
+ *                              required when sc_out is requested
+ *   lm_head  [vocab, d_model]  separate LM head, or NULL for a tied head
+ *   wq       [n_q_heads*head_dim, d_model]
+ *   wk, wv   [n_kv_heads*head_dim, d_model]
+ *   wo       [d_model, n_q_heads*head_dim] */
+typedef struct {
+    const void *embed, *embed_t, *lm_head, *wq, *wk, *wv, *wo;
+} dg_weights;
+
+/* Cached prompt (encoder-mode) keys and values of every sequence, packed.
+ *   k, v        [total_len, n_kv_heads, head_dim] T, device
+ *   cu_seqlens  [batch+1] int32, device: sequence b owns rows cu[b] .. cu[b+1]-1;
+ *               must be non-decreasing with cu[batch] <= total_len
+ *   max_len     host: an upper bound on every cu[b+1]-cu[b] (sizes the split-KV grid)
+ *   total_len   host: number of rows allocated in k and v
+ * A sequence of length 0 attends to its canvas window only. */
+typedef struct {
+    const void *k, *v;
+    const int32_t *cu_seqlens;
+    int32_t max_len;
+    int64_t total_len;
+} dg_prompt_kv;
+
+/* Optional intermediate outputs (each may be NULL; pass NULL for the struct to
+ * skip them all).  Written in addition to the regular outputs.
+ *   attn_out    [batch, canvas, n_q_heads*head_dim] T   attention output o
+ *   hidden_out  [batch, canvas, d_model] T              block output h
+ *   logits_out  [batch, canvas, vocab] fp32             scaled logits l */
+typedef struct {
+    void *attn_out;
+    void *hidden_out;
+    float *logits_out;
+} dg_debug;
+
+/* Device-side input problems reported through *dev_flags (bitwise OR). */
+#define DG_FLAG_BAD_TOKEN   1  /* a canvas id outside [0, vocab): embedded as a zero row */
+#define DG_FLAG_BAD_SEQLENS 2  /* cu_seqlens not monotone / beyond total_len / longer than
+                                  max_len: the prompt range was clamped */
+
+/* Per-slot status codes of dg_slot_read (status[b*n_slots+s]). */
+#define DG_SLOT_OK        0
+#define DG_SLOT_BAD_POS   1  /* slot position outside [0, canvas): slot skipped */
+#define DG_SLOT_BAD_COUNT 2  /* n_labels outside [1, 26]: slot skipped */
+#define DG_SLOT_BAD_LABEL 3  /* a label id outside [0, vocab): slot skipped */
+#define DG_SLOT_BAD_NOISE 4  /* a noise id outside [0, vocab): the mask id was used instead */
+
+/* Bytes of workspace dg_denoise_step needs for `batch` sequences whose prompts
+ * are at most `max_prompt` long.  Returns 0 for invalid dims. */
+size_t dg_denoise_step_workspace(const dg_dims *dims, int32_t batch, int32_t max_prompt);
+
+/* One denoise step over `batch` canvases.
+ *   canvas_ids   [batch, canvas] int32   token ids (mask_id at undecided positions)
+ *   sc_in        [batch, canvas, d_model] T or NULL (= zero) self-conditioning input
+ *   logit_scale  logits are multiplied by logit_scale * row_scale[b, i]
+ *   row_scale    [batch, canvas] fp32 or NULL (= 1)
+ *   conf         [batch, canvas] fp32  out: max probability
+ *   entropy      [batch, canvas] fp32  out: softmax entropy in nats
+ *   argmax       [batch, canvas] int32 out: most probable id (lowest on ties)
+ *   sc_out       [batch, canvas, d_model] T or NULL: out: sum_v p_v E_v
+ *   debug        optional intermediates (may be NULL)
+ *   dev_flags    [1] int32 device or NULL: OR of DG_FLAG_* (the call clears it first)
+ *   workspace    device buffer of at least dg_denoise_step_workspace(...) bytes,
+ *                256-byte aligned
+ * Errors: DG_ERR_INVALID_ARG (bad dims/pointers/sizes), DG_ERR_UNSUPPORTED
+ * (head_dim not 64/512, dtype unknown), DG_ERR_WORKSPACE (ws_bytes too small),
+ * DG_ERR_HIP. */
+dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                          int32_t batch, const int32_t *canvas_ids, const void *sc_in,
+                          float logit_scale, const float *row_scale,
+                          float *conf, float *entropy, int32_t *argmax, void *sc_out,
+                          const dg_debug *debug, int32_t *dev_flags,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/* Entropy-bounded commit of `batch` canvases of `canvas` positions each
+ * (1 <= canvas <= DG_MAX_CANVAS).  Candidates are positions whose id equals
+ * mask_id; they are ranked by (conf descending, position ascending); the
+ * candidate at rank k is accepted iff the fp32 sum of the entropies at ranks
+ * < k is <= threshold_nats (the candidate that crosses the threshold is
+ * accepted; at least one is accepted whenever a candidate exists and the
+ * threshold is >= 0).
+ *   canvas_ids, argmax [batch, canvas] int32; conf, entropy [batch, canvas] fp32
+ *   commit_mask  [batch, canvas] uint8 out: 1 where accepted
+ *   out_ids      [batch, canvas] int32 out: argmax where accepted, else canvas_ids
+ *   n_committed  [batch] int32 out (may be NULL)
+ * out_ids may alias canvas_ids (in-place commit).
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_HIP. */
+dg_status dg_commit(int32_t batch, int32_t canvas, int32_t mask_id,
+                    const int32_t *canvas_ids, const float *conf, const float *entropy,
+                    const int32_t *argmax, float threshold_nats,
+                    uint8_t *commit_mask, int32_t *out_ids, int32_t *n_committed,
+                    void *stream);
+
+/* Bytes of workspace dg_slot_read needs. */
+size_t dg_slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                              int32_t max_prompt, int32_t n_draws);
+
+/* Structured read of `n_slots` slots in each of `batch` caller-prefilled canvases.
+ * The canvas is never modified and nothing is committed.
+ *   canvas_ids   [batch, canvas] int32   prefilled skeleton (slots usually mask_id)
+ *   slot_pos     [batch, n_slots] int32  slot positions
+ *   label_ids    [batch, n_slots, 26] int32 allowed label ids, first n_labels used
+ *   n_labels     [batch, n_slots] int32  1..26
+ *   noise_ids    [n_draws, batch, n_slots] int32: token that draw d writes at slot s
+ *                of canvas b (ignored when n_draws == 1; may then be NULL)
+ *   logit_scale, row_scale ([batch, n_slots] fp32 or NULL) scale the slot logits
+ *   entropy_threshold  a slot is re-read iff n_draws > 1 and its first-read
+ *                entropy is > this
+ *   n_draws      1 .. 16; 1 = never re-read
+ * Outputs (fp32 unless noted; entries j >= n_labels are 0):
+ *   logprobs [batch, n_slots, 26]  ln p(label_j) under the full-vocabulary softmax
+ *                                  (draw-averaged in probability space if re-read)
+ *   probs    [batch, n_slots, 26]  distribution renormalised over the labels
+ *   entropy, first_entropy [batch, n_slots]  entropy of probs; of the first read
+ *   best     [batch, n_slots] int32  index j of the most probable label (lowest on ties)
+ *   draws_used [batch, n_slots] int32  1, or n_draws if re-read (0 if skipped)
+ *   status   [batch, n_slots] int32  DG_SLOT_* code
+ * A re-read replaces every slot token of its canvas by that draw's noise id and
+ * runs the whole step again; the draws (not the first read) are averaged.
+ * Errors: DG_ERR_TOO_MANY_LABELS never arises here (label arrays are fixed at 26;
+ * counts are checked per slot); DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED,
+ * DG_ERR_WORKSPACE, DG_ERR_HIP. */
+dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                       int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                       const int32_t *slot_pos, const int32_t *label_ids,
+                       const int32_t *n_labels, const int32_t *noise_ids,
+                       float logit_scale, const float *row_scale,
+                       float entropy_threshold, int32_t n_draws,
+                       float *logprobs, float *probs, float *entropy, float *first_entropy,
+                       int32_t *best, int32_t *draws_used, int32_t *status,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Writes embed_t = embed^T ([d_model, vocab] from [vocab, d_model]), the layout
+ * the self-conditioning contraction streams.  Weight preparation, done once. */
+dg_status dg_prepare_embed_t(const dg_dims *dims, const void *embed, void *embed_t,
+                             void *stream);
+
+/* Host-only validation (no HIP calls; usable without a GPU).  Same checks the
+ * calls above make before launching anything. */
+dg_status dg_denoise_step_validate(const dg_dims *dims, int32_t batch, int32_t max_prompt,
+                                   const dg_weights *w, const dg_prompt_kv *kv);
+dg_status dg_slot_read_validate(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                                int32_t n_draws, float entropy_threshold);
+dg_status dg_commit_validate(int32_t batch, int32_t canvas);
+
+/* Checks a question's alternative count before a slot is built: more than
+ * DG_MAX_LABELS alternatives cannot be given single-token labels A..Z. */
+dg_status dg_check_label_count(int32_t n_alternatives);
+
+const char *dg_status_string(dg_status s);
+/* Detail message of the last non-OK return on the calling thread ("" if none). */
+const char *dg_last_error(void);
+/* Library version string. */
+const char *dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

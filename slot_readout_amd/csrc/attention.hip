@@ -1,0 +1,317 @@
+// Decoder-mode attention for gfx950: every canvas query attends to all cached
+// prompt keys of its sequence plus the canvas keys within +-W of it
+// (bidirectional, no causal mask).
+//
+// Work split: one workgroup = (canvas, query head, tile of NQ consecutive
+// canvas positions, split of the prompt keys).  The last split also takes the
+// canvas-window keys.  With one split the workgroup writes the normalised
+// output; otherwise it writes (m, l, unnormalised O) partials that a second
+// kernel merges in a fixed order.
+//
+// Inside a workgroup the 4 waves each own QB x 16 query columns.  Scores are
+// computed transposed, S^T = K Q^T, so that a lane holds one query column and
+// the running max / sum of that query stay in the lane (plus one exchange
+// across the four 16-lane groups).  P^T then feeds O^T += V^T P^T directly
+// from registers; V is staged in LDS transposed, its keys permuted so each
+// lane's 8 bf16 values of a fragment are contiguous.
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+template <typename T> struct AttnCfg;
+
+template <typename T, int HD> struct AttnShape;
+template <> struct AttnShape<bf16, 64> { static constexpr int QB = 4, NK = 64; };
+template <> struct AttnShape<float, 64> { static constexpr int QB = 4, NK = 64; };
+template <> struct AttnShape<bf16, 512> { static constexpr int QB = 1, NK = 32; };
+
+// LDS position of key kk within a block for the transposed V tile
+template <typename T> __device__ inline int vt_pos(int kk);
+template <> __device__ inline int vt_pos<bf16>(int kk) {
+  const int t = kk >> 5, u = kk & 31;
+  const int uu = u & 15;
+  return (t << 5) + ((uu >> 2) << 3) + (u >= 16 ? 4 : 0) + (uu & 3);
+}
+template <> __device__ inline int vt_pos<float>(int kk) { return kk; }
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  using MF = Mfma<T>;
+  using frag = typename MF::frag;
+  constexpr int QB = AttnShape<T, HD>::QB;
+  constexpr int NK = AttnShape<T, HD>::NK;
+  constexpr int NQ = 4 * QB * 16;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int KP = HD + VEC;
+  constexpr int VP = NK + VEC;
+  constexpr int KS = HD / MF::KI;
+  __shared__ __attribute__((aligned(16))) T Ks[NK * KP];
+  __shared__ __attribute__((aligned(16))) T Vt[HD * VP];
+
+  const int s = blockIdx.x, qt = blockIdx.y;
+  const int cb = blockIdx.z / a.Hq, h = blockIdx.z % a.Hq;
+  if (a.active && !a.active[cb]) return;
+  const int G = a.Hq / a.Hkv, g = h / G;
+  const int C = a.C, W = a.W;
+  const int i0 = qt * NQ;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // prompt rows of this sequence, clamped against corrupt offsets
+  const int pb = cb / a.canvas_per_prompt;
+  int64_t p0 = a.cu[pb], p1 = a.cu[pb + 1];
+  bool bad = false;
+  if (p0 < 0) { p0 = 0; bad = true; }
+  if (p1 > a.total_len) { p1 = a.total_len; bad = true; }
+  if (p1 < p0) { p1 = p0; bad = true; }
+  if (p1 - p0 > a.max_len) { p1 = p0 + a.max_len; bad = true; }
+  if (bad && a.flags && threadIdx.x == 0 && s == 0 && qt == 0 && h == 0)
+    atomicOr(a.flags, DG_FLAG_BAD_SEQLENS);
+  const int64_t plen = p1 - p0;
+  const int64_t cs = (int64_t)s * a.chunk;
+  const int64_t ps = p0 + (cs < plen ? cs : plen);
+  const int64_t pe = p0 + (cs + a.chunk < plen ? cs + a.chunk : plen);
+
+  const int64_t kv_stride = (int64_t)a.Hkv * HD;   // elements between consecutive keys
+  const int64_t q_stride = (int64_t)a.Hq * HD;
+  const T *qbase = static_cast<const T *>(a.q) + (int64_t)cb * C * q_stride + (int64_t)h * HD;
+
+  frag qf[QB][KS];
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) {
+    const int qi = i0 + w * QB * 16 + jb * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (qi < C)
+        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qi * q_stride + ks * MF::KI +
+                                                      grp * MF::KPL);
+      else
+        qf[jb][ks] = frag{};
+    }
+  }
+
+  f32x4 oacc[HD / 16][QB];
+#pragma unroll
+  for (int rb = 0; rb < HD / 16; ++rb)
+#pragma unroll
+    for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = zero4();
+  float mrun[QB], lrun[QB];
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) { mrun[jb] = -INFINITY; lrun[jb] = 0.f; }
+
+  auto block = [&](const T *kb, const T *vb, int64_t k0, int64_t kend, bool canvas) {
+    constexpr int CPK = HD / VEC;
+    for (int c = threadIdx.x; c < NK * CPK; c += 256) {
+      const int kk = c / CPK, cc = c % CPK;
+      const int64_t key = k0 + kk;
+      Chunk<T> kc, vc;
+      if (key < kend) {
+        kc.u = *reinterpret_cast<const uint4 *>(kb + key * kv_stride + cc * VEC);
+        vc.u = *reinterpret_cast<const uint4 *>(vb + key * kv_stride + cc * VEC);
+      } else {
+        kc.u = uint4{0, 0, 0, 0};
+        vc.u = uint4{0, 0, 0, 0};
+      }
+      *reinterpret_cast<uint4 *>(Ks + kk * KP + cc * VEC) = kc.u;
+      const int pos = vt_pos<T>(kk);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Vt[(cc * VEC + e) * VP + pos] = vc.v[e];
+    }
+    __syncthreads();
+
+    f32x4 sacc[NK / 16][QB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+      for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb2 = 0; kb2 < NK / 16; ++kb2) {
+        const frag af = *reinterpret_cast<const frag *>(Ks + (kb2 * 16 + col) * KP + ks * MF::KI +
+                                                         grp * MF::KPL);
+#pragma unroll
+        for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] = MF::mma(af, qf[jb][ks], sacc[kb2][jb]);
+      }
+
+#pragma unroll
+    for (int jb = 0; jb < QB; ++jb) {
+      const int qi = i0 + w * QB * 16 + jb * 16 + col;
+      float bm = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t key = k0 + kb2 * 16 + grp * 4 + r;
+          bool ok = key < kend;
+          if (canvas) {
+            const int64_t dd = key - qi;
+            ok = ok && dd <= W && -dd <= W;
+          }
+          const float x = ok ? sacc[kb2][jb][r] * a.scale_log2 : -INFINITY;
+          sacc[kb2][jb][r] = x;
+          bm = fmaxf(bm, x);
+        }
+      bm = group4_max(bm);
+      const float mnew = fmaxf(mrun[jb], bm);
+      const float msub = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(mrun[jb] - msub);
+      float ps_ = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(sacc[kb2][jb][r] - msub);
+          sacc[kb2][jb][r] = p;
+          ps_ += p;
+        }
+      lrun[jb] = lrun[jb] * alpha + ps_;
+      mrun[jb] = mnew;
+#pragma unroll
+      for (int rb = 0; rb < HD / 16; ++rb) oacc[rb][jb] *= alpha;
+    }
+
+    if constexpr (MF::KPL == 8) {
+#pragma unroll
+      for (int t = 0; t < NK / 32; ++t)
+#pragma unroll
+        for (int jb = 0; jb < QB; ++jb) {
+          frag pf;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pf[j] = (bf16)sacc[2 * t][jb][j];
+            pf[4 + j] = (bf16)sacc[2 * t + 1][jb][j];
+          }
+#pragma unroll
+          for (int rb = 0; rb < HD / 16; ++rb) {
+            const frag af = *reinterpret_cast<const frag *>(Vt + (rb * 16 + col) * VP + t * 32 + grp * 8);
+            oacc[rb][jb] = MF::mma(af, pf, oacc[rb][jb]);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int rb = 0; rb < HD / 16; ++rb) {
+            const frag af = Vt[(rb * 16 + col) * VP + kb2 * 16 + grp * 4 + r];
+#pragma unroll
+            for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = MF::mma(af, sacc[kb2][jb][r], oacc[rb][jb]);
+          }
+    }
+    __syncthreads();
+  };
+
+  {
+    const T *kb = static_cast<const T *>(a.kp) + (int64_t)g * HD;
+    const T *vb = static_cast<const T *>(a.vp) + (int64_t)g * HD;
+    for (int64_t k0 = ps; k0 < pe; k0 += NK) block(kb, vb, k0, pe, false);
+  }
+  if (s == a.nsplit - 1) {
+    const int lo = i0 - W > 0 ? i0 - W : 0;
+    const int hi = i0 + NQ + W < C ? i0 + NQ + W : C;   // exclusive
+    const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
+    const T *kb = static_cast<const T *>(a.k) + cbase;
+    const T *vb = static_cast<const T *>(a.v) + cbase;
+    for (int k0 = lo; k0 < hi; k0 += NK) block(kb, vb, k0, hi, true);
+  }
+
+  const int64_t R = (int64_t)a.nc * a.Hq * C;
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) {
+    const int qi = i0 + w * QB * 16 + jb * 16 + col;
+    const float L = group4_sum(lrun[jb]);
+    if (qi >= C) continue;
+    if (a.nsplit == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      T *o = static_cast<T *>(a.o) + (((int64_t)cb * C + qi) * a.Hq + h) * HD;
+#pragma unroll
+      for (int rb = 0; rb < HD / 16; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<T>(oacc[rb][jb][r] * inv);
+    } else {
+      const int64_t row = ((int64_t)cb * a.Hq + h) * C + qi;
+      float *po = a.part_o + ((int64_t)s * R + row) * HD;
+#pragma unroll
+      for (int rb = 0; rb < HD / 16; ++rb)
+        *reinterpret_cast<float4 *>(po + rb * 16 + grp * 4) =
+            make_float4(oacc[rb][jb][0], oacc[rb][jb][1], oacc[rb][jb][2], oacc[rb][jb][3]);
+      if (grp == 0) a.part_ml[(int64_t)s * R + row] = make_float2(mrun[jb], L);
+    }
+  }
+}
+
+// fixed-order log-sum-exp merge of the split partials (scores are in log2 units)
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+  const int64_t R = (int64_t)a.nc * a.Hq * a.C;
+  const int64_t row = blockIdx.x;
+  const int C = a.C;
+  const int qi = (int)(row % C);
+  const int64_t ch = row / C;
+  const int h = (int)(ch % a.Hq);
+  const int64_t cb = ch / a.Hq;
+  if (a.active && !a.active[cb]) return;
+  float mstar = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[(int64_t)s * R + row].x);
+  constexpr int PER = HD / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float2 ml = a.part_ml[(int64_t)s * R + row];
+    if (ml.x == -INFINITY) continue;
+    const float wgt = exp2f(ml.x - mstar);
+    L += ml.y * wgt;
+    const float *po = a.part_o + ((int64_t)s * R + row) * HD;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += po[threadIdx.x + 64 * e] * wgt;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  T *o = static_cast<T *>(a.o) + ((cb * C + qi) * a.Hq + h) * HD;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[threadIdx.x + 64 * e] = from_f<T>(acc[e] * inv);
+}
+
+int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 256; }
+
+void attn_plan(int nc, int C, int Hq, int Hkv, int head_dim, int max_len, int *nsplit, int *chunk) {
+  const int nq = attn_query_tile(head_dim);
+  const int nk = head_dim == 512 ? 32 : 64;
+  const int64_t base = (int64_t)nc * Hq * cdiv64(C, nq);
+  int ns = 1;
+  if (max_len > 0 && base < 512) {
+    ns = (int)cdiv64(512, base);
+    const int64_t maxs = cdiv64(max_len, nk);
+    if (ns > maxs) ns = (int)maxs;
+  }
+  int ck = max_len > 0 ? (int)(cdiv64(cdiv64(max_len, ns), nk) * nk) : nk;
+  if (max_len > 0) ns = (int)cdiv64(max_len, ck);
+  if (ns < 1) ns = 1;
+  *nsplit = ns;
+  *chunk = ck;
+}
+
+template <typename T, int HD>
+static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
+  constexpr int NQ = 4 * AttnShape<T, HD>::QB * 16;
+  dim3 grid((unsigned)a.nsplit, (unsigned)cdiv64(a.C, NQ), (unsigned)(a.nc * a.Hq));
+  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const int64_t R = (int64_t)a.nc * a.Hq * a.C;
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)R), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st) {
+  if (bf && head_dim == 64) return launch_attn_t<bf16, 64>(a, st);
+  if (bf && head_dim == 512) return launch_attn_t<bf16, 512>(a, st);
+  if (!bf && head_dim == 64) return launch_attn_t<float, 64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dg

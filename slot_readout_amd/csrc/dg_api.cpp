@@ -1,0 +1,540 @@
+// C-ABI entry points: host-side validation, workspace planning and the launch
+// sequence of each call.  Nothing here allocates device memory or
+// synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dg.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dg_status fail(dg_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+dg_status ok() {
+  g_err.clear();
+  return DG_OK;
+}
+
+dg_status hip_check(hipError_t e, const char *what) {
+  if (e == hipSuccess) return DG_OK;
+  return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DG_TRY_HIP(expr, what)                       \
+  do {                                               \
+    dg_status _s = hip_check((expr), (what));        \
+    if (_s != DG_OK) return _s;                      \
+  } while (0)
+
+bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+size_t tsize(const dg_dims &d) { return d.dtype == DG_BF16 ? 2 : 4; }
+
+dg_status check_dims(const dg_dims *d) {
+  if (!d) return fail(DG_ERR_INVALID_ARG, "dims is NULL");
+  if (d->dtype != DG_F32 && d->dtype != DG_BF16)
+    return fail(DG_ERR_UNSUPPORTED, "dtype %d is neither DG_F32 nor DG_BF16", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 512)
+    return fail(DG_ERR_UNSUPPORTED, "head_dim %d: supported head widths are 64 and 512", d->head_dim);
+  if (d->head_dim == 512 && d->dtype == DG_F32)
+    return fail(DG_ERR_UNSUPPORTED, "head_dim 512 is supported with bf16 storage only");
+  if (d->d_model <= 0 || d->d_model % 32 != 0)
+    return fail(DG_ERR_INVALID_ARG, "d_model %d must be a positive multiple of 32", d->d_model);
+  if (d->n_kv_heads <= 0 || d->n_q_heads <= 0 || d->n_q_heads % d->n_kv_heads != 0)
+    return fail(DG_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->vocab <= 0 || d->vocab % dg::VTILE != 0)
+    return fail(DG_ERR_INVALID_ARG, "vocab %d must be a positive multiple of %d", d->vocab, dg::VTILE);
+  if (d->canvas < 1 || d->canvas > DG_MAX_CANVAS)
+    return fail(DG_ERR_INVALID_ARG, "canvas %d outside [1, %d]", d->canvas, DG_MAX_CANVAS);
+  if (d->window < 0) return fail(DG_ERR_INVALID_ARG, "window %d < 0", d->window);
+  if (d->mask_id < 0 || d->mask_id >= d->vocab)
+    return fail(DG_ERR_INVALID_ARG, "mask_id %d outside [0, vocab)", d->mask_id);
+  return DG_OK;
+}
+
+dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const dg_weights *w,
+                      const dg_prompt_kv *kv) {
+  dg_status s = check_dims(d);
+  if (s != DG_OK) return s;
+  if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (max_prompt < 0) return fail(DG_ERR_INVALID_ARG, "max_prompt %d < 0", max_prompt);
+  if (!w) return fail(DG_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->embed || !w->wq || !w->wk || !w->wv || !w->wo)
+    return fail(DG_ERR_INVALID_ARG, "embed, wq, wk, wv and wo are required");
+  if (!kv) return fail(DG_ERR_INVALID_ARG, "prompt_kv is NULL");
+  if (!kv->cu_seqlens) return fail(DG_ERR_INVALID_ARG, "prompt_kv.cu_seqlens is NULL");
+  if (kv->max_len < 0 || kv->total_len < 0)
+    return fail(DG_ERR_INVALID_ARG, "prompt_kv max_len/total_len must be >= 0");
+  if (kv->max_len > max_prompt)
+    return fail(DG_ERR_INVALID_ARG, "prompt_kv.max_len %d exceeds the planned max_prompt %d",
+                kv->max_len, max_prompt);
+  if (kv->max_len > 0 && (!kv->k || !kv->v))
+    return fail(DG_ERR_INVALID_ARG, "prompt_kv.k/v are NULL but max_len > 0");
+  const void *ptrs[] = {w->embed, w->embed_t, w->lm_head, w->wq, w->wk, w->wv, w->wo, kv->k, kv->v};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(DG_ERR_INVALID_ARG, "weight / KV pointers must be 16-byte aligned");
+  return DG_OK;
+}
+
+struct Arena {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  }
+};
+
+struct AttnPlan {
+  int nsplit = 1, chunk = 64;
+  size_t part_o = 0, part_ml = 0;
+};
+
+AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt) {
+  AttnPlan p;
+  dg::attn_plan(nc, d.canvas, d.n_q_heads, d.n_kv_heads, d.head_dim, max_prompt, &p.nsplit, &p.chunk);
+  if (p.nsplit > 1) {
+    const size_t R = (size_t)nc * d.n_q_heads * d.canvas;
+    p.part_o = (size_t)p.nsplit * R * d.head_dim * sizeof(float);
+    p.part_ml = (size_t)p.nsplit * R * sizeof(float2);
+  }
+  return p;
+}
+
+struct StepPlan {
+  size_t q, k, v, o, part_o, part_ml, h, stats, ptilde, fscale, sc_part, total;
+  AttnPlan attn;
+  int ksplit;
+};
+
+StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
+  StepPlan p{};
+  const size_t M = (size_t)B * d.canvas, ts = tsize(d);
+  const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
+  const int nvt = d.vocab / dg::VTILE;
+  const bool bf = d.dtype == DG_BF16;
+  Arena a;
+  p.q = a.take(M * nq * ts);
+  p.k = a.take(M * nkv * ts);
+  p.v = a.take(M * nkv * ts);
+  p.o = a.take(M * nq * ts);
+  p.attn = plan_attention(d, B, max_prompt);
+  p.part_o = a.take(p.attn.part_o);
+  p.part_ml = a.take(p.attn.part_ml);
+  p.h = a.take(M * d.d_model * ts);
+  p.stats = a.take(M * nvt * sizeof(float4));
+  p.ptilde = a.take(M * d.vocab * ts);
+  p.fscale = a.take(M * nvt * sizeof(float));
+  p.ksplit = dg::sc_ksplit((int64_t)M, d.d_model, d.vocab, bf);
+  p.sc_part = a.take(p.ksplit > 1 ? (size_t)p.ksplit * M * d.d_model * sizeof(float) : 0);
+  p.total = a.off;
+  return p;
+}
+
+struct SlotPlan {
+  size_t q, k, v, o, part_o, part_ml, h, rows, stats, rowstat, flags, draw_active, draw_ids,
+      row_active, rs_draw, total;
+  AttnPlan first, draws;
+};
+
+SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
+  SlotPlan p{};
+  const int ncmax = nd > 1 ? B * nd : B;
+  const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
+  const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
+  const int nvt = d.vocab / dg::VTILE;
+  const size_t nrows = (size_t)B * S * (nd > 1 ? nd : 1);
+  Arena a;
+  p.q = a.take(M * nq * ts);
+  p.k = a.take(M * nkv * ts);
+  p.v = a.take(M * nkv * ts);
+  p.o = a.take(M * nq * ts);
+  p.first = plan_attention(d, B, max_prompt);
+  p.draws = plan_attention(d, ncmax, max_prompt);
+  const size_t po = p.first.part_o > p.draws.part_o ? p.first.part_o : p.draws.part_o;
+  const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
+  p.part_o = a.take(po);
+  p.part_ml = a.take(pm);
+  p.h = a.take(M * d.d_model * ts);
+  p.rows = a.take(nrows * sizeof(int32_t));
+  p.stats = a.take(nrows * nvt * sizeof(float4));
+  p.rowstat = a.take(nrows * sizeof(float2));
+  p.flags = a.take(((size_t)B + (size_t)B * S) * sizeof(int32_t));
+  p.draw_active = a.take((size_t)B * (nd > 1 ? nd : 1) * sizeof(int32_t));
+  p.draw_ids = a.take(nd > 1 ? (size_t)B * nd * d.canvas * sizeof(int32_t) : 0);
+  p.row_active = a.take(nrows * sizeof(int32_t));
+  p.rs_draw = a.take(nrows * sizeof(float));
+  p.total = a.off;
+  return p;
+}
+
+template <typename P> P *at(void *ws, size_t off) {
+  return reinterpret_cast<P *>(static_cast<char *>(ws) + off);
+}
+
+// S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
+dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *kv, int nc,
+                    int canvas_per_prompt, const int32_t *ids, const void *sc_in,
+                    const int32_t *active, int32_t *flags, void *q, void *k, void *v, void *o,
+                    const AttnPlan &ap, float *part_o, float2 *part_ml, void *h, hipStream_t st) {
+  const bool bf = d.dtype == DG_BF16;
+  const int64_t M = (int64_t)nc * d.canvas;
+  dg::QkvArgs qa{};
+  qa.ids = ids;
+  qa.embed = w->embed;
+  qa.sc_in = sc_in;
+  qa.wq = w->wq;
+  qa.wk = w->wk;
+  qa.wv = w->wv;
+  qa.q = q;
+  qa.k = k;
+  qa.v = v;
+  qa.active = active;
+  qa.flags = flags;
+  qa.M = M;
+  qa.d = d.d_model;
+  qa.nq = d.n_q_heads * d.head_dim;
+  qa.nkv = d.n_kv_heads * d.head_dim;
+  qa.vocab = d.vocab;
+  qa.C = d.canvas;
+  DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "qkv projection launch");
+
+  dg::AttnArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.kp = kv->k;
+  aa.vp = kv->v;
+  aa.cu = kv->cu_seqlens;
+  aa.active = active;
+  aa.flags = flags;
+  aa.o = o;
+  aa.part_o = part_o;
+  aa.part_ml = part_ml;
+  aa.total_len = kv->total_len;
+  aa.nc = nc;
+  aa.C = d.canvas;
+  aa.Hq = d.n_q_heads;
+  aa.Hkv = d.n_kv_heads;
+  aa.W = d.window;
+  aa.max_len = kv->max_len;
+  aa.nsplit = ap.nsplit;
+  aa.chunk = ap.chunk;
+  aa.canvas_per_prompt = canvas_per_prompt;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
+
+  dg::OprojArgs oa{};
+  oa.o = o;
+  oa.wo = w->wo;
+  oa.ids = ids;
+  oa.embed = w->embed;
+  oa.sc_in = sc_in;
+  oa.h = h;
+  oa.active = active;
+  oa.M = M;
+  oa.d = d.d_model;
+  oa.kdim = d.n_q_heads * d.head_dim;
+  oa.vocab = d.vocab;
+  oa.C = d.canvas;
+  DG_TRY_HIP(dg::launch_oproj(oa, bf, st), "output projection launch");
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_TOO_MANY_LABELS: return "too many labels (at most 26 alternatives)";
+    case DG_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *dg_last_error(void) { return g_err.c_str(); }
+
+const char *dg_version(void) { return "dg 0.1.0 (gfx950)"; }
+
+dg_status dg_check_label_count(int32_t n) {
+  if (n < 1) return fail(DG_ERR_INVALID_ARG, "a question needs at least one alternative (got %d)", n);
+  if (n > DG_MAX_LABELS)
+    return fail(DG_ERR_TOO_MANY_LABELS, "at most %d alternatives (got %d)", DG_MAX_LABELS, n);
+  return ok();
+}
+
+dg_status dg_denoise_step_validate(const dg_dims *dims, int32_t batch, int32_t max_prompt,
+                                   const dg_weights *w, const dg_prompt_kv *kv) {
+  dg_status s = check_model(dims, batch, max_prompt, w, kv);
+  return s == DG_OK ? ok() : s;
+}
+
+dg_status dg_slot_read_validate(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                                int32_t n_draws, float entropy_threshold) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (n_slots < 0) return fail(DG_ERR_INVALID_ARG, "n_slots %d < 0", n_slots);
+  if (n_draws < 1 || n_draws > 16) return fail(DG_ERR_INVALID_ARG, "n_draws %d outside [1, 16]", n_draws);
+  if (!(entropy_threshold >= 0.f)) return fail(DG_ERR_INVALID_ARG, "entropy_threshold must be >= 0");
+  return ok();
+}
+
+dg_status dg_commit_validate(int32_t batch, int32_t canvas) {
+  if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (canvas < 1 || canvas > DG_MAX_CANVAS)
+    return fail(DG_ERR_INVALID_ARG, "canvas %d outside [1, %d]", canvas, DG_MAX_CANVAS);
+  return ok();
+}
+
+size_t dg_denoise_step_workspace(const dg_dims *dims, int32_t batch, int32_t max_prompt) {
+  if (check_dims(dims) != DG_OK || batch < 0 || max_prompt < 0) return 0;
+  return plan_step(*dims, batch, max_prompt).total;
+}
+
+dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                          int32_t batch, const int32_t *canvas_ids, const void *sc_in,
+                          float logit_scale, const float *row_scale, float *conf, float *entropy,
+                          int32_t *argmax, void *sc_out, const dg_debug *debug,
+                          int32_t *dev_flags, void *workspace, size_t ws_bytes, void *stream) {
+  dg_status s = check_model(dims, batch, kv ? kv->max_len : 0, w, kv);
+  if (s != DG_OK) return s;
+  const dg_dims &d = *dims;
+  if (batch == 0) return ok();
+  if (!canvas_ids || !conf || !entropy || !argmax)
+    return fail(DG_ERR_INVALID_ARG, "canvas_ids, conf, entropy and argmax are required");
+  if (sc_out && !w->embed_t)
+    return fail(DG_ERR_INVALID_ARG, "sc_out requires weights.embed_t (see dg_prepare_embed_t)");
+  if (!aligned16(sc_in) || !aligned16(sc_out) || !aligned16(workspace))
+    return fail(DG_ERR_INVALID_ARG, "sc_in, sc_out and workspace must be 16-byte aligned");
+  if (debug && (!aligned16(debug->attn_out) || !aligned16(debug->hidden_out)))
+    return fail(DG_ERR_INVALID_ARG, "debug outputs must be 16-byte aligned");
+  const StepPlan p = plan_step(d, batch, kv->max_len);
+  if (!workspace || ws_bytes < p.total)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                ws_bytes, p.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = d.dtype == DG_BF16;
+  const int64_t M = (int64_t)batch * d.canvas;
+  const int nvt = d.vocab / dg::VTILE;
+  void *o = (debug && debug->attn_out) ? debug->attn_out : at<char>(workspace, p.o);
+  void *h = (debug && debug->hidden_out) ? debug->hidden_out : at<char>(workspace, p.h);
+  if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
+  s = run_block(d, w, kv, batch, 1, canvas_ids, sc_in, nullptr, dev_flags, at<char>(workspace, p.q),
+                at<char>(workspace, p.k), at<char>(workspace, p.v), o, p.attn,
+                at<float>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st);
+  if (s != DG_OK) return s;
+
+  dg::LmheadArgs la{};
+  la.head = w->lm_head ? w->lm_head : w->embed;
+  la.h = h;
+  la.logit_scale = logit_scale;
+  la.row_scale = row_scale;
+  la.stats = at<float4>(workspace, p.stats);
+  la.ptilde = sc_out ? at<char>(workspace, p.ptilde) : nullptr;
+  la.logits = debug ? debug->logits_out : nullptr;
+  la.nrows = M;
+  la.d = d.d_model;
+  la.vocab = d.vocab;
+  la.nvt = nvt;
+  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "LM head launch");
+
+  dg::VocabMergeArgs va{};
+  va.stats = la.stats;
+  va.nrows = M;
+  va.nvt = nvt;
+  va.conf = conf;
+  va.entropy = entropy;
+  va.argmax = argmax;
+  va.fscale = sc_out ? at<float>(workspace, p.fscale) : nullptr;
+  DG_TRY_HIP(dg::launch_vocab_merge(va, st), "vocabulary merge launch");
+
+  if (sc_out) {
+    dg::ScArgs sa{};
+    sa.ptilde = la.ptilde;
+    sa.fscale = va.fscale;
+    sa.embed_t = w->embed_t;
+    sa.part = at<float>(workspace, p.sc_part);
+    sa.out = sc_out;
+    sa.M = M;
+    sa.d = d.d_model;
+    sa.vocab = d.vocab;
+    sa.nvt = nvt;
+    sa.ksplit = p.ksplit;
+    DG_TRY_HIP(dg::launch_scgemm(sa, bf, st), "self-conditioning launch");
+  }
+  return ok();
+}
+
+dg_status dg_commit(int32_t batch, int32_t canvas, int32_t mask_id, const int32_t *canvas_ids,
+                    const float *conf, const float *entropy, const int32_t *argmax,
+                    float threshold_nats, uint8_t *commit_mask, int32_t *out_ids,
+                    int32_t *n_committed, void *stream) {
+  dg_status s = dg_commit_validate(batch, canvas);
+  if (s != DG_OK) return s;
+  if (std::isnan(threshold_nats)) return fail(DG_ERR_INVALID_ARG, "threshold is NaN");
+  if (batch == 0) return ok();
+  if (!canvas_ids || !conf || !entropy || !argmax || !commit_mask || !out_ids)
+    return fail(DG_ERR_INVALID_ARG, "commit arrays must not be NULL (n_committed may be)");
+  dg::CommitArgs ca{};
+  ca.ids = canvas_ids;
+  ca.conf = conf;
+  ca.entropy = entropy;
+  ca.argmax = argmax;
+  ca.mask = commit_mask;
+  ca.out_ids = out_ids;
+  ca.n_committed = n_committed;
+  ca.B = batch;
+  ca.C = canvas;
+  ca.mask_id = mask_id;
+  ca.tau = threshold_nats;
+  DG_TRY_HIP(dg::launch_commit(ca, static_cast<hipStream_t>(stream)), "commit launch");
+  return ok();
+}
+
+size_t dg_slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                              int32_t max_prompt, int32_t n_draws) {
+  if (check_dims(dims) != DG_OK || batch < 0 || n_slots < 0 || max_prompt < 0 || n_draws < 1 ||
+      n_draws > 16)
+    return 0;
+  return plan_slot(*dims, batch, n_slots, max_prompt, n_draws).total;
+}
+
+dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                       int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                       const int32_t *slot_pos, const int32_t *label_ids, const int32_t *n_labels,
+                       const int32_t *noise_ids, float logit_scale, const float *row_scale,
+                       float entropy_threshold, int32_t n_draws, float *logprobs, float *probs,
+                       float *entropy, float *first_entropy, int32_t *best, int32_t *draws_used,
+                       int32_t *status, void *workspace, size_t ws_bytes, void *stream) {
+  dg_status s = dg_slot_read_validate(dims, batch, n_slots, n_draws, entropy_threshold);
+  if (s != DG_OK) return s;
+  s = check_model(dims, batch, kv ? kv->max_len : 0, w, kv);
+  if (s != DG_OK) return s;
+  const dg_dims &d = *dims;
+  if (batch == 0 || n_slots == 0) return ok();
+  if (!canvas_ids || !slot_pos || !label_ids || !n_labels || !logprobs || !probs || !entropy ||
+      !first_entropy || !best || !draws_used || !status)
+    return fail(DG_ERR_INVALID_ARG, "slot-read input and output arrays must not be NULL");
+  if (n_draws > 1 && !noise_ids) return fail(DG_ERR_INVALID_ARG, "noise_ids is required when n_draws > 1");
+  if (!aligned16(workspace)) return fail(DG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const SlotPlan p = plan_slot(d, batch, n_slots, kv->max_len, n_draws);
+  if (!workspace || ws_bytes < p.total)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                ws_bytes, p.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = d.dtype == DG_BF16;
+  const int nvt = d.vocab / dg::VTILE;
+  void *q = at<char>(workspace, p.q), *k = at<char>(workspace, p.k), *v = at<char>(workspace, p.v);
+  void *o = at<char>(workspace, p.o), *h = at<char>(workspace, p.h);
+  float *part_o = at<float>(workspace, p.part_o);
+  float2 *part_ml = at<float2>(workspace, p.part_ml);
+
+  dg::SlotArgs sa{};
+  sa.slot_pos = slot_pos;
+  sa.label_ids = label_ids;
+  sa.n_labels = n_labels;
+  sa.noise_ids = noise_ids;
+  sa.head = w->lm_head ? w->lm_head : w->embed;
+  sa.h = h;
+  sa.rowstat = at<float2>(workspace, p.rowstat);
+  sa.row_scale = row_scale;
+  sa.logit_scale = logit_scale;
+  sa.threshold = entropy_threshold;
+  sa.B = batch;
+  sa.S = n_slots;
+  sa.C = d.canvas;
+  sa.V = d.vocab;
+  sa.d = d.d_model;
+  sa.n_draws = n_draws;
+  sa.rows = at<int32_t>(workspace, p.rows);
+  sa.status = status;
+  sa.logprobs = logprobs;
+  sa.probs = probs;
+  sa.entropy = entropy;
+  sa.first_entropy = first_entropy;
+  sa.best = best;
+  sa.draws_used = draws_used;
+  sa.canvas_flag = at<int32_t>(workspace, p.flags);
+  sa.draw_active = at<int32_t>(workspace, p.draw_active);
+  sa.canvas_ids = canvas_ids;
+  sa.draw_ids = at<int32_t>(workspace, p.draw_ids);
+  sa.mask_id = d.mask_id;
+
+  // first read over the prefilled canvases
+  s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
+                part_o, part_ml, h, st);
+  if (s != DG_OK) return s;
+  DG_TRY_HIP(dg::launch_slot_rows(sa, bf, st), "slot row launch");
+  dg::LmheadArgs la{};
+  la.head = sa.head;
+  la.h = h;
+  la.row_index = sa.rows;
+  la.logit_scale = logit_scale;
+  la.row_scale = row_scale;
+  la.stats = at<float4>(workspace, p.stats);
+  la.nrows = (int64_t)batch * n_slots;
+  la.d = d.d_model;
+  la.vocab = d.vocab;
+  la.nvt = nvt;
+  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "slot LM head launch");
+  dg::VocabMergeArgs va{};
+  va.stats = la.stats;
+  va.nrows = la.nrows;
+  va.nvt = nvt;
+  va.rowstat = at<float2>(workspace, p.rowstat);
+  DG_TRY_HIP(dg::launch_vocab_merge(va, st), "slot vocabulary merge launch");
+  DG_TRY_HIP(dg::launch_slot_first(sa, bf, st), "slot first-read launch");
+  if (n_draws == 1) return ok();
+
+  // re-read of flagged canvases: n_draws noise copies in one batched pass
+  DG_TRY_HIP(dg::launch_slot_build_draws(sa, st), "draw canvas launch");
+  s = run_block(d, w, kv, batch * n_draws, n_draws, sa.draw_ids, nullptr, sa.draw_active, nullptr,
+                q, k, v, o, p.draws, part_o, part_ml, h, st);
+  if (s != DG_OK) return s;
+  int32_t *row_active = at<int32_t>(workspace, p.row_active);
+  float *rs_draw = at<float>(workspace, p.rs_draw);
+  DG_TRY_HIP(dg::launch_slot_draw_rows2(sa, row_active, rs_draw, st), "draw row launch");
+  la.nrows = (int64_t)batch * n_draws * n_slots;
+  la.active_rows = row_active;
+  la.rows_per_flag = 1;
+  la.row_scale = rs_draw;
+  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "draw LM head launch");
+  va.nrows = la.nrows;
+  DG_TRY_HIP(dg::launch_vocab_merge(va, st), "draw vocabulary merge launch");
+  DG_TRY_HIP(dg::launch_slot_average(sa, bf, st), "draw average launch");
+  return ok();
+}
+
+dg_status dg_prepare_embed_t(const dg_dims *dims, const void *embed, void *embed_t, void *stream) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (!embed || !embed_t) return fail(DG_ERR_INVALID_ARG, "embed and embed_t are required");
+  DG_TRY_HIP(dg::launch_transpose(embed, embed_t, dims->vocab, dims->d_model,
+                                  dims->dtype == DG_BF16, static_cast<hipStream_t>(stream)),
+             "transpose launch");
+  return ok();
+}
+
+}  // extern "C"

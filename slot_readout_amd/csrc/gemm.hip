@@ -1,0 +1,550 @@
+// MFMA-tiled "NT" GEMMs (both operands K-contiguous) for gfx950, with the
+// prologues and epilogues of the denoise step fused in:
+//   qkv_kernel     q,k,v = (E[ids] + sc_in) [Wq;Wk;Wv]^T      (embedding gather fused)
+//   oproj_kernel   h = x + o Wo^T                              (residual fused)
+//   lmhead_kernel  l = s_i h E^T, per-(row, vocab tile) max / sum e^(l-m) /
+//                  sum e^(l-m)(l-m) / argmax, optional p~ = e^(l - m_tile)
+//   scgemm_kernel  sc = sum_v p_v E_v over a vocabulary range (split-K)
+//
+// One workgroup computes a BM x BN tile with WGM x WGN waves; each wave owns a
+// (BM/WGM) x (BN/WGN) block of 16x16 MFMA tiles.  Operand tiles stream through
+// double-buffered LDS (16-byte global loads -> registers -> LDS, one barrier per
+// K step); fragments are read from LDS with 16-byte (bf16) or 4-byte (fp32)
+// reads.  Accumulation is fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+template <typename T> struct BKOf;
+template <> struct BKOf<bf16> { static constexpr int v = 32; };
+template <> struct BKOf<float> { static constexpr int v = 16; };
+
+template <typename T, int BM, int BN, int WGM, int WGN>
+struct Gemm {
+  static constexpr int BK = BKOf<T>::v;
+  static constexpr int NW = WGM * WGN;
+  static constexpr int NT = NW * WAVE;
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int CPR = BK / VEC;      // 16-byte chunks per tile row
+  static constexpr int PITCH = BK + VEC;    // 16 bytes of padding per LDS row
+  static constexpr int AI = BM * CPR / NT;  // A chunks per thread per K step
+  static constexpr int BI = BN * CPR / NT;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int LDS_BYTES = 2 * (BM + BN) * PITCH * (int)sizeof(T);
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be 16-aligned");
+  using MF = Mfma<T>;
+  using frag = typename MF::frag;
+
+  __device__ static inline int a_row(int it) { return (it * NT + (int)threadIdx.x) / CPR; }
+  __device__ static inline int a_kc(int it) { return (it * NT + (int)threadIdx.x) % CPR; }
+
+  // acc += A[rows of tile, kbeg:kend] * B[rows of tile, kbeg:kend]^T
+  template <class AL, class BL>
+  __device__ static void run(char *smem, const AL &al, const BL &bl, int kbeg, int kend,
+                             f32x4 (&acc)[TM][TN]) {
+    T *lds = reinterpret_cast<T *>(smem);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w / WGN, wn = w % WGN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+    const int nk = (kend - kbeg) / BK;
+    if (nk <= 0) return;
+    uint4 ra[AI], rb[BI];
+    auto gload = [&](int kt) {
+      const int k0 = kbeg + kt * BK;
+#pragma unroll
+      for (int it = 0; it < AI; ++it) ra[it] = al.fetch(it, k0 + a_kc(it) * VEC);
+#pragma unroll
+      for (int it = 0; it < BI; ++it) rb[it] = bl.fetch(it, k0 + a_kc(it) * VEC);
+    };
+    auto sstore = [&](int buf) {
+      T *As = lds + buf * (BM + BN) * PITCH;
+      T *Bs = As + BM * PITCH;
+#pragma unroll
+      for (int it = 0; it < AI; ++it)
+        *reinterpret_cast<uint4 *>(As + a_row(it) * PITCH + a_kc(it) * VEC) = ra[it];
+#pragma unroll
+      for (int it = 0; it < BI; ++it)
+        *reinterpret_cast<uint4 *>(Bs + a_row(it) * PITCH + a_kc(it) * VEC) = rb[it];
+    };
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) gload(kt + 1);
+      const T *As = lds + (kt & 1) * (BM + BN) * PITCH;
+      const T *Bs = As + BM * PITCH;
+#pragma unroll
+      for (int ks = 0; ks < BK / MF::KI; ++ks) {
+        frag a[TM], b[TN];
+        const int kk = ks * MF::KI + (lane >> 4) * MF::KPL;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          a[i] = *reinterpret_cast<const frag *>(As + (wm * WM + i * 16 + (lane & 15)) * PITCH + kk);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          b[j] = *reinterpret_cast<const frag *>(Bs + (wn * WN + j * 16 + (lane & 15)) * PITCH + kk);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(a[i], b[j], acc[i][j]);
+      }
+      if (kt + 1 < nk) sstore((kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// operand loaders: fetch(it, k) returns the 16-byte chunk at column k of the
+// row this thread loads in chunk slot `it` (zero for rows outside the matrix)
+// ---------------------------------------------------------------------------
+template <typename T, int N> struct RowLoader {
+  const T *p[N];
+  __device__ inline uint4 fetch(int it, int k) const {
+    return p[it] ? *reinterpret_cast<const uint4 *>(p[it] + k) : uint4{0, 0, 0, 0};
+  }
+};
+
+// x = E[id] + sc_in, rounded to T
+template <typename T, int N> struct GatherLoader {
+  const T *e[N];
+  const T *s[N];
+  __device__ inline uint4 fetch(int it, int k) const {
+    if (!e[it]) return uint4{0, 0, 0, 0};
+    Chunk<T> a;
+    a.u = *reinterpret_cast<const uint4 *>(e[it] + k);
+    if (s[it]) {
+      Chunk<T> b;
+      b.u = *reinterpret_cast<const uint4 *>(s[it] + k);
+#pragma unroll
+      for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) + to_f(b.v[i]));
+    }
+    return a.u;
+  }
+};
+
+// p = p~ * f[row][k / VTILE], rounded to T  (p~ = e^(l - m_tile))
+template <typename T, int N> struct ScaledRowLoader {
+  const T *p[N];
+  const float *f[N];
+  __device__ inline uint4 fetch(int it, int k) const {
+    if (!p[it]) return uint4{0, 0, 0, 0};
+    Chunk<T> a;
+    a.u = *reinterpret_cast<const uint4 *>(p[it] + k);
+    const float fac = f[it][k / VTILE];
+#pragma unroll
+    for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) * fac);
+    return a.u;
+  }
+};
+
+__device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t rows, int64_t M,
+                                   int C) {
+  if (!active) return true;
+  const int64_t m1 = (m0 + rows < M ? m0 + rows : M) - 1;
+  for (int64_t c = m0 / C; c <= m1 / C; ++c)
+    if (active[c]) return true;
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// S0+S1: q,k,v projection with the embedding gather in the A prologue
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
+  using G = Gemm<T, BM, BN, WGM, WGN>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+  if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
+  const T *E = static_cast<const T *>(a.embed);
+  const T *sc = static_cast<const T *>(a.sc_in);
+  const int nq = a.nq, nk = a.nkv, ntot = nq + 2 * nk, d = a.d;
+  GatherLoader<T, G::AI> al;
+#pragma unroll
+  for (int it = 0; it < G::AI; ++it) {
+    const int64_t row = m0 + G::a_row(it);
+    al.e[it] = nullptr;
+    al.s[it] = nullptr;
+    if (row < a.M) {
+      const int id = a.ids[row];
+      if (id >= 0 && id < a.vocab) {
+        al.e[it] = E + (int64_t)id * d;
+        al.s[it] = sc ? sc + row * d : nullptr;
+      } else if (a.flags && G::a_kc(it) == 0) {
+        atomicOr(a.flags, DG_FLAG_BAD_TOKEN);
+      }
+    }
+  }
+  RowLoader<T, G::BI> bl;
+#pragma unroll
+  for (int it = 0; it < G::BI; ++it) {
+    const int n = n0 + G::a_row(it);
+    const T *p = nullptr;
+    if (n < nq) p = static_cast<const T *>(a.wq) + (int64_t)n * d;
+    else if (n < nq + nk) p = static_cast<const T *>(a.wk) + (int64_t)(n - nq) * d;
+    else if (n < ntot) p = static_cast<const T *>(a.wv) + (int64_t)(n - nq - nk) * d;
+    bl.p[it] = p;
+  }
+  f32x4 acc[G::TM][G::TN];
+  G::run(smem, al, bl, 0, d, acc);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  T *q = static_cast<T *>(a.q), *k = static_cast<T *>(a.k), *v = static_cast<T *>(a.v);
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const int col = n0 + wn * G::WN + j * 16 + (lane & 15);
+    if (col >= ntot) continue;
+    T *base;
+    int ld, c;
+    if (col < nq) { base = q; ld = nq; c = col; }
+    else if (col < nq + nk) { base = k; ld = nk; c = col - nq; }
+    else { base = v; ld = nk; c = col - nq - nk; }
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
+        if (row < a.M) base[row * ld + c] = from_f<T>(acc[i][j][r]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S3: h = x + o Wo^T, x recomputed from the embedding (fp32, unrounded)
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
+  using G = Gemm<T, BM, BN, WGM, WGN>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+  if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
+  const int K = a.kdim, d = a.d;
+  RowLoader<T, G::AI> al;
+#pragma unroll
+  for (int it = 0; it < G::AI; ++it) {
+    const int64_t row = m0 + G::a_row(it);
+    al.p[it] = row < a.M ? static_cast<const T *>(a.o) + row * K : nullptr;
+  }
+  RowLoader<T, G::BI> bl;
+#pragma unroll
+  for (int it = 0; it < G::BI; ++it) {
+    const int n = n0 + G::a_row(it);
+    bl.p[it] = n < d ? static_cast<const T *>(a.wo) + (int64_t)n * K : nullptr;
+  }
+  f32x4 acc[G::TM][G::TN];
+  G::run(smem, al, bl, 0, K, acc);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const T *E = static_cast<const T *>(a.embed);
+  const T *sc = static_cast<const T *>(a.sc_in);
+  T *h = static_cast<T *>(a.h);
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
+      if (row >= a.M) continue;
+      const int id = a.ids[row];
+      const bool ok = id >= 0 && id < a.vocab;
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+        const int col = n0 + wn * G::WN + j * 16 + (lane & 15);
+        if (col >= d) continue;
+        float x = ok ? to_f(E[(int64_t)id * d + col]) : 0.f;
+        if (sc) x += to_f(sc[row * d + col]);
+        h[row * d + col] = from_f<T>(acc[i][j][r] + x);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// S4+S5 (tile part): logits of a VTILE-wide vocabulary tile for BN rows, with
+// per-(row, tile) softmax statistics.  Computed as C^T: MFMA rows are
+// vocabulary entries, MFMA columns are canvas rows, so each row's reduction
+// over the vocabulary runs mostly inside a lane.
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
+  using G = Gemm<T, BM, BN, WGM, WGN>;
+  static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  __shared__ float red_m[WGM][BN];
+  __shared__ int red_i[WGM][BN];
+  __shared__ float red_s[WGM][BN];
+  __shared__ float red_t[WGM][BN];
+  const int vt = blockIdx.x;
+  const int v0 = vt * BM;
+  const int64_t n0 = (int64_t)blockIdx.y * BN;
+  const int d = a.d;
+  if (a.active_rows && !tile_active(a.active_rows, n0, BN, a.nrows, a.rows_per_flag)) return;
+  RowLoader<T, G::AI> al;
+#pragma unroll
+  for (int it = 0; it < G::AI; ++it) {
+    const int v = v0 + G::a_row(it);
+    al.p[it] = v < a.vocab ? static_cast<const T *>(a.head) + (int64_t)v * d : nullptr;
+  }
+  RowLoader<T, G::BI> bl;
+#pragma unroll
+  for (int it = 0; it < G::BI; ++it) {
+    const int64_t n = n0 + G::a_row(it);
+    const T *p = nullptr;
+    if (n < a.nrows) {
+      const int64_t src = a.row_index ? (int64_t)a.row_index[n] : n;
+      if (src >= 0) p = static_cast<const T *>(a.h) + src * d;
+    }
+    bl.p[it] = p;
+  }
+  f32x4 acc[G::TM][G::TN];
+  G::run(smem, al, bl, 0, d, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  // scale, then pass 1: max and lowest argmax per column (= canvas row)
+  float mx[G::TN];
+  int ix[G::TN];
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
+    float s = a.logit_scale;
+    if (a.row_scale && n < a.nrows) s *= a.row_scale[n];
+    float m = -INFINITY;
+    int id = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l = acc[i][j][r] * s;
+        acc[i][j][r] = l;
+        const int v = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
+        if (l > m) { m = l; id = v; }
+      }
+    // across the four lane groups: larger value, then lower id
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float m2 = __shfl_xor(m, o);
+      const int i2 = __shfl_xor(id, o);
+      if (m2 > m || (m2 == m && i2 < id)) { m = m2; id = i2; }
+    }
+    mx[j] = m;
+    ix[j] = id;
+  }
+  if ((lane >> 4) == 0) {
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      red_m[wm][wn * G::WN + j * 16 + lane] = mx[j];
+      red_i[wm][wn * G::WN + j * 16 + lane] = ix[j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const int c = wn * G::WN + j * 16 + (lane & 15);
+    float m = red_m[0][c];
+    int id = red_i[0][c];
+#pragma unroll
+    for (int q = 1; q < WGM; ++q) {
+      const float m2 = red_m[q][c];
+      const int i2 = red_i[q][c];
+      if (m2 > m || (m2 == m && i2 < id)) { m = m2; id = i2; }
+    }
+    mx[j] = m;
+    ix[j] = id;
+  }
+  // pass 2: sum e^(l-m) and sum e^(l-m)(l-m); p~ and logits out
+  T *pt = static_cast<T *>(a.ptilde);
+  float ss[G::TN], tt[G::TN];
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
+    const bool live = n < a.nrows;
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int vb = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = acc[i][j][r] - mx[j];
+        const float e = __expf(x);
+        s += e;
+        t += e * x;
+        if (live && pt) pt[n * a.vocab + vb + r] = from_f<T>(e);
+        if (live && a.logits) a.logits[n * a.vocab + vb + r] = acc[i][j][r];
+      }
+    }
+    s += __shfl_xor(s, 16);
+    t += __shfl_xor(t, 16);
+    s += __shfl_xor(s, 32);
+    t += __shfl_xor(t, 32);
+    ss[j] = s;
+    tt[j] = t;
+  }
+  if ((lane >> 4) == 0) {
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      red_s[wm][wn * G::WN + j * 16 + lane] = ss[j];
+      red_t[wm][wn * G::WN + j * 16 + lane] = tt[j];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && (lane >> 4) == 0) {
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      const int c = wn * G::WN + j * 16 + lane;
+      const int64_t n = n0 + c;
+      if (n >= a.nrows) continue;
+      float s = 0.f, t = 0.f;
+#pragma unroll
+      for (int q = 0; q < WGM; ++q) { s += red_s[q][c]; t += red_t[q][c]; }
+      float4 st;
+      st.x = mx[j];
+      st.y = s;
+      st.z = t;
+      st.w = __int_as_float(ix[j]);
+      a.stats[n * a.nvt + vt] = st;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// S6: sc = p E over a range of the vocabulary (A = p~ scaled, B = E^T rows)
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
+  using G = Gemm<T, BM, BN, WGM, WGN>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  const int n0 = blockIdx.x * BN;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int z = blockIdx.z;
+  const int nk = a.vocab / G::BK;
+  const int kbeg = (int)((int64_t)z * nk / a.ksplit) * G::BK;
+  const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * G::BK;
+  ScaledRowLoader<T, G::AI> al;
+#pragma unroll
+  for (int it = 0; it < G::AI; ++it) {
+    const int64_t row = m0 + G::a_row(it);
+    al.p[it] = row < a.M ? static_cast<const T *>(a.ptilde) + row * a.vocab : nullptr;
+    al.f[it] = row < a.M ? a.fscale + row * a.nvt : nullptr;
+  }
+  RowLoader<T, G::BI> bl;
+#pragma unroll
+  for (int it = 0; it < G::BI; ++it) {
+    const int n = n0 + G::a_row(it);
+    bl.p[it] = n < a.d ? static_cast<const T *>(a.embed_t) + (int64_t)n * a.vocab : nullptr;
+  }
+  f32x4 acc[G::TM][G::TN];
+  G::run(smem, al, bl, kbeg, kend, acc);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+        const int col = n0 + wn * G::WN + j * 16 + (lane & 15);
+        if (col >= a.d) continue;
+        if (a.ksplit == 1)
+          static_cast<T *>(a.out)[row * a.d + col] = from_f<T>(acc[i][j][r]);
+        else
+          a.part[((int64_t)z * a.M + row) * a.d + col] = acc[i][j][r];
+      }
+    }
+}
+
+// fixed-order sum of the split-K partials
+template <typename T>
+__global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, void *out, int64_t n,
+                                                        int ksplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < ksplit; ++z) s += part[(int64_t)z * n + i];
+  static_cast<T *>(out)[i] = from_f<T>(s);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN>
+static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
+  dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.nq + 2 * a.nkv, BN));
+  hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
+  const int64_t ntot = a.nq + 2 * a.nkv;
+  if (bf) {
+    if (cdiv64(a.M, 128) * cdiv64(ntot, 128) >= 512) return launch_qkv_t<bf16, 128, 128, 2, 2>(a, st);
+    return launch_qkv_t<bf16, 64, 64, 2, 2>(a, st);
+  }
+  return launch_qkv_t<float, 64, 64, 2, 2>(a, st);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN>
+static hipError_t launch_oproj_t(const OprojArgs &a, hipStream_t st) {
+  dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.d, BN));
+  hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
+  if (bf) {
+    if (cdiv64(a.M, 128) * cdiv64(a.d, 128) >= 512) return launch_oproj_t<bf16, 128, 128, 2, 2>(a, st);
+    return launch_oproj_t<bf16, 64, 64, 2, 2>(a, st);
+  }
+  return launch_oproj_t<float, 64, 64, 2, 2>(a, st);
+}
+
+hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
+  if (bf) {
+    dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 256));
+    hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4>), grid, dim3(8 * WAVE), 0, st, a);
+  } else {
+    dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 64));
+    hipLaunchKernelGGL((lmhead_kernel<float, VTILE, 64, 4, 1>), grid, dim3(4 * WAVE), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
+  const int64_t tiles = bf ? cdiv64(M, 256) * cdiv64(d, 256) : cdiv64(M, 64) * cdiv64(d, 64);
+  const int nk = vocab / (bf ? BKOf<bf16>::v : BKOf<float>::v);
+  int64_t ks = 256 / tiles;  // about one workgroup per compute unit, no partial second wave
+  if (ks > nk) ks = nk;
+  if (ks > 64) ks = 64;
+  if (ks < 1) ks = 1;
+  return (int)ks;
+}
+
+hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
+  if (bf) {
+    dim3 grid((unsigned)cdiv64(a.d, 256), (unsigned)cdiv64(a.M, 256), (unsigned)a.ksplit);
+    hipLaunchKernelGGL((scgemm_kernel<bf16, 256, 256, 4, 2>), grid, dim3(8 * WAVE), 0, st, a);
+  } else {
+    dim3 grid((unsigned)cdiv64(a.d, 64), (unsigned)cdiv64(a.M, 64), (unsigned)a.ksplit);
+    hipLaunchKernelGGL((scgemm_kernel<float, 64, 64, 2, 2>), grid, dim3(4 * WAVE), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const int64_t n = a.M * a.d;
+  if (bf)
+    hipLaunchKernelGGL((sc_reduce_kernel<bf16>), dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st,
+                       a.part, a.out, n, a.ksplit);
+  else
+    hipLaunchKernelGGL((sc_reduce_kernel<float>), dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st,
+                       a.part, a.out, n, a.ksplit);
+  return hipGetLastError();
+}
+
+}  // namespace dg

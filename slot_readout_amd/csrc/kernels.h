@@ -1,0 +1,144 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg.h"
+
+namespace dg {
+
+// Vocabulary tile of the LM-head statistics (and of the p~ rescale factors).
+constexpr int VTILE = 256;
+
+struct QkvArgs {
+  const int32_t *ids;      // [M] token ids
+  const void *embed;       // [V, d]
+  const void *sc_in;       // [M, d] or null
+  const void *wq, *wk, *wv;
+  void *q, *k, *v;         // [M, nq], [M, nkv], [M, nkv]
+  const int32_t *active;   // per-canvas flag or null (rows of inactive canvases skipped)
+  int32_t *flags;          // device flag word or null
+  int64_t M;
+  int d, nq, nkv, vocab, C;
+};
+
+struct OprojArgs {
+  const void *o;           // [M, kdim]
+  const void *wo;          // [d, kdim]
+  const int32_t *ids;
+  const void *embed, *sc_in;
+  void *h;                 // [M, d]
+  const int32_t *active;
+  int64_t M;
+  int d, kdim, vocab, C;
+};
+
+struct LmheadArgs {
+  const void *head;        // [V, d]
+  const void *h;           // [*, d]
+  const int32_t *row_index;  // [nrows] rows of h to use (-1 = none) or null (identity)
+  const int32_t *active_rows;  // per-group flag (groups of rows_per_flag rows) or null
+  int rows_per_flag;
+  float logit_scale;
+  const float *row_scale;  // [nrows] or null
+  float4 *stats;           // [nrows, nvt] (m, sum e, sum e*(l-m), argmax bits)
+  void *ptilde;            // [nrows, V] T or null
+  float *logits;           // [nrows, V] or null
+  int64_t nrows;
+  int d, vocab, nvt;
+};
+
+struct ScArgs {
+  const void *ptilde;      // [M, V]
+  const float *fscale;     // [M, nvt]
+  const void *embed_t;     // [d, V]
+  float *part;             // [ksplit, M, d]
+  void *out;               // [M, d] T
+  int64_t M;
+  int d, vocab, nvt, ksplit;
+};
+
+struct VocabMergeArgs {
+  const float4 *stats;     // [nrows, nvt]
+  int64_t nrows;
+  int nvt;
+  float *conf, *entropy;   // [nrows] or null
+  int32_t *argmax;         // [nrows] or null
+  float2 *rowstat;         // [nrows] (m, lse) or null
+  float *fscale;           // [nrows, nvt] e^(m_t - m)/Z or null
+};
+
+struct AttnArgs {
+  const void *q, *k, *v;       // canvas [nc, C, Hq, hd], [nc, C, Hkv, hd]
+  const void *kp, *vp;         // prompt [total, Hkv, hd]
+  const int32_t *cu;           // [nprompt + 1]
+  const int32_t *active;       // per-canvas flag or null
+  int32_t *flags;
+  void *o;                     // [nc, C, Hq, hd]
+  float *part_o;               // [nsplit, nc*Hq*C, hd]
+  float2 *part_ml;             // [nsplit, nc*Hq*C]
+  int64_t total_len;
+  int nc, C, Hq, Hkv, W, max_len, nsplit, chunk, canvas_per_prompt;
+  float scale_log2;            // log2(e) / sqrt(hd)
+};
+
+struct CommitArgs {
+  const int32_t *ids;
+  const float *conf, *entropy;
+  const int32_t *argmax;
+  uint8_t *mask;
+  int32_t *out_ids;
+  int32_t *n_committed;
+  int B, C, mask_id;
+  float tau;
+};
+
+hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st);
+hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st);
+hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st);
+hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st);
+int sc_ksplit(int64_t M, int d, int vocab, bool bf);
+hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st);
+
+// attention: query rows per workgroup, split-KV planning, launch (+ merge)
+int attn_query_tile(int head_dim);
+void attn_plan(int nc, int C, int Hq, int Hkv, int head_dim, int max_len, int *nsplit, int *chunk);
+hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
+
+hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
+hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,
+                            hipStream_t st);
+hipError_t launch_clear_i32(int32_t *p, int64_t n, hipStream_t st);
+
+// slot read pieces
+struct SlotArgs {
+  const int32_t *slot_pos;     // [B, S]
+  const int32_t *label_ids;    // [B, S, 26]
+  const int32_t *n_labels;     // [B, S]
+  const int32_t *noise_ids;    // [n_draws, B, S]
+  const void *head;            // [V, d] LM head rows (for label logits)
+  const void *h;               // hidden rows [rows, d] of the pass
+  const float2 *rowstat;       // [B*(S or nd*S)] (m, lse) per gathered slot row
+  const float *row_scale;      // [B, S] or null
+  float logit_scale;
+  float threshold;
+  int B, S, C, V, d, n_draws;
+  int32_t *rows;               // [B*nd*S] gathered row index (out of the build kernels)
+  int32_t *status;             // [B, S]
+  float *logprobs, *probs, *entropy, *first_entropy;
+  int32_t *best, *draws_used;
+  int32_t *canvas_flag;        // [B + B*S]: canvas has a slot to re-read, then per-slot flags
+  int32_t *draw_active;        // [B*nd]
+  const int32_t *canvas_ids;   // [B, C]
+  int32_t *draw_ids;           // [B*nd, C]
+  int mask_id;
+};
+
+hipError_t launch_slot_rows(const SlotArgs &a, bool bf, hipStream_t st);
+hipError_t launch_slot_first(const SlotArgs &a, bool bf, hipStream_t st);
+hipError_t launch_slot_build_draws(const SlotArgs &a, hipStream_t st);
+hipError_t launch_slot_draw_rows2(const SlotArgs &a, int32_t *row_active, float *rs_draw,
+                                  hipStream_t st);
+hipError_t launch_slot_average(const SlotArgs &a, bool bf, hipStream_t st);
+
+}  // namespace dg

@@ -1,0 +1,254 @@
+// Structured slot read: label logprobs at decision slots, renormalisation over
+// the allowed labels, entropy, and the averaged noise-draw re-read.
+//
+// The first pass runs the denoise step over the whole canvas; the LM head and
+// its softmax statistics run only on the slot rows (gathered by row index).
+// A slot whose renormalised entropy exceeds the threshold flags its canvas;
+// flagged canvases get n_draws copies with a noise token written at every slot
+// and a second batched pass, decided on the device (no host synchronisation).
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+__device__ inline int validate_slot(const SlotArgs &a, int64_t bs) {
+  const int pos = a.slot_pos[bs];
+  const int k = a.n_labels[bs];
+  if (pos < 0 || pos >= a.C) return DG_SLOT_BAD_POS;
+  if (k < 1 || k > DG_MAX_LABELS) return DG_SLOT_BAD_COUNT;
+  for (int j = 0; j < k; ++j) {
+    const int lab = a.label_ids[bs * DG_MAX_LABELS + j];
+    if (lab < 0 || lab >= a.V) return DG_SLOT_BAD_LABEL;
+  }
+  return DG_SLOT_OK;
+}
+
+// rows of the first pass: slot (b, s) reads hidden row b*C + pos
+__global__ __launch_bounds__(256) void slot_rows_kernel(SlotArgs a) {
+  const int64_t bs = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (bs >= (int64_t)a.B * a.S) return;
+  const int st = validate_slot(a, bs);
+  a.status[bs] = st;
+  const int64_t b = bs / a.S;
+  a.rows[bs] = st == DG_SLOT_OK ? (int32_t)(b * a.C + a.slot_pos[bs]) : -1;
+}
+
+// label logits of one hidden row, lp_j = min(s * h.head[label_j] - lse, 0), in lane j
+template <typename T>
+__device__ inline float label_logprob(const SlotArgs &a, const T *hrow, const int32_t *labs, int k,
+                                      float scale, float lse, int lane) {
+  const T *head = static_cast<const T *>(a.head);
+  float mine = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    const T *er = head + (int64_t)labs[j] * a.d;
+    float acc = 0.f;
+    for (int e = lane; e < a.d; e += 64) acc += to_f(hrow[e]) * to_f(er[e]);
+    acc = wave_sum(acc);
+    if (lane == j) mine = fminf(acc * scale - lse, 0.f);
+  }
+  return mine;
+}
+
+struct LabelDist {
+  float r;      // renormalised probability in lane j (0 beyond k)
+  float H;      // entropy of r (every lane)
+  int best;     // lowest index of max r (every lane)
+};
+
+__device__ inline LabelDist renormalise(float lp, int k, int lane) {
+  const bool on = lane < k;
+  const float mx = wave_max(on ? lp : -INFINITY);
+  const float e = on ? __expf(lp - mx) : 0.f;
+  const float sum = wave_sum(e);
+  LabelDist d;
+  d.r = e / sum;
+  return d;
+}
+
+__device__ inline void finish_dist(LabelDist &d, int k, int lane) {
+  const bool on = lane < k;
+  const float term = (on && d.r > 0.f) ? -d.r * __logf(d.r) : 0.f;
+  d.H = fmaxf(wave_sum(term), 0.f);
+  float bv = on ? d.r : -1.f;
+  int bi = on ? lane : 0x7fffffff;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o);
+    const int i2 = __shfl_xor(bi, o);
+    if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+  }
+  d.best = bi;
+}
+
+// first read: one wave per slot; also decides which canvases need draws
+template <typename T>
+__global__ __launch_bounds__(256) void slot_first_kernel(SlotArgs a) {
+  __shared__ int any_flag;
+  const int b = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) any_flag = 0;
+  __syncthreads();
+  const T *h = static_cast<const T *>(a.h);
+  for (int s = w; s < a.S; s += 4) {
+    const int64_t bs = (int64_t)b * a.S + s;
+    float *lp_out = a.logprobs + bs * DG_MAX_LABELS;
+    float *pr_out = a.probs + bs * DG_MAX_LABELS;
+    if (a.status[bs] != DG_SLOT_OK) {
+      if (lane < DG_MAX_LABELS) { lp_out[lane] = 0.f; pr_out[lane] = 0.f; }
+      if (lane == 0) {
+        a.entropy[bs] = 0.f;
+        a.first_entropy[bs] = 0.f;
+        a.best[bs] = -1;
+        a.draws_used[bs] = 0;
+        a.canvas_flag[a.B + bs] = 0;   // per-slot flag lives after the per-canvas flags
+      }
+      continue;
+    }
+    const int k = a.n_labels[bs];
+    const int pos = a.slot_pos[bs];
+    float scale = a.logit_scale;
+    if (a.row_scale) scale *= a.row_scale[bs];
+    const float lse = a.rowstat[bs].y;
+    const float lp = label_logprob<T>(a, h + ((int64_t)b * a.C + pos) * a.d,
+                                      a.label_ids + bs * DG_MAX_LABELS, k, scale, lse, lane);
+    LabelDist dd = renormalise(lp, k, lane);
+    finish_dist(dd, k, lane);
+    if (lane < DG_MAX_LABELS) {
+      lp_out[lane] = lane < k ? lp : 0.f;
+      pr_out[lane] = lane < k ? dd.r : 0.f;
+    }
+    const bool flag = a.n_draws > 1 && dd.H > a.threshold;
+    if (lane == 0) {
+      a.entropy[bs] = dd.H;
+      a.first_entropy[bs] = dd.H;
+      a.best[bs] = dd.best;
+      a.draws_used[bs] = 1;
+      a.canvas_flag[a.B + bs] = flag ? 1 : 0;
+      if (flag) any_flag = 1;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.canvas_flag[b] = any_flag;
+}
+
+// draw canvases: copy of canvas b with noise_ids[d, b, s] at every slot position
+__global__ __launch_bounds__(256) void slot_build_draws_kernel(SlotArgs a) {
+  const int bd = blockIdx.x;
+  const int b = bd / a.n_draws, d = bd % a.n_draws;
+  const int act = a.canvas_flag[b];
+  if (threadIdx.x == 0) a.draw_active[bd] = act;
+  if (!act) return;
+  int32_t *dst = a.draw_ids + (int64_t)bd * a.C;
+  const int32_t *src = a.canvas_ids + (int64_t)b * a.C;
+  for (int i = threadIdx.x; i < a.C; i += 256) dst[i] = src[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int s = 0; s < a.S; ++s) {
+      const int64_t bs = (int64_t)b * a.S + s;
+      const int pos = a.slot_pos[bs];
+      if (pos < 0 || pos >= a.C) continue;
+      int nid = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
+      if (nid < 0 || nid >= a.V) {
+        nid = a.mask_id;
+        if (a.status[bs] == DG_SLOT_OK) a.status[bs] = DG_SLOT_BAD_NOISE;
+      }
+      dst[pos] = nid;
+    }
+  }
+}
+
+// rows of the draw pass: (b, d, s) reads row (b*nd + d)*C + pos when slot (b, s) is flagged
+__global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t *row_active,
+                                                             float *rs_draw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)a.B * a.n_draws * a.S;
+  if (i >= n) return;
+  const int s = (int)(i % a.S);
+  const int64_t bd = i / a.S;
+  const int64_t b = bd / a.n_draws;
+  const int64_t bs = b * a.S + s;
+  const bool on = a.canvas_flag[a.B + bs] != 0;
+  a.rows[i] = on ? (int32_t)(bd * a.C + a.slot_pos[bs]) : -1;
+  row_active[i] = on ? 1 : 0;
+  rs_draw[i] = a.row_scale ? a.row_scale[bs] : 1.f;
+}
+
+// average of the draws in probability space: r = mean r_d, lp = ln mean e^(lp_d)
+template <typename T>
+__global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
+  const int64_t bs = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (bs >= (int64_t)a.B * a.S) return;
+  if (!a.canvas_flag[a.B + bs]) return;
+  const int64_t b = bs / a.S;
+  const int s = (int)(bs % a.S);
+  const int k = a.n_labels[bs];
+  const int pos = a.slot_pos[bs];
+  float scale = a.logit_scale;
+  if (a.row_scale) scale *= a.row_scale[bs];
+  const T *h = static_cast<const T *>(a.h);
+  float racc = 0.f, eacc = 0.f;
+  for (int d = 0; d < a.n_draws; ++d) {
+    const int64_t bd = b * a.n_draws + d;
+    const float lse = a.rowstat[bd * a.S + s].y;
+    const float lp = label_logprob<T>(a, h + (bd * a.C + pos) * a.d,
+                                      a.label_ids + bs * DG_MAX_LABELS, k, scale, lse, lane);
+    const LabelDist dd = renormalise(lp, k, lane);
+    racc += dd.r;
+    eacc += lane < k ? __expf(lp) : 0.f;
+  }
+  LabelDist fin;
+  fin.r = racc / (float)a.n_draws;
+  finish_dist(fin, k, lane);
+  if (lane < DG_MAX_LABELS) {
+    a.logprobs[bs * DG_MAX_LABELS + lane] = lane < k ? __logf(eacc / (float)a.n_draws) : 0.f;
+    a.probs[bs * DG_MAX_LABELS + lane] = lane < k ? fin.r : 0.f;
+  }
+  if (lane == 0) {
+    a.entropy[bs] = fin.H;
+    a.best[bs] = fin.best;
+    a.draws_used[bs] = a.n_draws;
+  }
+}
+
+hipError_t launch_slot_rows(const SlotArgs &a, bool, hipStream_t st) {
+  const int64_t n = (int64_t)a.B * a.S;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_rows_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_first(const SlotArgs &a, bool bf, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  if (bf)
+    hipLaunchKernelGGL((slot_first_kernel<bf16>), dim3((unsigned)a.B), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((slot_first_kernel<float>), dim3((unsigned)a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_build_draws(const SlotArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(slot_build_draws_kernel, dim3((unsigned)(a.B * a.n_draws)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_draw_rows2(const SlotArgs &a, int32_t *row_active, float *rs_draw,
+                                  hipStream_t st) {
+  const int64_t n = (int64_t)a.B * a.n_draws * a.S;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_draw_rows_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, a,
+                     row_active, rs_draw);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_average(const SlotArgs &a, bool bf, hipStream_t st) {
+  const int64_t n = (int64_t)a.B * a.S;
+  if (n == 0) return hipSuccess;
+  if (bf)
+    hipLaunchKernelGGL((slot_average_kernel<bf16>), dim3((unsigned)cdiv64(n, 4)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((slot_average_kernel<float>), dim3((unsigned)cdiv64(n, 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dg

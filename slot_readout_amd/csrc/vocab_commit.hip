@@ -1,0 +1,172 @@
+// Vocabulary-statistics merge, entropy-bounded commit and small helpers.
+#include "common.h"
+#include "kernels.h"
+
+namespace dg {
+
+// ---------------------------------------------------------------------------
+// Merge the per-(row, vocabulary tile) statistics written by the LM-head
+// kernel into the row's softmax summary.  For tile t with (m_t, s_t, t_t):
+//   m = max m_t,  Z = sum s_t e^(m_t-m),  T = sum e^(m_t-m) (t_t + (m_t-m) s_t)
+//   conf = 1/Z,  H = ln Z - T/Z,  lse = m + ln Z,  argmax = lowest id with l = m.
+// One wave per row; tiles are assigned to lanes in a fixed pattern and combined
+// with a fixed butterfly, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void vocab_merge_kernel(VocabMergeArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.nrows) return;
+  const float4 *st = a.stats + row * a.nvt;
+  float m = -INFINITY;
+  int id = 0x7fffffff;
+  for (int t = lane; t < a.nvt; t += 64) {
+    const float4 v = st[t];
+    const int i = __float_as_int(v.w);
+    if (v.x > m || (v.x == m && i < id)) { m = v.x; id = i; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int i2 = __shfl_xor(id, o);
+    if (m2 > m || (m2 == m && i2 < id)) { m = m2; id = i2; }
+  }
+  float Z = 0.f, T = 0.f;
+  for (int t = lane; t < a.nvt; t += 64) {
+    const float4 v = st[t];
+    const float dm = v.x - m;
+    const float w = __expf(dm);
+    Z += v.y * w;
+    T += w * (v.z + dm * v.y);
+  }
+  Z = wave_sum(Z);
+  T = wave_sum(T);
+  const float lnZ = __logf(Z);
+  if (lane == 0) {
+    float H = lnZ - T / Z;
+    if (H < 0.f) H = 0.f;
+    if (a.conf) a.conf[row] = 1.f / Z;
+    if (a.entropy) a.entropy[row] = H;
+    if (a.argmax) a.argmax[row] = id;
+    if (a.rowstat) a.rowstat[row] = make_float2(m, m + lnZ);
+  }
+  if (a.fscale) {
+    const float invZ = 1.f / Z;
+    for (int t = lane; t < a.nvt; t += 64) a.fscale[row * a.nvt + t] = __expf(st[t].x - m) * invZ;
+  }
+}
+
+hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st) {
+  if (a.nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vocab_merge_kernel, dim3((unsigned)cdiv64(a.nrows, 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Entropy-bounded commit: one workgroup per canvas, one thread per position.
+// rank = number of candidates ahead in (conf desc, position asc) order; the
+// entropies are scattered to their ranks, an exclusive prefix is formed by a
+// fixed Hillis-Steele scan in LDS, and rank k is accepted iff prefix_k <= tau.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
+  __shared__ float sconf[DG_MAX_CANVAS];
+  __shared__ int scand[DG_MAX_CANVAS];
+  __shared__ float scan[2][DG_MAX_CANVAS];
+  const int b = blockIdx.x, i = threadIdx.x, C = a.C, n = blockDim.x;
+  const int64_t base = (int64_t)b * C;
+  const bool live = i < C;
+  int id = 0;
+  float c = 0.f, H = 0.f;
+  bool cand = false;
+  if (live) {
+    id = a.ids[base + i];
+    cand = id == a.mask_id;
+    c = a.conf[base + i];
+    H = a.entropy[base + i];
+  }
+  sconf[i] = c;
+  scand[i] = cand ? 1 : 0;
+  scan[0][i] = 0.f;
+  __syncthreads();
+  int rank = 0;
+  if (cand) {
+    for (int j = 0; j < C; ++j) {
+      if (!scand[j]) continue;
+      const float cj = sconf[j];
+      rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
+    }
+    scan[0][rank] = H;
+  }
+  __syncthreads();
+  int src = 0;
+  for (int off = 1; off < n; off <<= 1) {
+    float x = scan[src][i];
+    if (i >= off) x += scan[src][i - off];
+    scan[src ^ 1][i] = x;
+    __syncthreads();
+    src ^= 1;
+  }
+  // scan[src] now holds the inclusive prefix in rank order
+  bool accept = false;
+  if (cand) {
+    const float excl = rank == 0 ? 0.f : scan[src][rank - 1];
+    accept = excl <= a.tau;
+  }
+  const int total = __syncthreads_count(accept);
+  if (live) {
+    a.mask[base + i] = accept ? 1 : 0;
+    a.out_ids[base + i] = accept ? a.argmax[base + i] : id;
+  }
+  if (i == 0 && a.n_committed) a.n_committed[b] = total;
+}
+
+hipError_t launch_commit(const CommitArgs &a, hipStream_t st) {
+  int n = 64;
+  while (n < a.C) n <<= 1;
+  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)a.B), dim3((unsigned)n), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c]  (64 x 64 tiles through LDS)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T *src, T *dst, int rows, int cols) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int r = r0 + y, c = c0 + tx;
+    if (r < rows && c < cols) tile[y][tx] = src[(int64_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int c = c0 + y, r = r0 + tx;
+    if (r < rows && c < cols) dst[(int64_t)c * rows + r] = tile[tx][y];
+  }
+}
+
+hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,
+                            hipStream_t st) {
+  dim3 grid((unsigned)cdiv64(cols, 64), (unsigned)cdiv64(rows, 64));
+  if (bf)
+    hipLaunchKernelGGL((transpose_kernel<bf16>), grid, dim3(256), 0, st,
+                       static_cast<const bf16 *>(src), static_cast<bf16 *>(dst), rows, cols);
+  else
+    hipLaunchKernelGGL((transpose_kernel<float>), grid, dim3(256), 0, st,
+                       static_cast<const float *>(src), static_cast<float *>(dst), rows, cols);
+  return hipGetLastError();
+}
+
+// zero-fill with a kernel (kept out of memset nodes so callers can capture it)
+__global__ __launch_bounds__(256) void clear_i32_kernel(int32_t *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_clear_i32(int32_t *p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,151 @@
+"""Device-side plumbing around the C-ABI: move host arrays into HBM as torch
+tensors, allocate outputs and workspaces, and call the library.  No step of
+the computation happens here.
+"""
+import numpy as np
+import torch
+
+from . import dg
+
+
+def _dtype(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def to_device(a, dtype=None, device="cuda"):
+    """numpy -> torch device tensor (float arrays converted to `dtype`)."""
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+class DeviceProblem:
+    """A workload's weights, prompt KV and canvases resident in device memory."""
+
+    def __init__(self, inp, device="cuda", with_embed_t=True):
+        dm = inp["dims"]
+        self.inp = inp
+        self.device = device
+        self.dims = dg.make_dims(dm.d_model, dm.n_q_heads, dm.n_kv_heads, dm.head_dim, dm.vocab,
+                                 dm.canvas, dm.window, dm.mask_id, dm.dtype)
+        self.tdt = _dtype(dm.dtype)
+        self.B = inp["batch"]
+        self.C = dm.canvas
+        self.d = dm.d_model
+        self.V = dm.vocab
+        T = self.tdt
+        self.embed = to_device(inp["embed"], T, device)
+        self.wq = to_device(inp["wq"], T, device)
+        self.wk = to_device(inp["wk"], T, device)
+        self.wv = to_device(inp["wv"], T, device)
+        self.wo = to_device(inp["wo"], T, device)
+        self.lm_head = to_device(inp["lm_head"], T, device) if inp.get("lm_head") is not None else None
+        self.embed_t = None
+        if with_embed_t:
+            self.embed_t = torch.empty((self.d, self.V), dtype=T, device=device)
+            dg.dg_prepare_embed_t(self.dims, self.embed, self.embed_t)
+        total = int(inp["cu_seqlens"][-1])
+        kshape = (max(total, 1),) + inp["prompt_k"].shape[1:]
+        self.prompt_k = torch.zeros(kshape, dtype=T, device=device)
+        self.prompt_v = torch.zeros(kshape, dtype=T, device=device)
+        if total:
+            self.prompt_k[:total] = to_device(inp["prompt_k"], T, device)
+            self.prompt_v[:total] = to_device(inp["prompt_v"], T, device)
+        self.cu = to_device(inp["cu_seqlens"].astype(np.int32), None, device)
+        self.max_prompt = int(inp["max_prompt"])
+        self.total_len = total
+        self.canvas_ids = to_device(inp["canvas_ids"].astype(np.int32), None, device)
+        self.slot_pos = to_device(inp["slot_pos"].astype(np.int32), None, device)
+        self.label_ids = to_device(inp["label_ids"].astype(np.int32), None, device)
+        self.n_labels = to_device(inp["n_labels"].astype(np.int32), None, device)
+        self.noise_ids = to_device(inp["noise_ids"].astype(np.int32), None, device)
+        self.S = int(inp["slot_pos"].shape[1])
+        self.weights = dg.make_weights(self.embed, self.wq, self.wk, self.wv, self.wo,
+                                       embed_t=self.embed_t, lm_head=self.lm_head)
+        self.kv = dg.make_prompt_kv(self.prompt_k, self.prompt_v, self.cu, self.max_prompt,
+                                    total)
+        self._ws = {}
+
+    # ---------------------------------------------------------------- step --
+    def workspace(self, key, nbytes):
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
+
+    def step_outputs(self, want_sc=True, debug=False):
+        B, C, d, V = self.B, self.C, self.d, self.V
+        dm = self.inp["dims"]
+        out = {
+            "conf": torch.empty((B, C), dtype=torch.float32, device=self.device),
+            "entropy": torch.empty((B, C), dtype=torch.float32, device=self.device),
+            "argmax": torch.empty((B, C), dtype=torch.int32, device=self.device),
+            "sc_out": torch.empty((B, C, d), dtype=self.tdt, device=self.device) if want_sc else None,
+            "flags": torch.zeros(1, dtype=torch.int32, device=self.device),
+        }
+        if debug:
+            out["attn_out"] = torch.empty((B, C, dm.n_q_heads * dm.head_dim), dtype=self.tdt,
+                                          device=self.device)
+            out["hidden_out"] = torch.empty((B, C, d), dtype=self.tdt, device=self.device)
+            out["logits"] = torch.empty((B, C, V), dtype=torch.float32, device=self.device)
+        return out
+
+    def step(self, sc_in=None, row_scale=None, want_sc=True, debug=False, out=None,
+             canvas_ids=None, stream=None):
+        """One dg_denoise_step over every canvas; returns the output tensors."""
+        if out is None:
+            out = self.step_outputs(want_sc, debug)
+        ws = self.workspace("step", dg.dg_denoise_step_workspace(self.dims, self.B, self.max_prompt))
+        dbg = None
+        if debug:
+            dbg = dg.make_debug(out["attn_out"], out["hidden_out"], out["logits"])
+        dg.dg_denoise_step(self.dims, self.weights, self.kv, self.B,
+                           self.canvas_ids if canvas_ids is None else canvas_ids, sc_in,
+                           self.inp["logit_scale"], row_scale, out["conf"], out["entropy"],
+                           out["argmax"], out["sc_out"], dbg, out["flags"], ws, stream)
+        return out
+
+    # -------------------------------------------------------------- commit --
+    def commit_outputs(self):
+        B, C = self.B, self.C
+        return {"mask": torch.empty((B, C), dtype=torch.uint8, device=self.device),
+                "out_ids": torch.empty((B, C), dtype=torch.int32, device=self.device),
+                "n": torch.empty((B,), dtype=torch.int32, device=self.device)}
+
+    def commit(self, conf, entropy, argmax, tau=None, canvas_ids=None, out=None, stream=None):
+        if out is None:
+            out = self.commit_outputs()
+        ids = self.canvas_ids if canvas_ids is None else canvas_ids
+        dg.dg_commit(self.B, self.C, self.inp["dims"].mask_id, ids, conf, entropy, argmax,
+                     self.inp["tau"] if tau is None else tau, out["mask"], out["out_ids"], out["n"],
+                     stream)
+        return out
+
+    # ----------------------------------------------------------- slot read --
+    def slot_outputs(self):
+        B, S = self.B, self.S
+        f = lambda *s: torch.empty(s, dtype=torch.float32, device=self.device)  # noqa: E731
+        i = lambda *s: torch.empty(s, dtype=torch.int32, device=self.device)    # noqa: E731
+        return {"logprobs": f(B, S, dg.DG_MAX_LABELS), "probs": f(B, S, dg.DG_MAX_LABELS),
+                "entropy": f(B, S), "first_entropy": f(B, S), "best": i(B, S),
+                "draws_used": i(B, S), "status": i(B, S)}
+
+    def slot_read(self, row_scale=None, n_draws=None, threshold=None, out=None, stream=None,
+                  label_ids=None, n_labels=None, slot_pos=None, noise_ids=None):
+        nd = self.inp["n_draws"] if n_draws is None else n_draws
+        th = self.inp["entropy_threshold"] if threshold is None else threshold
+        if out is None:
+            out = self.slot_outputs()
+        ws = self.workspace("slot", dg.dg_slot_read_workspace(self.dims, self.B, self.S,
+                                                               self.max_prompt, nd))
+        dg.dg_slot_read(self.dims, self.weights, self.kv, self.B, self.canvas_ids, self.S,
+                        self.slot_pos if slot_pos is None else slot_pos,
+                        self.label_ids if label_ids is None else label_ids,
+                        self.n_labels if n_labels is None else n_labels,
+                        self.noise_ids if noise_ids is None else noise_ids,
+                        self.inp["logit_scale"], row_scale, th, nd, out["logprobs"], out["probs"],
+                        out["entropy"], out["first_entropy"], out["best"], out["draws_used"],
+                        out["status"], ws, stream)
+        return out

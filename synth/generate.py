@@ -147,12 +147,14 @@ def make_inputs(cfg: Config, with_sc_in: bool = False, batch: int = None,
     return out
 
 
-def companion_row_scale(inp: dict, shape, lo: float = 8.0, hi: float = 128.0) -> np.ndarray:
-    """Per-row logit multipliers ~ logUniform(lo, hi), float32.
+def companion_row_scale(inp: dict, shape, lo: float = 16.0, hi: float = 512.0) -> np.ndarray:
+    """Per-row logit multipliers such that logit_scale * multiplier ~ logUniform(lo, hi).
 
     With the literal weight scales nearly every vocabulary row is flat, so
     argmax and commit order would be decided by rounding noise; these
     multipliers give a mix of peaked and flat rows so those checks have teeth.
     """
     rng = inp["_row_scale_rng"]
-    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float32)
+    total = np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape))
+    # the multipliers scale on top of the workload's own logit scale
+    return (total / inp["logit_scale"]).astype(np.float32)

@@ -1,0 +1,130 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every symbol
+include/dg.h declares, and its host-side validation rejects bad arguments
+before anything is launched (no compute calls here)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def _lib_or_skip():
+    from slot_readout_amd import dg
+    if not os.path.exists(dg.LIB_PATH):
+        pytest.skip("libdg.so not built (run __graft_entry__.build())")
+    return dg
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_functions()
+    for n in ("dg_denoise_step", "dg_commit", "dg_slot_read"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    dg = _lib_or_skip()
+    L = dg.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert set(_declared_functions()) == set(dg.exported_symbols())
+    assert "gfx950" in dg.dg_version()
+
+
+def _dims(dg, **kw):
+    base = dict(d_model=256, n_q_heads=4, n_kv_heads=4, head_dim=64, vocab=2048, canvas=256,
+                window=16, mask_id=2047, dtype="bf16")
+    base.update(kw)
+    return dg.make_dims(**base)
+
+
+def _weights(dg):
+    return dg.make_weights(256, 256, 256, 256, 256)   # non-null, aligned fake addresses
+
+
+def _kv(dg, max_len=128, total=128):
+    return dg.make_prompt_kv(512, 512, 1024, max_len, total)
+
+
+def test_validation_accepts_the_workload_dims():
+    dg = _lib_or_skip()
+    assert dg.dg_denoise_step_validate(_dims(dg), 1, 128, _weights(dg), _kv(dg)) == dg.DG_OK
+    big = _dims(dg, d_model=2816, n_q_heads=8, n_kv_heads=2, head_dim=512, vocab=262144,
+                window=128, mask_id=262143)
+    assert dg.dg_denoise_step_validate(big, 1, 2048, _weights(dg), _kv(dg, 2048, 2048)) == dg.DG_OK
+    assert dg.dg_denoise_step_workspace(big, 1, 2048) > 256 * 262144 * 2  # holds p~
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=128), "DG_ERR_UNSUPPORTED"),
+    (dict(head_dim=512, dtype="f32"), "DG_ERR_UNSUPPORTED"),
+    (dict(dtype=7), "DG_ERR_UNSUPPORTED"),
+    (dict(d_model=250), "DG_ERR_INVALID_ARG"),
+    (dict(n_q_heads=6, n_kv_heads=4), "DG_ERR_INVALID_ARG"),
+    (dict(vocab=2000), "DG_ERR_INVALID_ARG"),
+    (dict(canvas=0), "DG_ERR_INVALID_ARG"),
+    (dict(canvas=1025), "DG_ERR_INVALID_ARG"),
+    (dict(window=-1), "DG_ERR_INVALID_ARG"),
+    (dict(mask_id=2048), "DG_ERR_INVALID_ARG"),
+])
+def test_validation_rejects_bad_dims(kw, code):
+    dg = _lib_or_skip()
+    s = dg.dg_denoise_step_validate(_dims(dg, **kw), 1, 128, _weights(dg), _kv(dg))
+    assert s == getattr(dg, code), (kw, s, dg.dg_last_error())
+    assert dg.dg_last_error()
+
+
+def test_validation_rejects_bad_pointers_and_sizes():
+    dg = _lib_or_skip()
+    d = _dims(dg)
+    assert dg.dg_denoise_step_validate(None, 1, 128, _weights(dg), _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_denoise_step_validate(d, -1, 128, _weights(dg), _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_denoise_step_validate(d, 1, 128, None, _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    w = dg.make_weights(256, 0, 256, 256, 256)
+    assert dg.dg_denoise_step_validate(d, 1, 128, w, _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    w = dg.make_weights(258, 256, 256, 256, 256)        # misaligned embedding
+    assert dg.dg_denoise_step_validate(d, 1, 128, w, _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    kv = dg.make_prompt_kv(512, 512, 0, 128, 128)         # no cu_seqlens
+    assert dg.dg_denoise_step_validate(d, 1, 128, _weights(dg), kv) == dg.DG_ERR_INVALID_ARG
+    kv = dg.make_prompt_kv(0, 0, 1024, 128, 128)          # KV missing with a prompt
+    assert dg.dg_denoise_step_validate(d, 1, 128, _weights(dg), kv) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_denoise_step_validate(d, 1, 64, _weights(dg), _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    kv0 = dg.make_prompt_kv(0, 0, 1024, 0, 0)             # empty prompts are fine
+    assert dg.dg_denoise_step_validate(d, 1, 0, _weights(dg), kv0) == dg.DG_OK
+
+
+def test_slot_read_and_commit_validation():
+    dg = _lib_or_skip()
+    d = _dims(dg)
+    assert dg.dg_slot_read_validate(d, 2, 4, 4, 0.1) == dg.DG_OK
+    assert dg.dg_slot_read_validate(d, 2, 4, 0, 0.1) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_slot_read_validate(d, 2, 4, 17, 0.1) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_slot_read_validate(d, 2, -1, 4, 0.1) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_slot_read_validate(d, 2, 4, 4, -0.5) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_slot_read_validate(d, 2, 4, 4, float("nan")) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_commit_validate(3, 256) == dg.DG_OK
+    assert dg.dg_commit_validate(3, 0) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_commit_validate(3, 1025) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_commit_validate(-1, 4) == dg.DG_ERR_INVALID_ARG
+    assert dg.dg_slot_read_workspace(d, 512, 4, 1024, 4) > 0
+    assert dg.dg_slot_read_workspace(d, 512, 4, 1024, 0) == 0
+
+
+def test_label_count_rule():
+    """sotaaz, 'The server takes at most 26 alternatives': 77 alternatives in one
+    question are refused; up to 26 single-token labels A..Z are accepted."""
+    dg = _lib_or_skip()
+    assert dg.dg_check_label_count(26) == dg.DG_OK
+    assert dg.dg_check_label_count(1) == dg.DG_OK
+    assert dg.dg_check_label_count(27) == dg.DG_ERR_TOO_MANY_LABELS
+    assert dg.dg_check_label_count(0) == dg.DG_ERR_INVALID_ARG
+    with pytest.raises(ValueError, match="question 'intent': at most 26 alternatives"):
+        dg.check_alternatives("intent", [f"i{k}" for k in range(77)])
+    dg.check_alternatives("urgent", ["yes", "no"])
