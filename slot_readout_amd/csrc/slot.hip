@@ -187,7 +187,9 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
   float scale = a.logit_scale;
   if (a.row_scale) scale *= a.row_scale[bs];
   const T *h = static_cast<const T *>(a.h);
-  float racc = 0.f, eacc = 0.f;
+  // r is averaged directly; ln mean_d e^(lp_d) is kept as an online log-sum-exp
+  // (lp can sit far below the fp32 range of e^x)
+  float racc = 0.f, lm = -INFINITY, ls = 0.f;
   for (int d = 0; d < a.n_draws; ++d) {
     const int64_t bd = b * a.n_draws + d;
     const float lse = a.rowstat[bd * a.S + s].y;
@@ -195,13 +197,18 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
                                       a.label_ids + bs * DG_MAX_LABELS, k, scale, lse, lane);
     const LabelDist dd = renormalise(lp, k, lane);
     racc += dd.r;
-    eacc += lane < k ? __expf(lp) : 0.f;
+    if (lane < k) {
+      const float mn = fmaxf(lm, lp);
+      ls = ls * __expf(lm - mn) + __expf(lp - mn);
+      lm = mn;
+    }
   }
   LabelDist fin;
   fin.r = racc / (float)a.n_draws;
   finish_dist(fin, k, lane);
   if (lane < DG_MAX_LABELS) {
-    a.logprobs[bs * DG_MAX_LABELS + lane] = lane < k ? __logf(eacc / (float)a.n_draws) : 0.f;
+    a.logprobs[bs * DG_MAX_LABELS + lane] =
+        lane < k ? lm + __logf(ls) - __logf((float)a.n_draws) : 0.f;
     a.probs[bs * DG_MAX_LABELS + lane] = lane < k ? fin.r : 0.f;
   }
   if (lane == 0) {

@@ -2,7 +2,7 @@
 import numpy as np
 
 # Tolerances (elementwise: |g - o| <= rtol * max(|o|, RMS of o's row)):
-#   fp32 storage: 1e-4 on every float output.
+#   fp32 storage: 1e-4 relative on every float output (entropies and logprobs too).
 #   bf16 storage: 2e-2 on attention output, hidden state and self-conditioning;
 #                 1e-2 absolute on logprobs and entropies; 2e-2 relative on
 #                 confidences and label probabilities.
@@ -59,3 +59,17 @@ def assert_abs(g, o, atol, name):
         i = np.unravel_index(np.argmax(err), err.shape)
         raise AssertionError(f"{name}: max abs err {float(err.max()):.3g} at {i} "
                              f"(got {float(g[i])}, want {float(o[i])}), atol {atol}")
+
+
+def assert_float(g, o, dtype, kind, name):
+    """Apply the bar for `kind` at `dtype`: bf16 entropies/logprobs are absolute,
+    everything else (and everything in fp32) is row-relative."""
+    t = TOL[dtype]
+    if kind in ("entropy", "logprob"):
+        key = "entropy_abs" if kind == "entropy" else "logprob_abs"
+        if dtype == "bf16":
+            assert_abs(g, o, t[key], name)
+        else:
+            assert_row_rel(np.atleast_2d(g), np.atleast_2d(o), t[key], name)
+    else:
+        assert_row_rel(g, o, t[kind], name)

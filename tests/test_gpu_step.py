@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from synth import config, make_inputs, companion_row_scale
-from tests.helpers import TOL, TIE_EPS, to_np, assert_row_rel, assert_abs
+from tests.helpers import TOL, TIE_EPS, to_np, assert_row_rel, assert_float
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def _check_step(inp, out, refs, dtype, row_scale=None, label=""):
         assert_row_rel(to_np(out["hidden_out"][b]), ref["hidden_out"], tol["hidden_out"], f"{tag} hidden_out")
         assert_row_rel(to_np(out["logits"][b]), ref["logits"], tol["logits"], f"{tag} logits")
         assert_row_rel(to_np(out["conf"][b])[None], ref["conf"][None], tol["conf"], f"{tag} conf")
-        assert_abs(to_np(out["entropy"][b]), ref["entropy"], tol["entropy_abs"], f"{tag} entropy")
+        assert_float(to_np(out["entropy"][b]), ref["entropy"], dtype, "entropy", f"{tag} entropy")
         if out.get("sc_out") is not None:
             assert_row_rel(to_np(out["sc_out"][b]), ref["sc_out"], tol["sc_out"], f"{tag} sc_out")
         near = oracle.argmax_near_ties(ref["logits"], TIE_EPS[dtype]).mask
