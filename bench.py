@@ -1,0 +1,243 @@
+"""Throughput of one full pass of the hot path on one MI355X.
+
+A step = dg_denoise_step (attention, LM head, fused softmax/entropy, p.E
+self-conditioning) + dg_commit + dg_slot_read (8 slots x 4 labels, first read
+plus averaged noise draws) over one bf16 canvas of 256 tokens with a 2048-token
+cached prompt: d_model 2816, 8 query / 2 KV heads x 512, window +-128, vocab
+262,144.  Inputs are seeded and synthetic and already in HBM when timing
+starts.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+WORKLOAD = "bf16_step"
+
+
+def _hip():
+    L = ctypes.CDLL("libamdhip64.so.7")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+class Events:
+    """A block of raw hipEvents (timing enabled), recorded on a given stream."""
+
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.arr[i] = e
+        self.n = n
+
+    def record(self, i, stream):
+        assert self.hip.hipEventRecord(self.arr[i], stream) == 0
+
+    def ms(self, i, j):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.arr[i], self.arr[j]) == 0
+        return float(out.value)
+
+    def sub(self, offset):
+        return ctypes.cast(ctypes.byref(self.arr, offset * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def destroy(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "slot_readout_amd", "csrc"))):
+        with open(os.path.join(ROOT, "slot_readout_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, launch_rows):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_bf16_step.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_hash") != kernel_source_hash():
+        return None
+    k = c.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp):
+    """The CPU oracle as it stands, timed on this host on the same workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    st = oracle.denoise_step(inp)[0]
+    t1 = time.perf_counter()
+    oracle.commit_canvas(inp["canvas_ids"][0], st["conf"], st["entropy"], st["argmax"],
+                         inp["dims"].mask_id, inp["tau"])
+    t2 = time.perf_counter()
+    rd = oracle.slot_read(inp)
+    t3 = time.perf_counter()
+    B, C, S = inp["batch"], inp["dims"].canvas, inp["slot_pos"].shape[1]
+    total = t3 - t0
+    return {
+        "value": B * C / total, "unit": "canvas tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"the whole step of the same workload in float64 numpy: denoise step "
+                   f"{t1 - t0:.2f} s + commit {t2 - t1:.3f} s + slot read of {S} slots "
+                   f"({int(np.max(rd['draws_used']))} draws) {t3 - t2:.2f} s"),
+        "seconds": round(total, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build is a single-GPU hot path "
+              "(see the sharding notes in the design document); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from slot_readout_amd import dg
+    from slot_readout_amd.runtime import DeviceProblem
+    from synth import config, make_inputs
+
+    dg.lib()   # fails loudly without the HIP library
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = config(WORKLOAD)
+    t_in = time.perf_counter()
+    inp = make_inputs(cfg)
+    dev = DeviceProblem(inp, device="cuda:0")
+    dm = inp["dims"]
+    B, C, S, V, d = dev.B, dev.C, dev.S, dm.vocab, dm.d_model
+    stream = torch.cuda.current_stream().cuda_stream
+    so = dev.step_outputs(want_sc=True)
+    co = dev.commit_outputs()
+    ro = dev.slot_outputs()
+    hip = _hip()
+    K, W = args.steps, args.warmup
+    n_st = 2 * dg.DG_N_STAGES
+    marks = Events(hip, 4 * K)
+    stage_ev = Events(hip, n_st * K)
+    dbg_per_step = [dg.make_debug(stage_events=stage_ev.sub(k * n_st)) for k in range(K)]
+
+    def one_step(k=None):
+        dbg = dbg_per_step[k] if k is not None else None
+        if k is not None:
+            marks.record(4 * k, stream)
+        dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, B, dev.canvas_ids, None,
+                           inp["logit_scale"], None, so["conf"], so["entropy"], so["argmax"],
+                           so["sc_out"], dbg, so["flags"],
+                           dev.workspace("step", dg.dg_denoise_step_workspace(dev.dims, B, dev.max_prompt)),
+                           stream)
+        if k is not None:
+            marks.record(4 * k + 1, stream)
+        dg.dg_commit(B, C, dm.mask_id, dev.canvas_ids, so["conf"], so["entropy"], so["argmax"],
+                     inp["tau"], co["mask"], co["out_ids"], co["n"], stream)
+        if k is not None:
+            marks.record(4 * k + 2, stream)
+        dev.slot_read(out=ro, stream=stream)
+        if k is not None:
+            marks.record(4 * k + 3, stream)
+
+    for _ in range(W):
+        one_step()
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_in
+    t0 = time.perf_counter()
+    for k in range(K):
+        one_step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_total = marks.ms(0, 4 * K - 1)
+    ms_per_step = ms_total / K
+    step_ms = float(np.mean([marks.ms(4 * k, 4 * k + 1) for k in range(K)]))
+    commit_ms = float(np.mean([marks.ms(4 * k + 1, 4 * k + 2) for k in range(K)]))
+    read_ms = float(np.mean([marks.ms(4 * k + 2, 4 * k + 3) for k in range(K)]))
+    stages = {}
+    for i, name in enumerate(dg.DG_STAGES):
+        stages[name] = float(np.mean([stage_ev.ms(k * n_st + 2 * i, k * n_st + 2 * i + 1)
+                                      for k in range(K)]))
+    M = B * C
+    nvt = V // 256
+    # algorithmic work per launch of the two vocabulary-sized kernels
+    lm_bytes = V * d * 2 + M * d * 2 + M * V * 2 + M * nvt * 16
+    lm_flops = 2.0 * M * V * d
+    sc_bytes = d * V * 2 + M * V * 2 + M * nvt * 4 + M * d * 2
+    sc_flops = 2.0 * M * V * d
+    cand = {"lmhead": (stages["lmhead"], lm_bytes, lm_flops),
+            "selfcond": (stages["selfcond"], sc_bytes, sc_flops)}
+    dom = max(cand, key=lambda k: cand[k][0])
+    t_ms, nbytes, flops = cand[dom]
+    achieved_gbs = nbytes / (t_ms * 1e-3) / 1e9
+    roofline = {"kernel": {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
+                           "selfcond": "scgemm_kernel + sc_reduce_kernel (S6)"}[dom],
+                "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, M),
+                "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(t_ms, 4),
+                "mfma_tflops": round(flops / (t_ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(flops / (t_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    stage_roof = {}
+    for name, (tm, nb, fl) in cand.items():
+        stage_roof[name] = {"ms": round(tm, 4), "GB/s": round(nb / (tm * 1e-3) / 1e9, 1),
+                            "TFLOP/s": round(fl / (tm * 1e-3) / 1e12, 1)}
+
+    value = M / (ms_per_step * 1e-3)
+    line = {
+        "metric": "canvas tokens/s per denoise step + slot reads/s; % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "canvas tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; weights N(0,0.02), prompt K/V N(0,1))",
+        "config": {"workload": f"{WORKLOAD}: one canvas of 256 tokens, 2048-token cached prompt, "
+                               f"d_model 2816, 8q/2kv heads x 512, window +-128, vocab 262144, "
+                               f"commit tau 2.0, slot read 8 slots x 4 labels (4 noise draws)",
+                   "batch": B, "canvas": C, "prompt": int(inp["max_prompt"]), "slots": S},
+        "slot_reads_per_s": round(B * S / (ms_per_step * 1e-3), 1),
+        "breakdown_ms": {"denoise_step": round(step_ms, 4), "commit": round(commit_ms, 4),
+                         "slot_read": round(read_ms, 4),
+                         "stages": {k: round(v, 4) for k, v in stages.items()}},
+        "roofline": roofline,
+        "stage_roofline": stage_roof,
+        "host_wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
+    }
+    marks.destroy()
+    stage_ev.destroy()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -118,15 +118,32 @@ typedef struct {
     int64_t total_len;
 } dg_prompt_kv;
 
-/* Optional intermediate outputs (each may be NULL; pass NULL for the struct to
- * skip them all).  Written in addition to the regular outputs.
- *   attn_out    [batch, canvas, n_q_heads*head_dim] T   attention output o
- *   hidden_out  [batch, canvas, d_model] T              block output h
- *   logits_out  [batch, canvas, vocab] fp32             scaled logits l */
+/* Stages of dg_denoise_step, in launch order. */
+enum {
+    DG_STAGE_QKV = 0,         /* embedding gather + q/k/v projection */
+    DG_STAGE_ATTENTION = 1,   /* prompt + windowed canvas attention (and split merge) */
+    DG_STAGE_OPROJ = 2,       /* output projection + residual */
+    DG_STAGE_LMHEAD = 3,      /* LM head with per-tile softmax statistics */
+    DG_STAGE_VOCAB_MERGE = 4, /* confidence / entropy / argmax per row */
+    DG_STAGE_SELFCOND = 5,    /* p.E self-conditioning (and split-K reduce) */
+    DG_N_STAGES = 6
+};
+
+/* Optional intermediate outputs and instrumentation (each member may be NULL;
+ * pass NULL for the struct to skip them all).  Written in addition to the
+ * regular outputs.
+ *   attn_out     [batch, canvas, n_q_heads*head_dim] T   attention output o
+ *   hidden_out   [batch, canvas, d_model] T              block output h
+ *   logits_out   [batch, canvas, vocab] fp32             scaled logits l
+ *   stage_events 2*DG_N_STAGES hipEvent_t handles created by the caller, or NULL:
+ *                event 2i is recorded on the call's stream just before stage i
+ *                and event 2i+1 just after it (a stage that is skipped records
+ *                both back to back) */
 typedef struct {
     void *attn_out;
     void *hidden_out;
     float *logits_out;
+    void **stage_events;
 } dg_debug;
 
 /* Device-side input problems reported through *dev_flags (bitwise OR). */

@@ -184,6 +184,23 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   return p;
 }
 
+// records the caller's stage events (if any) around each stage of a call
+struct Stages {
+  void **ev = nullptr;
+  hipStream_t st = nullptr;
+  dg_status mark(int stage, int edge) const {
+    if (!ev) return DG_OK;
+    return hip_check(hipEventRecord(static_cast<hipEvent_t>(ev[2 * stage + edge]), st),
+                     "stage event record");
+  }
+};
+
+#define DG_MARK(stages, stage, edge)                  \
+  do {                                                 \
+    dg_status _m = (stages).mark((stage), (edge));     \
+    if (_m != DG_OK) return _m;                        \
+  } while (0)
+
 template <typename P> P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<char *>(ws) + off);
 }
@@ -192,7 +209,8 @@ template <typename P> P *at(void *ws, size_t off) {
 dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *kv, int nc,
                     int canvas_per_prompt, const int32_t *ids, const void *sc_in,
                     const int32_t *active, int32_t *flags, void *q, void *k, void *v, void *o,
-                    const AttnPlan &ap, float *part_o, float2 *part_ml, void *h, hipStream_t st) {
+                    const AttnPlan &ap, float *part_o, float2 *part_ml, void *h, hipStream_t st,
+                    const Stages &sg = Stages()) {
   const bool bf = d.dtype == DG_BF16;
   const int64_t M = (int64_t)nc * d.canvas;
   dg::QkvArgs qa{};
@@ -213,7 +231,9 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   qa.nkv = d.n_kv_heads * d.head_dim;
   qa.vocab = d.vocab;
   qa.C = d.canvas;
+  DG_MARK(sg, DG_STAGE_QKV, 0);
   DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "qkv projection launch");
+  DG_MARK(sg, DG_STAGE_QKV, 1);
 
   dg::AttnArgs aa{};
   aa.q = q;
@@ -238,7 +258,9 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.chunk = ap.chunk;
   aa.canvas_per_prompt = canvas_per_prompt;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
+  DG_MARK(sg, DG_STAGE_ATTENTION, 1);
 
   dg::OprojArgs oa{};
   oa.o = o;
@@ -253,7 +275,9 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   oa.kdim = d.n_q_heads * d.head_dim;
   oa.vocab = d.vocab;
   oa.C = d.canvas;
+  DG_MARK(sg, DG_STAGE_OPROJ, 0);
   DG_TRY_HIP(dg::launch_oproj(oa, bf, st), "output projection launch");
+  DG_MARK(sg, DG_STAGE_OPROJ, 1);
   return DG_OK;
 }
 
@@ -340,10 +364,13 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   const int nvt = d.vocab / dg::VTILE;
   void *o = (debug && debug->attn_out) ? debug->attn_out : at<char>(workspace, p.o);
   void *h = (debug && debug->hidden_out) ? debug->hidden_out : at<char>(workspace, p.h);
+  Stages sg;
+  sg.ev = debug ? debug->stage_events : nullptr;
+  sg.st = st;
   if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
   s = run_block(d, w, kv, batch, 1, canvas_ids, sc_in, nullptr, dev_flags, at<char>(workspace, p.q),
                 at<char>(workspace, p.k), at<char>(workspace, p.v), o, p.attn,
-                at<float>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st);
+                at<float>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st, sg);
   if (s != DG_OK) return s;
 
   dg::LmheadArgs la{};
@@ -358,7 +385,9 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   la.d = d.d_model;
   la.vocab = d.vocab;
   la.nvt = nvt;
+  DG_MARK(sg, DG_STAGE_LMHEAD, 0);
   DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "LM head launch");
+  DG_MARK(sg, DG_STAGE_LMHEAD, 1);
 
   dg::VocabMergeArgs va{};
   va.stats = la.stats;
@@ -368,8 +397,11 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   va.entropy = entropy;
   va.argmax = argmax;
   va.fscale = sc_out ? at<float>(workspace, p.fscale) : nullptr;
+  DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 0);
   DG_TRY_HIP(dg::launch_vocab_merge(va, st), "vocabulary merge launch");
+  DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 1);
 
+  DG_MARK(sg, DG_STAGE_SELFCOND, 0);
   if (sc_out) {
     dg::ScArgs sa{};
     sa.ptilde = la.ptilde;
@@ -384,6 +416,7 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
     sa.ksplit = p.ksplit;
     DG_TRY_HIP(dg::launch_scgemm(sa, bf, st), "self-conditioning launch");
   }
+  DG_MARK(sg, DG_STAGE_SELFCOND, 1);
   return ok();
 }
 

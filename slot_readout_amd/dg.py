@@ -45,7 +45,11 @@ class PromptKV(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [("attn_out", ctypes.c_void_p), ("hidden_out", ctypes.c_void_p),
-                ("logits_out", ctypes.c_void_p)]
+                ("logits_out", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
+DG_STAGES = ("qkv", "attention", "oproj", "lmhead", "vocab_merge", "selfcond")
+DG_N_STAGES = len(DG_STAGES)
 
 
 _P = ctypes.c_void_p
@@ -133,8 +137,10 @@ def make_prompt_kv(k, v, cu_seqlens, max_len, total_len):
     return PromptKV(_ptr(k), _ptr(v), _ptr(cu_seqlens), int(max_len), int(total_len))
 
 
-def make_debug(attn_out=None, hidden_out=None, logits_out=None):
-    return Debug(_ptr(attn_out), _ptr(hidden_out), _ptr(logits_out))
+def make_debug(attn_out=None, hidden_out=None, logits_out=None, stage_events=None):
+    """stage_events: a ctypes array of 2*DG_N_STAGES hipEvent_t handles, or None."""
+    ev = ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None
+    return Debug(_ptr(attn_out), _ptr(hidden_out), _ptr(logits_out), ev)
 
 
 # ---------------------------------------------------------------- calls -----
