@@ -20,9 +20,9 @@ template <typename T> struct BKOf;
 template <> struct BKOf<bf16> { static constexpr int v = 32; };
 template <> struct BKOf<float> { static constexpr int v = 16; };
 
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF = 1, int BK_ = BKOf<T>::v>
 struct Gemm {
-  static constexpr int BK = BKOf<T>::v;
+  static constexpr int BK = BK_;
   static constexpr int NW = WGM * WGN;
   static constexpr int NT = NW * WAVE;
   static constexpr int VEC = 16 / sizeof(T);
@@ -35,6 +35,7 @@ struct Gemm {
   static constexpr int LDS_BYTES = 2 * (BM + BN) * PITCH * (int)sizeof(T);
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be 16-aligned");
+  static_assert(PF >= 1 && PF <= 4, "prefetch depth");
   using MF = Mfma<T>;
   using frag = typename MF::frag;
 
@@ -42,6 +43,10 @@ struct Gemm {
   __device__ static inline int a_kc(int it) { return (it * NT + (int)threadIdx.x) % CPR; }
 
   // acc += A[rows of tile, kbeg:kend] * B[rows of tile, kbeg:kend]^T
+  //
+  // Global loads run PF K-steps ahead of the MFMAs through a ring of PF
+  // register stages; LDS is double-buffered with one barrier per K step.  The
+  // K loop is unrolled by PF so every ring index is a compile-time constant.
   template <class AL, class BL>
   __device__ static void run(char *smem, const AL &al, const BL &bl, int kbeg, int kend,
                              f32x4 (&acc)[TM][TN]) {
@@ -54,30 +59,31 @@ struct Gemm {
       for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
     const int nk = (kend - kbeg) / BK;
     if (nk <= 0) return;
-    uint4 ra[AI], rb[BI];
-    auto gload = [&](int kt) {
+    using RA = typename AL::Raw;
+    using RB = typename BL::Raw;
+    RA ra[PF][AI];
+    RB rb[PF][BI];
+    // issue the global loads of step kt; nothing consumes them until sstore
+    auto gload = [&](int kt, RA (&xa)[AI], RB (&xb)[BI]) {
       const int k0 = kbeg + kt * BK;
 #pragma unroll
-      for (int it = 0; it < AI; ++it) ra[it] = al.fetch(it, k0 + a_kc(it) * VEC);
+      for (int it = 0; it < AI; ++it) xa[it] = al.load(it, k0 + a_kc(it) * VEC);
 #pragma unroll
-      for (int it = 0; it < BI; ++it) rb[it] = bl.fetch(it, k0 + a_kc(it) * VEC);
+      for (int it = 0; it < BI; ++it) xb[it] = bl.load(it, k0 + a_kc(it) * VEC);
     };
-    auto sstore = [&](int buf) {
+    // finish (mask / transform) the loaded chunks and write them to LDS
+    auto sstore = [&](int buf, const RA (&xa)[AI], const RB (&xb)[BI]) {
       T *As = lds + buf * (BM + BN) * PITCH;
       T *Bs = As + BM * PITCH;
 #pragma unroll
       for (int it = 0; it < AI; ++it)
-        *reinterpret_cast<uint4 *>(As + a_row(it) * PITCH + a_kc(it) * VEC) = ra[it];
+        *reinterpret_cast<uint4 *>(As + a_row(it) * PITCH + a_kc(it) * VEC) = al.finish(it, xa[it]);
 #pragma unroll
       for (int it = 0; it < BI; ++it)
-        *reinterpret_cast<uint4 *>(Bs + a_row(it) * PITCH + a_kc(it) * VEC) = rb[it];
+        *reinterpret_cast<uint4 *>(Bs + a_row(it) * PITCH + a_kc(it) * VEC) = bl.finish(it, xb[it]);
     };
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) gload(kt + 1);
-      const T *As = lds + (kt & 1) * (BM + BN) * PITCH;
+    auto compute = [&](int buf) {
+      const T *As = lds + buf * (BM + BN) * PITCH;
       const T *Bs = As + BM * PITCH;
 #pragma unroll
       for (int ks = 0; ks < BK / MF::KI; ++ks) {
@@ -94,53 +100,108 @@ struct Gemm {
 #pragma unroll
           for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(a[i], b[j], acc[i][j]);
       }
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
-      __syncthreads();
+    };
+#pragma unroll
+    for (int s = 0; s < PF; ++s)
+      if (s < nk) gload(s, ra[s], rb[s]);
+    sstore(0, ra[0], rb[0]);
+    __syncthreads();
+    for (int k0 = 0; k0 < nk; k0 += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int kt = k0 + j;
+        if (kt < nk) {
+          // ring slot j held step kt, already in LDS: refill it with step kt+PF
+          if (kt + PF < nk) gload(kt + PF, ra[j], rb[j]);
+          compute(kt & 1);
+          if (kt + 1 < nk) sstore((kt + 1) & 1, ra[(j + 1) % PF], rb[(j + 1) % PF]);
+          __syncthreads();
+        }
+      }
     }
   }
 };
 
 // ---------------------------------------------------------------------------
 // operand loaders: fetch(it, k) returns the 16-byte chunk at column k of the
-// row this thread loads in chunk slot `it` (zero for rows outside the matrix)
+// row this thread loads in chunk slot `it`.  They are branch-free: a row outside
+// the matrix points at a valid row and its chunk is replaced by zeros with a
+// select, so no load sits behind divergent control flow.
 // ---------------------------------------------------------------------------
+template <typename T> __device__ inline void store4(T *p, f32x4 v);
+template <> __device__ inline void store4<float>(float *p, f32x4 v) {
+  *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <> __device__ inline void store4<bf16>(bf16 *p, f32x4 v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b[r] = (bf16)v[r];
+  *reinterpret_cast<bf16x4 *>(p) = b;
+}
+
+__device__ inline uint4 keep_if(uint4 v, bool live) {
+  return live ? v : uint4{0, 0, 0, 0};
+}
+
 template <typename T, int N> struct RowLoader {
-  const T *p[N];
-  __device__ inline uint4 fetch(int it, int k) const {
-    return p[it] ? *reinterpret_cast<const uint4 *>(p[it] + k) : uint4{0, 0, 0, 0};
+  using Raw = uint4;
+  const T *p[N];     // always a dereferenceable row
+  bool live[N];
+  __device__ inline void set(int it, const T *row, bool ok, const T *fallback) {
+    p[it] = ok ? row : fallback;
+    live[it] = ok;
   }
+  __device__ inline Raw load(int it, int k) const {
+    return *reinterpret_cast<const uint4 *>(p[it] + k);
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const { return keep_if(r, live[it]); }
 };
 
-// x = E[id] + sc_in, rounded to T
+// x = E[id] + sc_in, rounded to T (sc_in present or absent for the whole launch)
 template <typename T, int N> struct GatherLoader {
+  struct Raw { uint4 e, s; };
   const T *e[N];
   const T *s[N];
-  __device__ inline uint4 fetch(int it, int k) const {
-    if (!e[it]) return uint4{0, 0, 0, 0};
+  bool live[N];
+  bool has_sc;
+  __device__ inline Raw load(int it, int k) const {
+    Raw r;
+    r.e = *reinterpret_cast<const uint4 *>(e[it] + k);
+    r.s = has_sc ? *reinterpret_cast<const uint4 *>(s[it] + k) : uint4{0, 0, 0, 0};
+    return r;
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
     Chunk<T> a;
-    a.u = *reinterpret_cast<const uint4 *>(e[it] + k);
-    if (s[it]) {
+    a.u = r.e;
+    if (has_sc) {
       Chunk<T> b;
-      b.u = *reinterpret_cast<const uint4 *>(s[it] + k);
+      b.u = r.s;
 #pragma unroll
       for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) + to_f(b.v[i]));
     }
-    return a.u;
+    return keep_if(a.u, live[it]);
   }
 };
 
 // p = p~ * f[row][k / VTILE], rounded to T  (p~ = e^(l - m_tile))
 template <typename T, int N> struct ScaledRowLoader {
+  struct Raw { uint4 p; float f; };
   const T *p[N];
   const float *f[N];
-  __device__ inline uint4 fetch(int it, int k) const {
-    if (!p[it]) return uint4{0, 0, 0, 0};
+  bool live[N];
+  __device__ inline Raw load(int it, int k) const {
+    Raw r;
+    r.p = *reinterpret_cast<const uint4 *>(p[it] + k);
+    r.f = f[it][k / VTILE];
+    return r;
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
     Chunk<T> a;
-    a.u = *reinterpret_cast<const uint4 *>(p[it] + k);
-    const float fac = f[it][k / VTILE];
+    a.u = r.p;
 #pragma unroll
-    for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) * fac);
-    return a.u;
+    for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) * r.f);
+    return keep_if(a.u, live[it]);
   }
 };
 
@@ -167,30 +228,28 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   const T *sc = static_cast<const T *>(a.sc_in);
   const int nq = a.nq, nk = a.nkv, ntot = nq + 2 * nk, d = a.d;
   GatherLoader<T, G::AI> al;
+  al.has_sc = sc != nullptr;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
-    al.e[it] = nullptr;
-    al.s[it] = nullptr;
-    if (row < a.M) {
-      const int id = a.ids[row];
-      if (id >= 0 && id < a.vocab) {
-        al.e[it] = E + (int64_t)id * d;
-        al.s[it] = sc ? sc + row * d : nullptr;
-      } else if (a.flags && G::a_kc(it) == 0) {
-        atomicOr(a.flags, DG_FLAG_BAD_TOKEN);
-      }
-    }
+    const bool in = row < a.M;
+    const int id = in ? a.ids[row] : 0;
+    const bool ok = in && id >= 0 && id < a.vocab;
+    if (in && !ok && a.flags && G::a_kc(it) == 0) atomicOr(a.flags, DG_FLAG_BAD_TOKEN);
+    al.e[it] = E + (ok ? (int64_t)id * d : 0);
+    al.s[it] = sc ? sc + (ok ? row * d : 0) : E;
+    al.live[it] = ok;
   }
   RowLoader<T, G::BI> bl;
+  const T *wq = static_cast<const T *>(a.wq);
 #pragma unroll
   for (int it = 0; it < G::BI; ++it) {
     const int n = n0 + G::a_row(it);
-    const T *p = nullptr;
-    if (n < nq) p = static_cast<const T *>(a.wq) + (int64_t)n * d;
+    const T *p;
+    if (n < nq) p = wq + (int64_t)n * d;
     else if (n < nq + nk) p = static_cast<const T *>(a.wk) + (int64_t)(n - nq) * d;
-    else if (n < ntot) p = static_cast<const T *>(a.wv) + (int64_t)(n - nq - nk) * d;
-    bl.p[it] = p;
+    else p = static_cast<const T *>(a.wv) + (int64_t)(n < ntot ? n - nq - nk : 0) * d;
+    bl.set(it, p, n < ntot, wq);
   }
   f32x4 acc[G::TM][G::TN];
   G::run(smem, al, bl, 0, d, acc);
@@ -227,17 +286,19 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
   const int n0 = blockIdx.y * BN;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const int K = a.kdim, d = a.d;
+  const T *o = static_cast<const T *>(a.o);
+  const T *wo = static_cast<const T *>(a.wo);
   RowLoader<T, G::AI> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
-    al.p[it] = row < a.M ? static_cast<const T *>(a.o) + row * K : nullptr;
+    al.set(it, o + row * K, row < a.M, o);
   }
   RowLoader<T, G::BI> bl;
 #pragma unroll
   for (int it = 0; it < G::BI; ++it) {
     const int n = n0 + G::a_row(it);
-    bl.p[it] = n < d ? static_cast<const T *>(a.wo) + (int64_t)n * K : nullptr;
+    bl.set(it, wo + (int64_t)n * K, n < d, wo);
   }
   f32x4 acc[G::TM][G::TN];
   G::run(smem, al, bl, 0, K, acc);
@@ -271,9 +332,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
 // vocabulary entries, MFMA columns are canvas rows, so each row's reduction
 // over the vocabulary runs mostly inside a lane.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
-  using G = Gemm<T, BM, BN, WGM, WGN>;
+  using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   __shared__ float red_m[WGM][BN];
@@ -285,22 +346,21 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   const int64_t n0 = (int64_t)blockIdx.y * BN;
   const int d = a.d;
   if (a.active_rows && !tile_active(a.active_rows, n0, BN, a.nrows, a.rows_per_flag)) return;
+  const T *head = static_cast<const T *>(a.head);
+  const T *hh = static_cast<const T *>(a.h);
   RowLoader<T, G::AI> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int v = v0 + G::a_row(it);
-    al.p[it] = v < a.vocab ? static_cast<const T *>(a.head) + (int64_t)v * d : nullptr;
+    al.set(it, head + (int64_t)v * d, v < a.vocab, head);
   }
   RowLoader<T, G::BI> bl;
 #pragma unroll
   for (int it = 0; it < G::BI; ++it) {
     const int64_t n = n0 + G::a_row(it);
-    const T *p = nullptr;
-    if (n < a.nrows) {
-      const int64_t src = a.row_index ? (int64_t)a.row_index[n] : n;
-      if (src >= 0) p = static_cast<const T *>(a.h) + src * d;
-    }
-    bl.p[it] = p;
+    int64_t src = -1;
+    if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
+    bl.set(it, hh + (src >= 0 ? src : 0) * d, src >= 0, hh);
   }
   f32x4 acc[G::TM][G::TN];
   G::run(smem, al, bl, 0, d, acc);
@@ -369,15 +429,18 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
       const int vb = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4);
+      f32x4 e4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x = acc[i][j][r] - mx[j];
         const float e = __expf(x);
         s += e;
         t += e * x;
-        if (live && pt) pt[n * a.vocab + vb + r] = from_f<T>(e);
-        if (live && a.logits) a.logits[n * a.vocab + vb + r] = acc[i][j][r];
+        e4[r] = e;
       }
+      // four consecutive vocabulary entries of one row: one 8- (bf16) or 16-byte store
+      if (pt && live) store4<T>(pt + n * a.vocab + vb, e4);
+      if (a.logits && live) *reinterpret_cast<f32x4 *>(a.logits + n * a.vocab + vb) = acc[i][j];
     }
     s += __shfl_xor(s, 16);
     t += __shfl_xor(t, 16);
@@ -416,9 +479,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
 // ---------------------------------------------------------------------------
 // S6: sc = p E over a range of the vocabulary (A = p~ scaled, B = E^T rows)
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
-  using G = Gemm<T, BM, BN, WGM, WGN>;
+  using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   const int n0 = blockIdx.x * BN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
@@ -426,18 +489,22 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
   const int nk = a.vocab / G::BK;
   const int kbeg = (int)((int64_t)z * nk / a.ksplit) * G::BK;
   const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * G::BK;
+  const T *ptl = static_cast<const T *>(a.ptilde);
+  const T *et = static_cast<const T *>(a.embed_t);
   ScaledRowLoader<T, G::AI> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
-    al.p[it] = row < a.M ? static_cast<const T *>(a.ptilde) + row * a.vocab : nullptr;
-    al.f[it] = row < a.M ? a.fscale + row * a.nvt : nullptr;
+    const bool ok = row < a.M;
+    al.p[it] = ptl + (ok ? row * a.vocab : 0);
+    al.f[it] = a.fscale + (ok ? row * a.nvt : 0);
+    al.live[it] = ok;
   }
   RowLoader<T, G::BI> bl;
 #pragma unroll
   for (int it = 0; it < G::BI; ++it) {
     const int n = n0 + G::a_row(it);
-    bl.p[it] = n < a.d ? static_cast<const T *>(a.embed_t) + (int64_t)n * a.vocab : nullptr;
+    bl.set(it, et + (int64_t)n * a.vocab, n < a.d, et);
   }
   f32x4 acc[G::TM][G::TN];
   G::run(smem, al, bl, kbeg, kend, acc);
@@ -509,17 +576,17 @@ hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
   if (bf) {
     dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 256));
-    hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4>), grid, dim3(8 * WAVE), 0, st, a);
+    hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
     dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 64));
-    hipLaunchKernelGGL((lmhead_kernel<float, VTILE, 64, 4, 1>), grid, dim3(4 * WAVE), 0, st, a);
+    hipLaunchKernelGGL((lmhead_kernel<float, VTILE, 64, 4, 1, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
   }
   return hipGetLastError();
 }
 
 int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
   const int64_t tiles = bf ? cdiv64(M, 256) * cdiv64(d, 256) : cdiv64(M, 64) * cdiv64(d, 64);
-  const int nk = vocab / (bf ? BKOf<bf16>::v : BKOf<float>::v);
+  const int nk = vocab / (bf ? 64 : 16);
   int64_t ks = 256 / tiles;  // about one workgroup per compute unit, no partial second wave
   if (ks > nk) ks = nk;
   if (ks > 64) ks = 64;
@@ -530,10 +597,10 @@ int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
 hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
   if (bf) {
     dim3 grid((unsigned)cdiv64(a.d, 256), (unsigned)cdiv64(a.M, 256), (unsigned)a.ksplit);
-    hipLaunchKernelGGL((scgemm_kernel<bf16, 256, 256, 4, 2>), grid, dim3(8 * WAVE), 0, st, a);
+    hipLaunchKernelGGL((scgemm_kernel<bf16, 256, 256, 4, 2, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
     dim3 grid((unsigned)cdiv64(a.d, 64), (unsigned)cdiv64(a.M, 64), (unsigned)a.ksplit);
-    hipLaunchKernelGGL((scgemm_kernel<float, 64, 64, 2, 2>), grid, dim3(4 * WAVE), 0, st, a);
+    hipLaunchKernelGGL((scgemm_kernel<float, 64, 64, 2, 2, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
