@@ -3,10 +3,11 @@
 // (bidirectional, no causal mask).
 //
 // Work split: one workgroup = (canvas, query head, tile of NQ consecutive
-// canvas positions, split of the prompt keys).  The last split also takes the
-// canvas-window keys.  With one split the workgroup writes the normalised
-// output; otherwise it writes (m, l, unnormalised O) partials that a second
-// kernel merges in a fixed order.
+// canvas positions, split).  A query tile's keys -- every prompt key, then the
+// canvas keys its window can reach -- are cut into equal splits (split-KV).
+// With one split the workgroup writes the normalised output; otherwise it
+// writes (m, l, unnormalised O) partials that a second kernel merges in a
+// fixed order.
 //
 // Inside a workgroup the 4 waves each own QB x 16 query columns.  Scores are
 // computed transposed, S^T = K Q^T, so that a lane holds one query column and
@@ -18,8 +19,6 @@
 #include "kernels.h"
 
 namespace dg {
-
-template <typename T> struct AttnCfg;
 
 template <typename T, int HD> struct AttnShape;
 template <> struct AttnShape<bf16, 64> { static constexpr int QB = 4, NK = 64; };
@@ -69,9 +68,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   if (bad && a.flags && threadIdx.x == 0 && s == 0 && qt == 0 && h == 0)
     atomicOr(a.flags, DG_FLAG_BAD_SEQLENS);
   const int64_t plen = p1 - p0;
-  const int64_t cs = (int64_t)s * a.chunk;
-  const int64_t ps = p0 + (cs < plen ? cs : plen);
-  const int64_t pe = p0 + (cs + a.chunk < plen ? cs + a.chunk : plen);
+  // keys of this query tile, in order: every prompt key, then the canvas keys
+  // [lo, hi) that the tile's window can reach; split s takes an equal slice
+  const int lo = i0 - W > 0 ? i0 - W : 0;
+  const int hi = i0 + NQ + W < C ? i0 + NQ + W : C;   // exclusive
+  const int64_t nkeys = plen + (hi - lo);
+  const int64_t vb0 = (int64_t)s * a.chunk;
+  const int64_t vb1 = vb0 + a.chunk < nkeys ? vb0 + a.chunk : nkeys;
+  const int64_t ps = p0 + (vb0 < plen ? vb0 : plen);
+  const int64_t pe = p0 + (vb1 < plen ? vb1 : plen);
+  const int64_t cs0 = lo + (vb0 > plen ? vb0 - plen : 0);
+  const int64_t cs1 = lo + (vb1 > plen ? vb1 - plen : 0);
 
   const int64_t kv_stride = (int64_t)a.Hkv * HD;   // elements between consecutive keys
   const int64_t q_stride = (int64_t)a.Hq * HD;
@@ -102,18 +109,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   auto block = [&](const T *kb, const T *vb, int64_t k0, int64_t kend, bool canvas) {
     constexpr int CPK = HD / VEC;
+    // K: consecutive lanes take consecutive 16-byte chunks of a key row
     for (int c = threadIdx.x; c < NK * CPK; c += 256) {
       const int kk = c / CPK, cc = c % CPK;
       const int64_t key = k0 + kk;
-      Chunk<T> kc, vc;
-      if (key < kend) {
-        kc.u = *reinterpret_cast<const uint4 *>(kb + key * kv_stride + cc * VEC);
-        vc.u = *reinterpret_cast<const uint4 *>(vb + key * kv_stride + cc * VEC);
-      } else {
-        kc.u = uint4{0, 0, 0, 0};
-        vc.u = uint4{0, 0, 0, 0};
-      }
-      *reinterpret_cast<uint4 *>(Ks + kk * KP + cc * VEC) = kc.u;
+      const bool ok = key < kend;
+      uint4 kc = *reinterpret_cast<const uint4 *>(kb + (ok ? key : k0) * kv_stride + cc * VEC);
+      if (!ok) kc = uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4 *>(Ks + kk * KP + cc * VEC) = kc;
+    }
+    // V, transposed: consecutive lanes take consecutive keys of one chunk, so each
+    // element store writes neighbouring positions of one V^T row
+    for (int c = threadIdx.x; c < NK * CPK; c += 256) {
+      const int kk = c % NK, cc = c / NK;
+      const int64_t key = k0 + kk;
+      const bool ok = key < kend;
+      Chunk<T> vc;
+      vc.u = *reinterpret_cast<const uint4 *>(vb + (ok ? key : k0) * kv_stride + cc * VEC);
+      if (!ok) vc.u = uint4{0, 0, 0, 0};
       const int pos = vt_pos<T>(kk);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) Vt[(cc * VEC + e) * VP + pos] = vc.v[e];
@@ -209,13 +222,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const T *vb = static_cast<const T *>(a.vp) + (int64_t)g * HD;
     for (int64_t k0 = ps; k0 < pe; k0 += NK) block(kb, vb, k0, pe, false);
   }
-  if (s == a.nsplit - 1) {
-    const int lo = i0 - W > 0 ? i0 - W : 0;
-    const int hi = i0 + NQ + W < C ? i0 + NQ + W : C;   // exclusive
+  if (cs1 > cs0) {
     const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
     const T *kb = static_cast<const T *>(a.k) + cbase;
     const T *vb = static_cast<const T *>(a.v) + cbase;
-    for (int k0 = lo; k0 < hi; k0 += NK) block(kb, vb, k0, hi, true);
+    for (int64_t k0 = cs0; k0 < cs1; k0 += NK) block(kb, vb, k0, cs1, true);
   }
 
   const int64_t R = (int64_t)a.nc * a.Hq * C;
@@ -278,18 +289,22 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 
 int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 256; }
 
-void attn_plan(int nc, int C, int Hq, int Hkv, int head_dim, int max_len, int *nsplit, int *chunk) {
+void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len, int *nsplit,
+               int *chunk) {
   const int nq = attn_query_tile(head_dim);
   const int nk = head_dim == 512 ? 32 : 64;
   const int64_t base = (int64_t)nc * Hq * cdiv64(C, nq);
+  // most keys one query tile can see: the prompt plus its window span
+  const int64_t span = (int64_t)max_len + (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
   int ns = 1;
-  if (max_len > 0 && base < 512) {
+  if (base < 512) {
     ns = (int)cdiv64(512, base);
-    const int64_t maxs = cdiv64(max_len, nk);
+    const int64_t maxs = cdiv64(span, 4 * nk);   // keep at least ~4 key blocks per split
     if (ns > maxs) ns = (int)maxs;
+    if (ns < 1) ns = 1;
   }
-  int ck = max_len > 0 ? (int)(cdiv64(cdiv64(max_len, ns), nk) * nk) : nk;
-  if (max_len > 0) ns = (int)cdiv64(max_len, ck);
+  const int ck = (int)(cdiv64(cdiv64(span, ns), nk) * nk);
+  ns = (int)cdiv64(span, ck);
   if (ns < 1) ns = 1;
   *nsplit = ns;
   *chunk = ck;

@@ -108,7 +108,8 @@ struct AttnPlan {
 
 AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt) {
   AttnPlan p;
-  dg::attn_plan(nc, d.canvas, d.n_q_heads, d.n_kv_heads, d.head_dim, max_prompt, &p.nsplit, &p.chunk);
+  dg::attn_plan(nc, d.canvas, d.n_q_heads, d.n_kv_heads, d.window, d.head_dim, max_prompt, &p.nsplit,
+                &p.chunk);
   if (p.nsplit > 1) {
     const size_t R = (size_t)nc * d.n_q_heads * d.canvas;
     p.part_o = (size_t)p.nsplit * R * d.head_dim * sizeof(float);

@@ -102,7 +102,8 @@ hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st);
 
 // attention: query rows per workgroup, split-KV planning, launch (+ merge)
 int attn_query_tile(int head_dim);
-void attn_plan(int nc, int C, int Hq, int Hkv, int head_dim, int max_len, int *nsplit, int *chunk);
+void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len, int *nsplit,
+               int *chunk);
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
