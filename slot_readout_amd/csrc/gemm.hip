@@ -574,7 +574,12 @@ hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
 }
 
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
-  if (bf) {
+  if (bf && a.nrows <= 64) {
+    // few rows (slot reads): a 64-row tile keeps the MFMA work proportional to
+    // the rows and three workgroups per CU keep the vocabulary stream busy
+    dim3 grid((unsigned)(a.vocab / VTILE), 1);
+    hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
+  } else if (bf) {
     dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 256));
     hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {

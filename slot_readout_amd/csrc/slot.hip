@@ -33,18 +33,46 @@ __global__ __launch_bounds__(256) void slot_rows_kernel(SlotArgs a) {
   a.rows[bs] = st == DG_SLOT_OK ? (int32_t)(b * a.C + a.slot_pos[bs]) : -1;
 }
 
-// label logits of one hidden row, lp_j = min(s * h.head[label_j] - lse, 0), in lane j
+// Label logits of one hidden row: lp_j = min(s * h.head[label_j] - lse, 0),
+// returned in lane j.  Lanes stride over 16-byte chunks of the row; each hidden
+// chunk is loaded once and reused for every label, so the k dot products run
+// side by side, then each is reduced across the wave.
 template <typename T>
 __device__ inline float label_logprob(const SlotArgs &a, const T *hrow, const int32_t *labs, int k,
                                       float scale, float lse, int lane) {
+  constexpr int VEC = 16 / sizeof(T);
   const T *head = static_cast<const T *>(a.head);
+  float acc[DG_MAX_LABELS];
+#pragma unroll
+  for (int j = 0; j < DG_MAX_LABELS; ++j) acc[j] = 0.f;
+  const T *er[DG_MAX_LABELS];
+#pragma unroll
+  for (int j = 0; j < DG_MAX_LABELS; ++j) er[j] = head + (int64_t)(j < k ? labs[j] : labs[0]) * a.d;
+  for (int e = lane * VEC; e < a.d; e += 64 * VEC) {
+    Chunk<T> hc;
+    hc.u = *reinterpret_cast<const uint4 *>(hrow + e);
+    float hf[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) hf[i] = to_f(hc.v[i]);
+#pragma unroll
+    for (int j = 0; j < DG_MAX_LABELS; ++j) {
+      if (j < k) {
+        Chunk<T> ec;
+        ec.u = *reinterpret_cast<const uint4 *>(er[j] + e);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s += hf[i] * to_f(ec.v[i]);
+        acc[j] += s;
+      }
+    }
+  }
   float mine = -INFINITY;
-  for (int j = 0; j < k; ++j) {
-    const T *er = head + (int64_t)labs[j] * a.d;
-    float acc = 0.f;
-    for (int e = lane; e < a.d; e += 64) acc += to_f(hrow[e]) * to_f(er[e]);
-    acc = wave_sum(acc);
-    if (lane == j) mine = fminf(acc * scale - lse, 0.f);
+#pragma unroll
+  for (int j = 0; j < DG_MAX_LABELS; ++j) {
+    if (j < k) {
+      const float t = wave_sum(acc[j]);
+      if (lane == j) mine = fminf(t * scale - lse, 0.f);
+    }
   }
   return mine;
 }
