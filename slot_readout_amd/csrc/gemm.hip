@@ -111,9 +111,14 @@ struct Gemm {
       for (int j = 0; j < PF; ++j) {
         const int kt = k0 + j;
         if (kt < nk) {
-          // ring slot j held step kt, already in LDS: refill it with step kt+PF
+          // ring slot j held step kt, already in LDS: refill it with step kt+PF.
+          // Scheduling fences keep the order loads -> MFMAs -> finish/store, so
+          // the conversion of freshly loaded data is not hoisted next to the
+          // loads (which would wait on them before any MFMA).
           if (kt + PF < nk) gload(kt + PF, ra[j], rb[j]);
+          __builtin_amdgcn_sched_barrier(0);
           compute(kt & 1);
+          __builtin_amdgcn_sched_barrier(0);
           if (kt + 1 < nk) sstore((kt + 1) & 1, ra[(j + 1) % PF], rb[(j + 1) % PF]);
           __syncthreads();
         }
@@ -140,6 +145,14 @@ template <> __device__ inline void store4<bf16>(bf16 *p, f32x4 v) {
   *reinterpret_cast<bf16x4 *>(p) = b;
 }
 
+// Makes a loaded value opaque at this point: uses of it cannot be hoisted
+// above, so the wait for the load lands here (at the LDS store), not next to
+// the load.
+__device__ inline void pin(uint4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ inline void pin(float &v) { asm volatile("" : "+v"(v)); }
+
 __device__ inline uint4 keep_if(uint4 v, bool live) {
   return live ? v : uint4{0, 0, 0, 0};
 }
@@ -155,7 +168,11 @@ template <typename T, int N> struct RowLoader {
   __device__ inline Raw load(int it, int k) const {
     return *reinterpret_cast<const uint4 *>(p[it] + k);
   }
-  __device__ inline uint4 finish(int it, const Raw &r) const { return keep_if(r, live[it]); }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
+    uint4 v = r;
+    pin(v);
+    return keep_if(v, live[it]);
+  }
 };
 
 // x = E[id] + sc_in, rounded to T (sc_in present or absent for the whole launch)
@@ -174,9 +191,11 @@ template <typename T, int N> struct GatherLoader {
   __device__ inline uint4 finish(int it, const Raw &r) const {
     Chunk<T> a;
     a.u = r.e;
+    pin(a.u);
     if (has_sc) {
       Chunk<T> b;
       b.u = r.s;
+      pin(b.u);
 #pragma unroll
       for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) + to_f(b.v[i]));
     }
@@ -199,8 +218,11 @@ template <typename T, int N> struct ScaledRowLoader {
   __device__ inline uint4 finish(int it, const Raw &r) const {
     Chunk<T> a;
     a.u = r.p;
+    pin(a.u);
+    float fac = r.f;
+    pin(fac);
 #pragma unroll
-    for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) * r.f);
+    for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) * fac);
     return keep_if(a.u, live[it]);
   }
 };
