@@ -239,9 +239,9 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
 // ---------------------------------------------------------------------------
 // S0+S1: q,k,v projection with the embedding gather in the A prologue
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
-  using G = Gemm<T, BM, BN, WGM, WGN>;
+  using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   const int64_t m0 = (int64_t)blockIdx.x * BM;
   const int n0 = blockIdx.y * BN;
@@ -300,9 +300,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
 // ---------------------------------------------------------------------------
 // S3: h = x + o Wo^T, x recomputed from the embedding (fp32, unrounded)
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
-  using G = Gemm<T, BM, BN, WGM, WGN>;
+  using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   const int64_t m0 = (int64_t)blockIdx.x * BM;
   const int n0 = blockIdx.y * BN;
@@ -564,35 +564,39 @@ __global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, void 
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
   dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.nq + 2 * a.nkv, BN));
-  hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+  hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   return hipGetLastError();
 }
 
+// Projections at small M are weight-streaming: small tiles for parallelism and
+// a 4-stage prefetch to keep enough bytes in flight per CU.
 hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
   const int64_t ntot = a.nq + 2 * a.nkv;
   if (bf) {
-    if (cdiv64(a.M, 128) * cdiv64(ntot, 128) >= 512) return launch_qkv_t<bf16, 128, 128, 2, 2>(a, st);
-    return launch_qkv_t<bf16, 64, 64, 2, 2>(a, st);
+    if (cdiv64(a.M, 128) * cdiv64(ntot, 128) >= 512)
+      return launch_qkv_t<bf16, 128, 128, 2, 2, 2, 64>(a, st);
+    return launch_qkv_t<bf16, 64, 64, 2, 2, 4, 64>(a, st);
   }
-  return launch_qkv_t<float, 64, 64, 2, 2>(a, st);
+  return launch_qkv_t<float, 64, 64, 2, 2, 1, 16>(a, st);
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_oproj_t(const OprojArgs &a, hipStream_t st) {
   dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.d, BN));
-  hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+  hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN, PF, BK>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
   if (bf) {
-    if (cdiv64(a.M, 128) * cdiv64(a.d, 128) >= 512) return launch_oproj_t<bf16, 128, 128, 2, 2>(a, st);
-    return launch_oproj_t<bf16, 64, 64, 2, 2>(a, st);
+    if (cdiv64(a.M, 128) * cdiv64(a.d, 128) >= 512)
+      return launch_oproj_t<bf16, 128, 128, 2, 2, 2, 64>(a, st);
+    return launch_oproj_t<bf16, 64, 64, 2, 2, 4, 64>(a, st);
   }
-  return launch_oproj_t<float, 64, 64, 2, 2>(a, st);
+  return launch_oproj_t<float, 64, 64, 2, 2, 1, 16>(a, st);
 }
 
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {

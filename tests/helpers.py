@@ -73,3 +73,4 @@ def assert_float(g, o, dtype, kind, name):
             assert_row_rel(np.atleast_2d(g), np.atleast_2d(o), t[key], name)
     else:
         assert_row_rel(g, o, t[kind], name)
+

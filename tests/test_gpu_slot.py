@@ -31,8 +31,8 @@ def _check_slots(g, ref, inp, dtype, label=""):
     tol = TOL[dtype]
     assert np.array_equal(g["status"], ref["status"]), f"{label} status"
     th = inp["entropy_threshold"]
-    # a first entropy within the entropy tolerance of the threshold may decide the
-    # re-read either way: such slots are excused (declared from the oracle's values)
+    # a first entropy within the entropy bar of the threshold may decide the re-read
+    # either way: such slots are excused (declared from the oracle's values)
     near = np.abs(ref["first_entropy"] - th) < tol["entropy_abs"]
     ok = (ref["status"] == oracle.SLOT_OK) & ~near
     assert np.array_equal(g["draws_used"][ok], ref["draws_used"][ok]), f"{label} draws_used"
@@ -126,3 +126,4 @@ def test_slot_read_deterministic(torch_cuda):
     b = _read(inp)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
