@@ -63,6 +63,19 @@ class Events:
             self.hip.hipEventDestroy(self.arr[i])
 
 
+def attention_work(inp):
+    """Algorithmic bytes and flops of the attention stage (all canvases)."""
+    dm = inp["dims"]
+    C, Hq, Hkv, hd, W = dm.canvas, dm.n_q_heads, dm.n_kv_heads, dm.head_dim, dm.window
+    es = 2 if dm.dtype == "bf16" else 4
+    lens = inp["prompt_lens"].astype("int64")
+    kv_bytes = int(lens.sum()) * Hkv * hd * 2 * es
+    canvas_bytes = len(lens) * C * (2 * Hq + 2 * Hkv) * hd * es      # q, o, canvas k, v
+    win = sum(min(C, i + W + 1) - max(0, i - W) for i in range(C))    # visible canvas keys
+    flops = 4.0 * Hq * hd * (C * float(lens.sum()) + len(lens) * win)
+    return kv_bytes + canvas_bytes, flops, kv_bytes
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "slot_readout_amd", "csrc"))):
@@ -116,6 +129,13 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=["bf16_step", "long_read", "ragged32"],
+                    help="bf16_step (default) times step + commit + slot read; long_read and "
+                         "ragged32 time step + commit and report the attention stage")
+    ap.add_argument("--cold", action="store_true",
+                    help="evict the caches (write 1 GiB) before every timed step; the default "
+                         "for long_read, whose prompt KV would otherwise sit in the 256 MB MALL")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build is a single-GPU hot path "
@@ -131,7 +151,10 @@ def main():
     dg.lib()   # fails loudly without the HIP library
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    cfg = config(WORKLOAD)
+    workload = args.workload
+    cold = args.cold or workload == "long_read"
+    with_read = workload == "bf16_step"
+    cfg = config(workload)
     t_in = time.perf_counter()
     inp = make_inputs(cfg)
     dev = DeviceProblem(inp, device="cuda:0")
@@ -148,8 +171,12 @@ def main():
     stage_ev = Events(hip, n_st * K)
     dbg_per_step = [dg.make_debug(stage_events=stage_ev.sub(k * n_st)) for k in range(K)]
 
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0") if cold else None
+
     def one_step(k=None):
         dbg = dbg_per_step[k] if k is not None else None
+        if flush is not None:
+            flush.fill_(k if k is not None else 0)      # evicts L2 and the MALL (1 GiB of writes)
         if k is not None:
             marks.record(4 * k, stream)
         dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, B, dev.canvas_ids, None,
@@ -163,7 +190,8 @@ def main():
                      inp["tau"], co["mask"], co["out_ids"], co["n"], stream)
         if k is not None:
             marks.record(4 * k + 2, stream)
-        dev.slot_read(out=ro, stream=stream)
+        if with_read:
+            dev.slot_read(out=ro, stream=stream)
         if k is not None:
             marks.record(4 * k + 3, stream)
 
@@ -177,8 +205,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms_total = marks.ms(0, 4 * K - 1)
-    ms_per_step = ms_total / K
+    if cold:   # cache flushes sit between the steps: sum the steps themselves
+        ms_per_step = float(np.mean([marks.ms(4 * k, 4 * k + 3) for k in range(K)]))
+    else:
+        ms_per_step = marks.ms(0, 4 * K - 1) / K
     step_ms = float(np.mean([marks.ms(4 * k, 4 * k + 1) for k in range(K)]))
     commit_ms = float(np.mean([marks.ms(4 * k + 1, 4 * k + 2) for k in range(K)]))
     read_ms = float(np.mean([marks.ms(4 * k + 2, 4 * k + 3) for k in range(K)]))
@@ -193,13 +223,17 @@ def main():
     lm_flops = 2.0 * M * V * d
     sc_bytes = d * V * 2 + M * V * 2 + M * nvt * 4 + M * d * 2
     sc_flops = 2.0 * M * V * d
+    at_bytes, at_flops, kv_bytes = attention_work(inp)
     cand = {"lmhead": (stages["lmhead"], lm_bytes, lm_flops),
-            "selfcond": (stages["selfcond"], sc_bytes, sc_flops)}
+            "selfcond": (stages["selfcond"], sc_bytes, sc_flops),
+            "attention": (stages["attention"], at_bytes, at_flops)}
+    names = {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
+             "selfcond": "scgemm_kernel + sc_reduce_kernel (S6)",
+             "attention": "attn_kernel + attn_merge_kernel (S2)"}
     dom = max(cand, key=lambda k: cand[k][0])
     t_ms, nbytes, flops = cand[dom]
     achieved_gbs = nbytes / (t_ms * 1e-3) / 1e9
-    roofline = {"kernel": {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
-                           "selfcond": "scgemm_kernel + sc_reduce_kernel (S6)"}[dom],
+    roofline = {"kernel": names[dom],
                 "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom, M),
@@ -212,27 +246,38 @@ def main():
                             "TFLOP/s": round(fl / (tm * 1e-3) / 1e12, 1)}
 
     value = M / (ms_per_step * 1e-3)
+    wl_desc = {
+        "bf16_step": (f"bf16_step: one canvas of 256 tokens, 2048-token cached prompt, d_model 2816, "
+                      f"8q/2kv heads x 512, window +-128, vocab 262144, commit tau 2.0, slot read "
+                      f"8 slots x 4 labels (4 noise draws)"),
+        "long_read": ("long_read: one canvas of 256 tokens over a 110,707-token cached prompt read "
+                      "cold, d_model 256, 4 heads x 64, window +-128, vocab 2048; step + commit"),
+        "ragged32": ("ragged32: 32 canvases of 256 tokens, prompts U{512..8192}, d_model 256, "
+                     "4 heads x 64, window +-16, vocab 2048; step + commit"),
+    }[workload]
     line = {
         "metric": "canvas tokens/s per denoise step + slot reads/s; % of MFMA/HBM roofline",
         "value": round(value, 1), "unit": "canvas tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; weights N(0,0.02), prompt K/V N(0,1))",
-        "config": {"workload": f"{WORKLOAD}: one canvas of 256 tokens, 2048-token cached prompt, "
-                               f"d_model 2816, 8q/2kv heads x 512, window +-128, vocab 262144, "
-                               f"commit tau 2.0, slot read 8 slots x 4 labels (4 noise draws)",
-                   "batch": B, "canvas": C, "prompt": int(inp["max_prompt"]), "slots": S},
-        "slot_reads_per_s": round(B * S / (ms_per_step * 1e-3), 1),
+        "config": {"workload": wl_desc, "batch": B, "canvas": C,
+                   "prompt": int(inp["max_prompt"]), "slots": S if with_read else 0,
+                   "cold_cache": bool(cold)},
+        "slot_reads_per_s": round(B * S / (ms_per_step * 1e-3), 1) if with_read else None,
         "breakdown_ms": {"denoise_step": round(step_ms, 4), "commit": round(commit_ms, 4),
                          "slot_read": round(read_ms, 4),
                          "stages": {k: round(v, 4) for k, v in stages.items()}},
         "roofline": roofline,
         "stage_roofline": stage_roof,
+        "attention_kv_read": {"kv_bytes": int(kv_bytes), "ms": round(stages["attention"], 4),
+                              "GB/s": round(at_bytes / (stages["attention"] * 1e-3) / 1e9, 1),
+                              "hbm_frac": round(at_bytes / (stages["attention"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "host_wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
     }
     marks.destroy()
     stage_ev.destroy()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and workload == WORKLOAD:
         line["cpu_baseline"] = cpu_baseline(inp)
     else:
         line["cpu_baseline"] = None

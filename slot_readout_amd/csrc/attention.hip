@@ -21,9 +21,11 @@
 namespace dg {
 
 template <typename T, int HD> struct AttnShape;
-template <> struct AttnShape<bf16, 64> { static constexpr int QB = 4, NK = 64; };
-template <> struct AttnShape<float, 64> { static constexpr int QB = 4, NK = 64; };
-template <> struct AttnShape<bf16, 512> { static constexpr int QB = 1, NK = 32; };
+// QB: 16-query column blocks per wave; NK: keys per LDS block; PF: prefetch the
+// next K/V block into registers while the current one is computed
+template <> struct AttnShape<bf16, 64> { static constexpr int QB = 2, NK = 64; static constexpr bool PF = true; };
+template <> struct AttnShape<float, 64> { static constexpr int QB = 2, NK = 64; static constexpr bool PF = true; };
+template <> struct AttnShape<bf16, 512> { static constexpr int QB = 1, NK = 32; static constexpr bool PF = false; };
 
 // LDS position of key kk within a block for the transposed V tile
 template <typename T> __device__ inline int vt_pos(int kk);
@@ -34,17 +36,25 @@ template <> __device__ inline int vt_pos<bf16>(int kk) {
 }
 template <> __device__ inline int vt_pos<float>(int kk) { return kk; }
 
+__device__ inline void pin4(uint4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int QB = AttnShape<T, HD>::QB;
   constexpr int NK = AttnShape<T, HD>::NK;
+  constexpr bool PF = AttnShape<T, HD>::PF;
   constexpr int NQ = 4 * QB * 16;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KP = HD + VEC;
   constexpr int VP = NK + VEC;
   constexpr int KS = HD / MF::KI;
+  constexpr int CPK = HD / VEC;                 // 16-byte chunks per key row
+  constexpr int CH = NK * CPK / 256;            // chunks of K (and of V) per thread per block
+  static_assert(NK * CPK % 256 == 0, "block/thread mismatch");
   __shared__ __attribute__((aligned(16))) T Ks[NK * KP];
   __shared__ __attribute__((aligned(16))) T Vt[HD * VP];
 
@@ -56,6 +66,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int i0 = qt * NQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const float c2 = a.scale_log2;   // scores are kept raw; exponents use s*c2 - m
 
   // prompt rows of this sequence, clamped against corrupt offsets
   const int pb = cb / a.canvas_per_prompt;
@@ -77,12 +88,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int64_t vb1 = vb0 + a.chunk < nkeys ? vb0 + a.chunk : nkeys;
   const int64_t ps = p0 + (vb0 < plen ? vb0 : plen);
   const int64_t pe = p0 + (vb1 < plen ? vb1 : plen);
-  const int64_t cs0 = lo + (vb0 > plen ? vb0 - plen : 0);
-  const int64_t cs1 = lo + (vb1 > plen ? vb1 - plen : 0);
+  const int cs0 = lo + (int)(vb0 > plen ? vb0 - plen : 0);
+  const int cs1 = lo + (int)(vb1 > plen ? vb1 - plen : 0);
+  const int np = pe > ps ? (int)((pe - ps + NK - 1) / NK) : 0;   // prompt blocks
+  const int nc = cs1 > cs0 ? (cs1 - cs0 + NK - 1) / NK : 0;     // canvas blocks
 
   const int64_t kv_stride = (int64_t)a.Hkv * HD;   // elements between consecutive keys
   const int64_t q_stride = (int64_t)a.Hq * HD;
   const T *qbase = static_cast<const T *>(a.q) + (int64_t)cb * C * q_stride + (int64_t)h * HD;
+  const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
+  const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
+  const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
+  const T *kc = static_cast<const T *>(a.k) + cbase;
+  const T *vc = static_cast<const T *>(a.v) + cbase;
 
   frag qf[QB][KS];
 #pragma unroll
@@ -107,32 +125,55 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) { mrun[jb] = -INFINITY; lrun[jb] = 0.f; }
 
-  auto block = [&](const T *kb, const T *vb, int64_t k0, int64_t kend, bool canvas) {
-    constexpr int CPK = HD / VEC;
-    // K: consecutive lanes take consecutive 16-byte chunks of a key row
-    for (int c = threadIdx.x; c < NK * CPK; c += 256) {
-      const int kk = c / CPK, cc = c % CPK;
-      const int64_t key = k0 + kk;
-      const bool ok = key < kend;
-      uint4 kc = *reinterpret_cast<const uint4 *>(kb + (ok ? key : k0) * kv_stride + cc * VEC);
-      if (!ok) kc = uint4{0, 0, 0, 0};
-      *reinterpret_cast<uint4 *>(Ks + kk * KP + cc * VEC) = kc;
+  // block b: prompt blocks first, then canvas-window blocks
+  struct Blk { const T *kb, *vb; int64_t k0; int rem; bool canvas; };
+  auto desc = [&](int b) {
+    Blk d;
+    if (b < np) {
+      d.kb = kp; d.vb = vp; d.k0 = ps + (int64_t)b * NK;
+      d.rem = (int)((pe - d.k0) < NK ? (pe - d.k0) : NK);
+      d.canvas = false;
+    } else {
+      d.kb = kc; d.vb = vc; d.k0 = cs0 + (int64_t)(b - np) * NK;
+      d.rem = (int)((cs1 - d.k0) < NK ? (cs1 - d.k0) : NK);
+      d.canvas = true;
     }
-    // V, transposed: consecutive lanes take consecutive keys of one chunk, so each
-    // element store writes neighbouring positions of one V^T row
-    for (int c = threadIdx.x; c < NK * CPK; c += 256) {
-      const int kk = c % NK, cc = c / NK;
-      const int64_t key = k0 + kk;
-      const bool ok = key < kend;
-      Chunk<T> vc;
-      vc.u = *reinterpret_cast<const uint4 *>(vb + (ok ? key : k0) * kv_stride + cc * VEC);
-      if (!ok) vc.u = uint4{0, 0, 0, 0};
-      const int pos = vt_pos<T>(kk);
+    return d;
+  };
+  // K chunk i of this thread: key c / CPK, chunk c % CPK (lanes along a row);
+  // V chunk i: key c % NK, chunk c / NK (lanes along keys, for the transposed store)
+  uint4 kr[CH], vr[CH];
+  auto fetch = [&](const Blk &d) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) Vt[(cc * VEC + e) * VP + pos] = vc.v[e];
+    for (int i = 0; i < CH; ++i) {
+      const int c = i * 256 + threadIdx.x;
+      const int kk = c / CPK, cc = c % CPK;
+      const int kv = c % NK, cv = c / NK;
+      kr[i] = *reinterpret_cast<const uint4 *>(d.kb + (d.k0 + (kk < d.rem ? kk : 0)) * kv_stride + cc * VEC);
+      vr[i] = *reinterpret_cast<const uint4 *>(d.vb + (d.k0 + (kv < d.rem ? kv : 0)) * kv_stride + cv * VEC);
     }
-    __syncthreads();
+  };
+  auto stage = [&](const Blk &d) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = i * 256 + threadIdx.x;
+      const int kk = c / CPK, cc = c % CPK;
+      const int kv = c % NK, cv = c / NK;
+      uint4 kx = kr[i], vx = vr[i];
+      pin4(kx);
+      pin4(vx);
+      if (kk >= d.rem) kx = uint4{0, 0, 0, 0};
+      if (kv >= d.rem) vx = uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4 *>(Ks + kk * KP + cc * VEC) = kx;
+      Chunk<T> vch;
+      vch.u = vx;
+      const int pos = vt_pos<T>(kv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Vt[(cv * VEC + e) * VP + pos] = vch.v[e];
+    }
+  };
 
+  auto compute = [&](const Blk &d) {
     f32x4 sacc[NK / 16][QB];
 #pragma unroll
     for (int kb2 = 0; kb2 < NK / 16; ++kb2)
@@ -148,25 +189,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] = MF::mma(af, qf[jb][ks], sacc[kb2][jb]);
       }
 
+    const bool full = !d.canvas && d.rem == NK;   // uniform: no key of the block is masked
 #pragma unroll
     for (int jb = 0; jb < QB; ++jb) {
-      const int qi = i0 + w * QB * 16 + jb * 16 + col;
+      if (!full) {
+        const int qi = i0 + w * QB * 16 + jb * 16 + col;
+        const int qrel = qi - (int)d.k0;            // canvas: |key - qi| <= W
+#pragma unroll
+        for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kl = kb2 * 16 + grp * 4 + r;
+            bool ok = kl < d.rem;
+            if (d.canvas) ok = ok && kl - qrel <= W && qrel - kl <= W;
+            if (!ok) sacc[kb2][jb][r] = -INFINITY;
+          }
+      }
       float bm = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t key = k0 + kb2 * 16 + grp * 4 + r;
-          bool ok = key < kend;
-          if (canvas) {
-            const int64_t dd = key - qi;
-            ok = ok && dd <= W && -dd <= W;
-          }
-          const float x = ok ? sacc[kb2][jb][r] * a.scale_log2 : -INFINITY;
-          sacc[kb2][jb][r] = x;
-          bm = fmaxf(bm, x);
-        }
-      bm = group4_max(bm);
+        for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sacc[kb2][jb][r]);
+      bm = group4_max(bm) * c2;
       const float mnew = fmaxf(mrun[jb], bm);
       const float msub = mnew == -INFINITY ? 0.f : mnew;
       const float alpha = exp2f(mrun[jb] - msub);
@@ -175,14 +219,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(sacc[kb2][jb][r] - msub);
+          const float p = exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
           sacc[kb2][jb][r] = p;
           ps_ += p;
         }
       lrun[jb] = lrun[jb] * alpha + ps_;
       mrun[jb] = mnew;
+      if (__any(alpha != 1.f)) {   // skip the rescale when no running max moved
 #pragma unroll
-      for (int rb = 0; rb < HD / 16; ++rb) oacc[rb][jb] *= alpha;
+        for (int rb = 0; rb < HD / 16; ++rb) oacc[rb][jb] *= alpha;
+      }
     }
 
     if constexpr (MF::KPL == 8) {
@@ -214,19 +260,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = MF::mma(af, sacc[kb2][jb][r], oacc[rb][jb]);
           }
     }
-    __syncthreads();
   };
 
-  {
-    const T *kb = static_cast<const T *>(a.kp) + (int64_t)g * HD;
-    const T *vb = static_cast<const T *>(a.vp) + (int64_t)g * HD;
-    for (int64_t k0 = ps; k0 < pe; k0 += NK) block(kb, vb, k0, pe, false);
-  }
-  if (cs1 > cs0) {
-    const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
-    const T *kb = static_cast<const T *>(a.k) + cbase;
-    const T *vb = static_cast<const T *>(a.v) + cbase;
-    for (int64_t k0 = cs0; k0 < cs1; k0 += NK) block(kb, vb, k0, cs1, true);
+  const int nb = np + nc;
+  if (nb > 0) fetch(desc(0));
+  for (int b = 0; b < nb; ++b) {
+    const Blk d = desc(b);
+    stage(d);
+    __syncthreads();
+    if (PF && b + 1 < nb) fetch(desc(b + 1));   // in flight during the MFMAs below
+    __builtin_amdgcn_sched_barrier(0);
+    compute(d);
+    __syncthreads();
+    if (!PF && b + 1 < nb) fetch(desc(b + 1));
   }
 
   const int64_t R = (int64_t)a.nc * a.Hq * C;
@@ -254,9 +300,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// fixed-order log-sum-exp merge of the split partials (scores are in log2 units)
+// Fixed-order log-sum-exp merge of the split partials (scores in log2 units).
+// One workgroup per output row: wave w folds splits w, w+4, ... in order, then
+// the four wave partials are combined in wave order.
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int PER = HD / 64;
+  __shared__ float sm[4], sl[4];
+  __shared__ float so[4][HD];
   const int64_t R = (int64_t)a.nc * a.Hq * a.C;
   const int64_t row = blockIdx.x;
   const int C = a.C;
@@ -265,29 +316,48 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   const int h = (int)(ch % a.Hq);
   const int64_t cb = ch / a.Hq;
   if (a.active && !a.active[cb]) return;
-  float mstar = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[(int64_t)s * R + row].x);
-  constexpr int PER = HD / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float m = -INFINITY;
+  for (int s = w; s < a.nsplit; s += 4) m = fmaxf(m, a.part_ml[(int64_t)s * R + row].x);
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float L = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float2 ml = a.part_ml[(int64_t)s * R + row];
-    if (ml.x == -INFINITY) continue;
-    const float wgt = exp2f(ml.x - mstar);
-    L += ml.y * wgt;
-    const float *po = a.part_o + ((int64_t)s * R + row) * HD;
+  if (m != -INFINITY) {
+#pragma unroll 4
+    for (int s = w; s < a.nsplit; s += 4) {
+      const float2 ml = a.part_ml[(int64_t)s * R + row];
+      const float wgt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - m);
+      L += ml.y * wgt;
+      const float *po = a.part_o + ((int64_t)s * R + row) * HD;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += po[threadIdx.x + 64 * e] * wgt;
+      for (int e = 0; e < PER; ++e) acc[e] += po[lane + 64 * e] * wgt;
+    }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (lane == 0) { sm[w] = m; sl[w] = L; }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) so[w][lane + 64 * e] = acc[e];
+  __syncthreads();
+  if (w != 0) return;
+  float mt = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float wq[4], Lt = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wq[q] = sm[q] == -INFINITY ? 0.f : exp2f(sm[q] - mt);
+    Lt += sl[q] * wq[q];
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
   T *o = static_cast<T *>(a.o) + ((cb * C + qi) * a.Hq + h) * HD;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[threadIdx.x + 64 * e] = from_f<T>(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v += so[q][lane + 64 * e] * wq[q];
+    o[lane + 64 * e] = from_f<T>(v * inv);
+  }
 }
 
-int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 256; }
+int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 128; }
 
 void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len, int *nsplit,
                int *chunk) {
@@ -318,7 +388,7 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * a.C;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)R), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)R), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
