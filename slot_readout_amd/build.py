@@ -30,6 +30,9 @@ def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
             # packed fp32 vector ops are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results stay in VGPRs (no AGPR round trips when the accumulators
+            # are also touched by vector ALU code, e.g. the softmax rescale)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-result"]
 
 

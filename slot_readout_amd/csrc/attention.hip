@@ -130,46 +130,55 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   auto desc = [&](int b) {
     Blk d;
     if (b < np) {
-      d.kb = kp; d.vb = vp; d.k0 = ps + (int64_t)b * NK;
+      d.k0 = ps + (int64_t)b * NK;
+      d.kb = kp + d.k0 * kv_stride;
+      d.vb = vp + d.k0 * kv_stride;
       d.rem = (int)((pe - d.k0) < NK ? (pe - d.k0) : NK);
       d.canvas = false;
     } else {
-      d.kb = kc; d.vb = vc; d.k0 = cs0 + (int64_t)(b - np) * NK;
+      d.k0 = cs0 + (int64_t)(b - np) * NK;
+      d.kb = kc + d.k0 * kv_stride;
+      d.vb = vc + d.k0 * kv_stride;
       d.rem = (int)((cs1 - d.k0) < NK ? (cs1 - d.k0) : NK);
       d.canvas = true;
     }
     return d;
   };
-  // K chunk i of this thread: key c / CPK, chunk c % CPK (lanes along a row);
-  // V chunk i: key c % NK, chunk c / NK (lanes along keys, for the transposed store)
+  // Per-thread chunk assignment, fixed for every block.  K chunk i: key c / CPK,
+  // chunk c % CPK (lanes along a row); V chunk i: key c % NK, chunk c / NK (lanes
+  // along keys, so the transposed element stores hit neighbouring positions).
+  int kkey[CH], vkey[CH], kgo[CH], vgo[CH], klo[CH], vlo[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = i * 256 + threadIdx.x;
+    kkey[i] = c / CPK;
+    vkey[i] = c % NK;
+    kgo[i] = kkey[i] * (int)kv_stride + (c % CPK) * VEC;
+    vgo[i] = vkey[i] * (int)kv_stride + (c / NK) * VEC;
+    klo[i] = kkey[i] * KP + (c % CPK) * VEC;
+    vlo[i] = (c / NK) * VEC * VP + vt_pos<T>(vkey[i]);
+  }
   uint4 kr[CH], vr[CH];
   auto fetch = [&](const Blk &d) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = i * 256 + threadIdx.x;
-      const int kk = c / CPK, cc = c % CPK;
-      const int kv = c % NK, cv = c / NK;
-      kr[i] = *reinterpret_cast<const uint4 *>(d.kb + (d.k0 + (kk < d.rem ? kk : 0)) * kv_stride + cc * VEC);
-      vr[i] = *reinterpret_cast<const uint4 *>(d.vb + (d.k0 + (kv < d.rem ? kv : 0)) * kv_stride + cv * VEC);
+      kr[i] = *reinterpret_cast<const uint4 *>(d.kb + (kkey[i] < d.rem ? kgo[i] : 0));
+      vr[i] = *reinterpret_cast<const uint4 *>(d.vb + (vkey[i] < d.rem ? vgo[i] : 0));
     }
   };
   auto stage = [&](const Blk &d) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = i * 256 + threadIdx.x;
-      const int kk = c / CPK, cc = c % CPK;
-      const int kv = c % NK, cv = c / NK;
       uint4 kx = kr[i], vx = vr[i];
       pin4(kx);
       pin4(vx);
-      if (kk >= d.rem) kx = uint4{0, 0, 0, 0};
-      if (kv >= d.rem) vx = uint4{0, 0, 0, 0};
-      *reinterpret_cast<uint4 *>(Ks + kk * KP + cc * VEC) = kx;
+      if (kkey[i] >= d.rem) kx = uint4{0, 0, 0, 0};
+      if (vkey[i] >= d.rem) vx = uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4 *>(Ks + klo[i]) = kx;
       Chunk<T> vch;
       vch.u = vx;
-      const int pos = vt_pos<T>(kv);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) Vt[(cv * VEC + e) * VP + pos] = vch.v[e];
+      for (int e = 0; e < VEC; ++e) Vt[vlo[i] + e * VP] = vch.v[e];
     }
   };
 
@@ -194,15 +203,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int jb = 0; jb < QB; ++jb) {
       if (!full) {
         const int qi = i0 + w * QB * 16 + jb * 16 + col;
-        const int qrel = qi - (int)d.k0;            // canvas: |key - qi| <= W
+        // canvas keys: visible iff |key - qi| <= W, i.e. kl in [qrel - W, qrel + W]
+        const int qrel = qi - (int)d.k0;
+        const int klo_ok = d.canvas ? qrel - W : -1;
+        const int khi_ok = d.canvas ? min(qrel + W, d.rem - 1) : d.rem - 1;
 #pragma unroll
         for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int kl = kb2 * 16 + grp * 4 + r;
-            bool ok = kl < d.rem;
-            if (d.canvas) ok = ok && kl - qrel <= W && qrel - kl <= W;
-            if (!ok) sacc[kb2][jb][r] = -INFINITY;
+            const bool ok = kl >= klo_ok && kl <= khi_ok;
+            sacc[kb2][jb][r] = ok ? sacc[kb2][jb][r] : -INFINITY;
           }
       }
       float bm = -INFINITY;
@@ -213,13 +224,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       bm = group4_max(bm) * c2;
       const float mnew = fmaxf(mrun[jb], bm);
       const float msub = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(mrun[jb] - msub);
+      // raw v_exp_f32: every argument here is <= 0, so no range handling is needed
+      const float alpha = __builtin_amdgcn_exp2f(mrun[jb] - msub);
       float ps_ = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
           sacc[kb2][jb][r] = p;
           ps_ += p;
         }
