@@ -11,30 +11,32 @@
 //
 // Inside a workgroup the 4 waves each own QB x 16 query columns.  Scores are
 // computed transposed, S^T = K Q^T, so that a lane holds one query column and
-// the running max / sum of that query stay in the lane (plus one exchange
-// across the four 16-lane groups).  P^T then feeds O^T += V^T P^T directly
-// from registers; V is staged in LDS transposed, its keys permuted so each
-// lane's 8 bf16 values of a fragment are contiguous.
+// the running max of that query stays in the lane (plus one exchange across
+// the four 16-lane groups).  P^T then feeds O^T += V^T P^T directly from
+// registers.  For bf16, K and V are both staged row-major in LDS from
+// coalesced loads; the V^T fragments come from transposing LDS reads
+// (ds_read_b64_tr_b16).  V carries an extra column of ones, so the same MFMA
+// also accumulates the softmax denominator sum_key p.
 #include "common.h"
 #include "kernels.h"
 
 namespace dg {
 
 template <typename T, int HD> struct AttnShape;
-// QB: 16-query column blocks per wave; NK: keys per LDS block; PF: prefetch the
-// next K/V block into registers while the current one is computed
-template <> struct AttnShape<bf16, 64> { static constexpr int QB = 2, NK = 64; static constexpr bool PF = true; };
-template <> struct AttnShape<float, 64> { static constexpr int QB = 2, NK = 64; static constexpr bool PF = true; };
-template <> struct AttnShape<bf16, 512> { static constexpr int QB = 1, NK = 32; static constexpr bool PF = false; };
+// QB: 16-query column blocks per wave; NK: keys per LDS block; PF: K/V blocks
+// whose global loads are in flight ahead of the one being computed (a ring of
+// register stages; 1 = load the next block only after the current one)
+template <> struct AttnShape<bf16, 64> { static constexpr int QB = 2, NK = 64, PF = 3; };
+template <> struct AttnShape<float, 64> { static constexpr int QB = 2, NK = 64, PF = 2; };
+template <> struct AttnShape<bf16, 512> { static constexpr int QB = 1, NK = 32, PF = 1; };
 
-// LDS position of key kk within a block for the transposed V tile
-template <typename T> __device__ inline int vt_pos(int kk);
-template <> __device__ inline int vt_pos<bf16>(int kk) {
-  const int t = kk >> 5, u = kk & 31;
-  const int uu = u & 15;
-  return (t << 5) + ((uu >> 2) << 3) + (u >= 16 ? 4 : 0) + (uu & 3);
+typedef short v4s __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each 16-lane group, output lane 4a+b element j is
+// element b of the 8 bytes addressed by source lane a+4j of the group
+__device__ inline v4s ds_read_tr16(const void *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s *)(p));
 }
-template <> __device__ inline int vt_pos<float>(int kk) { return kk; }
 
 __device__ inline void pin4(uint4 &v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   using frag = typename MF::frag;
   constexpr int QB = AttnShape<T, HD>::QB;
   constexpr int NK = AttnShape<T, HD>::NK;
-  constexpr bool PF = AttnShape<T, HD>::PF;
+  constexpr int PF = AttnShape<T, HD>::PF;
   constexpr int NQ = 4 * QB * 16;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KP = HD + VEC;
@@ -56,7 +58,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int CH = NK * CPK / 256;            // chunks of K (and of V) per thread per block
   static_assert(NK * CPK % 256 == 0, "block/thread mismatch");
   __shared__ __attribute__((aligned(16))) T Ks[NK * KP];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * VP];
+  // V plus one extra 16-wide block whose first element is 1: the PV MFMA then
+  // also yields sum_key p (the softmax denominator).  bf16: V row-major [NK][VKP]
+  // read through transposing LDS reads; fp32: V^T [RB*16][VP] staged element-wise.
+  constexpr int RB = HD / 16 + 1;
+  constexpr bool TR = sizeof(T) == 2;
+  constexpr int VKP = HD + 16 + VEC;
+  constexpr int VSZ = TR ? NK * VKP : RB * 16 * VP;
+  __shared__ __attribute__((aligned(16))) T Vt[VSZ];
 
   const int s = blockIdx.x, qt = blockIdx.y;
   const int cb = blockIdx.z / a.Hq, h = blockIdx.z % a.Hq;
@@ -116,14 +125,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  f32x4 oacc[HD / 16][QB];
+  f32x4 oacc[RB][QB];
 #pragma unroll
-  for (int rb = 0; rb < HD / 16; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = zero4();
-  float mrun[QB], lrun[QB];
+  float mrun[QB];
 #pragma unroll
-  for (int jb = 0; jb < QB; ++jb) { mrun[jb] = -INFINITY; lrun[jb] = 0.f; }
+  for (int jb = 0; jb < QB; ++jb) mrun[jb] = -INFINITY;
+  if constexpr (TR) {
+    for (int i = threadIdx.x; i < NK * 16; i += 256)
+      Vt[(i / 16) * VKP + HD + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
+  } else {
+    for (int i = threadIdx.x; i < 16 * VP; i += 256)
+      Vt[HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
+  }
 
   // block b: prompt blocks first, then canvas-window blocks
   struct Blk { const T *kb, *vb; int64_t k0; int rem; bool canvas; };
@@ -145,40 +161,51 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     return d;
   };
   // Per-thread chunk assignment, fixed for every block.  K chunk i: key c / CPK,
-  // chunk c % CPK (lanes along a row); V chunk i: key c % NK, chunk c / NK (lanes
-  // along keys, so the transposed element stores hit neighbouring positions).
+  // chunk c % CPK (lanes along a row).  bf16 V is loaded the same way; fp32 V
+  // takes key c % NK, chunk c / NK (lanes along keys, so the element-wise
+  // transposed stores hit neighbouring positions).
   int kkey[CH], vkey[CH], kgo[CH], vgo[CH], klo[CH], vlo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = i * 256 + threadIdx.x;
     kkey[i] = c / CPK;
-    vkey[i] = c % NK;
     kgo[i] = kkey[i] * (int)kv_stride + (c % CPK) * VEC;
-    vgo[i] = vkey[i] * (int)kv_stride + (c / NK) * VEC;
     klo[i] = kkey[i] * KP + (c % CPK) * VEC;
-    vlo[i] = (c / NK) * VEC * VP + vt_pos<T>(vkey[i]);
+    if constexpr (TR) {   // V row-major, same coalesced pattern as K
+      vkey[i] = kkey[i];
+      vgo[i] = kgo[i];
+      vlo[i] = kkey[i] * VKP + (c % CPK) * VEC;
+    } else {
+      vkey[i] = c % NK;
+      vgo[i] = vkey[i] * (int)kv_stride + (c / NK) * VEC;
+      vlo[i] = (c / NK) * VEC * VP + vkey[i];
+    }
   }
-  uint4 kr[CH], vr[CH];
-  auto fetch = [&](const Blk &d) {
+  uint4 kr[PF][CH], vr[PF][CH];
+  auto fetch = [&](const Blk &d, uint4 (&xk)[CH], uint4 (&xv)[CH]) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      kr[i] = *reinterpret_cast<const uint4 *>(d.kb + (kkey[i] < d.rem ? kgo[i] : 0));
-      vr[i] = *reinterpret_cast<const uint4 *>(d.vb + (vkey[i] < d.rem ? vgo[i] : 0));
+      xk[i] = *reinterpret_cast<const uint4 *>(d.kb + (kkey[i] < d.rem ? kgo[i] : 0));
+      xv[i] = *reinterpret_cast<const uint4 *>(d.vb + (vkey[i] < d.rem ? vgo[i] : 0));
     }
   };
-  auto stage = [&](const Blk &d) {
+  auto stage = [&](const Blk &d, const uint4 (&xk)[CH], const uint4 (&xv)[CH]) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      uint4 kx = kr[i], vx = vr[i];
+      uint4 kx = xk[i], vx = xv[i];
       pin4(kx);
       pin4(vx);
       if (kkey[i] >= d.rem) kx = uint4{0, 0, 0, 0};
       if (vkey[i] >= d.rem) vx = uint4{0, 0, 0, 0};
       *reinterpret_cast<uint4 *>(Ks + klo[i]) = kx;
-      Chunk<T> vch;
-      vch.u = vx;
+      if constexpr (TR) {
+        *reinterpret_cast<uint4 *>(Vt + vlo[i]) = vx;
+      } else {
+        Chunk<T> vch;
+        vch.u = vx;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) Vt[vlo[i] + e * VP] = vch.v[e];
+        for (int e = 0; e < VEC; ++e) Vt[vlo[i] + e * VP] = vch.v[e];
+      }
     }
   };
 
@@ -226,20 +253,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const float msub = mnew == -INFINITY ? 0.f : mnew;
       // raw v_exp_f32: every argument here is <= 0, so no range handling is needed
       const float alpha = __builtin_amdgcn_exp2f(mrun[jb] - msub);
-      float ps_ = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
-          sacc[kb2][jb][r] = p;
-          ps_ += p;
-        }
-      lrun[jb] = lrun[jb] * alpha + ps_;
+        for (int r = 0; r < 4; ++r)
+          sacc[kb2][jb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
       mrun[jb] = mnew;
       if (__any(alpha != 1.f)) {   // skip the rescale when no running max moved
 #pragma unroll
-        for (int rb = 0; rb < HD / 16; ++rb) oacc[rb][jb] *= alpha;
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][jb] *= alpha;
       }
     }
 
@@ -255,8 +277,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             pf[4 + j] = (bf16)sacc[2 * t + 1][jb][j];
           }
 #pragma unroll
-          for (int rb = 0; rb < HD / 16; ++rb) {
-            const frag af = *reinterpret_cast<const frag *>(Vt + (rb * 16 + col) * VP + t * 32 + grp * 8);
+          for (int rb = 0; rb < RB; ++rb) {
+            // A = V^T block: lane (col=d, grp) needs keys 32t+4grp+0..3 and
+            // 32t+16+4grp+0..3 for d = rb*16 + col.  A transposing read where
+            // source lane s of the group points at V[key0 + s/4][d0 + 4(s%4)]
+            // returns V[key0 + 0..3][d0 + lane%16] in each lane.
+            const T *src0 = Vt + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
+            const v4s lo4 = ds_read_tr16(src0);
+            const v4s hi4 = ds_read_tr16(src0 + 16 * VKP);
+            frag af;
+            __builtin_memcpy(&af, &lo4, 8);
+            __builtin_memcpy(reinterpret_cast<char *>(&af) + 8, &hi4, 8);
             oacc[rb][jb] = MF::mma(af, pf, oacc[rb][jb]);
           }
         }
@@ -266,7 +297,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int rb = 0; rb < HD / 16; ++rb) {
+          for (int rb = 0; rb < RB; ++rb) {
             const frag af = Vt[(rb * 16 + col) * VP + kb2 * 16 + grp * 4 + r];
 #pragma unroll
             for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = MF::mma(af, sacc[kb2][jb][r], oacc[rb][jb]);
@@ -274,24 +305,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   };
 
+  // Blocks are processed in groups of PF so every ring slot index is a
+  // compile-time constant: slot j holds block b0+j; once it is staged into LDS
+  // it is refilled with block b0+j+PF, which stays in flight for PF blocks.
   const int nb = np + nc;
-  if (nb > 0) fetch(desc(0));
-  for (int b = 0; b < nb; ++b) {
-    const Blk d = desc(b);
-    stage(d);
-    __syncthreads();
-    if (PF && b + 1 < nb) fetch(desc(b + 1));   // in flight during the MFMAs below
-    __builtin_amdgcn_sched_barrier(0);
-    compute(d);
-    __syncthreads();
-    if (!PF && b + 1 < nb) fetch(desc(b + 1));
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (j < nb) fetch(desc(j), kr[j], vr[j]);
+  for (int b0 = 0; b0 < nb; b0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int b = b0 + j;
+      if (b < nb) {
+        const Blk d = desc(b);
+        stage(d, kr[j], vr[j]);
+        __syncthreads();
+        if (b + PF < nb) fetch(desc(b + PF), kr[j], vr[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(d);
+        __syncthreads();
+      }
+    }
   }
 
   const int64_t R = (int64_t)a.nc * a.Hq * C;
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int qi = i0 + w * QB * 16 + jb * 16 + col;
-    const float L = group4_sum(lrun[jb]);
+    const float L = group4_sum(grp == 0 ? oacc[HD / 16][jb][0] : 0.f);
     if (qi >= C) continue;
     if (a.nsplit == 1) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -378,9 +419,12 @@ void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len,
   const int64_t base = (int64_t)nc * Hq * cdiv64(C, nq);
   // most keys one query tile can see: the prompt plus its window span
   const int64_t span = (int64_t)max_len + (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
+  // about two workgroups per CU; the K/V loads of a workgroup run several blocks
+  // ahead (register ring), so longer chains do not stall on memory latency
+  constexpr int kTargetWorkgroups = 512;
   int ns = 1;
-  if (base < 512) {
-    ns = (int)cdiv64(512, base);
+  if (base < kTargetWorkgroups) {
+    ns = (int)cdiv64(kTargetWorkgroups, base);
     const int64_t maxs = cdiv64(span, 4 * nk);   // keep at least ~4 key blocks per split
     if (ns > maxs) ns = (int)maxs;
     if (ns < 1) ns = 1;
