@@ -134,7 +134,7 @@ def main():
                     help="bf16_step (default) times step + commit + slot read; long_read and "
                          "ragged32 time step + commit and report the attention stage")
     ap.add_argument("--cold", action="store_true",
-                    help="evict the caches (write 1 GiB) before every timed step; the default "
+                    help="evict the caches (read 1 GiB) before every timed step; the default "
                          "for long_read, whose prompt KV would otherwise sit in the 256 MB MALL")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -171,12 +171,17 @@ def main():
     stage_ev = Events(hip, n_st * K)
     dbg_per_step = [dg.make_debug(stage_events=stage_ev.sub(k * n_st)) for k in range(K)]
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0") if cold else None
+    flush = None
+    if cold:
+        # a read sweep of 1 GiB evicts L2 and the 256 MB MALL without leaving dirty
+        # lines behind, whose write-back would otherwise compete with the timed reads
+        flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda:0")
+        torch.cuda.synchronize()
 
     def one_step(k=None):
         dbg = dbg_per_step[k] if k is not None else None
         if flush is not None:
-            flush.fill_(k if k is not None else 0)      # evicts L2 and the MALL (1 GiB of writes)
+            torch.amax(flush)
         if k is not None:
             marks.record(4 * k, stream)
         dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, B, dev.canvas_ids, None,

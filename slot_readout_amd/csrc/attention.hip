@@ -23,12 +23,13 @@
 namespace dg {
 
 template <typename T, int HD> struct AttnShape;
-// QB: 16-query column blocks per wave; NK: keys per LDS block; PF: K/V blocks
-// whose global loads are in flight ahead of the one being computed (a ring of
-// register stages; 1 = load the next block only after the current one)
-template <> struct AttnShape<bf16, 64> { static constexpr int QB = 2, NK = 64, PF = 3; };
-template <> struct AttnShape<float, 64> { static constexpr int QB = 2, NK = 64, PF = 2; };
-template <> struct AttnShape<bf16, 512> { static constexpr int QB = 1, NK = 32, PF = 1; };
+// NW: waves per workgroup; QB: 16-query column blocks per wave; NK: keys per
+// LDS block; PF: K/V blocks whose global loads are in flight ahead of the one
+// being computed (a ring of register stages; 1 = load the next block only
+// after the current one)
+template <> struct AttnShape<bf16, 64> { static constexpr int NW = 8, QB = 1, NK = 64, PF = 2; };
+template <> struct AttnShape<float, 64> { static constexpr int NW = 4, QB = 2, NK = 64, PF = 2; };
+template <> struct AttnShape<bf16, 512> { static constexpr int NW = 4, QB = 1, NK = 32, PF = 1; };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 // ds_read_b64_tr_b16: within each 16-lane group, output lane 4a+b element j is
@@ -43,29 +44,36 @@ __device__ inline void pin4(uint4 &v) {
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int QB = AttnShape<T, HD>::QB;
   constexpr int NK = AttnShape<T, HD>::NK;
   constexpr int PF = AttnShape<T, HD>::PF;
-  constexpr int NQ = 4 * QB * 16;
+  constexpr int NW = AttnShape<T, HD>::NW;
+  constexpr int NT = 64 * NW;
+  constexpr int NQ = NW * QB * 16;
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int KP = HD + VEC;
+  constexpr bool TR = sizeof(T) == 2;
+  // bf16 rows of K and V are HD + 16 elements apart: with that stride both the
+  // 16-byte K fragment reads and the transposing V reads are free of LDS bank
+  // conflicts (measured on gfx950; a 16-byte pad leaves 2-way conflicts)
+  constexpr int KP = TR ? HD + 16 : HD + VEC;
   constexpr int VP = NK + VEC;
   constexpr int KS = HD / MF::KI;
   constexpr int CPK = HD / VEC;                 // 16-byte chunks per key row
-  constexpr int CH = NK * CPK / 256;            // chunks of K (and of V) per thread per block
-  static_assert(NK * CPK % 256 == 0, "block/thread mismatch");
-  __shared__ __attribute__((aligned(16))) T Ks[NK * KP];
+  constexpr int CH = NK * CPK / NT;             // chunks of K (and of V) per thread per block
+  static_assert(NK * CPK % NT == 0, "block/thread mismatch");
+  // K and V tiles are double-buffered: block b lives in buffer b % 2, so the
+  // next block can be staged while the current one is read, one barrier apart
+  __shared__ __attribute__((aligned(16))) T Ks[2][NK * KP];
   // V plus one extra 16-wide block whose first element is 1: the PV MFMA then
   // also yields sum_key p (the softmax denominator).  bf16: V row-major [NK][VKP]
   // read through transposing LDS reads; fp32: V^T [RB*16][VP] staged element-wise.
   constexpr int RB = HD / 16 + 1;
-  constexpr bool TR = sizeof(T) == 2;
-  constexpr int VKP = HD + 16 + VEC;
+  constexpr int VKP = HD + 16;
   constexpr int VSZ = TR ? NK * VKP : RB * 16 * VP;
-  __shared__ __attribute__((aligned(16))) T Vt[VSZ];
+  __shared__ __attribute__((aligned(16))) T Vt[2][VSZ];
 
   const int s = blockIdx.x, qt = blockIdx.y;
   const int cb = blockIdx.z / a.Hq, h = blockIdx.z % a.Hq;
@@ -124,6 +132,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         qf[jb][ks] = frag{};
     }
   }
+  // Q is complete before the K/V ring starts: otherwise the wait for the Q
+  // loads inside the loop would also drain every ring load issued after them
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint32_t *u = reinterpret_cast<uint32_t *>(&qf[jb][ks]);
+#pragma unroll
+      for (int e = 0; e < (int)(sizeof(frag) / 4); ++e) asm volatile("" : "+v"(u[e]));
+    }
 
   f32x4 oacc[RB][QB];
 #pragma unroll
@@ -133,29 +151,47 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   float mrun[QB];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) mrun[jb] = -INFINITY;
-  if constexpr (TR) {
-    for (int i = threadIdx.x; i < NK * 16; i += 256)
-      Vt[(i / 16) * VKP + HD + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
-  } else {
-    for (int i = threadIdx.x; i < 16 * VP; i += 256)
-      Vt[HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
+#pragma unroll
+  for (int bf = 0; bf < 2; ++bf) {
+    if constexpr (TR) {
+      for (int i = threadIdx.x; i < NK * 16; i += NT)
+        Vt[bf][(i / 16) * VKP + HD + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
+    } else {
+      for (int i = threadIdx.x; i < 16 * VP; i += NT)
+        Vt[bf][HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
+    }
   }
 
-  // block b: prompt blocks first, then canvas-window blocks
-  struct Blk { const T *kb, *vb; int64_t k0; int rem; bool canvas; };
+  // block b: prompt blocks first, then canvas-window blocks; b >= nb names an
+  // empty block (every lane loads the first canvas key, and nothing is used)
+  const int nb = np + nc;
+  const int64_t bstride = (int64_t)NK * kv_stride;   // elements between consecutive blocks
+  const T *kp0 = kp + ps * kv_stride, *vp0 = vp + ps * kv_stride;
+  const T *kc0 = kc + (int64_t)cs0 * kv_stride, *vc0 = vc + (int64_t)cs0 * kv_stride;
+  const int prem = (int)(pe - ps), crem = cs1 - cs0;   // prompt / canvas keys of the split
+  // Blocks are read through buffer resources whose size covers only the block's
+  // valid keys: loads of rows past the end return zeros without touching memory.
+  struct Blk { const T *kb, *vb; int k0; int rem; bool canvas; };
   auto desc = [&](int b) {
     Blk d;
-    if (b < np) {
-      d.k0 = ps + (int64_t)b * NK;
-      d.kb = kp + d.k0 * kv_stride;
-      d.vb = vp + d.k0 * kv_stride;
-      d.rem = (int)((pe - d.k0) < NK ? (pe - d.k0) : NK);
+    if (b >= nb) {
+      d.k0 = 0;
+      d.kb = kc;
+      d.vb = vc;
+      d.rem = 0;
+      d.canvas = true;
+    } else if (b < np) {
+      d.k0 = 0;   // prompt keys are visible to every query: no position needed
+      d.kb = kp0 + b * bstride;
+      d.vb = vp0 + b * bstride;
+      d.rem = min(prem - b * NK, NK);
       d.canvas = false;
     } else {
-      d.k0 = cs0 + (int64_t)(b - np) * NK;
-      d.kb = kc + d.k0 * kv_stride;
-      d.vb = vc + d.k0 * kv_stride;
-      d.rem = (int)((cs1 - d.k0) < NK ? (cs1 - d.k0) : NK);
+      const int bc = b - np;
+      d.k0 = cs0 + bc * NK;
+      d.kb = kc0 + bc * bstride;
+      d.vb = vc0 + bc * bstride;
+      d.rem = min(crem - bc * NK, NK);
       d.canvas = true;
     }
     return d;
@@ -167,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   int kkey[CH], vkey[CH], kgo[CH], vgo[CH], klo[CH], vlo[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = i * 256 + threadIdx.x;
+    const int c = i * NT + threadIdx.x;
     kkey[i] = c / CPK;
     kgo[i] = kkey[i] * (int)kv_stride + (c % CPK) * VEC;
     klo[i] = kkey[i] * KP + (c % CPK) * VEC;
@@ -181,35 +217,37 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       vlo[i] = (c / NK) * VEC * VP + vkey[i];
     }
   }
-  uint4 kr[PF][CH], vr[PF][CH];
-  auto fetch = [&](const Blk &d, uint4 (&xk)[CH], uint4 (&xv)[CH]) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 kr[PF][CH], vr[PF][CH];
+  auto fetch = [&](const Blk &d, u32x4 (&xk)[CH], u32x4 (&xv)[CH]) {
+    const int nbytes = d.rem * (int)kv_stride * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(d.kb), (short)0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(d.vb), (short)0, nbytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      xk[i] = *reinterpret_cast<const uint4 *>(d.kb + (kkey[i] < d.rem ? kgo[i] : 0));
-      xv[i] = *reinterpret_cast<const uint4 *>(d.vb + (vkey[i] < d.rem ? vgo[i] : 0));
+      xk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, kgo[i] * (int)sizeof(T), 0, 0);
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vgo[i] * (int)sizeof(T), 0, 0);
     }
   };
-  auto stage = [&](const Blk &d, const uint4 (&xk)[CH], const uint4 (&xv)[CH]) {
+  auto stage = [&](const u32x4 (&xk)[CH], const u32x4 (&xv)[CH], int bf) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      uint4 kx = xk[i], vx = xv[i];
+      uint4 kx{xk[i].x, xk[i].y, xk[i].z, xk[i].w}, vx{xv[i].x, xv[i].y, xv[i].z, xv[i].w};
       pin4(kx);
       pin4(vx);
-      if (kkey[i] >= d.rem) kx = uint4{0, 0, 0, 0};
-      if (vkey[i] >= d.rem) vx = uint4{0, 0, 0, 0};
-      *reinterpret_cast<uint4 *>(Ks + klo[i]) = kx;
+      *reinterpret_cast<uint4 *>(Ks[bf] + klo[i]) = kx;
       if constexpr (TR) {
-        *reinterpret_cast<uint4 *>(Vt + vlo[i]) = vx;
+        *reinterpret_cast<uint4 *>(Vt[bf] + vlo[i]) = vx;
       } else {
         Chunk<T> vch;
         vch.u = vx;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) Vt[vlo[i] + e * VP] = vch.v[e];
+        for (int e = 0; e < VEC; ++e) Vt[bf][vlo[i] + e * VP] = vch.v[e];
       }
     }
   };
 
-  auto compute = [&](const Blk &d) {
+  auto compute = [&](const Blk &d, int bf) {
     f32x4 sacc[NK / 16][QB];
 #pragma unroll
     for (int kb2 = 0; kb2 < NK / 16; ++kb2)
@@ -219,7 +257,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2) {
-        const frag af = *reinterpret_cast<const frag *>(Ks + (kb2 * 16 + col) * KP + ks * MF::KI +
+        const frag af = *reinterpret_cast<const frag *>(Ks[bf] + (kb2 * 16 + col) * KP + ks * MF::KI +
                                                          grp * MF::KPL);
 #pragma unroll
         for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] = MF::mma(af, qf[jb][ks], sacc[kb2][jb]);
@@ -231,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       if (!full) {
         const int qi = i0 + w * QB * 16 + jb * 16 + col;
         // canvas keys: visible iff |key - qi| <= W, i.e. kl in [qrel - W, qrel + W]
-        const int qrel = qi - (int)d.k0;
+        const int qrel = qi - d.k0;
         const int klo_ok = d.canvas ? qrel - W : -1;
         const int khi_ok = d.canvas ? min(qrel + W, d.rem - 1) : d.rem - 1;
 #pragma unroll
@@ -282,7 +320,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             // 32t+16+4grp+0..3 for d = rb*16 + col.  A transposing read where
             // source lane s of the group points at V[key0 + s/4][d0 + 4(s%4)]
             // returns V[key0 + 0..3][d0 + lane%16] in each lane.
-            const T *src0 = Vt + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
+            const T *src0 = Vt[bf] + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
             const v4s lo4 = ds_read_tr16(src0);
             const v4s hi4 = ds_read_tr16(src0 + 16 * VKP);
             frag af;
@@ -298,33 +336,48 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const frag af = Vt[(rb * 16 + col) * VP + kb2 * 16 + grp * 4 + r];
+            const frag af = Vt[bf][(rb * 16 + col) * VP + kb2 * 16 + grp * 4 + r];
 #pragma unroll
             for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = MF::mma(af, sacc[kb2][jb][r], oacc[rb][jb]);
           }
     }
   };
 
-  // Blocks are processed in groups of PF so every ring slot index is a
-  // compile-time constant: slot j holds block b0+j; once it is staged into LDS
-  // it is refilled with block b0+j+PF, which stays in flight for PF blocks.
-  const int nb = np + nc;
+  // Pipeline: block b is computed from LDS buffer b % 2 while block b+1 is
+  // written into the other buffer from its register slot, (b+1) % PF, which is
+  // then refilled with block b+1+PF; one barrier per block separates the two.
+  // The loop is unrolled by U = lcm(PF, 2) so every slot and buffer index is a
+  // compile-time constant.  Inside the main loop slots are refilled
+  // unconditionally (past the end, with the empty block), so the loads retire
+  // in issue order and each stage waits only for its own slot.
+  constexpr int U = PF % 2 == 0 ? PF : 2 * PF;
+  if (nb > 0) {
 #pragma unroll
-  for (int j = 0; j < PF; ++j)
-    if (j < nb) fetch(desc(j), kr[j], vr[j]);
-  for (int b0 = 0; b0 < nb; b0 += PF) {
+    for (int j = 0; j < PF; ++j) fetch(desc(j), kr[j], vr[j]);
+    stage(kr[0], vr[0], 0);
+    fetch(desc(PF), kr[0], vr[0]);
+    __syncthreads();
+  }
+  int b0 = 0;
+  for (; b0 + U <= nb; b0 += U) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
+    for (int j = 0; j < U; ++j) {
       const int b = b0 + j;
-      if (b < nb) {
-        const Blk d = desc(b);
-        stage(d, kr[j], vr[j]);
-        __syncthreads();
-        if (b + PF < nb) fetch(desc(b + PF), kr[j], vr[j]);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(d);
-        __syncthreads();
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(desc(b), j % 2);
+      const int sl = (j + 1) % PF;
+      stage(kr[sl], vr[sl], (j + 1) % 2);
+      fetch(desc(b + 1 + PF), kr[sl], vr[sl]);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < U - 1; ++j) {   // fewer than U blocks remain
+    if (b0 + j < nb) {
+      compute(desc(b0 + j), j % 2);
+      const int sl = (j + 1) % PF;
+      if (b0 + j + 1 < nb) stage(kr[sl], vr[sl], (j + 1) % 2);
+      __syncthreads();
     }
   }
 
@@ -411,6 +464,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 }
 
 int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 128; }
+static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
+              AttnShape<float, 64>::NW * AttnShape<float, 64>::QB * 16 == 128 &&
+              AttnShape<bf16, 512>::NW * AttnShape<bf16, 512>::QB * 16 == 64,
+              "query tile sizes");
 
 void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len, int *nsplit,
                int *chunk) {
@@ -438,9 +495,10 @@ void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len,
 
 template <typename T, int HD>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-  constexpr int NQ = 4 * AttnShape<T, HD>::QB * 16;
+  constexpr int NW = AttnShape<T, HD>::NW;
+  constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
   dim3 grid((unsigned)a.nsplit, (unsigned)cdiv64(a.C, NQ), (unsigned)(a.nc * a.Hq));
-  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * a.C;

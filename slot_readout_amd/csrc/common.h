@@ -69,15 +69,34 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 // reduce across the four 16-lane groups that hold the same MFMA column
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap moves: permlane16_swap(x, x) leaves x of rows {0,0,2,2}
+// in one result and of rows {1,1,3,3} in the other; permlane32_swap(x, x) leaves
+// rows {0,1,0,1} and {2,3,2,3}.  Every lane combines the same operands in the
+// same order, so all four rows hold bitwise identical results.
+__device__ inline float row_swap16(float v, float *other) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *other = __uint_as_float(r[1]);
+  return __uint_as_float(r[0]);
+}
+__device__ inline float row_swap32(float v, float *other) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *other = __uint_as_float(r[1]);
+  return __uint_as_float(r[0]);
+}
 __device__ inline float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float b;
+  float a = row_swap16(v, &b);
+  v = fmaxf(a, b);
+  a = row_swap32(v, &b);
+  return fmaxf(a, b);
 }
 __device__ inline float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float b;
+  float a = row_swap16(v, &b);
+  v = a + b;
+  a = row_swap32(v, &b);
+  return a + b;
 }
 
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
