@@ -43,6 +43,29 @@ __device__ inline void pin4(uint4 &v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
+constexpr float kLazy = 8.f;
+
+// Keys of the query tile starting at canvas position i0 of canvas cb, in the
+// order the splits cut them: every prompt key of the canvas's sequence (rows
+// [p0, p0 + plen) of the cache, offsets clamped against corrupt cu_seqlens, in
+// which case true is returned), then the canvas keys [lo, hi) that the tile's
+// +-W window can reach.
+__device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int64_t *p0o,
+                                 int64_t *plen, int *lo, int *hi) {
+  const int pb = cb / a.canvas_per_prompt;
+  int64_t p0 = a.cu[pb], p1 = a.cu[pb + 1];
+  bool bad = false;
+  if (p0 < 0) { p0 = 0; bad = true; }
+  if (p1 > a.total_len) { p1 = a.total_len; bad = true; }
+  if (p1 < p0) { p1 = p0; bad = true; }
+  if (p1 - p0 > a.max_len) { p1 = p0 + a.max_len; bad = true; }
+  *p0o = p0;
+  *plen = p1 - p0;
+  *lo = i0 - a.W > 0 ? i0 - a.W : 0;
+  *hi = i0 + nq + a.W < a.C ? i0 + nq + a.W : a.C;   // exclusive
+  return bad;
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
@@ -85,23 +108,16 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const int col = lane & 15, grp = lane >> 4;
   const float c2 = a.scale_log2;   // scores are kept raw; exponents use s*c2 - m
 
-  // prompt rows of this sequence, clamped against corrupt offsets
-  const int pb = cb / a.canvas_per_prompt;
-  int64_t p0 = a.cu[pb], p1 = a.cu[pb + 1];
-  bool bad = false;
-  if (p0 < 0) { p0 = 0; bad = true; }
-  if (p1 > a.total_len) { p1 = a.total_len; bad = true; }
-  if (p1 < p0) { p1 = p0; bad = true; }
-  if (p1 - p0 > a.max_len) { p1 = p0 + a.max_len; bad = true; }
+  int64_t p0, plen;
+  int lo, hi;
+  const bool bad = tile_keys(a, cb, i0, NQ, &p0, &plen, &lo, &hi);
   if (bad && a.flags && threadIdx.x == 0 && s == 0 && qt == 0 && h == 0)
     atomicOr(a.flags, DG_FLAG_BAD_SEQLENS);
-  const int64_t plen = p1 - p0;
-  // keys of this query tile, in order: every prompt key, then the canvas keys
-  // [lo, hi) that the tile's window can reach; split s takes an equal slice
-  const int lo = i0 - W > 0 ? i0 - W : 0;
-  const int hi = i0 + NQ + W < C ? i0 + NQ + W : C;   // exclusive
   const int64_t nkeys = plen + (hi - lo);
   const int64_t vb0 = (int64_t)s * a.chunk;
+  // splits past this tile's keys (shorter prompts of a ragged batch) have
+  // nothing to do; the merge reads only the splits that hold keys
+  if (vb0 >= nkeys && a.nsplit > 1) return;
   const int64_t vb1 = vb0 + a.chunk < nkeys ? vb0 + a.chunk : nkeys;
   const int64_t ps = p0 + (vb0 < plen ? vb0 : plen);
   const int64_t pe = p0 + (vb1 < plen ? vb1 : plen);
@@ -287,17 +303,23 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 #pragma unroll
         for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sacc[kb2][jb][r]);
       bm = group4_max(bm) * c2;
-      const float mnew = fmaxf(mrun[jb], bm);
+      // The reference max is raised only when the block's max exceeds it by
+      // more than kLazy (log2 units); until then the exponentials stay below
+      // 2^kLazy and nothing is rescaled.  The sum of p (the ones row) shares the
+      // reference, so the normalised result does not depend on it.
+      const bool grow = bm > mrun[jb] + kLazy;
+      const float mnew = grow ? bm : mrun[jb];
       const float msub = mnew == -INFINITY ? 0.f : mnew;
-      // raw v_exp_f32: every argument here is <= 0, so no range handling is needed
-      const float alpha = __builtin_amdgcn_exp2f(mrun[jb] - msub);
+      // raw v_exp_f32: every argument here is <= kLazy or -inf, so no range
+      // handling is needed
+      const float alpha = grow ? __builtin_amdgcn_exp2f(mrun[jb] - msub) : 1.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           sacc[kb2][jb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
       mrun[jb] = mnew;
-      if (__any(alpha != 1.f)) {   // skip the rescale when no running max moved
+      if (__any(grow)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) oacc[rb][jb] *= alpha;
       }
@@ -407,59 +429,85 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 }
 
 // Fixed-order log-sum-exp merge of the split partials (scores in log2 units).
-// One workgroup per output row: wave w folds splits w, w+4, ... in order, then
-// the four wave partials are combined in wave order.
+// One wave per output row, over the splits that hold keys of the row's query
+// tile.  Pass 1 takes the maximum of the split maxima; pass 2 sums the weighted
+// partials.  For HD = 64 a split's row is 16 float4 chunks, so the wave reads
+// four splits per load (lane group g = lane / 16 takes splits g, g+4, ...) and
+// the groups are added by a fixed butterfly; wider heads take one split per load.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int PER = HD / 64;
-  __shared__ float sm[4], sl[4];
-  __shared__ float so[4][HD];
+  constexpr int C4 = HD / 4;                     // float4 chunks per row
+  constexpr int SG = C4 >= 64 ? 1 : 64 / C4;     // splits read side by side
+  constexpr int CPL = C4 >= 64 ? C4 / 64 : 1;    // chunks per lane
+  constexpr int NQ = AttnShape<T, HD>::NW * AttnShape<T, HD>::QB * 16;
   const int64_t R = (int64_t)a.nc * a.Hq * a.C;
-  const int64_t row = blockIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
   const int C = a.C;
   const int qi = (int)(row % C);
   const int64_t ch = row / C;
   const int h = (int)(ch % a.Hq);
   const int64_t cb = ch / a.Hq;
   if (a.active && !a.active[cb]) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float m = -INFINITY;
-  for (int s = w; s < a.nsplit; s += 4) m = fmaxf(m, a.part_ml[(int64_t)s * R + row].x);
-  float acc[PER];
+  const int lane = threadIdx.x & 63;
+  const int g = SG > 1 ? lane / C4 : 0;
+  const int c0 = SG > 1 ? lane % C4 : lane;
+  int64_t p0, plen;
+  int lo, hi;
+  tile_keys(a, (int)cb, qi / NQ * NQ, NQ, &p0, &plen, &lo, &hi);
+  const int64_t nk = plen + (hi - lo);
+  const int ns = (int)(cdiv64(nk, a.chunk) < a.nsplit ? cdiv64(nk, a.chunk) : a.nsplit);
+  const float2 *ml = a.part_ml + row;
+  const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + row * C4 + c0;
+  const int64_t sstride = R * C4;   // float4 chunks between splits
+
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[(int64_t)s * R].x);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int off = 1; off < 64; off *= 2) M = fmaxf(M, __shfl_xor(M, off));
   float L = 0.f;
-  if (m != -INFINITY) {
-#pragma unroll 4
-    for (int s = w; s < a.nsplit; s += 4) {
-      const float2 ml = a.part_ml[(int64_t)s * R + row];
-      const float wgt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - m);
-      L += ml.y * wgt;
-      const float *po = a.part_o + ((int64_t)s * R + row) * HD;
+  float4 acc[CPL];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += po[lane + 64 * e] * wgt;
+  for (int c = 0; c < CPL; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = g; s < ns; s += SG) {
+      const float2 v = ml[(int64_t)s * R];
+      // raw v_exp_f32: the argument is <= 0 or -inf
+      const float w = __builtin_amdgcn_exp2f(v.x - M);
+      L += v.y * w;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float4 o = po[s * sstride + 64 * c];
+        acc[c].x += w * o.x; acc[c].y += w * o.y; acc[c].z += w * o.z; acc[c].w += w * o.w;
+      }
     }
   }
-  if (lane == 0) { sm[w] = m; sl[w] = L; }
+  if constexpr (SG > 1) {
+    // add the groups' sums (lanes c0 + C4 * g): partners combine the same two
+    // values in the same order, so every group ends with identical sums
 #pragma unroll
-  for (int e = 0; e < PER; ++e) so[w][lane + 64 * e] = acc[e];
-  __syncthreads();
-  if (w != 0) return;
-  float mt = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-  float wq[4], Lt = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    wq[q] = sm[q] == -INFINITY ? 0.f : exp2f(sm[q] - mt);
-    Lt += sl[q] * wq[q];
+    for (int off = C4; off < 64; off *= 2) {
+      const bool low = (lane & off) == 0;
+      const float Lo = __shfl_xor(L, off);
+      L = low ? L + Lo : Lo + L;
+      float4 &x = acc[0];
+      const float4 y = make_float4(__shfl_xor(x.x, off), __shfl_xor(x.y, off),
+                                   __shfl_xor(x.z, off), __shfl_xor(x.w, off));
+      x = low ? make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w)
+              : make_float4(y.x + x.x, y.y + x.y, y.z + x.z, y.w + x.w);
+    }
   }
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  if (g != 0) return;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   T *o = static_cast<T *>(a.o) + ((cb * C + qi) * a.Hq + h) * HD;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v += so[q][lane + 64 * e] * wq[q];
-    o[lane + 64 * e] = from_f<T>(v * inv);
+  for (int c = 0; c < CPL; ++c) {
+    const int d = 4 * (c0 + 64 * c);
+    o[d + 0] = from_f<T>(acc[c].x * inv);
+    o[d + 1] = from_f<T>(acc[c].y * inv);
+    o[d + 2] = from_f<T>(acc[c].z * inv);
+    o[d + 3] = from_f<T>(acc[c].w * inv);
   }
 }
 
@@ -476,12 +524,11 @@ void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len,
   const int64_t base = (int64_t)nc * Hq * cdiv64(C, nq);
   // most keys one query tile can see: the prompt plus its window span
   const int64_t span = (int64_t)max_len + (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
-  // about two workgroups per CU; the K/V loads of a workgroup run several blocks
-  // ahead (register ring), so longer chains do not stall on memory latency
-  constexpr int kTargetWorkgroups = 512;
+  // about two workgroups per CU
+  const int target = 512;
   int ns = 1;
-  if (base < kTargetWorkgroups) {
-    ns = (int)cdiv64(kTargetWorkgroups, base);
+  if (base < target) {
+    ns = (int)cdiv64(target, base);
     const int64_t maxs = cdiv64(span, 4 * nk);   // keep at least ~4 key blocks per split
     if (ns > maxs) ns = (int)maxs;
     if (ns < 1) ns = 1;
@@ -502,7 +549,7 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * a.C;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)R), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
