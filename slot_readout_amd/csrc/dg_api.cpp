@@ -149,24 +149,41 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
 }
 
 struct SlotPlan {
-  size_t q, k, v, o, part_o, part_ml, h, rows, stats, rowstat, flags, draw_active, draw_ids,
-      row_active, rs_draw, total;
+  size_t q, k, v, o, part_o, part_ml, h, rows, stats, rowstat, lab_logit, flags, draw_active,
+      draw_ids, row_active, rs_draw, total;
   AttnPlan first, draws;
+  bool spec;
 };
+
+// Whether the draws are computed for every canvas in the first read's pass.
+// That saves one stream of the LM-head weights (V x d), and costs the draws'
+// forward pass when no slot turns out to need a re-read.  Both are estimated
+// with sustained rates of about 5 TB/s and 1 PFLOP/s (bf16; 0.1 PFLOP/s fp32).
+bool speculate_draws(const dg_dims &d, int B, int nd, int max_prompt) {
+  if (nd <= 1 || B <= 0) return false;
+  const double head_s = (double)d.vocab * d.d_model * (double)tsize(d) / 5e12;
+  const double hq = (double)d.n_q_heads * d.head_dim, hkv = (double)d.n_kv_heads * d.head_dim;
+  const double per_row = 2.0 * d.d_model * (hq + 2.0 * hkv) + 2.0 * hq * d.d_model +
+                         4.0 * hq * ((double)max_prompt + 2.0 * d.window + 1.0);
+  const double draw_s =
+      (double)B * nd * d.canvas * per_row / (d.dtype == DG_BF16 ? 1e15 : 1e14);
+  return draw_s < head_s;
+}
 
 SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   SlotPlan p{};
-  const int ncmax = nd > 1 ? B * nd : B;
+  p.spec = speculate_draws(d, B, nd, max_prompt);
+  const int ncmax = p.spec ? B * (nd + 1) : (nd > 1 ? B * nd : B);
   const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
   const int nvt = d.vocab / dg::VTILE;
-  const size_t nrows = (size_t)B * S * (nd > 1 ? nd : 1);
+  const size_t nrows = (size_t)B * S * (p.spec ? nd + 1 : (nd > 1 ? nd : 1));
   Arena a;
   p.q = a.take(M * nq * ts);
   p.k = a.take(M * nkv * ts);
   p.v = a.take(M * nkv * ts);
   p.o = a.take(M * nq * ts);
-  p.first = plan_attention(d, B, max_prompt);
+  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt);
   p.draws = plan_attention(d, ncmax, max_prompt);
   const size_t po = p.first.part_o > p.draws.part_o ? p.first.part_o : p.draws.part_o;
   const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
@@ -176,9 +193,10 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   p.rows = a.take(nrows * sizeof(int32_t));
   p.stats = a.take(nrows * nvt * sizeof(float4));
   p.rowstat = a.take(nrows * sizeof(float2));
+  p.lab_logit = a.take(nrows * DG_MAX_LABELS * sizeof(float));
   p.flags = a.take(((size_t)B + (size_t)B * S) * sizeof(int32_t));
   p.draw_active = a.take((size_t)B * (nd > 1 ? nd : 1) * sizeof(int32_t));
-  p.draw_ids = a.take(nd > 1 ? (size_t)B * nd * d.canvas * sizeof(int32_t) : 0);
+  p.draw_ids = a.take(nd > 1 ? (size_t)ncmax * d.canvas * sizeof(int32_t) : 0);
   p.row_active = a.take(nrows * sizeof(int32_t));
   p.rs_draw = a.take(nrows * sizeof(float));
   p.total = a.off;
@@ -490,9 +508,8 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.label_ids = label_ids;
   sa.n_labels = n_labels;
   sa.noise_ids = noise_ids;
-  sa.head = w->lm_head ? w->lm_head : w->embed;
-  sa.h = h;
   sa.rowstat = at<float2>(workspace, p.rowstat);
+  sa.lab_logit = at<float>(workspace, p.lab_logit);
   sa.row_scale = row_scale;
   sa.logit_scale = logit_scale;
   sa.threshold = entropy_threshold;
@@ -516,30 +533,63 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.draw_ids = at<int32_t>(workspace, p.draw_ids);
   sa.mask_id = d.mask_id;
 
-  // first read over the prefilled canvases
-  s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
-                part_o, part_ml, h, st);
-  if (s != DG_OK) return s;
-  DG_TRY_HIP(dg::launch_slot_rows(sa, bf, st), "slot row launch");
   dg::LmheadArgs la{};
-  la.head = sa.head;
+  la.head = w->lm_head ? w->lm_head : w->embed;
   la.h = h;
   la.row_index = sa.rows;
   la.logit_scale = logit_scale;
-  la.row_scale = row_scale;
   la.stats = at<float4>(workspace, p.stats);
-  la.nrows = (int64_t)batch * n_slots;
+  la.lab_ids = label_ids;
+  la.lab_n = n_labels;
+  la.lab_logit = at<float>(workspace, p.lab_logit);
+  la.lab_S = n_slots;
   la.d = d.d_model;
   la.vocab = d.vocab;
   la.nvt = nvt;
-  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "slot LM head launch");
   dg::VocabMergeArgs va{};
   va.stats = la.stats;
-  va.nrows = la.nrows;
   va.nvt = nvt;
   va.rowstat = at<float2>(workspace, p.rowstat);
+  float *rs_draw = at<float>(workspace, p.rs_draw);
+
+  if (p.spec) {
+    // first read and every draw in one pass: canvas b*(1+nd) + j, slot rows
+    // n = (b*(1+nd) + j)*S + s; the draws are used only where a slot is flagged
+    const int G = n_draws + 1;
+    sa.grp_first = G;
+    sa.grp_draw = G;
+    sa.off_draw = 1;
+    DG_TRY_HIP(dg::launch_slot_spec_build(sa, sa.draw_ids, rs_draw, st), "read canvas launch");
+    s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
+                  p.draws, part_o, part_ml, h, st);
+    if (s != DG_OK) return s;
+    la.nrows = (int64_t)batch * G * n_slots;
+    la.row_scale = rs_draw;
+    la.lab_span = G * n_slots;
+    DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "slot LM head launch");
+    va.nrows = la.nrows;
+    DG_TRY_HIP(dg::launch_vocab_merge(va, st), "slot vocabulary merge launch");
+    DG_TRY_HIP(dg::launch_slot_first(sa, st), "slot first-read launch");
+    DG_TRY_HIP(dg::launch_slot_noise_status(sa, st), "slot noise status launch");
+    DG_TRY_HIP(dg::launch_slot_average(sa, st), "draw average launch");
+    return ok();
+  }
+
+  // first read over the prefilled canvases
+  sa.grp_first = 1;
+  sa.grp_draw = n_draws;
+  sa.off_draw = 0;
+  s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
+                part_o, part_ml, h, st);
+  if (s != DG_OK) return s;
+  DG_TRY_HIP(dg::launch_slot_rows(sa, st), "slot row launch");
+  la.nrows = (int64_t)batch * n_slots;
+  la.row_scale = row_scale;
+  la.lab_span = n_slots;
+  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "slot LM head launch");
+  va.nrows = la.nrows;
   DG_TRY_HIP(dg::launch_vocab_merge(va, st), "slot vocabulary merge launch");
-  DG_TRY_HIP(dg::launch_slot_first(sa, bf, st), "slot first-read launch");
+  DG_TRY_HIP(dg::launch_slot_first(sa, st), "slot first-read launch");
   if (n_draws == 1) return ok();
 
   // re-read of flagged canvases: n_draws noise copies in one batched pass
@@ -548,16 +598,16 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
                 q, k, v, o, p.draws, part_o, part_ml, h, st);
   if (s != DG_OK) return s;
   int32_t *row_active = at<int32_t>(workspace, p.row_active);
-  float *rs_draw = at<float>(workspace, p.rs_draw);
   DG_TRY_HIP(dg::launch_slot_draw_rows2(sa, row_active, rs_draw, st), "draw row launch");
   la.nrows = (int64_t)batch * n_draws * n_slots;
   la.active_rows = row_active;
   la.rows_per_flag = 1;
   la.row_scale = rs_draw;
+  la.lab_span = n_draws * n_slots;
   DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "draw LM head launch");
   va.nrows = la.nrows;
   DG_TRY_HIP(dg::launch_vocab_merge(va, st), "draw vocabulary merge launch");
-  DG_TRY_HIP(dg::launch_slot_average(sa, bf, st), "draw average launch");
+  DG_TRY_HIP(dg::launch_slot_average(sa, st), "draw average launch");
   return ok();
 }
 

@@ -418,6 +418,29 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     mx[j] = m;
     ix[j] = id;
   }
+  // label logits of slot rows: the lane holding (label, row) writes it
+  if (a.lab_logit) {
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) {
+      const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
+      if (n >= a.nrows) continue;
+      const int64_t bs = (n / a.lab_span) * a.lab_S + n % a.lab_S;
+      int k = a.lab_n[bs];
+      k = k < 0 ? 0 : (k > DG_MAX_LABELS ? DG_MAX_LABELS : k);
+      const int32_t *labs = a.lab_ids + bs * DG_MAX_LABELS;
+      for (int q = 0; q < k; ++q) {
+        const int rel = labs[q] - (v0 + wm * G::WM);   // = i*16 + 4*(lane group) + r
+        if (rel < 0 || rel >= G::WM || ((rel >> 2) & 3) != (lane >> 4)) continue;
+        float val = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (i == (rel >> 4) && r == (rel & 3)) val = acc[i][j][r];
+        a.lab_logit[n * DG_MAX_LABELS + q] = val;
+      }
+    }
+  }
   if ((lane >> 4) == 0) {
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) {

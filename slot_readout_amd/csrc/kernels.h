@@ -44,6 +44,13 @@ struct LmheadArgs {
   float4 *stats;           // [nrows, nvt] (m, sum e, sum e*(l-m), argmax bits)
   void *ptilde;            // [nrows, V] T or null
   float *logits;           // [nrows, V] or null
+  // label logits of slot rows (optional): row n belongs to slot
+  // bs = (n / lab_span) * lab_S + n % lab_S, whose lab_n[bs] label ids are
+  // lab_ids[bs * 26 + q]; the scaled logit of label q goes to lab_logit[n * 26 + q]
+  const int32_t *lab_ids;
+  const int32_t *lab_n;
+  float *lab_logit;
+  int lab_span, lab_S;
   int64_t nrows;
   int d, vocab, nvt;
 };
@@ -117,9 +124,12 @@ struct SlotArgs {
   const int32_t *label_ids;    // [B, S, 26]
   const int32_t *n_labels;     // [B, S]
   const int32_t *noise_ids;    // [n_draws, B, S]
-  const void *head;            // [V, d] LM head rows (for label logits)
-  const void *h;               // hidden rows [rows, d] of the pass
-  const float2 *rowstat;       // [B*(S or nd*S)] (m, lse) per gathered slot row
+  // Slot rows of an LM-head pass are laid out as n = (b * grp + j) * S + s:
+  // pass j of canvas b (the first read, or draw d), slot s.  The first read is
+  // j = 0 with grp_first; draw d is j = off_draw + d with grp_draw.
+  const float2 *rowstat;       // per row n: (m, lse)
+  const float *lab_logit;      // per row n: scaled label logits [26]
+  int grp_first, grp_draw, off_draw;
   const float *row_scale;      // [B, S] or null
   float logit_scale;
   float threshold;
@@ -135,11 +145,15 @@ struct SlotArgs {
   int mask_id;
 };
 
-hipError_t launch_slot_rows(const SlotArgs &a, bool bf, hipStream_t st);
-hipError_t launch_slot_first(const SlotArgs &a, bool bf, hipStream_t st);
+hipError_t launch_slot_rows(const SlotArgs &a, hipStream_t st);
+hipError_t launch_slot_first(const SlotArgs &a, hipStream_t st);
 hipError_t launch_slot_build_draws(const SlotArgs &a, hipStream_t st);
 hipError_t launch_slot_draw_rows2(const SlotArgs &a, int32_t *row_active, float *rs_draw,
                                   hipStream_t st);
-hipError_t launch_slot_average(const SlotArgs &a, bool bf, hipStream_t st);
+hipError_t launch_slot_average(const SlotArgs &a, hipStream_t st);
+// one pass over the first read and every draw: ids of the B*(1+nd) canvases,
+// hidden-row indices of their slot rows, and the status of draws with bad noise
+hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st);
+hipError_t launch_slot_noise_status(const SlotArgs &a, hipStream_t st);
 
 }  // namespace dg

@@ -2,10 +2,14 @@
 // the allowed labels, entropy, and the averaged noise-draw re-read.
 //
 // The first pass runs the denoise step over the whole canvas; the LM head and
-// its softmax statistics run only on the slot rows (gathered by row index).
-// A slot whose renormalised entropy exceeds the threshold flags its canvas;
-// flagged canvases get n_draws copies with a noise token written at every slot
-// and a second batched pass, decided on the device (no host synchronisation).
+// its softmax statistics run only on the slot rows (gathered by row index), and
+// its epilogue also writes the logits of each slot's allowed labels.  A slot
+// whose renormalised entropy exceeds the threshold flags its canvas; flagged
+// canvases get n_draws copies with a noise token written at every slot and a
+// second batched pass, decided on the device (no host synchronisation).  When
+// the LM head's weight stream costs more than the draws' forward pass, the
+// draws are instead computed for every canvas in the same pass as the first
+// read and used only where a slot is flagged (same results, one weight stream).
 #include "common.h"
 #include "kernels.h"
 
@@ -33,48 +37,11 @@ __global__ __launch_bounds__(256) void slot_rows_kernel(SlotArgs a) {
   a.rows[bs] = st == DG_SLOT_OK ? (int32_t)(b * a.C + a.slot_pos[bs]) : -1;
 }
 
-// Label logits of one hidden row: lp_j = min(s * h.head[label_j] - lse, 0),
-// returned in lane j.  Lanes stride over 16-byte chunks of the row; each hidden
-// chunk is loaded once and reused for every label, so the k dot products run
-// side by side, then each is reduced across the wave.
-template <typename T>
-__device__ inline float label_logprob(const SlotArgs &a, const T *hrow, const int32_t *labs, int k,
-                                      float scale, float lse, int lane) {
-  constexpr int VEC = 16 / sizeof(T);
-  const T *head = static_cast<const T *>(a.head);
-  float acc[DG_MAX_LABELS];
-#pragma unroll
-  for (int j = 0; j < DG_MAX_LABELS; ++j) acc[j] = 0.f;
-  const T *er[DG_MAX_LABELS];
-#pragma unroll
-  for (int j = 0; j < DG_MAX_LABELS; ++j) er[j] = head + (int64_t)(j < k ? labs[j] : labs[0]) * a.d;
-  for (int e = lane * VEC; e < a.d; e += 64 * VEC) {
-    Chunk<T> hc;
-    hc.u = *reinterpret_cast<const uint4 *>(hrow + e);
-    float hf[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) hf[i] = to_f(hc.v[i]);
-#pragma unroll
-    for (int j = 0; j < DG_MAX_LABELS; ++j) {
-      if (j < k) {
-        Chunk<T> ec;
-        ec.u = *reinterpret_cast<const uint4 *>(er[j] + e);
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) s += hf[i] * to_f(ec.v[i]);
-        acc[j] += s;
-      }
-    }
-  }
-  float mine = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < DG_MAX_LABELS; ++j) {
-    if (j < k) {
-      const float t = wave_sum(acc[j]);
-      if (lane == j) mine = fminf(t * scale - lse, 0.f);
-    }
-  }
-  return mine;
+// label log-probability in lane j: lp_j = min(l_j - lse, 0) from the scaled
+// label logits the LM-head pass wrote for row n
+__device__ inline float label_logprob(const SlotArgs &a, int64_t n, int k, int lane) {
+  if (lane >= k) return -INFINITY;
+  return fminf(a.lab_logit[n * DG_MAX_LABELS + lane] - a.rowstat[n].y, 0.f);
 }
 
 struct LabelDist {
@@ -109,14 +76,12 @@ __device__ inline void finish_dist(LabelDist &d, int k, int lane) {
 }
 
 // first read: one wave per slot; also decides which canvases need draws
-template <typename T>
 __global__ __launch_bounds__(256) void slot_first_kernel(SlotArgs a) {
   __shared__ int any_flag;
   const int b = blockIdx.x;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) any_flag = 0;
   __syncthreads();
-  const T *h = static_cast<const T *>(a.h);
   for (int s = w; s < a.S; s += 4) {
     const int64_t bs = (int64_t)b * a.S + s;
     float *lp_out = a.logprobs + bs * DG_MAX_LABELS;
@@ -133,12 +98,7 @@ __global__ __launch_bounds__(256) void slot_first_kernel(SlotArgs a) {
       continue;
     }
     const int k = a.n_labels[bs];
-    const int pos = a.slot_pos[bs];
-    float scale = a.logit_scale;
-    if (a.row_scale) scale *= a.row_scale[bs];
-    const float lse = a.rowstat[bs].y;
-    const float lp = label_logprob<T>(a, h + ((int64_t)b * a.C + pos) * a.d,
-                                      a.label_ids + bs * DG_MAX_LABELS, k, scale, lse, lane);
+    const float lp = label_logprob(a, ((int64_t)b * a.grp_first) * a.S + s, k, lane);
     LabelDist dd = renormalise(lp, k, lane);
     finish_dist(dd, k, lane);
     if (lane < DG_MAX_LABELS) {
@@ -202,7 +162,6 @@ __global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t
 }
 
 // average of the draws in probability space: r = mean r_d, lp = ln mean e^(lp_d)
-template <typename T>
 __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
   const int64_t bs = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -211,18 +170,11 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
   const int64_t b = bs / a.S;
   const int s = (int)(bs % a.S);
   const int k = a.n_labels[bs];
-  const int pos = a.slot_pos[bs];
-  float scale = a.logit_scale;
-  if (a.row_scale) scale *= a.row_scale[bs];
-  const T *h = static_cast<const T *>(a.h);
   // r is averaged directly; ln mean_d e^(lp_d) is kept as an online log-sum-exp
   // (lp can sit far below the fp32 range of e^x)
   float racc = 0.f, lm = -INFINITY, ls = 0.f;
   for (int d = 0; d < a.n_draws; ++d) {
-    const int64_t bd = b * a.n_draws + d;
-    const float lse = a.rowstat[bd * a.S + s].y;
-    const float lp = label_logprob<T>(a, h + (bd * a.C + pos) * a.d,
-                                      a.label_ids + bs * DG_MAX_LABELS, k, scale, lse, lane);
+    const float lp = label_logprob(a, (b * a.grp_draw + a.off_draw + d) * a.S + s, k, lane);
     const LabelDist dd = renormalise(lp, k, lane);
     racc += dd.r;
     if (lane < k) {
@@ -246,19 +198,78 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
   }
 }
 
-hipError_t launch_slot_rows(const SlotArgs &a, bool, hipStream_t st) {
+// One pass over the first read and every draw.  Block cb = b*(1+nd) + j
+// writes canvas cb: canvas b itself (j = 0) or draw j-1 of it, with its noise
+// token at every valid slot position (the mask id for an out-of-range noise
+// id; the status for that is set only once the canvas is known to re-read).
+// It also writes the hidden-row index and row scale of the canvas's slot rows
+// n = cb*S + s, and for j = 0 the slot's validation status.
+__global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_t *ids, float *rs) {
+  const int cb = blockIdx.x;
+  const int G = a.n_draws + 1;
+  const int b = cb / G, j = cb % G;
+  int32_t *dst = ids + (int64_t)cb * a.C;
+  const int32_t *src = a.canvas_ids + (int64_t)b * a.C;
+  for (int i = threadIdx.x; i < a.C; i += 256) dst[i] = src[i];
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.S; s += 256) {
+    const int64_t bs = (int64_t)b * a.S + s;
+    const int st = validate_slot(a, bs);
+    if (j == 0) a.status[bs] = st;
+    const int64_t n = (int64_t)cb * a.S + s;
+    a.rows[n] = st == DG_SLOT_OK ? (int32_t)((int64_t)cb * a.C + a.slot_pos[bs]) : -1;
+    rs[n] = a.row_scale ? a.row_scale[bs] : 1.f;
+  }
+  // slots are written in order, as in the separate draw pass
+  if (j > 0 && threadIdx.x == 0) {
+    for (int s = 0; s < a.S; ++s) {
+      const int64_t bs = (int64_t)b * a.S + s;
+      const int pos = a.slot_pos[bs];
+      if (pos < 0 || pos >= a.C) continue;
+      int nid = a.noise_ids[((int64_t)(j - 1) * a.B + b) * a.S + s];
+      if (nid < 0 || nid >= a.V) nid = a.mask_id;
+      dst[pos] = nid;
+    }
+  }
+}
+
+// status of the slots of re-read canvases whose noise id is out of range
+__global__ __launch_bounds__(256) void slot_noise_status_kernel(SlotArgs a) {
+  const int64_t bs = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (bs >= (int64_t)a.B * a.S) return;
+  const int64_t b = bs / a.S;
+  if (!a.canvas_flag[b] || a.status[bs] != DG_SLOT_OK) return;
+  const int s = (int)(bs % a.S);
+  for (int d = 0; d < a.n_draws; ++d) {
+    const int nid = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
+    if (nid < 0 || nid >= a.V) { a.status[bs] = DG_SLOT_BAD_NOISE; return; }
+  }
+}
+
+hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st) {
+  const int64_t n = (int64_t)a.B * (a.n_draws + 1);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_spec_build_kernel, dim3((unsigned)n), dim3(256), 0, st, a, ids, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_noise_status(const SlotArgs &a, hipStream_t st) {
+  const int64_t n = (int64_t)a.B * a.S;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_noise_status_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_rows(const SlotArgs &a, hipStream_t st) {
   const int64_t n = (int64_t)a.B * a.S;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(slot_rows_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_slot_first(const SlotArgs &a, bool bf, hipStream_t st) {
+hipError_t launch_slot_first(const SlotArgs &a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  if (bf)
-    hipLaunchKernelGGL((slot_first_kernel<bf16>), dim3((unsigned)a.B), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((slot_first_kernel<float>), dim3((unsigned)a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(slot_first_kernel, dim3((unsigned)a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -276,13 +287,10 @@ hipError_t launch_slot_draw_rows2(const SlotArgs &a, int32_t *row_active, float 
   return hipGetLastError();
 }
 
-hipError_t launch_slot_average(const SlotArgs &a, bool bf, hipStream_t st) {
+hipError_t launch_slot_average(const SlotArgs &a, hipStream_t st) {
   const int64_t n = (int64_t)a.B * a.S;
   if (n == 0) return hipSuccess;
-  if (bf)
-    hipLaunchKernelGGL((slot_average_kernel<bf16>), dim3((unsigned)cdiv64(n, 4)), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((slot_average_kernel<float>), dim3((unsigned)cdiv64(n, 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(slot_average_kernel, dim3((unsigned)cdiv64(n, 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
