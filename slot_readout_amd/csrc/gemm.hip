@@ -102,26 +102,38 @@ struct Gemm {
       }
     };
 #pragma unroll
-    for (int s = 0; s < PF; ++s)
-      if (s < nk) gload(s, ra[s], rb[s]);
+    for (int s = 0; s < PF; ++s) gload(s < nk ? s : nk - 1, ra[s], rb[s]);
     sstore(0, ra[0], rb[0]);
     __syncthreads();
-    for (int k0 = 0; k0 < nk; k0 += PF) {
+    // Main loop: whole groups of PF steps with no conditional loads, so the
+    // loads retire in issue order and each store waits only for its own ring
+    // slot (a load behind a branch makes the compiler drain every load in
+    // flight).  Ring slot j holds step kt, already in LDS: it is refilled with
+    // step kt+PF (past the end: the last step again, never used).  Scheduling
+    // fences keep the order loads -> MFMAs -> finish/store, so the conversion
+    // of freshly loaded data is not hoisted next to the loads.
+    int k0 = 0;
+    for (; k0 + PF <= nk; k0 += PF) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
         const int kt = k0 + j;
-        if (kt < nk) {
-          // ring slot j held step kt, already in LDS: refill it with step kt+PF.
-          // Scheduling fences keep the order loads -> MFMAs -> finish/store, so
-          // the conversion of freshly loaded data is not hoisted next to the
-          // loads (which would wait on them before any MFMA).
-          if (kt + PF < nk) gload(kt + PF, ra[j], rb[j]);
-          __builtin_amdgcn_sched_barrier(0);
-          compute(kt & 1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (kt + 1 < nk) sstore((kt + 1) & 1, ra[(j + 1) % PF], rb[(j + 1) % PF]);
-          __syncthreads();
-        }
+        gload(kt + PF < nk ? kt + PF : nk - 1, ra[j], rb[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        sstore((kt + 1) & 1, ra[(j + 1) % PF], rb[(j + 1) % PF]);
+        __syncthreads();
+      }
+    }
+    // the last nk - k0 < PF steps, already in their ring slots
+#pragma unroll
+    for (int j = 0; j < PF - 1; ++j) {
+      const int kt = k0 + j;
+      if (kt < nk) {
+        compute(kt & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) sstore((kt + 1) & 1, ra[(j + 1) % PF], rb[(j + 1) % PF]);
+        __syncthreads();
       }
     }
   }
@@ -157,8 +169,11 @@ __device__ inline uint4 keep_if(uint4 v, bool live) {
   return live ? v : uint4{0, 0, 0, 0};
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 to_uint4(u32x4 v) { return uint4{v.x, v.y, v.z, v.w}; }
+
 template <typename T, int N> struct RowLoader {
-  using Raw = uint4;
+  using Raw = u32x4;
   const T *p[N];     // always a dereferenceable row
   bool live[N];
   __device__ inline void set(int it, const T *row, bool ok, const T *fallback) {
@@ -166,35 +181,36 @@ template <typename T, int N> struct RowLoader {
     live[it] = ok;
   }
   __device__ inline Raw load(int it, int k) const {
-    return *reinterpret_cast<const uint4 *>(p[it] + k);
+    return *reinterpret_cast<const u32x4 *>(p[it] + k);
   }
   __device__ inline uint4 finish(int it, const Raw &r) const {
-    uint4 v = r;
+    uint4 v = to_uint4(r);
     pin(v);
     return keep_if(v, live[it]);
   }
 };
 
-// x = E[id] + sc_in, rounded to T (sc_in present or absent for the whole launch)
-template <typename T, int N> struct GatherLoader {
-  struct Raw { uint4 e, s; };
+// x = E[id] + sc_in, rounded to T (SC: sc_in present for the whole launch; a
+// compile-time switch, so no load sits behind a branch)
+template <typename T, int N, bool SC> struct GatherLoader {
+  struct Raw { u32x4 e, s; };
   const T *e[N];
   const T *s[N];
   bool live[N];
-  bool has_sc;
   __device__ inline Raw load(int it, int k) const {
     Raw r;
-    r.e = *reinterpret_cast<const uint4 *>(e[it] + k);
-    r.s = has_sc ? *reinterpret_cast<const uint4 *>(s[it] + k) : uint4{0, 0, 0, 0};
+    r.e = *reinterpret_cast<const u32x4 *>(e[it] + k);
+    if constexpr (SC) r.s = *reinterpret_cast<const u32x4 *>(s[it] + k);
+    else r.s = u32x4{0, 0, 0, 0};
     return r;
   }
   __device__ inline uint4 finish(int it, const Raw &r) const {
     Chunk<T> a;
-    a.u = r.e;
+    a.u = to_uint4(r.e);
     pin(a.u);
-    if (has_sc) {
+    if constexpr (SC) {
       Chunk<T> b;
-      b.u = r.s;
+      b.u = to_uint4(r.s);
       pin(b.u);
 #pragma unroll
       for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) + to_f(b.v[i]));
@@ -205,19 +221,19 @@ template <typename T, int N> struct GatherLoader {
 
 // p = p~ * f[row][k / VTILE], rounded to T  (p~ = e^(l - m_tile))
 template <typename T, int N> struct ScaledRowLoader {
-  struct Raw { uint4 p; float f; };
+  struct Raw { u32x4 p; float f; };
   const T *p[N];
   const float *f[N];
   bool live[N];
   __device__ inline Raw load(int it, int k) const {
     Raw r;
-    r.p = *reinterpret_cast<const uint4 *>(p[it] + k);
+    r.p = *reinterpret_cast<const u32x4 *>(p[it] + k);
     r.f = f[it][k / VTILE];
     return r;
   }
   __device__ inline uint4 finish(int it, const Raw &r) const {
     Chunk<T> a;
-    a.u = r.p;
+    a.u = to_uint4(r.p);
     pin(a.u);
     float fac = r.f;
     pin(fac);
@@ -239,7 +255,7 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
 // ---------------------------------------------------------------------------
 // S0+S1: q,k,v projection with the embedding gather in the A prologue
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool SC>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
@@ -249,8 +265,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   const T *E = static_cast<const T *>(a.embed);
   const T *sc = static_cast<const T *>(a.sc_in);
   const int nq = a.nq, nk = a.nkv, ntot = nq + 2 * nk, d = a.d;
-  GatherLoader<T, G::AI> al;
-  al.has_sc = sc != nullptr;
+  GatherLoader<T, G::AI, SC> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
@@ -590,7 +605,10 @@ __global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, void 
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
   dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.nq + 2 * a.nkv, BN));
-  hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+  if (a.sc_in)
+    hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK, true>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+  else
+    hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK, false>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   return hipGetLastError();
 }
 
