@@ -27,7 +27,14 @@ struct Gemm {
   static constexpr int NT = NW * WAVE;
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int CPR = BK / VEC;      // 16-byte chunks per tile row
-  static constexpr int PITCH = BK + VEC;    // 16 bytes of padding per LDS row
+  // LDS rows.  The fragment reads (16 rows x 4 chunks of 16 bytes per
+  // instruction) are free of bank conflicts on gfx950 for 128-byte rows whose
+  // chunks are XOR-swizzled by (row & 7), and for 64-byte rows padded to 96
+  // bytes; a 16-byte pad on 128-byte rows costs 2x, no pad and no swizzle 4x
+  // (SQ_LDS_BANK_CONFLICT).  fp32 tiles keep a 16-byte pad.
+  static constexpr bool SWZ = sizeof(T) == 2 && BK == 64;
+  static constexpr int PITCH = SWZ ? BK : (sizeof(T) == 2 && BK == 32 ? 48 : BK + VEC);
+  __device__ static inline int chunk_at(int row, int c) { return SWZ ? c ^ (row & 7) : c; }
   static constexpr int AI = BM * CPR / NT;  // A chunks per thread per K step
   static constexpr int BI = BN * CPR / NT;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -77,10 +84,12 @@ struct Gemm {
       T *Bs = As + BM * PITCH;
 #pragma unroll
       for (int it = 0; it < AI; ++it)
-        *reinterpret_cast<uint4 *>(As + a_row(it) * PITCH + a_kc(it) * VEC) = al.finish(it, xa[it]);
+        *reinterpret_cast<uint4 *>(As + a_row(it) * PITCH + chunk_at(a_row(it), a_kc(it)) * VEC) =
+            al.finish(it, xa[it]);
 #pragma unroll
       for (int it = 0; it < BI; ++it)
-        *reinterpret_cast<uint4 *>(Bs + a_row(it) * PITCH + a_kc(it) * VEC) = bl.finish(it, xb[it]);
+        *reinterpret_cast<uint4 *>(Bs + a_row(it) * PITCH + chunk_at(a_row(it), a_kc(it)) * VEC) =
+            bl.finish(it, xb[it]);
     };
     auto compute = [&](int buf) {
       const T *As = lds + buf * (BM + BN) * PITCH;
@@ -89,12 +98,15 @@ struct Gemm {
       for (int ks = 0; ks < BK / MF::KI; ++ks) {
         frag a[TM], b[TN];
         const int kk = ks * MF::KI + (lane >> 4) * MF::KPL;
+        // rows differ from (lane & 15) by multiples of 16, so the swizzle
+        // depends on the lane only
+        const int ko = SWZ ? chunk_at(lane & 15, kk / VEC) * VEC : kk;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          a[i] = *reinterpret_cast<const frag *>(As + (wm * WM + i * 16 + (lane & 15)) * PITCH + kk);
+          a[i] = *reinterpret_cast<const frag *>(As + (wm * WM + i * 16 + (lane & 15)) * PITCH + ko);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          b[j] = *reinterpret_cast<const frag *>(Bs + (wn * WN + j * 16 + (lane & 15)) * PITCH + kk);
+          b[j] = *reinterpret_cast<const frag *>(Bs + (wn * WN + j * 16 + (lane & 15)) * PITCH + ko);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
