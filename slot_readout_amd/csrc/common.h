@@ -101,4 +101,14 @@ __device__ inline float group4_sum(float v) {
 
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Reference of a vocabulary tile whose largest logit is m: r = ceil(m log2 e),
+// an integer, so the tile's e^(l - r ln 2) are <= 1 and two tiles' references
+// differ by an exact power of two.  The LM head and the vocabulary merge both
+// derive r from the stored tile max with this one function.
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ inline int tile_ref(float m) {
+  return m > -1e30f ? (int)ceilf(m * kLog2e) : -(1 << 28);
+}
+
 }  // namespace dg

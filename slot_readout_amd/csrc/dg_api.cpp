@@ -119,7 +119,7 @@ AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt) {
 }
 
 struct StepPlan {
-  size_t q, k, v, o, part_o, part_ml, h, stats, ptilde, fscale, sc_part, total;
+  size_t q, k, v, o, part_o, part_ml, h, stats, ptilde, shift, inv_z, sc_part, total;
   AttnPlan attn;
   int ksplit;
 };
@@ -141,7 +141,8 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
   p.h = a.take(M * d.d_model * ts);
   p.stats = a.take(M * nvt * sizeof(float4));
   p.ptilde = a.take(M * d.vocab * ts);
-  p.fscale = a.take(M * nvt * sizeof(float));
+  p.shift = a.take(M * nvt * sizeof(int32_t));
+  p.inv_z = a.take(M * sizeof(float));
   p.ksplit = dg::sc_ksplit((int64_t)M, d.d_model, d.vocab, bf);
   p.sc_part = a.take(p.ksplit > 1 ? (size_t)p.ksplit * M * d.d_model * sizeof(float) : 0);
   p.total = a.off;
@@ -415,7 +416,8 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   va.conf = conf;
   va.entropy = entropy;
   va.argmax = argmax;
-  va.fscale = sc_out ? at<float>(workspace, p.fscale) : nullptr;
+  va.shift = sc_out ? at<int32_t>(workspace, p.shift) : nullptr;
+  va.inv_z = sc_out ? at<float>(workspace, p.inv_z) : nullptr;
   DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 0);
   DG_TRY_HIP(dg::launch_vocab_merge(va, st), "vocabulary merge launch");
   DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 1);
@@ -424,7 +426,8 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   if (sc_out) {
     dg::ScArgs sa{};
     sa.ptilde = la.ptilde;
-    sa.fscale = va.fscale;
+    sa.shift = va.shift;
+    sa.inv_z = va.inv_z;
     sa.embed_t = w->embed_t;
     sa.part = at<float>(workspace, p.sc_part);
     sa.out = sc_out;

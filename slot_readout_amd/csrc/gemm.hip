@@ -231,27 +231,39 @@ template <typename T, int N, bool SC> struct GatherLoader {
   }
 };
 
-// p = p~ * f[row][k / VTILE], rounded to T  (p~ = e^(l - m_tile))
-template <typename T, int N> struct ScaledRowLoader {
-  struct Raw { u32x4 p; float f; };
+// p = p~ * 2^-shift[row][k / VTILE] (the 1/Z of the row is applied to the
+// output).  p~ >= 0, so the scaling is a saturating subtract on the exponent
+// field: exact, and values that would leave the normal range become 0 (or,
+// at the boundary, a subnormal below 2^-126).
+__device__ inline uint4 pow2_down(uint4 v, int sh, bf16) {
+  typedef unsigned short us8 __attribute__((ext_vector_type(8)));
+  const us8 x = __builtin_bit_cast(us8, v);
+  const us8 d = (us8)(unsigned short)((sh < 255 ? sh : 255) << 7);
+  return __builtin_bit_cast(uint4, __builtin_elementwise_sub_sat(x, d));
+}
+__device__ inline uint4 pow2_down(uint4 v, int sh, float) {
+  const u32x4 x = __builtin_bit_cast(u32x4, v);
+  const u32x4 d = (u32x4)((unsigned)(sh < 255 ? sh : 255) << 23);
+  return __builtin_bit_cast(uint4, __builtin_elementwise_sub_sat(x, d));
+}
+
+template <typename T, int N> struct ShiftedRowLoader {
+  struct Raw { u32x4 p; int sh; };
   const T *p[N];
-  const float *f[N];
+  const int32_t *sh[N];
   bool live[N];
   __device__ inline Raw load(int it, int k) const {
     Raw r;
     r.p = *reinterpret_cast<const u32x4 *>(p[it] + k);
-    r.f = f[it][k / VTILE];
+    r.sh = sh[it][k / VTILE];
     return r;
   }
   __device__ inline uint4 finish(int it, const Raw &r) const {
-    Chunk<T> a;
-    a.u = to_uint4(r.p);
-    pin(a.u);
-    float fac = r.f;
-    pin(fac);
-#pragma unroll
-    for (int i = 0; i < Chunk<T>::N; ++i) a.v[i] = from_f<T>(to_f(a.v[i]) * fac);
-    return keep_if(a.u, live[it]);
+    uint4 v = to_uint4(r.p);
+    pin(v);
+    int s = r.sh;
+    asm volatile("" : "+v"(s));
+    return keep_if(pow2_down(v, s, T{}), live[it]);
   }
 };
 
@@ -264,6 +276,25 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
   return false;
 }
 
+// width of the d tiles of the bf16 self-conditioning GEMM: 15 tiles cover
+// d = 2816, so two vocabulary ranges (30 workgroups) fill an XCD's 32 CUs
+constexpr int kScTileD = 192;
+
+// Workgroup id -> (group g, tile t): the nt tiles of a group share an operand
+// (a weight tile, a slice of p~).  Workgroups are dealt to the 8 XCDs
+// round-robin by id, so whole groups are dealt to one XCD at a time and each
+// group's tiles share that XCD's L2.  Launch 8 * cdiv(ngroups, 8) * nt
+// workgroups; ids past the last group return false.
+__device__ inline bool xcd_group_tile(int ngroups, int nt, int *g, int *t) {
+  const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+  *g = xcd + 8 * (local / nt);
+  *t = local % nt;
+  return *g < ngroups;
+}
+static inline dim3 xcd_grid(int64_t ngroups, int64_t nt) {
+  return dim3((unsigned)(8 * cdiv64(ngroups, 8) * nt));
+}
+
 // ---------------------------------------------------------------------------
 // S0+S1: q,k,v projection with the embedding gather in the A prologue
 // ---------------------------------------------------------------------------
@@ -271,8 +302,10 @@ template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool SC>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int n0 = blockIdx.y * BN;
+  int nt, mt;   // the row tiles of one weight tile run on one XCD
+  if (!xcd_group_tile((int)cdiv64(a.nq + 2 * a.nkv, BN), (int)cdiv64(a.M, BM), &nt, &mt)) return;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int n0 = nt * BN;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const T *E = static_cast<const T *>(a.embed);
   const T *sc = static_cast<const T *>(a.sc_in);
@@ -331,8 +364,10 @@ template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int n0 = blockIdx.y * BN;
+  int nt, mt;   // the row tiles of one weight tile run on one XCD
+  if (!xcd_group_tile((int)cdiv64(a.d, BN), (int)cdiv64(a.M, BM), &nt, &mt)) return;
+  const int64_t m0 = (int64_t)mt * BM;
+  const int n0 = nt * BN;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const int K = a.kdim, d = a.d;
   const T *o = static_cast<const T *>(a.o);
@@ -490,13 +525,16 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     mx[j] = m;
     ix[j] = id;
   }
-  // pass 2: sum e^(l-m) and sum e^(l-m)(l-m); p~ and logits out
+  // pass 2: with the tile reference r = tile_ref(m), sum e and e (l - r ln2)
+  // for e = e^(l - r ln2) (kept in log2 units: x = l log2 e - r, e = 2^x);
+  // p~ = e and logits out
   T *pt = static_cast<T *>(a.ptilde);
   float ss[G::TN], tt[G::TN];
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
     const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
     const bool live = n < a.nrows;
+    const float rj = (float)tile_ref(mx[j]);
     float s = 0.f, t = 0.f;
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
@@ -504,8 +542,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
       f32x4 e4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = acc[i][j][r] - mx[j];
-        const float e = __expf(x);
+        const float x = fmaf(acc[i][j][r], kLog2e, -rj);
+        // raw v_exp_f32: x <= 0 (r >= m log2 e)
+        const float e = __builtin_amdgcn_exp2f(x);
         s += e;
         t += e * x;
         e4[r] = e;
@@ -541,7 +580,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
       float4 st;
       st.x = mx[j];
       st.y = s;
-      st.z = t;
+      st.z = t * kLn2;
       st.w = __int_as_float(ix[j]);
       a.stats[n * a.nvt + vt] = st;
     }
@@ -555,21 +594,25 @@ template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
-  const int n0 = blockIdx.x * BN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int z = blockIdx.z;
+  // group = vocabulary range z; its (row, d) tiles share the p~ slice and run
+  // on one XCD
+  const int ntn = (int)cdiv64(a.d, BN);
+  int z, t;
+  if (!xcd_group_tile(a.ksplit, ntn * (int)cdiv64(a.M, BM), &z, &t)) return;
+  const int n0 = (t % ntn) * BN;
+  const int64_t m0 = (int64_t)(t / ntn) * BM;
   const int nk = a.vocab / G::BK;
   const int kbeg = (int)((int64_t)z * nk / a.ksplit) * G::BK;
   const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * G::BK;
   const T *ptl = static_cast<const T *>(a.ptilde);
   const T *et = static_cast<const T *>(a.embed_t);
-  ScaledRowLoader<T, G::AI> al;
+  ShiftedRowLoader<T, G::AI> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
     const bool ok = row < a.M;
     al.p[it] = ptl + (ok ? row * a.vocab : 0);
-    al.f[it] = a.fscale + (ok ? row * a.nvt : 0);
+    al.sh[it] = a.shift + (ok ? row * a.nvt : 0);
     al.live[it] = ok;
   }
   RowLoader<T, G::BI> bl;
@@ -593,7 +636,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
         const int col = n0 + wn * G::WN + j * 16 + (lane & 15);
         if (col >= a.d) continue;
         if (a.ksplit == 1)
-          static_cast<T *>(a.out)[row * a.d + col] = from_f<T>(acc[i][j][r]);
+          static_cast<T *>(a.out)[row * a.d + col] = from_f<T>(acc[i][j][r] * a.inv_z[row]);
         else
           a.part[((int64_t)z * a.M + row) * a.d + col] = acc[i][j][r];
       }
@@ -602,13 +645,13 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
 
 // fixed-order sum of the split-K partials
 template <typename T>
-__global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, void *out, int64_t n,
-                                                        int ksplit) {
+__global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, const float *inv_z,
+                                                        void *out, int64_t n, int d, int ksplit) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
   for (int z = 0; z < ksplit; ++z) s += part[(int64_t)z * n + i];
-  static_cast<T *>(out)[i] = from_f<T>(s);
+  static_cast<T *>(out)[i] = from_f<T>(s * inv_z[i / d]);
 }
 
 // ---------------------------------------------------------------------------
@@ -616,7 +659,7 @@ __global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, void 
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
-  dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.nq + 2 * a.nkv, BN));
+  const dim3 grid = xcd_grid(cdiv64(a.nq + 2 * a.nkv, BN), cdiv64(a.M, BM));
   if (a.sc_in)
     hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK, true>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   else
@@ -638,7 +681,7 @@ hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
 
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_oproj_t(const OprojArgs &a, hipStream_t st) {
-  dim3 grid((unsigned)cdiv64(a.M, BM), (unsigned)cdiv64(a.d, BN));
+  const dim3 grid = xcd_grid(cdiv64(a.d, BN), cdiv64(a.M, BM));
   hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN, PF, BK>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   return hipGetLastError();
 }
@@ -668,10 +711,14 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Vocabulary ranges of the self-conditioning GEMM.  Each range's tiles run on
+// one XCD (xcd_group_tile); with one workgroup per CU and 32 CUs per XCD, as
+// many whole ranges per XCD as fit in 32 workgroups.
 int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
-  const int64_t tiles = bf ? cdiv64(M, 256) * cdiv64(d, 256) : cdiv64(M, 64) * cdiv64(d, 64);
+  const int64_t tiles = bf ? cdiv64(M, 256) * cdiv64(d, kScTileD) : cdiv64(M, 64) * cdiv64(d, 64);
   const int nk = vocab / (bf ? 64 : 16);
-  int64_t ks = 256 / tiles;  // about one workgroup per compute unit, no partial second wave
+  const int64_t per_xcd = 32 / tiles;
+  int64_t ks = per_xcd >= 1 ? 8 * per_xcd : 8;
   if (ks > nk) ks = nk;
   if (ks > 64) ks = 64;
   if (ks < 1) ks = 1;
@@ -680,10 +727,10 @@ int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
 
 hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
   if (bf) {
-    dim3 grid((unsigned)cdiv64(a.d, 256), (unsigned)cdiv64(a.M, 256), (unsigned)a.ksplit);
-    hipLaunchKernelGGL((scgemm_kernel<bf16, 256, 256, 4, 2, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
+    const dim3 grid = xcd_grid(a.ksplit, cdiv64(a.d, kScTileD) * cdiv64(a.M, 256));
+    hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
-    dim3 grid((unsigned)cdiv64(a.d, 64), (unsigned)cdiv64(a.M, 64), (unsigned)a.ksplit);
+    const dim3 grid = xcd_grid(a.ksplit, cdiv64(a.d, 64) * cdiv64(a.M, 64));
     hipLaunchKernelGGL((scgemm_kernel<float, 64, 64, 2, 2, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
   }
   hipError_t e = hipGetLastError();
@@ -691,10 +738,10 @@ hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
   const int64_t n = a.M * a.d;
   if (bf)
     hipLaunchKernelGGL((sc_reduce_kernel<bf16>), dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st,
-                       a.part, a.out, n, a.ksplit);
+                       a.part, a.inv_z, a.out, n, a.d, a.ksplit);
   else
     hipLaunchKernelGGL((sc_reduce_kernel<float>), dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st,
-                       a.part, a.out, n, a.ksplit);
+                       a.part, a.inv_z, a.out, n, a.d, a.ksplit);
   return hipGetLastError();
 }
 

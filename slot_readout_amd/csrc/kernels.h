@@ -41,8 +41,10 @@ struct LmheadArgs {
   int rows_per_flag;
   float logit_scale;
   const float *row_scale;  // [nrows] or null
-  float4 *stats;           // [nrows, nvt] (m, sum e, sum e*(l-m), argmax bits)
-  void *ptilde;            // [nrows, V] T or null
+  // per (row, tile): (m = max l, sum e, sum e*(l - r ln2), argmax bits) with
+  // e = e^(l - r ln2), r = tile_ref(m)
+  float4 *stats;           // [nrows, nvt]
+  void *ptilde;            // [nrows, V] T or null: e^(l - r ln2) of the row's tile
   float *logits;           // [nrows, V] or null
   // label logits of slot rows (optional): row n belongs to slot
   // bs = (n / lab_span) * lab_S + n % lab_S, whose lab_n[bs] label ids are
@@ -57,7 +59,8 @@ struct LmheadArgs {
 
 struct ScArgs {
   const void *ptilde;      // [M, V]
-  const float *fscale;     // [M, nvt]
+  const int32_t *shift;    // [M, nvt] p = p~ * 2^-shift / Z
+  const float *inv_z;      // [M] 1/Z
   const void *embed_t;     // [d, V]
   float *part;             // [ksplit, M, d]
   void *out;               // [M, d] T
@@ -72,7 +75,8 @@ struct VocabMergeArgs {
   float *conf, *entropy;   // [nrows] or null
   int32_t *argmax;         // [nrows] or null
   float2 *rowstat;         // [nrows] (m, lse) or null
-  float *fscale;           // [nrows, nvt] e^(m_t - m)/Z or null
+  int32_t *shift;          // [nrows, nvt] R - r_t (R = max_t r_t) or null
+  float *inv_z;            // [nrows] 1/Z, Z = sum_v e^(l_v - R ln2) (with shift)
 };
 
 struct AttnArgs {

@@ -18,40 +18,45 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(VocabMergeArgs a) {
   if (row >= a.nrows) return;
   const float4 *st = a.stats + row * a.nvt;
   float m = -INFINITY;
-  int id = 0x7fffffff;
+  int id = 0x7fffffff, R = -(1 << 30);
   for (int t = lane; t < a.nvt; t += 64) {
     const float4 v = st[t];
     const int i = __float_as_int(v.w);
     if (v.x > m || (v.x == m && i < id)) { m = v.x; id = i; }
+    R = max(R, tile_ref(v.x));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o);
     const int i2 = __shfl_xor(id, o);
     if (m2 > m || (m2 == m && i2 < id)) { m = m2; id = i2; }
+    R = max(R, __shfl_xor(R, o));
   }
-  float Z = 0.f, T = 0.f;
+  // Z = sum_t 2^(r_t - R) S_t and A = sum_t 2^(r_t - R) (T_t + (r_t - R) ln2 S_t),
+  // both relative to R ln2: then lse = R ln2 + ln Z and H = ln Z - A / Z
+  float Z = 0.f, A = 0.f;
   for (int t = lane; t < a.nvt; t += 64) {
     const float4 v = st[t];
-    const float dm = v.x - m;
-    const float w = __expf(dm);
+    const int dr = tile_ref(v.x) - R;   // <= 0
+    const float w = ldexpf(1.f, dr);
     Z += v.y * w;
-    T += w * (v.z + dm * v.y);
+    A += w * (v.z + (float)dr * kLn2 * v.y);
   }
   Z = wave_sum(Z);
-  T = wave_sum(T);
+  A = wave_sum(A);
   const float lnZ = __logf(Z);
+  const float lse = (float)R * kLn2 + lnZ;
   if (lane == 0) {
-    float H = lnZ - T / Z;
+    float H = lnZ - A / Z;
     if (H < 0.f) H = 0.f;
-    if (a.conf) a.conf[row] = 1.f / Z;
+    if (a.conf) a.conf[row] = __expf(fmaf(-(float)R, kLn2, m)) / Z;   // e^(m - lse)
     if (a.entropy) a.entropy[row] = H;
     if (a.argmax) a.argmax[row] = id;
-    if (a.rowstat) a.rowstat[row] = make_float2(m, m + lnZ);
+    if (a.rowstat) a.rowstat[row] = make_float2(m, lse);
+    if (a.inv_z) a.inv_z[row] = 1.f / Z;
   }
-  if (a.fscale) {
-    const float invZ = 1.f / Z;
-    for (int t = lane; t < a.nvt; t += 64) a.fscale[row * a.nvt + t] = __expf(st[t].x - m) * invZ;
+  if (a.shift) {
+    for (int t = lane; t < a.nvt; t += 64) a.shift[row * a.nvt + t] = R - tile_ref(st[t].x);
   }
 }
 
