@@ -425,9 +425,11 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   __shared__ int red_i[WGM][BN];
   __shared__ float red_s[WGM][BN];
   __shared__ float red_t[WGM][BN];
-  const int vt = blockIdx.x;
+  // group = vocabulary tile; its row tiles share the E tile and run on one XCD
+  int vt, rt;
+  if (!xcd_group_tile(a.vocab / BM, (int)cdiv64(a.nrows, BN), &vt, &rt)) return;
   const int v0 = vt * BM;
-  const int64_t n0 = (int64_t)blockIdx.y * BN;
+  const int64_t n0 = (int64_t)rt * BN;
   const int d = a.d;
   if (a.active_rows && !tile_active(a.active_rows, n0, BN, a.nrows, a.rows_per_flag)) return;
   const T *head = static_cast<const T *>(a.head);
@@ -695,17 +697,20 @@ hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
   return launch_oproj_t<float, 64, 64, 2, 2, 1, 16>(a, st);
 }
 
+// row count up to which the LM head uses 64-row tiles
+constexpr int64_t kLmFewRows = 64;
+
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
-  if (bf && a.nrows <= 64) {
+  if (bf && a.nrows <= kLmFewRows) {
     // few rows (slot reads): a 64-row tile keeps the MFMA work proportional to
     // the rows and three workgroups per CU keep the vocabulary stream busy
-    dim3 grid((unsigned)(a.vocab / VTILE), 1);
+    const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
     hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
   } else if (bf) {
-    dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 256));
+    const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
     hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
-    dim3 grid((unsigned)(a.vocab / VTILE), (unsigned)cdiv64(a.nrows, 64));
+    const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
     hipLaunchKernelGGL((lmhead_kernel<float, VTILE, 64, 4, 1, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
   }
   return hipGetLastError();
