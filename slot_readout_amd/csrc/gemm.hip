@@ -276,9 +276,12 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
   return false;
 }
 
-// width of the d tiles of the bf16 self-conditioning GEMM: 15 tiles cover
-// d = 2816, so two vocabulary ranges (30 workgroups) fill an XCD's 32 CUs
-constexpr int kScTileD = 192;
+// Self-conditioning GEMM: d tiles of 256 and about one workgroup per CU.
+// Keeping each vocabulary range's tiles on one XCD (kScGroup) cuts the p~
+// re-reads that reach HBM by ~40% but leaves CUs idle at d = 2816 (11 tiles
+// per range), and measured slower (555-618 us against 481 us), so it is off.
+constexpr int kScTileD = 256;
+constexpr bool kScGroup = false;
 
 // Workgroup id -> (group g, tile t): the nt tiles of a group share an operand
 // (a weight tile, a slice of p~).  Workgroups are dealt to the 8 XCDs
@@ -600,7 +603,14 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
   // on one XCD
   const int ntn = (int)cdiv64(a.d, BN);
   int z, t;
-  if (!xcd_group_tile(a.ksplit, ntn * (int)cdiv64(a.M, BM), &z, &t)) return;
+  if constexpr (kScGroup) {
+    if (!xcd_group_tile(a.ksplit, ntn * (int)cdiv64(a.M, BM), &z, &t)) return;
+  } else {
+    const int nt = ntn * (int)cdiv64(a.M, BM);
+    if ((int)blockIdx.x >= a.ksplit * nt) return;
+    z = blockIdx.x / nt;
+    t = blockIdx.x % nt;
+  }
   const int n0 = (t % ntn) * BN;
   const int64_t m0 = (int64_t)(t / ntn) * BM;
   const int nk = a.vocab / G::BK;
@@ -716,14 +726,13 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Vocabulary ranges of the self-conditioning GEMM.  Each range's tiles run on
-// one XCD (xcd_group_tile); with one workgroup per CU and 32 CUs per XCD, as
-// many whole ranges per XCD as fit in 32 workgroups.
+// Vocabulary ranges of the self-conditioning GEMM: about one workgroup per CU
+// (with XCD grouping: as many whole ranges per XCD as fit its 32 CUs).
 int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
   const int64_t tiles = bf ? cdiv64(M, 256) * cdiv64(d, kScTileD) : cdiv64(M, 64) * cdiv64(d, 64);
   const int nk = vocab / (bf ? 64 : 16);
   const int64_t per_xcd = 32 / tiles;
-  int64_t ks = per_xcd >= 1 ? 8 * per_xcd : 8;
+  int64_t ks = kScGroup ? (per_xcd >= 1 ? 8 * per_xcd : 8) : 256 / tiles;
   if (ks > nk) ks = nk;
   if (ks > 64) ks = 64;
   if (ks < 1) ks = 1;
@@ -732,10 +741,12 @@ int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
 
 hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
   if (bf) {
-    const dim3 grid = xcd_grid(a.ksplit, cdiv64(a.d, kScTileD) * cdiv64(a.M, 256));
+    const dim3 grid = kScGroup ? xcd_grid(a.ksplit, cdiv64(a.d, kScTileD) * cdiv64(a.M, 256))
+                               : dim3((unsigned)(a.ksplit * cdiv64(a.d, kScTileD) * cdiv64(a.M, 256)));
     hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
-    const dim3 grid = xcd_grid(a.ksplit, cdiv64(a.d, 64) * cdiv64(a.M, 64));
+    const int64_t nt = cdiv64(a.d, 64) * cdiv64(a.M, 64);
+    const dim3 grid = kScGroup ? xcd_grid(a.ksplit, nt) : dim3((unsigned)(a.ksplit * nt));
     hipLaunchKernelGGL((scgemm_kernel<float, 64, 64, 2, 2, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
   }
   hipError_t e = hipGetLastError();
