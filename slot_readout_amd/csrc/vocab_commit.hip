@@ -17,14 +17,29 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(VocabMergeArgs a) {
   const int lane = threadIdx.x & 63;
   if (row >= a.nrows) return;
   const float4 *st = a.stats + row * a.nvt;
+  // the row's tile statistics: up to 64 * KC of them stay in registers between
+  // the passes (all of them up to a 262,144-entry vocabulary)
+  constexpr int KC = 16;
+  float4 vc[KC];
+#pragma unroll
+  for (int q = 0; q < KC; ++q) {
+    const int t = lane + 64 * q;
+    vc[q] = t < a.nvt ? st[t] : make_float4(-INFINITY, 0.f, 0.f, __int_as_float(0x7fffffff));
+  }
+  // f(v) over the row's tiles: the register copies, then any beyond them
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int q = 0; q < KC; ++q)
+      if (lane + 64 * q < a.nvt) f(vc[q]);
+    for (int t = lane + 64 * KC; t < a.nvt; t += 64) f(st[t]);
+  };
   float m = -INFINITY;
   int id = 0x7fffffff, R = -(1 << 30);
-  for (int t = lane; t < a.nvt; t += 64) {
-    const float4 v = st[t];
+  each([&](const float4 &v) {
     const int i = __float_as_int(v.w);
     if (v.x > m || (v.x == m && i < id)) { m = v.x; id = i; }
     R = max(R, tile_ref(v.x));
-  }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(m, o);
@@ -35,13 +50,12 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(VocabMergeArgs a) {
   // Z = sum_t 2^(r_t - R) S_t and A = sum_t 2^(r_t - R) (T_t + (r_t - R) ln2 S_t),
   // both relative to R ln2: then lse = R ln2 + ln Z and H = ln Z - A / Z
   float Z = 0.f, A = 0.f;
-  for (int t = lane; t < a.nvt; t += 64) {
-    const float4 v = st[t];
+  each([&](const float4 &v) {
     const int dr = tile_ref(v.x) - R;   // <= 0
     const float w = ldexpf(1.f, dr);
     Z += v.y * w;
     A += w * (v.z + (float)dr * kLn2 * v.y);
-  }
+  });
   Z = wave_sum(Z);
   A = wave_sum(A);
   const float lnZ = __logf(Z);
@@ -56,7 +70,10 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(VocabMergeArgs a) {
     if (a.inv_z) a.inv_z[row] = 1.f / Z;
   }
   if (a.shift) {
-    for (int t = lane; t < a.nvt; t += 64) a.shift[row * a.nvt + t] = R - tile_ref(st[t].x);
+#pragma unroll
+    for (int q = 0; q < KC; ++q)
+      if (lane + 64 * q < a.nvt) a.shift[row * a.nvt + lane + 64 * q] = R - tile_ref(vc[q].x);
+    for (int t = lane + 64 * KC; t < a.nvt; t += 64) a.shift[row * a.nvt + t] = R - tile_ref(st[t].x);
   }
 }
 
@@ -73,8 +90,7 @@ hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st) {
 // fixed Hillis-Steele scan in LDS, and rank k is accepted iff prefix_k <= tau.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
-  __shared__ float sconf[DG_MAX_CANVAS];
-  __shared__ int scand[DG_MAX_CANVAS];
+  __shared__ __attribute__((aligned(16))) float sconf[DG_MAX_CANVAS];
   __shared__ float scan[2][DG_MAX_CANVAS];
   const int b = blockIdx.x, i = threadIdx.x, C = a.C, n = blockDim.x;
   const int64_t base = (int64_t)b * C;
@@ -88,17 +104,26 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
     c = a.conf[base + i];
     H = a.entropy[base + i];
   }
-  sconf[i] = c;
-  scand[i] = cand ? 1 : 0;
+  // non-candidates (and padding threads) rank below every candidate
+  sconf[i] = cand ? c : -INFINITY;
   scan[0][i] = 0.f;
   __syncthreads();
   int rank = 0;
   if (cand) {
-    for (int j = 0; j < C; ++j) {
-      if (!scand[j]) continue;
-      const float cj = sconf[j];
-      rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
+    // rank = #{candidates j : c_j > c, or c_j == c and j < i}; four positions
+    // per LDS read (a broadcast), no branches
+    const float4 *s4 = reinterpret_cast<const float4 *>(sconf);
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+#pragma unroll 4
+    for (int j4 = 0; j4 < n / 4; ++j4) {
+      const float4 q = s4[j4];
+      const int j = 4 * j4;
+      r0 += (q.x > c) | ((q.x == c) & (j < i));
+      r1 += (q.y > c) | ((q.y == c) & (j + 1 < i));
+      r2 += (q.z > c) | ((q.z == c) & (j + 2 < i));
+      r3 += (q.w > c) | ((q.w == c) & (j + 3 < i));
     }
+    rank = (r0 + r1) + (r2 + r3);
     scan[0][rank] = H;
   }
   __syncthreads();
