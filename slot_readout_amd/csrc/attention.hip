@@ -106,7 +106,6 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const int i0 = qt * NQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const float c2 = a.scale_log2;   // scores are kept raw; exponents use s*c2 - m
 
   int64_t p0, plen;
   int lo, hi;
@@ -263,12 +262,18 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
     }
   };
 
+  // Scores are in log2 units (q is pre-scaled).  Each query column keeps a
+  // reference mref (its running max, 0 before the first key); the score MFMAs
+  // start from -mref, so they produce s - mref directly.
+  float mref[QB];
+  f32x4 negm[QB];
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) {
+    mref[jb] = 0.f;
+    negm[jb] = zero4();
+  }
   auto compute = [&](const Blk &d, int bf) {
     f32x4 sacc[NK / 16][QB];
-#pragma unroll
-    for (int kb2 = 0; kb2 < NK / 16; ++kb2)
-#pragma unroll
-      for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -276,7 +281,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
         const frag af = *reinterpret_cast<const frag *>(Ks[bf] + (kb2 * 16 + col) * KP + ks * MF::KI +
                                                          grp * MF::KPL);
 #pragma unroll
-        for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] = MF::mma(af, qf[jb][ks], sacc[kb2][jb]);
+        for (int jb = 0; jb < QB; ++jb)
+          sacc[kb2][jb] = MF::mma(af, qf[jb][ks], ks == 0 ? negm[jb] : sacc[kb2][jb]);
       }
 
     const bool full = !d.canvas && d.rem == NK;   // uniform: no key of the block is masked
@@ -297,32 +303,37 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
             sacc[kb2][jb][r] = ok ? sacc[kb2][jb][r] : -INFINITY;
           }
       }
-      float bm = -INFINITY;
+      float bm = -INFINITY;   // block max relative to mref
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
         for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sacc[kb2][jb][r]);
-      bm = group4_max(bm) * c2;
-      // The reference max is raised only when the block's max exceeds it by
-      // more than kLazy (log2 units); until then the exponentials stay below
-      // 2^kLazy and nothing is rescaled.  The sum of p (the ones row) shares the
-      // reference, so the normalised result does not depend on it.
-      const bool grow = bm > mrun[jb] + kLazy;
-      const float mnew = grow ? bm : mrun[jb];
-      const float msub = mnew == -INFINITY ? 0.f : mnew;
-      // raw v_exp_f32: every argument here is <= kLazy or -inf, so no range
-      // handling is needed
-      const float alpha = grow ? __builtin_amdgcn_exp2f(mrun[jb] - msub) : 1.f;
+      bm = group4_max(bm);
+      // The reference is raised only when the block's max exceeds it by more
+      // than kLazy (or on the first keys); until then the exponentials stay
+      // below 2^kLazy and nothing is rescaled.  The sum of p (the ones row)
+      // shares the reference, so the normalised result does not depend on it.
+      const bool grow = bm > kLazy || (mrun[jb] == -INFINITY && bm != -INFINITY);
+      if (__any(grow)) {
+        const float delta = grow ? bm : 0.f;
+        const float alpha = mrun[jb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+        for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[kb2][jb][r] -= delta;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][jb] *= alpha;
+        if (grow) {
+          mref[jb] += delta;
+          mrun[jb] = mref[jb];
+          negm[jb] = f32x4{-mref[jb], -mref[jb], -mref[jb], -mref[jb]};
+        }
+      }
+      // raw v_exp_f32: every argument is <= kLazy or -inf
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sacc[kb2][jb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][jb][r], c2, -msub));
-      mrun[jb] = mnew;
-      if (__any(grow)) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) oacc[rb][jb] *= alpha;
-      }
+        for (int r = 0; r < 4; ++r) sacc[kb2][jb][r] = __builtin_amdgcn_exp2f(sacc[kb2][jb][r]);
     }
 
     if constexpr (MF::KPL == 8) {

@@ -251,6 +251,9 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   qa.nkv = d.n_kv_heads * d.head_dim;
   qa.vocab = d.vocab;
   qa.C = d.canvas;
+  // the softmax scale in log2 units rides on q, so attention exponentiates
+  // scores directly (one rounding of q either way)
+  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
   DG_MARK(sg, DG_STAGE_QKV, 0);
   DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "qkv projection launch");
   DG_MARK(sg, DG_STAGE_QKV, 1);
@@ -277,7 +280,6 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.nsplit = ap.nsplit;
   aa.chunk = ap.chunk;
   aa.canvas_per_prompt = canvas_per_prompt;
-  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
   DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
   DG_MARK(sg, DG_STAGE_ATTENTION, 1);

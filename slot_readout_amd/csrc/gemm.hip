@@ -31,10 +31,11 @@ struct Gemm {
   // instruction) are free of bank conflicts on gfx950 for 128-byte rows whose
   // chunks are XOR-swizzled by (row & 7), and for 64-byte rows padded to 96
   // bytes; a 16-byte pad on 128-byte rows costs 2x, no pad and no swizzle 4x
-  // (SQ_LDS_BANK_CONFLICT).  fp32 tiles keep a 16-byte pad.
-  static constexpr bool SWZ = sizeof(T) == 2 && BK == 64;
+  // (SQ_LDS_BANK_CONFLICT).  Longer rows swizzle over all their chunks.  fp32
+  // tiles keep a 16-byte pad.
+  static constexpr bool SWZ = sizeof(T) == 2 && BK >= 64;
   static constexpr int PITCH = SWZ ? BK : (sizeof(T) == 2 && BK == 32 ? 48 : BK + VEC);
-  __device__ static inline int chunk_at(int row, int c) { return SWZ ? c ^ (row & 7) : c; }
+  __device__ static inline int chunk_at(int row, int c) { return SWZ ? c ^ (row & (CPR - 1)) : c; }
   static constexpr int AI = BM * CPR / NT;  // A chunks per thread per K step
   static constexpr int BI = BN * CPR / NT;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -101,6 +102,7 @@ struct Gemm {
         // rows differ from (lane & 15) by multiples of 16, so the swizzle
         // depends on the lane only
         const int ko = SWZ ? chunk_at(lane & 15, kk / VEC) * VEC : kk;
+        static_assert(!SWZ || CPR <= 16, "swizzle assumes rows of at most 16 chunks");
 #pragma unroll
         for (int i = 0; i < TM; ++i)
           a[i] = *reinterpret_cast<const frag *>(As + (wm * WM + i * 16 + (lane & 15)) * PITCH + ko);
@@ -347,7 +349,8 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
     if (col >= ntot) continue;
     T *base;
     int ld, c;
-    if (col < nq) { base = q; ld = nq; c = col; }
+    float sc = 1.f;
+    if (col < nq) { base = q; ld = nq; c = col; sc = a.q_scale; }
     else if (col < nq + nk) { base = k; ld = nk; c = col - nq; }
     else { base = v; ld = nk; c = col - nq - nk; }
 #pragma unroll
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
-        if (row < a.M) base[row * ld + c] = from_f<T>(acc[i][j][r]);
+        if (row < a.M) base[row * ld + c] = from_f<T>(acc[i][j][r] * sc);
       }
   }
 }
@@ -684,7 +687,7 @@ static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
 hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
   const int64_t ntot = a.nq + 2 * a.nkv;
   if (bf) {
-    if (cdiv64(a.M, 128) * cdiv64(ntot, 128) >= 512)
+    if (cdiv64(a.M, 128) * cdiv64(ntot, 128) >= 256)
       return launch_qkv_t<bf16, 128, 128, 2, 2, 2, 64>(a, st);
     return launch_qkv_t<bf16, 64, 64, 2, 2, 4, 64>(a, st);
   }

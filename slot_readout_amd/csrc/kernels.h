@@ -18,6 +18,7 @@ struct QkvArgs {
   void *q, *k, *v;         // [M, nq], [M, nkv], [M, nkv]
   const int32_t *active;   // per-canvas flag or null (rows of inactive canvases skipped)
   int32_t *flags;          // device flag word or null
+  float q_scale;            // q is written as (x Wq^T) * q_scale
   int64_t M;
   int d, nq, nkv, vocab, C;
 };
@@ -90,7 +91,7 @@ struct AttnArgs {
   float2 *part_ml;             // [nsplit, nc*Hq*C]
   int64_t total_len;
   int nc, C, Hq, Hkv, W, max_len, nsplit, chunk, canvas_per_prompt;
-  float scale_log2;            // log2(e) / sqrt(hd)
+  // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
 };
 
 struct CommitArgs {
