@@ -265,6 +265,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   // Scores are in log2 units (q is pre-scaled).  Each query column keeps a
   // reference mref (its running max, 0 before the first key); the score MFMAs
   // start from -mref, so they produce s - mref directly.
+  // (at hd 512 the four registers of -mref are not spared: the scores start
+  // from zero and mref is subtracted afterwards, 8 values per lane)
+  constexpr bool INIT_NEG = HD <= 64;
   float mref[QB];
   f32x4 negm[QB];
 #pragma unroll
@@ -282,8 +285,14 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
                                                          grp * MF::KPL);
 #pragma unroll
         for (int jb = 0; jb < QB; ++jb)
-          sacc[kb2][jb] = MF::mma(af, qf[jb][ks], ks == 0 ? negm[jb] : sacc[kb2][jb]);
+          sacc[kb2][jb] = MF::mma(af, qf[jb][ks], ks == 0 ? (INIT_NEG ? negm[jb] : zero4()) : sacc[kb2][jb]);
       }
+    if constexpr (!INIT_NEG) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+        for (int jb = 0; jb < QB; ++jb) sacc[kb2][jb] -= mref[jb];
+    }
 
     const bool full = !d.canvas && d.rem == NK;   // uniform: no key of the block is masked
 #pragma unroll
@@ -326,7 +335,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
         if (grow) {
           mref[jb] += delta;
           mrun[jb] = mref[jb];
-          negm[jb] = f32x4{-mref[jb], -mref[jb], -mref[jb], -mref[jb]};
+          if constexpr (INIT_NEG) negm[jb] = f32x4{-mref[jb], -mref[jb], -mref[jb], -mref[jb]};
         }
       }
       // raw v_exp_f32: every argument is <= kLazy or -inf
