@@ -45,6 +45,27 @@ __device__ inline void pin4(uint4 &v) {
 
 constexpr float kLazy = 8.f;
 
+// Split partials of O are kept in the storage type: fp32, or bf16 whose
+// rounding (2^-9 relative) matches that of the final bf16 output.
+template <typename T> __device__ inline void store4v(T *p, f32x4 v);
+template <> __device__ inline void store4v<float>(float *p, f32x4 v) {
+  *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <> __device__ inline void store4v<bf16>(bf16 *p, f32x4 v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  *reinterpret_cast<bf16x4 *>(p) = b;
+}
+template <typename T> __device__ inline float4 load4v(const T *p);
+template <> __device__ inline float4 load4v<float>(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+template <> __device__ inline float4 load4v<bf16>(const bf16 *p) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+  return make_float4((float)b[0], (float)b[1], (float)b[2], (float)b[3]);
+}
+
 // Keys of the query tile starting at canvas position i0 of canvas cb, in the
 // order the splits cut them: every prompt key of the canvas's sequence (rows
 // [p0, p0 + plen) of the cache, offsets clamped against corrupt cu_seqlens, in
@@ -438,11 +459,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
         for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<T>(oacc[rb][jb][r] * inv);
     } else {
       const int64_t row = ((int64_t)cb * a.Hq + h) * C + qi;
-      float *po = a.part_o + ((int64_t)s * R + row) * HD;
+      T *po = static_cast<T *>(a.part_o) + ((int64_t)s * R + row) * HD;
 #pragma unroll
-      for (int rb = 0; rb < HD / 16; ++rb)
-        *reinterpret_cast<float4 *>(po + rb * 16 + grp * 4) =
-            make_float4(oacc[rb][jb][0], oacc[rb][jb][1], oacc[rb][jb][2], oacc[rb][jb][3]);
+      for (int rb = 0; rb < HD / 16; ++rb) store4v<T>(po + rb * 16 + grp * 4, oacc[rb][jb]);
       if (grp == 0) a.part_ml[(int64_t)s * R + row] = make_float2(mrun[jb], L);
     }
   }
@@ -478,8 +497,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int64_t nk = plen + (hi - lo);
   const int ns = (int)(cdiv64(nk, a.chunk) < a.nsplit ? cdiv64(nk, a.chunk) : a.nsplit);
   const float2 *ml = a.part_ml + row;
-  const float4 *po = reinterpret_cast<const float4 *>(a.part_o) + row * C4 + c0;
-  const int64_t sstride = R * C4;   // float4 chunks between splits
+  const T *po = static_cast<const T *>(a.part_o) + (row * C4 + c0) * 4;
+  const int64_t sstride = R * C4 * 4;   // elements between splits
 
   float M = -INFINITY;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[(int64_t)s * R].x);
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       L += v.y * w;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float4 o = po[s * sstride + 64 * c];
+        const float4 o = load4v<T>(po + s * sstride + 256 * c);
         acc[c].x += w * o.x; acc[c].y += w * o.y; acc[c].z += w * o.z; acc[c].w += w * o.w;
       }
     }

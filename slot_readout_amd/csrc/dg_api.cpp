@@ -112,7 +112,7 @@ AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt) {
                 &p.chunk);
   if (p.nsplit > 1) {
     const size_t R = (size_t)nc * d.n_q_heads * d.canvas;
-    p.part_o = (size_t)p.nsplit * R * d.head_dim * sizeof(float);
+    p.part_o = (size_t)p.nsplit * R * d.head_dim * tsize(d);
     p.part_ml = (size_t)p.nsplit * R * sizeof(float2);
   }
   return p;
@@ -229,7 +229,7 @@ template <typename P> P *at(void *ws, size_t off) {
 dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *kv, int nc,
                     int canvas_per_prompt, const int32_t *ids, const void *sc_in,
                     const int32_t *active, int32_t *flags, void *q, void *k, void *v, void *o,
-                    const AttnPlan &ap, float *part_o, float2 *part_ml, void *h, hipStream_t st,
+                    const AttnPlan &ap, void *part_o, float2 *part_ml, void *h, hipStream_t st,
                     const Stages &sg = Stages()) {
   const bool bf = d.dtype == DG_BF16;
   const int64_t M = (int64_t)nc * d.canvas;
@@ -392,7 +392,7 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
   s = run_block(d, w, kv, batch, 1, canvas_ids, sc_in, nullptr, dev_flags, at<char>(workspace, p.q),
                 at<char>(workspace, p.k), at<char>(workspace, p.v), o, p.attn,
-                at<float>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st, sg);
+                at<char>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st, sg);
   if (s != DG_OK) return s;
 
   dg::LmheadArgs la{};
@@ -505,7 +505,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   const int nvt = d.vocab / dg::VTILE;
   void *q = at<char>(workspace, p.q), *k = at<char>(workspace, p.k), *v = at<char>(workspace, p.v);
   void *o = at<char>(workspace, p.o), *h = at<char>(workspace, p.h);
-  float *part_o = at<float>(workspace, p.part_o);
+  void *part_o = at<char>(workspace, p.part_o);
   float2 *part_ml = at<float2>(workspace, p.part_ml);
 
   dg::SlotArgs sa{};

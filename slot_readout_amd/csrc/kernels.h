@@ -87,7 +87,7 @@ struct AttnArgs {
   const int32_t *active;       // per-canvas flag or null
   int32_t *flags;
   void *o;                     // [nc, C, Hq, hd]
-  float *part_o;               // [nsplit, nc*Hq*C, hd]
+  void *part_o;                // [nsplit, nc*Hq*C, hd] storage type
   float2 *part_ml;             // [nsplit, nc*Hq*C]
   int64_t total_len;
   int nc, C, Hq, Hkv, W, max_len, nsplit, chunk, canvas_per_prompt;
