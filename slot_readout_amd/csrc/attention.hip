@@ -119,8 +119,14 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   constexpr int VSZ = TR ? NK * VKP : RB * 16 * VP;
   __shared__ __attribute__((aligned(16))) T Vt[2][VSZ];
 
-  const int s = blockIdx.x, qt = blockIdx.y;
-  const int cb = blockIdx.z / a.Hq, h = blockIdx.z % a.Hq;
+  // group = (canvas, kv head, split); its tiles (the query heads sharing the
+  // kv head x the query tiles) read the same K/V blocks and run on one XCD
+  const int nqt = (a.C + NQ - 1) / NQ;
+  int grpi, tile;
+  if (!xcd_group_tile(a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * nqt, &grpi, &tile)) return;
+  const int s = grpi % a.nsplit;
+  const int cb = grpi / a.nsplit / a.Hkv;
+  const int h = (grpi / a.nsplit % a.Hkv) * (a.Hq / a.Hkv) + tile / nqt, qt = tile % nqt;
   if (a.active && !a.active[cb]) return;
   const int G = a.Hq / a.Hkv, g = h / G;
   const int C = a.C, W = a.W;
@@ -583,7 +589,7 @@ template <typename T, int HD>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NW = AttnShape<T, HD>::NW;
   constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
-  dim3 grid((unsigned)a.nsplit, (unsigned)cdiv64(a.C, NQ), (unsigned)(a.nc * a.Hq));
+  const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * cdiv64(a.C, NQ));
   hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;

@@ -111,4 +111,19 @@ __device__ inline int tile_ref(float m) {
   return m > -1e30f ? (int)ceilf(m * kLog2e) : -(1 << 28);
 }
 
+// Workgroup id -> (group g, tile t): the nt tiles of a group share an operand
+// (a weight tile, a slice of p~).  Workgroups are dealt to the 8 XCDs
+// round-robin by id, so whole groups are dealt to one XCD at a time and each
+// group's tiles share that XCD's L2.  Launch 8 * cdiv(ngroups, 8) * nt
+// workgroups; ids past the last group return false.
+__device__ inline bool xcd_group_tile(int ngroups, int nt, int *g, int *t) {
+  const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
+  *g = xcd + 8 * (local / nt);
+  *t = local % nt;
+  return *g < ngroups;
+}
+static inline dim3 xcd_grid(int64_t ngroups, int64_t nt) {
+  return dim3((unsigned)(8 * cdiv64(ngroups, 8) * nt));
+}
+
 }  // namespace dg

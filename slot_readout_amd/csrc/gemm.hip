@@ -285,20 +285,6 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
 constexpr int kScTileD = 256;
 constexpr bool kScGroup = false;
 
-// Workgroup id -> (group g, tile t): the nt tiles of a group share an operand
-// (a weight tile, a slice of p~).  Workgroups are dealt to the 8 XCDs
-// round-robin by id, so whole groups are dealt to one XCD at a time and each
-// group's tiles share that XCD's L2.  Launch 8 * cdiv(ngroups, 8) * nt
-// workgroups; ids past the last group return false.
-__device__ inline bool xcd_group_tile(int ngroups, int nt, int *g, int *t) {
-  const int id = blockIdx.x, xcd = id & 7, local = id >> 3;
-  *g = xcd + 8 * (local / nt);
-  *t = local % nt;
-  return *g < ngroups;
-}
-static inline dim3 xcd_grid(int64_t ngroups, int64_t nt) {
-  return dim3((unsigned)(8 * cdiv64(ngroups, 8) * nt));
-}
 
 // ---------------------------------------------------------------------------
 // S0+S1: q,k,v projection with the embedding gather in the A prologue
