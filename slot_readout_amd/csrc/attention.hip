@@ -5,6 +5,9 @@
 // Work split: one workgroup = (canvas, query head, tile of NQ consecutive
 // canvas positions, split).  A query tile's keys -- every prompt key, then the
 // canvas keys its window can reach -- are cut into equal splits (split-KV).
+// Queries may instead be gathered (a few positions per canvas, e.g. the slots
+// a read needs): a tile then holds NQ of them and every canvas key is a
+// candidate, masked per query.
 // With one split the workgroup writes the normalised output; otherwise it
 // writes (m, l, unnormalised O) partials that a second kernel merges in a
 // fixed order.
@@ -66,11 +69,11 @@ template <> __device__ inline float4 load4v<bf16>(const bf16 *p) {
   return make_float4((float)b[0], (float)b[1], (float)b[2], (float)b[3]);
 }
 
-// Keys of the query tile starting at canvas position i0 of canvas cb, in the
-// order the splits cut them: every prompt key of the canvas's sequence (rows
+// Keys of the query tile starting at query i0 of canvas cb, in the order the
+// splits cut them: every prompt key of the canvas's sequence (rows
 // [p0, p0 + plen) of the cache, offsets clamped against corrupt cu_seqlens, in
 // which case true is returned), then the canvas keys [lo, hi) that the tile's
-// +-W window can reach.
+// +-W window can reach (every canvas key for gathered queries).
 __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int64_t *p0o,
                                  int64_t *plen, int *lo, int *hi) {
   const int pb = cb / a.canvas_per_prompt;
@@ -82,8 +85,13 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
   if (p1 - p0 > a.max_len) { p1 = p0 + a.max_len; bad = true; }
   *p0o = p0;
   *plen = p1 - p0;
-  *lo = i0 - a.W > 0 ? i0 - a.W : 0;
-  *hi = i0 + nq + a.W < a.C ? i0 + nq + a.W : a.C;   // exclusive
+  if (a.qpos) {
+    *lo = 0;
+    *hi = a.C;
+  } else {
+    *lo = i0 - a.W > 0 ? i0 - a.W : 0;
+    *hi = i0 + nq + a.W < a.C ? i0 + nq + a.W : a.C;   // exclusive
+  }
   return bad;
 }
 
@@ -121,7 +129,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 
   // group = (canvas, kv head, split); its tiles (the query heads sharing the
   // kv head x the query tiles) read the same K/V blocks and run on one XCD
-  const int nqt = (a.C + NQ - 1) / NQ;
+  const int QN = a.qpos ? a.qn : a.C;   // queries per canvas
+  const int nqt = (QN + NQ - 1) / NQ;
   int grpi, tile;
   if (!xcd_group_tile(a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * nqt, &grpi, &tile)) return;
   const int s = grpi % a.nsplit;
@@ -161,14 +170,24 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const T *kc = static_cast<const T *>(a.k) + cbase;
   const T *vc = static_cast<const T *>(a.v) + cbase;
 
-  frag qf[QB][KS];
+  // canvas position of each query column of the lane; a column past the
+  // canvas (or a gathered query without a position) loads zeros and sees no
+  // canvas key
+  int qp[QB];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int qi = i0 + w * QB * 16 + jb * 16 + col;
+    int p = qi;
+    if (a.qpos) p = qi < QN ? a.qpos[(int64_t)cb * QN + qi] : -1;
+    qp[jb] = p >= 0 && p < C ? p : -(1 << 20);
+  }
+  frag qf[QB][KS];
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (qi < C)
-        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qi * q_stride + ks * MF::KI +
+      if (qp[jb] >= 0)
+        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qp[jb] * q_stride + ks * MF::KI +
                                                       grp * MF::KPL);
       else
         qf[jb][ks] = frag{};
@@ -325,9 +344,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 #pragma unroll
     for (int jb = 0; jb < QB; ++jb) {
       if (!full) {
-        const int qi = i0 + w * QB * 16 + jb * 16 + col;
-        // canvas keys: visible iff |key - qi| <= W, i.e. kl in [qrel - W, qrel + W]
-        const int qrel = qi - d.k0;
+        // canvas keys: visible iff |key - qp| <= W, i.e. kl in [qrel - W, qrel + W]
+        const int qrel = qp[jb] - d.k0;
         const int klo_ok = d.canvas ? qrel - W : -1;
         const int khi_ok = d.canvas ? min(qrel + W, d.rem - 1) : d.rem - 1;
 #pragma unroll
@@ -450,21 +468,21 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
     }
   }
 
-  const int64_t R = (int64_t)a.nc * a.Hq * C;
+  const int64_t R = (int64_t)a.nc * a.Hq * QN;
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int qi = i0 + w * QB * 16 + jb * 16 + col;
     const float L = group4_sum(grp == 0 ? oacc[HD / 16][jb][0] : 0.f);
-    if (qi >= C) continue;
+    if (qi >= QN) continue;
     if (a.nsplit == 1) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      T *o = static_cast<T *>(a.o) + (((int64_t)cb * C + qi) * a.Hq + h) * HD;
+      T *o = static_cast<T *>(a.o) + (((int64_t)cb * QN + qi) * a.Hq + h) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<T>(oacc[rb][jb][r] * inv);
     } else {
-      const int64_t row = ((int64_t)cb * a.Hq + h) * C + qi;
+      const int64_t row = ((int64_t)cb * a.Hq + h) * QN + qi;
       T *po = static_cast<T *>(a.part_o) + ((int64_t)s * R + row) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb) store4v<T>(po + rb * 16 + grp * 4, oacc[rb][jb]);
@@ -485,12 +503,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int SG = C4 >= 64 ? 1 : 64 / C4;     // splits read side by side
   constexpr int CPL = C4 >= 64 ? C4 / 64 : 1;    // chunks per lane
   constexpr int NQ = AttnShape<T, HD>::NW * AttnShape<T, HD>::QB * 16;
-  const int64_t R = (int64_t)a.nc * a.Hq * a.C;
+  const int QN = a.qpos ? a.qn : a.C;
+  const int64_t R = (int64_t)a.nc * a.Hq * QN;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= R) return;
-  const int C = a.C;
-  const int qi = (int)(row % C);
-  const int64_t ch = row / C;
+  const int qi = (int)(row % QN);
+  const int64_t ch = row / QN;
   const int h = (int)(ch % a.Hq);
   const int64_t cb = ch / a.Hq;
   if (a.active && !a.active[cb]) return;
@@ -545,7 +563,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
   if (g != 0) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T *o = static_cast<T *>(a.o) + ((cb * C + qi) * a.Hq + h) * HD;
+  T *o = static_cast<T *>(a.o) + ((cb * QN + qi) * a.Hq + h) * HD;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int d = 4 * (c0 + 64 * c);
@@ -562,13 +580,14 @@ static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               AttnShape<bf16, 512>::NW * AttnShape<bf16, 512>::QB * 16 == 64,
               "query tile sizes");
 
-void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len, int *nsplit,
-               int *chunk) {
+void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
+               int max_len, int *nsplit, int *chunk) {
   const int nq = attn_query_tile(head_dim);
   const int nk = head_dim == 512 ? 32 : 64;
-  const int64_t base = (int64_t)nc * Hq * cdiv64(C, nq);
+  const int64_t base = (int64_t)nc * Hq * cdiv64(qn, nq);
   // most keys one query tile can see: the prompt plus its window span
-  const int64_t span = (int64_t)max_len + (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
+  const int64_t win = gathered ? C : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
+  const int64_t span = (int64_t)max_len + win;
   // about two workgroups per CU
   const int target = 512;
   int ns = 1;
@@ -589,11 +608,13 @@ template <typename T, int HD>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NW = AttnShape<T, HD>::NW;
   constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
-  const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * cdiv64(a.C, NQ));
+  const int QN = a.qpos ? a.qn : a.C;
+  if (QN <= 0) return hipSuccess;
+  const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * cdiv64(QN, NQ));
   hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(64 * NW), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  const int64_t R = (int64_t)a.nc * a.Hq * a.C;
+  const int64_t R = (int64_t)a.nc * a.Hq * QN;
   hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }

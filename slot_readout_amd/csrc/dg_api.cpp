@@ -106,12 +106,15 @@ struct AttnPlan {
   size_t part_o = 0, part_ml = 0;
 };
 
-AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt) {
+// qn queries per canvas: every position, or qn gathered ones
+AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1) {
   AttnPlan p;
-  dg::attn_plan(nc, d.canvas, d.n_q_heads, d.n_kv_heads, d.window, d.head_dim, max_prompt, &p.nsplit,
-                &p.chunk);
+  const bool gathered = qn >= 0;
+  if (!gathered) qn = d.canvas;
+  dg::attn_plan(nc, d.canvas, qn, gathered, d.n_q_heads, d.n_kv_heads, d.window, d.head_dim,
+                max_prompt, &p.nsplit, &p.chunk);
   if (p.nsplit > 1) {
-    const size_t R = (size_t)nc * d.n_q_heads * d.canvas;
+    const size_t R = (size_t)nc * d.n_q_heads * qn;
     p.part_o = (size_t)p.nsplit * R * d.head_dim * tsize(d);
     p.part_ml = (size_t)p.nsplit * R * sizeof(float2);
   }
@@ -150,30 +153,38 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
 }
 
 struct SlotPlan {
-  size_t q, k, v, o, part_o, part_ml, h, rows, stats, rowstat, lab_logit, flags, draw_active,
-      draw_ids, row_active, rs_draw, total;
+  size_t q, k, v, o, part_o, part_ml, h, rows, qpos, qids, stats, rowstat, lab_logit, flags,
+      draw_active, draw_ids, row_active, rs_draw, total;
   AttnPlan first, draws;
   bool spec;
 };
 
 // Whether the draws are computed for every canvas in the first read's pass.
 // That saves one stream of the LM-head weights (V x d), and costs the draws'
-// forward pass when no slot turns out to need a re-read.  Both are estimated
-// with sustained rates of about 5 TB/s and 1 PFLOP/s (bf16; 0.1 PFLOP/s fp32).
-bool speculate_draws(const dg_dims &d, int B, int nd, int max_prompt) {
+// forward pass when no slot turns out to need a re-read: the q/k/v projection
+// of every canvas row, attention over the prompt and the canvas for the slot
+// rows (a whole query tile of them), and the output projection of the slot
+// rows.  Both are estimated with sustained rates of about 5 TB/s and
+// 1 PFLOP/s (bf16; 0.1 PFLOP/s fp32).
+bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt) {
   if (nd <= 1 || B <= 0) return false;
   const double head_s = (double)d.vocab * d.d_model * (double)tsize(d) / 5e12;
   const double hq = (double)d.n_q_heads * d.head_dim, hkv = (double)d.n_kv_heads * d.head_dim;
-  const double per_row = 2.0 * d.d_model * (hq + 2.0 * hkv) + 2.0 * hq * d.d_model +
-                         4.0 * hq * ((double)max_prompt + 2.0 * d.window + 1.0);
-  const double draw_s =
-      (double)B * nd * d.canvas * per_row / (d.dtype == DG_BF16 ? 1e15 : 1e14);
+  const int qt = dg::attn_query_tile(d.head_dim);
+  const double s_att = (double)((S + qt - 1) / qt) * qt;
+  const double per_canvas = 2.0 * d.d_model * (hq + 2.0 * hkv) * d.canvas +
+                            2.0 * hq * d.d_model * S +
+                            4.0 * hq * ((double)max_prompt + d.canvas) * s_att;
+  const double draw_s = (double)B * nd * per_canvas / (d.dtype == DG_BF16 ? 1e15 : 1e14);
   return draw_s < head_s;
 }
 
+// A read needs the hidden state only at its slot rows: the q/k/v projection
+// runs over every canvas row (all keys), attention and the output projection
+// over the slot rows alone (gathered queries, compact outputs).
 SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   SlotPlan p{};
-  p.spec = speculate_draws(d, B, nd, max_prompt);
+  p.spec = speculate_draws(d, B, S, nd, max_prompt);
   const int ncmax = p.spec ? B * (nd + 1) : (nd > 1 ? B * nd : B);
   const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
@@ -183,15 +194,17 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   p.q = a.take(M * nq * ts);
   p.k = a.take(M * nkv * ts);
   p.v = a.take(M * nkv * ts);
-  p.o = a.take(M * nq * ts);
-  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt);
-  p.draws = plan_attention(d, ncmax, max_prompt);
+  p.o = a.take(nrows * nq * ts);
+  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt, S);
+  p.draws = plan_attention(d, ncmax, max_prompt, S);
   const size_t po = p.first.part_o > p.draws.part_o ? p.first.part_o : p.draws.part_o;
   const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
   p.part_o = a.take(po);
   p.part_ml = a.take(pm);
-  p.h = a.take(M * d.d_model * ts);
+  p.h = a.take(nrows * d.d_model * ts);
   p.rows = a.take(nrows * sizeof(int32_t));
+  p.qpos = a.take(nrows * sizeof(int32_t));
+  p.qids = a.take(nrows * sizeof(int32_t));
   p.stats = a.take(nrows * nvt * sizeof(float4));
   p.rowstat = a.take(nrows * sizeof(float2));
   p.lab_logit = a.take(nrows * DG_MAX_LABELS * sizeof(float));
@@ -225,12 +238,20 @@ template <typename P> P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<char *>(ws) + off);
 }
 
+// Queries of a pass: every canvas position, or qn gathered rows per canvas
+// (positions qpos, token ids qids; -1 = none), for which attention and the
+// output projection write compact rows cb*qn + i.
+struct Gather {
+  const int32_t *qpos = nullptr, *qids = nullptr;
+  int qn = 0;
+};
+
 // S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
 dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *kv, int nc,
                     int canvas_per_prompt, const int32_t *ids, const void *sc_in,
                     const int32_t *active, int32_t *flags, void *q, void *k, void *v, void *o,
                     const AttnPlan &ap, void *part_o, float2 *part_ml, void *h, hipStream_t st,
-                    const Stages &sg = Stages()) {
+                    const Stages &sg = Stages(), const Gather &gq = Gather()) {
   const bool bf = d.dtype == DG_BF16;
   const int64_t M = (int64_t)nc * d.canvas;
   dg::QkvArgs qa{};
@@ -267,6 +288,8 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.cu = kv->cu_seqlens;
   aa.active = active;
   aa.flags = flags;
+  aa.qpos = gq.qpos;
+  aa.qn = gq.qpos ? gq.qn : d.canvas;
   aa.o = o;
   aa.part_o = part_o;
   aa.part_ml = part_ml;
@@ -287,16 +310,16 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   dg::OprojArgs oa{};
   oa.o = o;
   oa.wo = w->wo;
-  oa.ids = ids;
+  oa.ids = gq.qpos ? gq.qids : ids;
   oa.embed = w->embed;
-  oa.sc_in = sc_in;
+  oa.sc_in = gq.qpos ? nullptr : sc_in;
   oa.h = h;
   oa.active = active;
-  oa.M = M;
+  oa.M = gq.qpos ? (int64_t)nc * gq.qn : M;
   oa.d = d.d_model;
   oa.kdim = d.n_q_heads * d.head_dim;
   oa.vocab = d.vocab;
-  oa.C = d.canvas;
+  oa.C = gq.qpos ? gq.qn : d.canvas;
   DG_MARK(sg, DG_STAGE_OPROJ, 0);
   DG_TRY_HIP(dg::launch_oproj(oa, bf, st), "output projection launch");
   DG_MARK(sg, DG_STAGE_OPROJ, 1);
@@ -536,7 +559,13 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.draw_active = at<int32_t>(workspace, p.draw_active);
   sa.canvas_ids = canvas_ids;
   sa.draw_ids = at<int32_t>(workspace, p.draw_ids);
+  sa.qpos = at<int32_t>(workspace, p.qpos);
+  sa.qids = at<int32_t>(workspace, p.qids);
   sa.mask_id = d.mask_id;
+  Gather gq;
+  gq.qpos = sa.qpos;
+  gq.qids = sa.qids;
+  gq.qn = n_slots;
 
   dg::LmheadArgs la{};
   la.head = w->lm_head ? w->lm_head : w->embed;
@@ -566,7 +595,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     sa.off_draw = 1;
     DG_TRY_HIP(dg::launch_slot_spec_build(sa, sa.draw_ids, rs_draw, st), "read canvas launch");
     s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
-                  p.draws, part_o, part_ml, h, st);
+                  p.draws, part_o, part_ml, h, st, Stages(), gq);
     if (s != DG_OK) return s;
     la.nrows = (int64_t)batch * G * n_slots;
     la.row_scale = rs_draw;
@@ -584,10 +613,10 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.grp_first = 1;
   sa.grp_draw = n_draws;
   sa.off_draw = 0;
-  s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
-                part_o, part_ml, h, st);
-  if (s != DG_OK) return s;
   DG_TRY_HIP(dg::launch_slot_rows(sa, st), "slot row launch");
+  s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
+                part_o, part_ml, h, st, Stages(), gq);
+  if (s != DG_OK) return s;
   la.nrows = (int64_t)batch * n_slots;
   la.row_scale = row_scale;
   la.lab_span = n_slots;
@@ -599,11 +628,11 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
 
   // re-read of flagged canvases: n_draws noise copies in one batched pass
   DG_TRY_HIP(dg::launch_slot_build_draws(sa, st), "draw canvas launch");
-  s = run_block(d, w, kv, batch * n_draws, n_draws, sa.draw_ids, nullptr, sa.draw_active, nullptr,
-                q, k, v, o, p.draws, part_o, part_ml, h, st);
-  if (s != DG_OK) return s;
   int32_t *row_active = at<int32_t>(workspace, p.row_active);
   DG_TRY_HIP(dg::launch_slot_draw_rows2(sa, row_active, rs_draw, st), "draw row launch");
+  s = run_block(d, w, kv, batch * n_draws, n_draws, sa.draw_ids, nullptr, sa.draw_active, nullptr,
+                q, k, v, o, p.draws, part_o, part_ml, h, st, Stages(), gq);
+  if (s != DG_OK) return s;
   la.nrows = (int64_t)batch * n_draws * n_slots;
   la.active_rows = row_active;
   la.rows_per_flag = 1;

@@ -86,9 +86,15 @@ struct AttnArgs {
   const int32_t *cu;           // [nprompt + 1]
   const int32_t *active;       // per-canvas flag or null
   int32_t *flags;
-  void *o;                     // [nc, C, Hq, hd]
-  void *part_o;                // [nsplit, nc*Hq*C, hd] storage type
-  float2 *part_ml;             // [nsplit, nc*Hq*C]
+  // Queries: with qpos null, every canvas position (qn = C); otherwise canvas
+  // cb's queries are rows cb*qn + i (i < qn) at canvas positions
+  // qpos[cb*qn + i], where a position outside [0, C) names no query (its
+  // output row is written and meaningless).  Outputs are laid out by query row.
+  const int32_t *qpos;
+  int qn;
+  void *o;                     // [nc, qn, Hq, hd]
+  void *part_o;                // [nsplit, nc*Hq*qn, hd] storage type
+  float2 *part_ml;             // [nsplit, nc*Hq*qn]
   int64_t total_len;
   int nc, C, Hq, Hkv, W, max_len, nsplit, chunk, canvas_per_prompt;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
@@ -114,8 +120,10 @@ hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st);
 
 // attention: query rows per workgroup, split-KV planning, launch (+ merge)
 int attn_query_tile(int head_dim);
-void attn_plan(int nc, int C, int Hq, int Hkv, int W, int head_dim, int max_len, int *nsplit,
-               int *chunk);
+// qn queries per canvas; gathered: queries at arbitrary positions (every
+// canvas key is a candidate) instead of consecutive ones
+void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
+               int max_len, int *nsplit, int *chunk);
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
@@ -139,7 +147,10 @@ struct SlotArgs {
   float logit_scale;
   float threshold;
   int B, S, C, V, d, n_draws;
-  int32_t *rows;               // [B*nd*S] gathered row index (out of the build kernels)
+  // Per slot row n (out of the build kernels): its row of the LM-head pass
+  // (n itself, or -1 = not read), and for the forward pass its canvas
+  // position (-1 = none) and token id there
+  int32_t *rows, *qpos, *qids;
   int32_t *status;             // [B, S]
   float *logprobs, *probs, *entropy, *first_entropy;
   int32_t *best, *draws_used;

@@ -1,9 +1,10 @@
 // Structured slot read: label logprobs at decision slots, renormalisation over
 // the allowed labels, entropy, and the averaged noise-draw re-read.
 //
-// The first pass runs the denoise step over the whole canvas; the LM head and
-// its softmax statistics run only on the slot rows (gathered by row index), and
-// its epilogue also writes the logits of each slot's allowed labels.  A slot
+// The first pass projects q, k, v for the whole canvas (every key), and runs
+// attention, the output projection, the LM head and its softmax statistics
+// only at the slot rows (gathered by canvas position, compact rows); the LM
+// head's epilogue also writes the logits of each slot's allowed labels.  A slot
 // whose renormalised entropy exceeds the threshold flags its canvas; flagged
 // canvases get n_draws copies with a noise token written at every slot and a
 // second batched pass, decided on the device (no host synchronisation).  When
@@ -27,14 +28,18 @@ __device__ inline int validate_slot(const SlotArgs &a, int64_t bs) {
   return DG_SLOT_OK;
 }
 
-// rows of the first pass: slot (b, s) reads hidden row b*C + pos
+// rows of the first pass: slot (b, s) is row bs = b*S + s, at position pos of canvas b
 __global__ __launch_bounds__(256) void slot_rows_kernel(SlotArgs a) {
   const int64_t bs = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (bs >= (int64_t)a.B * a.S) return;
   const int st = validate_slot(a, bs);
   a.status[bs] = st;
   const int64_t b = bs / a.S;
-  a.rows[bs] = st == DG_SLOT_OK ? (int32_t)(b * a.C + a.slot_pos[bs]) : -1;
+  const int pos = a.slot_pos[bs];
+  const bool in = pos >= 0 && pos < a.C;
+  a.rows[bs] = st == DG_SLOT_OK ? (int32_t)bs : -1;
+  a.qpos[bs] = in ? pos : -1;
+  a.qids[bs] = in ? a.canvas_ids[b * a.C + pos] : 0;
 }
 
 // label log-probability in lane j: lp_j = min(l_j - lse, 0) from the scaled
@@ -145,7 +150,8 @@ __global__ __launch_bounds__(256) void slot_build_draws_kernel(SlotArgs a) {
   }
 }
 
-// rows of the draw pass: (b, d, s) reads row (b*nd + d)*C + pos when slot (b, s) is flagged
+// rows of the draw pass: (b, d, s) is row i = (b*nd + d)*S + s, read when slot
+// (b, s) is flagged; its query sits at the slot's position of draw canvas b*nd + d
 __global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t *row_active,
                                                              float *rs_draw) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -156,9 +162,14 @@ __global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t
   const int64_t b = bd / a.n_draws;
   const int64_t bs = b * a.S + s;
   const bool on = a.canvas_flag[a.B + bs] != 0;
-  a.rows[i] = on ? (int32_t)(bd * a.C + a.slot_pos[bs]) : -1;
+  a.rows[i] = on ? (int32_t)i : -1;
   row_active[i] = on ? 1 : 0;
   rs_draw[i] = a.row_scale ? a.row_scale[bs] : 1.f;
+  // draw canvases are written only for flagged canvases
+  const int pos = a.slot_pos[bs];
+  const bool in = pos >= 0 && pos < a.C && a.draw_active[bd];
+  a.qpos[i] = in ? pos : -1;
+  a.qids[i] = in ? a.draw_ids[bd * a.C + pos] : 0;
 }
 
 // average of the draws in probability space: r = mean r_d, lp = ln mean e^(lp_d)
@@ -202,8 +213,9 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
 // writes canvas cb: canvas b itself (j = 0) or draw j-1 of it, with its noise
 // token at every valid slot position (the mask id for an out-of-range noise
 // id; the status for that is set only once the canvas is known to re-read).
-// It also writes the hidden-row index and row scale of the canvas's slot rows
-// n = cb*S + s, and for j = 0 the slot's validation status.
+// It also writes, for the canvas's slot rows n = cb*S + s, the LM-head row
+// (n, or -1 for an invalid slot), the row scale, the query position and the
+// token id there, and for j = 0 the slot's validation status.
 __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_t *ids, float *rs) {
   const int cb = blockIdx.x;
   const int G = a.n_draws + 1;
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
     const int st = validate_slot(a, bs);
     if (j == 0) a.status[bs] = st;
     const int64_t n = (int64_t)cb * a.S + s;
-    a.rows[n] = st == DG_SLOT_OK ? (int32_t)((int64_t)cb * a.C + a.slot_pos[bs]) : -1;
+    a.rows[n] = st == DG_SLOT_OK ? (int32_t)n : -1;
     rs[n] = a.row_scale ? a.row_scale[bs] : 1.f;
   }
   // slots are written in order, as in the separate draw pass
@@ -230,6 +242,14 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
       if (nid < 0 || nid >= a.V) nid = a.mask_id;
       dst[pos] = nid;
     }
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.S; s += 256) {
+    const int pos = a.slot_pos[(int64_t)b * a.S + s];
+    const bool in = pos >= 0 && pos < a.C;
+    const int64_t n = (int64_t)cb * a.S + s;
+    a.qpos[n] = in ? pos : -1;
+    a.qids[n] = in ? dst[pos] : 0;
   }
 }
 

@@ -129,16 +129,20 @@ def test_slot_read_deterministic(torch_cuda):
 
 
 
-def _one_pass_draws(dims, B, nd, max_prompt):
+def _one_pass_draws(dims, B, S, nd, max_prompt):
     """The library's rule for computing the draws in the first read's pass:
     the LM-head weight stream (V x d at ~5 TB/s) outweighs the draws' forward
-    pass (~1 PFLOP/s bf16, ~0.1 fp32)."""
+    pass (~1 PFLOP/s bf16, ~0.1 fp32): q/k/v of every canvas row, attention of
+    the slot rows (rounded up to a query tile) over prompt + canvas, and the
+    output projection of the slot rows."""
     ts = 2 if dims.dtype == "bf16" else 4
     head_s = dims.vocab * dims.d_model * ts / 5e12
     hq, hkv = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
-    per_row = (2 * dims.d_model * (hq + 2 * hkv) + 2 * hq * dims.d_model
-               + 4 * hq * (max_prompt + 2 * dims.window + 1))
-    draw_s = B * nd * dims.canvas * per_row / (1e15 if dims.dtype == "bf16" else 1e14)
+    qt = 64 if dims.head_dim == 512 else 128
+    s_att = -(-S // qt) * qt
+    per_canvas = (2 * dims.d_model * (hq + 2 * hkv) * dims.canvas + 2 * hq * dims.d_model * S
+                  + 4 * hq * (max_prompt + dims.canvas) * s_att)
+    draw_s = B * nd * per_canvas / (1e15 if dims.dtype == "bf16" else 1e14)
     return nd > 1 and draw_s < head_s
 
 
@@ -148,7 +152,8 @@ def test_slot_read_one_pass_draws_f32(torch_cuda):
     the first read and some average their draws (checked at the fp32 bar)."""
     inp = make_inputs(config("reads512", dtype="f32", vocab=262144, mask_id=262143), batch=2,
                       prompt_override=("fixed", 64))
-    assert _one_pass_draws(inp["dims"], 2, inp["n_draws"], int(inp["max_prompt"]))
+    assert _one_pass_draws(inp["dims"], 2, inp["slot_pos"].shape[1], inp["n_draws"],
+                           int(inp["max_prompt"]))
     rs = companion_row_scale(inp, (2, 4), 64.0, 2048.0)
     g = _read(inp, row_scale=rs)
     ref = oracle.slot_read(inp, row_scale=rs)
@@ -161,7 +166,8 @@ def test_slot_read_one_pass_draws_bf16(torch_cuda):
     """Read-batch shape (1024-token prompts, k ~ U{2..26}) with a 262,144-token
     vocabulary, 8 canvases: draws computed in the first read's pass, bf16."""
     inp = make_inputs(config("reads512", vocab=262144, mask_id=262143), batch=8)
-    assert _one_pass_draws(inp["dims"], 8, inp["n_draws"], int(inp["max_prompt"]))
+    assert _one_pass_draws(inp["dims"], 8, inp["slot_pos"].shape[1], inp["n_draws"],
+                           int(inp["max_prompt"]))
     g = _read(inp)
     ref = oracle.slot_read(inp)
     _check_slots(g, ref, inp, "bf16", "one-pass draws bf16")
