@@ -163,7 +163,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 
   const int64_t kv_stride = (int64_t)a.Hkv * HD;   // elements between consecutive keys
   const int64_t q_stride = (int64_t)a.Hq * HD;
-  const T *qbase = static_cast<const T *>(a.q) + (int64_t)cb * C * q_stride + (int64_t)h * HD;
+  // q rows: canvas positions, or the compact rows of gathered queries
+  const T *qbase = static_cast<const T *>(a.q) + (int64_t)cb * (a.qpos ? QN : C) * q_stride +
+                   (int64_t)h * HD;
   const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
   const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
   const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
@@ -184,10 +186,11 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   frag qf[QB][KS];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
+    const int qrow = a.qpos ? i0 + w * QB * 16 + jb * 16 + col : qp[jb];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qp[jb] >= 0)
-        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qp[jb] * q_stride + ks * MF::KI +
+        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qrow * q_stride + ks * MF::KI +
                                                       grp * MF::KPL);
       else
         qf[jb][ks] = frag{};

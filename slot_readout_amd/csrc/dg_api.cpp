@@ -179,9 +179,9 @@ bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt) {
   return draw_s < head_s;
 }
 
-// A read needs the hidden state only at its slot rows: the q/k/v projection
-// runs over every canvas row (all keys), attention and the output projection
-// over the slot rows alone (gathered queries, compact outputs).
+// A read needs the hidden state only at its slot rows: the k/v projection runs
+// over every canvas row (all keys); the q projection, attention and the output
+// projection over the slot rows alone (gathered queries, compact rows).
 SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   SlotPlan p{};
   p.spec = speculate_draws(d, B, S, nd, max_prompt);
@@ -191,7 +191,7 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   const int nvt = d.vocab / dg::VTILE;
   const size_t nrows = (size_t)B * S * (p.spec ? nd + 1 : (nd > 1 ? nd : 1));
   Arena a;
-  p.q = a.take(M * nq * ts);
+  p.q = a.take(nrows * nq * ts);
   p.k = a.take(M * nkv * ts);
   p.v = a.take(M * nkv * ts);
   p.o = a.take(nrows * nq * ts);
@@ -275,8 +275,27 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   // the softmax scale in log2 units rides on q, so attention exponentiates
   // scores directly (one rounding of q either way)
   qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  qa.col0 = 0;
+  qa.col1 = qa.nq + 2 * qa.nkv;
   DG_MARK(sg, DG_STAGE_QKV, 0);
-  DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "qkv projection launch");
+  if (gq.qpos) {
+    // k, v of every canvas row; q of the gathered rows only (compact).  A
+    // gathered pass takes no self-conditioning input (reads have none).
+    if (sc_in) return fail(DG_ERR_INVALID_ARG, "gathered queries take no sc_in");
+    qa.col0 = qa.nq;
+    DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "k/v projection launch");
+    dg::QkvArgs qg = qa;
+    qg.ids = gq.qids;
+    qg.sc_in = nullptr;
+    qg.flags = nullptr;
+    qg.M = (int64_t)nc * gq.qn;
+    qg.C = gq.qn;
+    qg.col0 = 0;
+    qg.col1 = qa.nq;
+    DG_TRY_HIP(dg::launch_qkv(qg, bf, st), "q projection launch");
+  } else {
+    DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "qkv projection launch");
+  }
   DG_MARK(sg, DG_STAGE_QKV, 1);
 
   dg::AttnArgs aa{};

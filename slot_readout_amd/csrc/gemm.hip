@@ -294,13 +294,13 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   int nt, mt;   // the row tiles of one weight tile run on one XCD
-  if (!xcd_group_tile((int)cdiv64(a.nq + 2 * a.nkv, BN), (int)cdiv64(a.M, BM), &nt, &mt)) return;
+  if (!xcd_group_tile((int)cdiv64(a.col1 - a.col0, BN), (int)cdiv64(a.M, BM), &nt, &mt)) return;
   const int64_t m0 = (int64_t)mt * BM;
-  const int n0 = nt * BN;
+  const int n0 = a.col0 + nt * BN;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const T *E = static_cast<const T *>(a.embed);
   const T *sc = static_cast<const T *>(a.sc_in);
-  const int nq = a.nq, nk = a.nkv, ntot = nq + 2 * nk, d = a.d;
+  const int nq = a.nq, nk = a.nkv, ntot = a.col1, d = a.d;
   GatherLoader<T, G::AI, SC> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, const
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
-  const dim3 grid = xcd_grid(cdiv64(a.nq + 2 * a.nkv, BN), cdiv64(a.M, BM));
+  const dim3 grid = xcd_grid(cdiv64(a.col1 - a.col0, BN), cdiv64(a.M, BM));
   if (a.sc_in)
     hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK, true>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   else
@@ -671,7 +671,9 @@ static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
 // Projections at small M are weight-streaming: small tiles for parallelism and
 // a 4-stage prefetch to keep enough bytes in flight per CU.
 hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
-  const int64_t ntot = a.nq + 2 * a.nkv;
+  const int64_t ntot = a.col1 - a.col0;
+  if (a.M <= 0 || ntot <= 0) return hipSuccess;
+  if (a.col0 < 0 || a.col1 > a.nq + 2 * a.nkv) return hipErrorInvalidValue;
   if (bf) {
     if (cdiv64(a.M, 128) * cdiv64(ntot, 128) >= 256)
       return launch_qkv_t<bf16, 128, 128, 2, 2, 2, 64>(a, st);

@@ -21,6 +21,7 @@ struct QkvArgs {
   float q_scale;            // q is written as (x Wq^T) * q_scale
   int64_t M;
   int d, nq, nkv, vocab, C;
+  int col0, col1;          // output columns [col0, col1) of [q | k | v]
 };
 
 struct OprojArgs {
