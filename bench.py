@@ -133,6 +133,10 @@ def main():
                     choices=["bf16_step", "long_read", "ragged32"],
                     help="bf16_step (default) times step + commit + slot read; long_read and "
                          "ragged32 time step + commit and report the attention stage")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 1 GiB device to device twice: a plain "
+                         "copy of known size that scales the HBM byte counters of a "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run")
     ap.add_argument("--cold", action="store_true",
                     help="evict the caches (read 1 GiB) before every timed step; the default "
                          "for long_read, whose prompt KV would otherwise sit in the 256 MB MALL")
@@ -209,6 +213,13 @@ def main():
         one_step(k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_calibration:   # outside the timed region
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if cold:   # cache flushes sit between the steps: sum the steps themselves
         ms_per_step = float(np.mean([marks.ms(4 * k, 4 * k + 3) for k in range(K)]))

@@ -403,16 +403,103 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 K loop with direct-to-LDS staging (global_load_lds_dwordx4): each wave
+// instruction moves a block of 16 rows x 64 bytes (BK = 32) from global memory
+// straight into LDS.  NS stages give NS-1 steps of loads in flight without
+// holding staged tiles in registers.  The four 16-byte chunks of a 64-byte row
+// sit XOR-swizzled by (row >> 2) & 3, which keeps the 16-row fragment reads
+// free of bank conflicts; the swizzle is applied on the global side (each lane
+// fetches the chunk that belongs at its LDS slot).  Stages live in separate
+// LDS arrays, so the compiler can tell a stage being read from the stages
+// still being filled and waits only for the loads a read depends on.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int NS>
+struct DmaLoop {
+  static constexpr int BK = 32, NW = WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;
+  static constexpr int QA = BM / 16, NQ = (BM + BN) / 16, QW = NQ / NW;
+  static constexpr int STAGE = (BM + BN) * 64;   // bytes
+  static_assert(NQ % NW == 0, "16-row blocks must divide among the waves");
+  static_assert(NS >= 2 && (NS - 2) * QW < 64, "stage count");
+  using MF = Mfma<bf16>;
+  using frag = MF::frag;
+
+  // rowa(r) / rowb(r): first element of row r of the A / B tile (always a
+  // dereferenceable row); K must be a multiple of NS * BK
+  template <class RA, class RB>
+  __device__ static void run(char *const (&st)[NS], const RA &rowa, const RB &rowb, int K,
+                             f32x4 (&acc)[TM][TN]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WGN, wn = w % WGN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+    const int nk = K / BK;
+    // lane l fills slot (row l/4, chunk l%4) of each 16-row block it loads
+    const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+    const bf16 *gp[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      const int q = w * QW + i;
+      gp[i] = (q < QA ? rowa(16 * q + (lane >> 2)) : rowb(16 * (q - QA) + (lane >> 2))) + 8 * lc;
+    }
+    auto dma = [&](int kt, char *s) {
+#pragma unroll
+      for (int i = 0; i < QW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            gp[i] + kt * BK, (__attribute__((address_space(3))) void *)(s + (w * QW + i) * 1024), 16,
+            0, 0);
+    };
+    // fragment of row (16-aligned base) + lane%16, logical chunk lane/16
+    const int pc = 16 * ((lane >> 4) ^ ((lane >> 2) & 3)) + 64 * (lane & 15);
+    auto compute = [&](const char *s) {
+      frag a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const frag *>(s + (wm * WM + i * 16) * 64 + pc);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = *reinterpret_cast<const frag *>(s + (BM + wn * WN + j * 16) * 64 + pc);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = MF::mma(a[i], b[j], acc[i][j]);
+    };
+    // vmcnt(n) with the other counters left alone (gfx9 encoding)
+    constexpr int WN_ = (NS - 2) * QW;
+    constexpr int WAIT = (WN_ & 15) | ((WN_ >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) dma(s < nk ? s : nk - 1, st[s]);
+    for (int k0 = 0; k0 < nk; k0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int kt = k0 + j;
+        // this wave's loads of step kt have landed; after the barrier every
+        // wave's have, and every wave is done with step kt-1's stage
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        __builtin_amdgcn_s_barrier();
+        dma(kt + NS - 1 < nk ? kt + NS - 1 : nk - 1, st[(j + NS - 1) % NS]);
+        compute(st[j]);
+      }
+    }
+    // the last (repeated) loads land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  }
+};
+
+// ---------------------------------------------------------------------------
 // S4+S5 (tile part): logits of a VTILE-wide vocabulary tile for BN rows, with
 // per-(row, tile) softmax statistics.  Computed as C^T: MFMA rows are
 // vocabulary entries, MFMA columns are canvas rows, so each row's reduction
 // over the vocabulary runs mostly inside a lane.
 // ---------------------------------------------------------------------------
+// PF = 0 selects the direct-to-LDS K loop (bf16, BK = 32, kDmaStages stages).
+constexpr int kDmaStages = 4;
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
-  using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
+  using G = Gemm<T, BM, BN, WGM, WGN, PF == 0 ? 1 : PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   __shared__ float red_m[WGM][BN];
   __shared__ int red_i[WGM][BN];
   __shared__ float red_s[WGM][BN];
@@ -426,22 +513,40 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   if (a.active_rows && !tile_active(a.active_rows, n0, BN, a.nrows, a.rows_per_flag)) return;
   const T *head = static_cast<const T *>(a.head);
   const T *hh = static_cast<const T *>(a.h);
-  RowLoader<T, G::AI> al;
-#pragma unroll
-  for (int it = 0; it < G::AI; ++it) {
-    const int v = v0 + G::a_row(it);
-    al.set(it, head + (int64_t)v * d, v < a.vocab, head);
-  }
-  RowLoader<T, G::BI> bl;
-#pragma unroll
-  for (int it = 0; it < G::BI; ++it) {
-    const int64_t n = n0 + G::a_row(it);
-    int64_t src = -1;
-    if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
-    bl.set(it, hh + (src >= 0 ? src : 0) * d, src >= 0, hh);
-  }
   f32x4 acc[G::TM][G::TN];
-  G::run(smem, al, bl, 0, d, acc);
+  if constexpr (PF == 0) {
+    // rows past the matrix (or without a source row) read row 0: their
+    // columns are never stored and columns do not mix
+    using D = DmaLoop<BM, BN, WGM, WGN, kDmaStages>;
+    __shared__ __attribute__((aligned(1024))) char s0[D::STAGE], s1[D::STAGE], s2[D::STAGE],
+        s3[D::STAGE];
+    char *const st[kDmaStages] = {s0, s1, s2, s3};
+    auto rowa = [&](int r) { return head + (int64_t)(v0 + r) * d; };
+    auto rowb = [&](int r) {
+      const int64_t n = n0 + r;
+      int64_t src = -1;
+      if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
+      return hh + (src >= 0 ? src : 0) * d;
+    };
+    D::run(st, rowa, rowb, d, acc);
+  } else {
+    __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+    RowLoader<T, G::AI> al;
+#pragma unroll
+    for (int it = 0; it < G::AI; ++it) {
+      const int v = v0 + G::a_row(it);
+      al.set(it, head + (int64_t)v * d, v < a.vocab, head);
+    }
+    RowLoader<T, G::BI> bl;
+#pragma unroll
+    for (int it = 0; it < G::BI; ++it) {
+      const int64_t n = n0 + G::a_row(it);
+      int64_t src = -1;
+      if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
+      bl.set(it, hh + (src >= 0 ? src : 0) * d, src >= 0, hh);
+    }
+    G::run(smem, al, bl, 0, d, acc);
+  }
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w / WGN, wn = w % WGN;
@@ -709,7 +814,10 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
     hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
   } else if (bf) {
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
-    hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
+    if (a.d % (32 * kDmaStages) == 0)
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 0, 32>), grid, dim3(8 * WAVE), 0, st, a);
+    else
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
     hipLaunchKernelGGL((lmhead_kernel<float, VTILE, 64, 4, 1, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
