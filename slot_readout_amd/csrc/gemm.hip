@@ -425,9 +425,9 @@ struct DmaLoop {
   using frag = MF::frag;
 
   // rowa(r) / rowb(r): first element of row r of the A / B tile (always a
-  // dereferenceable row); K must be a multiple of NS * BK
+  // dereferenceable row); K must be a multiple of BK
   template <class RA, class RB>
-  __device__ static void run(char *const (&st)[NS], const RA &rowa, const RB &rowb, int K,
+  __device__ static void run(char *(&st)[NS], const RA &rowa, const RB &rowb, int K,
                              f32x4 (&acc)[TM][TN]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WGN, wn = w % WGN;
@@ -469,20 +469,26 @@ struct DmaLoop {
     // vmcnt(n) with the other counters left alone (gfx9 encoding)
     constexpr int WN_ = (NS - 2) * QW;
     constexpr int WAIT = (WN_ & 15) | ((WN_ >> 4) << 14) | (7 << 4) | (15 << 8);
+    // step kt lives in stage kt % NS; past the last step the loads repeat it
+    // (never read), so every step issues the same number of loads
+    auto step = [&](int kt, int j) {
+      // this wave's loads of step kt have landed; after the barrier every
+      // wave's have, and every wave is done with step kt-1's stage
+      __builtin_amdgcn_s_waitcnt(WAIT);
+      __builtin_amdgcn_s_barrier();
+      dma(kt + NS - 1 < nk ? kt + NS - 1 : nk - 1, st[(j + NS - 1) % NS]);
+      compute(st[j]);
+    };
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) dma(s < nk ? s : nk - 1, st[s]);
-    for (int k0 = 0; k0 < nk; k0 += NS) {
+    int k0 = 0;
+    for (; k0 + NS <= nk; k0 += NS) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const int kt = k0 + j;
-        // this wave's loads of step kt have landed; after the barrier every
-        // wave's have, and every wave is done with step kt-1's stage
-        __builtin_amdgcn_s_waitcnt(WAIT);
-        __builtin_amdgcn_s_barrier();
-        dma(kt + NS - 1 < nk ? kt + NS - 1 : nk - 1, st[(j + NS - 1) % NS]);
-        compute(st[j]);
-      }
+      for (int j = 0; j < NS; ++j) step(k0 + j, j);
     }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (k0 + j < nk) step(k0 + j, j);
     // the last (repeated) loads land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   }
@@ -494,11 +500,10 @@ struct DmaLoop {
 // vocabulary entries, MFMA columns are canvas rows, so each row's reduction
 // over the vocabulary runs mostly inside a lane.
 // ---------------------------------------------------------------------------
-// PF = 0 selects the direct-to-LDS K loop (bf16, BK = 32, kDmaStages stages).
-constexpr int kDmaStages = 4;
+// PF < 0 selects the direct-to-LDS K loop with -PF stages (bf16, BK = 32).
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
-  using G = Gemm<T, BM, BN, WGM, WGN, PF == 0 ? 1 : PF, BK>;
+  using G = Gemm<T, BM, BN, WGM, WGN, PF < 0 ? 1 : PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
   __shared__ float red_m[WGM][BN];
   __shared__ int red_i[WGM][BN];
@@ -514,13 +519,18 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   const T *head = static_cast<const T *>(a.head);
   const T *hh = static_cast<const T *>(a.h);
   f32x4 acc[G::TM][G::TN];
-  if constexpr (PF == 0) {
+  if constexpr (PF < 0) {
     // rows past the matrix (or without a source row) read row 0: their
     // columns are never stored and columns do not mix
-    using D = DmaLoop<BM, BN, WGM, WGN, kDmaStages>;
-    __shared__ __attribute__((aligned(1024))) char s0[D::STAGE], s1[D::STAGE], s2[D::STAGE],
-        s3[D::STAGE];
-    char *const st[kDmaStages] = {s0, s1, s2, s3};
+    constexpr int NS = -PF;
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    using D = DmaLoop<BM, BN, WGM, WGN, NS>;
+    __shared__ __attribute__((aligned(1024))) char s0[D::STAGE], s1[D::STAGE],
+        s2[NS > 2 ? D::STAGE : 16], s3[NS > 3 ? D::STAGE : 16];
+    char *const st4[4] = {s0, s1, s2, s3};
+    char *st[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st[s] = st4[s];
     auto rowa = [&](int r) { return head + (int64_t)(v0 + r) * d; };
     auto rowb = [&](int r) {
       const int64_t n = n0 + r;
@@ -805,6 +815,10 @@ hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
 
 // row count up to which the LM head uses 64-row tiles
 constexpr int64_t kLmFewRows = 64;
+// direct-to-LDS stages of the 256-row LM head's K loop.  (For the few-row
+// tile, a pure weight stream, 2-4 direct-to-LDS stages measured slower than
+// its register-staged loop, which keeps three workgroups per CU.)
+constexpr int kLmStages = 4;
 
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
   if (bf && a.nrows <= kLmFewRows) {
@@ -814,8 +828,8 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
     hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
   } else if (bf) {
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
-    if (a.d % (32 * kDmaStages) == 0)
-      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 0, 32>), grid, dim3(8 * WAVE), 0, st, a);
+    if (a.d % 32 == 0)
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, -kLmStages, 32>), grid, dim3(8 * WAVE), 0, st, a);
     else
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
