@@ -183,6 +183,12 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
     if (a.qpos) p = qi < QN ? a.qpos[(int64_t)cb * QN + qi] : -1;
     qp[jb] = p >= 0 && p < C ? p : -(1 << 20);
   }
+  // a wave none of whose columns holds a query (past the canvas end, or past
+  // the few gathered queries of a read) only helps stage K and V
+  bool has_q = false;
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) has_q |= qp[jb] >= 0;
+  const bool live = __builtin_amdgcn_readfirstlane((int)__any(has_q)) != 0;
   frag qf[QB][KS];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
@@ -454,7 +460,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
     for (int j = 0; j < U; ++j) {
       const int b = b0 + j;
       __builtin_amdgcn_sched_barrier(0);
-      compute(desc(b), j % 2);
+      if (live) compute(desc(b), j % 2);
       const int sl = (j + 1) % PF;
       stage(kr[sl], vr[sl], (j + 1) % 2);
       fetch(desc(b + 1 + PF), kr[sl], vr[sl]);
@@ -464,7 +470,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 #pragma unroll
   for (int j = 0; j < U - 1; ++j) {   // fewer than U blocks remain
     if (b0 + j < nb) {
-      compute(desc(b0 + j), j % 2);
+      if (live) compute(desc(b0 + j), j % 2);
       const int sl = (j + 1) % PF;
       if (b0 + j + 1 < nb) stage(kr[sl], vr[sl], (j + 1) % 2);
       __syncthreads();
