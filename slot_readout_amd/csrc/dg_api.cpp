@@ -153,8 +153,8 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
 }
 
 struct SlotPlan {
-  size_t q, k, v, o, part_o, part_ml, h, rows, qpos, qids, stats, rowstat, lab_logit, flags,
-      draw_active, draw_ids, row_active, rs_draw, total;
+  size_t q, k, v, o, part_o, part_ml, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
+      rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, total;
   AttnPlan first, draws;
   bool spec;
 };
@@ -205,6 +205,8 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   p.rows = a.take(nrows * sizeof(int32_t));
   p.qpos = a.take(nrows * sizeof(int32_t));
   p.qids = a.take(nrows * sizeof(int32_t));
+  p.kv_row_base = a.take(p.spec ? (size_t)B * d.canvas * sizeof(int32_t) : 0);
+  p.kv_row_slot = a.take(p.spec ? nrows * sizeof(int32_t) : 0);
   p.stats = a.take(nrows * nvt * sizeof(float4));
   p.rowstat = a.take(nrows * sizeof(float2));
   p.lab_logit = a.take(nrows * DG_MAX_LABELS * sizeof(float));
@@ -238,12 +240,19 @@ template <typename P> P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<char *>(ws) + off);
 }
 
+// The softmax scale in log2 units rides on q, so attention exponentiates
+// scores directly (one rounding of q either way).
+float q_scale_of(const dg_dims &d) {
+  return (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+}
+
 // Queries of a pass: every canvas position, or qn gathered rows per canvas
 // (positions qpos, token ids qids; -1 = none), for which attention and the
 // output projection write compact rows cb*qn + i.
 struct Gather {
   const int32_t *qpos = nullptr, *qids = nullptr;
   int qn = 0;
+  bool qkv_done = false;   // q (compact), k and v are already projected
 };
 
 // S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
@@ -272,13 +281,12 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   qa.nkv = d.n_kv_heads * d.head_dim;
   qa.vocab = d.vocab;
   qa.C = d.canvas;
-  // the softmax scale in log2 units rides on q, so attention exponentiates
-  // scores directly (one rounding of q either way)
-  qa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+  qa.q_scale = q_scale_of(d);
   qa.col0 = 0;
   qa.col1 = qa.nq + 2 * qa.nkv;
+  qa.kv_row = nullptr;
   DG_MARK(sg, DG_STAGE_QKV, 0);
-  if (gq.qpos) {
+  if (gq.qpos && !gq.qkv_done) {
     // k, v of every canvas row; q of the gathered rows only (compact).  A
     // gathered pass takes no self-conditioning input (reads have none).
     if (sc_in) return fail(DG_ERR_INVALID_ARG, "gathered queries take no sc_in");
@@ -293,7 +301,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
     qg.col0 = 0;
     qg.col1 = qa.nq;
     DG_TRY_HIP(dg::launch_qkv(qg, bf, st), "q projection launch");
-  } else {
+  } else if (!gq.qpos) {
     DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "qkv projection launch");
   }
   DG_MARK(sg, DG_STAGE_QKV, 1);
@@ -580,6 +588,8 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.draw_ids = at<int32_t>(workspace, p.draw_ids);
   sa.qpos = at<int32_t>(workspace, p.qpos);
   sa.qids = at<int32_t>(workspace, p.qids);
+  sa.kv_row_base = p.spec ? at<int32_t>(workspace, p.kv_row_base) : nullptr;
+  sa.kv_row_slot = p.spec ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
   sa.mask_id = d.mask_id;
   Gather gq;
   gq.qpos = sa.qpos;
@@ -613,8 +623,42 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     sa.grp_draw = G;
     sa.off_draw = 1;
     DG_TRY_HIP(dg::launch_slot_spec_build(sa, sa.draw_ids, rs_draw, st), "read canvas launch");
+    // The draws differ from canvas b only at the slot positions: k, v of
+    // canvas b are projected once, copied into its draws, and the draws' slot
+    // rows are projected with the q of every slot row.
+    dg::QkvArgs qa{};
+    qa.ids = canvas_ids;
+    qa.embed = w->embed;
+    qa.wq = w->wq;
+    qa.wk = w->wk;
+    qa.wv = w->wv;
+    qa.q = q;
+    qa.k = k;
+    qa.v = v;
+    qa.M = (int64_t)batch * d.canvas;
+    qa.d = d.d_model;
+    qa.nq = d.n_q_heads * d.head_dim;
+    qa.nkv = d.n_kv_heads * d.head_dim;
+    qa.vocab = d.vocab;
+    qa.C = d.canvas;
+    qa.q_scale = q_scale_of(d);
+    qa.col0 = qa.nq;
+    qa.col1 = qa.nq + 2 * qa.nkv;
+    qa.kv_row = sa.kv_row_base;
+    DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "k/v projection launch");
+    DG_TRY_HIP(dg::launch_kv_replicate(k, v, batch, G, d.canvas, qa.nkv, (int)tsize(d), st),
+               "k/v copy launch");
+    dg::QkvArgs qg = qa;
+    qg.ids = sa.qids;
+    qg.M = (int64_t)batch * G * n_slots;
+    qg.C = n_slots;
+    qg.col0 = 0;
+    qg.kv_row = sa.kv_row_slot;
+    DG_TRY_HIP(dg::launch_qkv(qg, bf, st), "slot-row projection launch");
+    Gather gd = gq;
+    gd.qkv_done = true;
     s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
-                  p.draws, part_o, part_ml, h, st, Stages(), gq);
+                  p.draws, part_o, part_ml, h, st, Stages(), gd);
     if (s != DG_OK) return s;
     la.nrows = (int64_t)batch * G * n_slots;
     la.row_scale = rs_draw;

@@ -339,12 +339,15 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
     if (col < nq) { base = q; ld = nq; c = col; sc = a.q_scale; }
     else if (col < nq + nk) { base = k; ld = nk; c = col - nq; }
     else { base = v; ld = nk; c = col - nq - nk; }
+    const bool remap = col >= nq && a.kv_row;
 #pragma unroll
     for (int i = 0; i < G::TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
-        if (row < a.M) base[row * ld + c] = from_f<T>(acc[i][j][r] * sc);
+        if (row >= a.M) continue;
+        const int64_t orow = remap ? (int64_t)a.kv_row[row] : row;
+        if (orow >= 0) base[orow * ld + c] = from_f<T>(acc[i][j][r] * sc);
       }
   }
 }

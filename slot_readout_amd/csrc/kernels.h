@@ -22,6 +22,8 @@ struct QkvArgs {
   int64_t M;
   int d, nq, nkv, vocab, C;
   int col0, col1;          // output columns [col0, col1) of [q | k | v]
+  // row of k and v that input row m writes (-1: none), or null (row m)
+  const int32_t *kv_row;
 };
 
 struct OprojArgs {
@@ -152,6 +154,9 @@ struct SlotArgs {
   // (n itself, or -1 = not read), and for the forward pass its canvas
   // position (-1 = none) and token id there
   int32_t *rows, *qpos, *qids;
+  // one-pass reads: k/v row written by base-canvas row b*C + i ([B*C]) and by
+  // slot row n ([B*(1+nd)*S], -1 = none: the base canvas already holds it)
+  int32_t *kv_row_base, *kv_row_slot;
   int32_t *status;             // [B, S]
   float *logprobs, *probs, *entropy, *first_entropy;
   int32_t *best, *draws_used;
@@ -172,5 +177,8 @@ hipError_t launch_slot_average(const SlotArgs &a, hipStream_t st);
 // hidden-row indices of their slot rows, and the status of draws with bad noise
 hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st);
 hipError_t launch_slot_noise_status(const SlotArgs &a, hipStream_t st);
+// copies k and v of canvas g*G (every position) into canvases g*G + 1 .. g*G + G-1
+hipError_t launch_kv_replicate(void *k, void *v, int groups, int G, int C, int nkv, int elem_bytes,
+                               hipStream_t st);
 
 }  // namespace dg
