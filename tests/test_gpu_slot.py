@@ -171,3 +171,32 @@ def test_slot_read_one_pass_draws_bf16(torch_cuda):
     g = _read(inp)
     ref = oracle.slot_read(inp)
     _check_slots(g, ref, inp, "bf16", "one-pass draws bf16")
+
+
+def test_slot_read_many_slots_two_pass(torch_cuda):
+    """150 slots on one canvas: more slot rows than one gathered query tile holds
+    (128 at head_dim 64), and the 22 slots past the 128 masked positions all sit
+    at position 0 (duplicates), read by the two-pass order."""
+    inp = make_inputs(config("tiny_f32", n_slots=150))
+    assert (inp["slot_pos"][0] == 0).sum() > 1
+    g = _read(inp)
+    ref = oracle.slot_read(inp)
+    _check_slots(g, ref, inp, "f32", "many slots")
+
+
+def test_slot_read_many_slots_one_pass(torch_cuda):
+    """130 slots of a 65,536-entry vocabulary, fp32, read in one pass with the
+    draws: two gathered query tiles per head, the k/v copy into the draw
+    canvases, a duplicated slot position and an out-of-range one."""
+    inp = make_inputs(config("reads512", dtype="f32", vocab=65536, mask_id=65535, n_slots=130),
+                      batch=1, prompt_override=("fixed", 64))
+    C = inp["dims"].canvas
+    inp["slot_pos"][0, 5] = inp["slot_pos"][0, 3]
+    inp["slot_pos"][0, 7] = C + 3
+    assert _one_pass_draws(inp["dims"], 1, inp["slot_pos"].shape[1], inp["n_draws"],
+                           int(inp["max_prompt"]))
+    rs = companion_row_scale(inp, (1, 130), 64.0, 2048.0)
+    g = _read(inp, row_scale=rs)
+    ref = oracle.slot_read(inp, row_scale=rs)
+    assert ref["status"][0, 7] == oracle.SLOT_BAD_POS
+    _check_slots(g, ref, inp, "f32", "many slots one pass")
