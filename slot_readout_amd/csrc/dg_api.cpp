@@ -666,9 +666,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "slot LM head launch");
     va.nrows = la.nrows;
     DG_TRY_HIP(dg::launch_vocab_merge(va, st), "slot vocabulary merge launch");
-    DG_TRY_HIP(dg::launch_slot_first(sa, st), "slot first-read launch");
-    DG_TRY_HIP(dg::launch_slot_noise_status(sa, st), "slot noise status launch");
-    DG_TRY_HIP(dg::launch_slot_average(sa, st), "draw average launch");
+    DG_TRY_HIP(dg::launch_slot_finish(sa, st), "slot read finish launch");
     return ok();
   }
 

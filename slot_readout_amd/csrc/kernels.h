@@ -176,7 +176,9 @@ hipError_t launch_slot_average(const SlotArgs &a, hipStream_t st);
 // one pass over the first read and every draw: ids of the B*(1+nd) canvases,
 // hidden-row indices of their slot rows, and the status of draws with bad noise
 hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st);
-hipError_t launch_slot_noise_status(const SlotArgs &a, hipStream_t st);
+// the rest of a one-pass read, one workgroup per canvas: first read, re-read
+// flags, noise-id status and draw average
+hipError_t launch_slot_finish(const SlotArgs &a, hipStream_t st);
 // copies k and v of canvas g*G (every position) into canvases g*G + 1 .. g*G + G-1
 hipError_t launch_kv_replicate(void *k, void *v, int groups, int G, int C, int nkv, int elem_bytes,
                                hipStream_t st);

@@ -80,6 +80,42 @@ __device__ inline void finish_dist(LabelDist &d, int k, int lane) {
   d.best = bi;
 }
 
+// First read of slot s of canvas b (one wave): outputs, and whether the slot
+// is re-read (its flag is stored after the per-canvas flags).
+__device__ bool slot_first_one(const SlotArgs &a, int b, int s, int lane) {
+  const int64_t bs = (int64_t)b * a.S + s;
+  float *lp_out = a.logprobs + bs * DG_MAX_LABELS;
+  float *pr_out = a.probs + bs * DG_MAX_LABELS;
+  if (a.status[bs] != DG_SLOT_OK) {
+    if (lane < DG_MAX_LABELS) { lp_out[lane] = 0.f; pr_out[lane] = 0.f; }
+    if (lane == 0) {
+      a.entropy[bs] = 0.f;
+      a.first_entropy[bs] = 0.f;
+      a.best[bs] = -1;
+      a.draws_used[bs] = 0;
+      a.canvas_flag[a.B + bs] = 0;
+    }
+    return false;
+  }
+  const int k = a.n_labels[bs];
+  const float lp = label_logprob(a, ((int64_t)b * a.grp_first) * a.S + s, k, lane);
+  LabelDist dd = renormalise(lp, k, lane);
+  finish_dist(dd, k, lane);
+  if (lane < DG_MAX_LABELS) {
+    lp_out[lane] = lane < k ? lp : 0.f;
+    pr_out[lane] = lane < k ? dd.r : 0.f;
+  }
+  const bool flag = a.n_draws > 1 && dd.H > a.threshold;
+  if (lane == 0) {
+    a.entropy[bs] = dd.H;
+    a.first_entropy[bs] = dd.H;
+    a.best[bs] = dd.best;
+    a.draws_used[bs] = 1;
+    a.canvas_flag[a.B + bs] = flag ? 1 : 0;
+  }
+  return flag;
+}
+
 // first read: one wave per slot; also decides which canvases need draws
 __global__ __launch_bounds__(256) void slot_first_kernel(SlotArgs a) {
   __shared__ int any_flag;
@@ -87,39 +123,8 @@ __global__ __launch_bounds__(256) void slot_first_kernel(SlotArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) any_flag = 0;
   __syncthreads();
-  for (int s = w; s < a.S; s += 4) {
-    const int64_t bs = (int64_t)b * a.S + s;
-    float *lp_out = a.logprobs + bs * DG_MAX_LABELS;
-    float *pr_out = a.probs + bs * DG_MAX_LABELS;
-    if (a.status[bs] != DG_SLOT_OK) {
-      if (lane < DG_MAX_LABELS) { lp_out[lane] = 0.f; pr_out[lane] = 0.f; }
-      if (lane == 0) {
-        a.entropy[bs] = 0.f;
-        a.first_entropy[bs] = 0.f;
-        a.best[bs] = -1;
-        a.draws_used[bs] = 0;
-        a.canvas_flag[a.B + bs] = 0;   // per-slot flag lives after the per-canvas flags
-      }
-      continue;
-    }
-    const int k = a.n_labels[bs];
-    const float lp = label_logprob(a, ((int64_t)b * a.grp_first) * a.S + s, k, lane);
-    LabelDist dd = renormalise(lp, k, lane);
-    finish_dist(dd, k, lane);
-    if (lane < DG_MAX_LABELS) {
-      lp_out[lane] = lane < k ? lp : 0.f;
-      pr_out[lane] = lane < k ? dd.r : 0.f;
-    }
-    const bool flag = a.n_draws > 1 && dd.H > a.threshold;
-    if (lane == 0) {
-      a.entropy[bs] = dd.H;
-      a.first_entropy[bs] = dd.H;
-      a.best[bs] = dd.best;
-      a.draws_used[bs] = 1;
-      a.canvas_flag[a.B + bs] = flag ? 1 : 0;
-      if (flag) any_flag = 1;
-    }
-  }
+  for (int s = w; s < a.S; s += 4)
+    if (slot_first_one(a, b, s, lane) && lane == 0) any_flag = 1;
   __syncthreads();
   if (threadIdx.x == 0) a.canvas_flag[b] = any_flag;
 }
@@ -173,11 +178,8 @@ __global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t
 }
 
 // average of the draws in probability space: r = mean r_d, lp = ln mean e^(lp_d)
-__global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
-  const int64_t bs = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (bs >= (int64_t)a.B * a.S) return;
-  if (!a.canvas_flag[a.B + bs]) return;
+// (slot bs of a flagged canvas, one wave)
+__device__ void slot_average_one(const SlotArgs &a, int64_t bs, int lane) {
   const int64_t b = bs / a.S;
   const int s = (int)(bs % a.S);
   const int k = a.n_labels[bs];
@@ -206,6 +208,42 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
     a.entropy[bs] = fin.H;
     a.best[bs] = fin.best;
     a.draws_used[bs] = a.n_draws;
+  }
+}
+
+__global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
+  const int64_t bs = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bs >= (int64_t)a.B * a.S) return;
+  if (!a.canvas_flag[a.B + bs]) return;
+  slot_average_one(a, bs, threadIdx.x & 63);
+}
+
+// The rest of a one-pass read for canvas b in one workgroup: first read of
+// every slot, the canvas's re-read flag, the status of slots whose noise id is
+// out of range (re-read canvases only), and the average of the flagged slots.
+__global__ __launch_bounds__(256) void slot_finish_kernel(SlotArgs a) {
+  __shared__ int any_flag;
+  const int b = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) any_flag = 0;
+  __syncthreads();
+  for (int s = w; s < a.S; s += 4)
+    if (slot_first_one(a, b, s, lane) && lane == 0) any_flag = 1;
+  __syncthreads();
+  const bool flagged = any_flag != 0;
+  if (threadIdx.x == 0) a.canvas_flag[b] = flagged ? 1 : 0;
+  if (!flagged) return;
+  for (int s = threadIdx.x; s < a.S; s += 256) {
+    const int64_t bs = (int64_t)b * a.S + s;
+    if (a.status[bs] != DG_SLOT_OK) continue;
+    for (int d = 0; d < a.n_draws; ++d) {
+      const int nid = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
+      if (nid < 0 || nid >= a.V) { a.status[bs] = DG_SLOT_BAD_NOISE; break; }
+    }
+  }
+  for (int s = w; s < a.S; s += 4) {
+    const int64_t bs = (int64_t)b * a.S + s;
+    if (a.canvas_flag[a.B + bs]) slot_average_one(a, bs, lane);
   }
 }
 
@@ -283,19 +321,6 @@ hipError_t launch_kv_replicate(void *k, void *v, int groups, int G, int C, int n
   return hipGetLastError();
 }
 
-// status of the slots of re-read canvases whose noise id is out of range
-__global__ __launch_bounds__(256) void slot_noise_status_kernel(SlotArgs a) {
-  const int64_t bs = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (bs >= (int64_t)a.B * a.S) return;
-  const int64_t b = bs / a.S;
-  if (!a.canvas_flag[b] || a.status[bs] != DG_SLOT_OK) return;
-  const int s = (int)(bs % a.S);
-  for (int d = 0; d < a.n_draws; ++d) {
-    const int nid = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
-    if (nid < 0 || nid >= a.V) { a.status[bs] = DG_SLOT_BAD_NOISE; return; }
-  }
-}
-
 hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st) {
   const int64_t n = (int64_t)a.B * (a.n_draws + 1);
   if (n == 0) return hipSuccess;
@@ -303,10 +328,9 @@ hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hi
   return hipGetLastError();
 }
 
-hipError_t launch_slot_noise_status(const SlotArgs &a, hipStream_t st) {
-  const int64_t n = (int64_t)a.B * a.S;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(slot_noise_status_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, a);
+hipError_t launch_slot_finish(const SlotArgs &a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_finish_kernel, dim3((unsigned)a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
