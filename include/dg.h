@@ -99,9 +99,15 @@ typedef struct {
  *   lm_head  [vocab, d_model]  separate LM head, or NULL for a tied head
  *   wq       [n_q_heads*head_dim, d_model]
  *   wk, wv   [n_kv_heads*head_dim, d_model]
- *   wo       [d_model, n_q_heads*head_dim] */
+ *   wo       [d_model, n_q_heads*head_dim]
+ *   lm_tiled the LM head (lm_head, else embed) in the blocked layout written by
+ *            dg_prepare_lm_tiled, or NULL.  Optional and bf16 only (ignored for
+ *            fp32); the results are the same either way, the blocked layout is
+ *            read faster.  Appended last, so a struct initialised with the first
+ *            seven fields leaves it NULL. */
 typedef struct {
     const void *embed, *embed_t, *lm_head, *wq, *wk, *wv, *wo;
+    const void *lm_tiled;
 } dg_weights;
 
 /* Cached prompt (encoder-mode) keys and values of every sequence, packed.
@@ -247,6 +253,16 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
  * the self-conditioning contraction streams.  Weight preparation, done once. */
 dg_status dg_prepare_embed_t(const dg_dims *dims, const void *embed, void *embed_t,
                              void *stream);
+
+/* Writes lm_tiled, the LM head [vocab, d_model] (bf16) in blocks of 256 vocabulary
+ * rows x 32 columns: element (v, k) sits at
+ *   ((v / 256) * (d_model / 32) + k / 32) * 8192 + (v % 256) * 32 + k % 32,
+ * so one K step of a 256-row vocabulary tile is 16 KB of contiguous memory.
+ * lm_tiled holds vocab * d_model elements.  Requires dtype DG_BF16 and d_model a
+ * multiple of 32 (DG_ERR_UNSUPPORTED otherwise).  Weight preparation, done once;
+ * head and lm_tiled are device pointers, 16-byte aligned. */
+dg_status dg_prepare_lm_tiled(const dg_dims *dims, const void *head, void *lm_tiled,
+                              void *stream);
 
 /* Host-only validation (no HIP calls; usable without a GPU).  Same checks the
  * calls above make before launching anything. */

@@ -86,7 +86,8 @@ dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const
                 kv->max_len, max_prompt);
   if (kv->max_len > 0 && (!kv->k || !kv->v))
     return fail(DG_ERR_INVALID_ARG, "prompt_kv.k/v are NULL but max_len > 0");
-  const void *ptrs[] = {w->embed, w->embed_t, w->lm_head, w->wq, w->wk, w->wv, w->wo, kv->k, kv->v};
+  const void *ptrs[] = {w->embed, w->embed_t, w->lm_head, w->wq, w->wk, w->wv, w->wo, w->lm_tiled,
+                        kv->k, kv->v};
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(DG_ERR_INVALID_ARG, "weight / KV pointers must be 16-byte aligned");
   return DG_OK;
@@ -238,6 +239,11 @@ struct Stages {
 
 template <typename P> P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<char *>(ws) + off);
+}
+
+// the blocked copy of the LM head, where the kernels read it (bf16, d % 32 == 0)
+const void *lm_tiled_of(const dg_dims &d, const dg_weights *w) {
+  return d.dtype == DG_BF16 && d.d_model % 32 == 0 ? w->lm_tiled : nullptr;
 }
 
 // The softmax scale in log2 units rides on q, so attention exponentiates
@@ -447,6 +453,7 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
 
   dg::LmheadArgs la{};
   la.head = w->lm_head ? w->lm_head : w->embed;
+  la.head_tiled = lm_tiled_of(d, w);
   la.h = h;
   la.logit_scale = logit_scale;
   la.row_scale = row_scale;
@@ -598,6 +605,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
 
   dg::LmheadArgs la{};
   la.head = w->lm_head ? w->lm_head : w->embed;
+  la.head_tiled = lm_tiled_of(d, w);
   la.h = h;
   la.row_index = sa.rows;
   la.logit_scale = logit_scale;
@@ -713,6 +721,21 @@ dg_status dg_prepare_embed_t(const dg_dims *dims, const void *embed, void *embed
   DG_TRY_HIP(dg::launch_transpose(embed, embed_t, dims->vocab, dims->d_model,
                                   dims->dtype == DG_BF16, static_cast<hipStream_t>(stream)),
              "transpose launch");
+  return ok();
+}
+
+dg_status dg_prepare_lm_tiled(const dg_dims *dims, const void *head, void *lm_tiled,
+                              void *stream) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (!head || !lm_tiled) return fail(DG_ERR_INVALID_ARG, "head and lm_tiled are required");
+  if (!aligned16(head) || !aligned16(lm_tiled))
+    return fail(DG_ERR_INVALID_ARG, "head and lm_tiled must be 16-byte aligned");
+  if (dims->dtype != DG_BF16 || dims->d_model % 32)
+    return fail(DG_ERR_UNSUPPORTED, "the blocked LM head needs bf16 and d_model %% 32 == 0");
+  DG_TRY_HIP(dg::launch_tile_lm(head, lm_tiled, dims->vocab, dims->d_model,
+                                static_cast<hipStream_t>(stream)),
+             "LM head tiling launch");
   return ok();
 }
 

@@ -11,6 +11,8 @@
 // double-buffered LDS (16-byte global loads -> registers -> LDS, one barrier per
 // K step); fragments are read from LDS with 16-byte (bf16) or 4-byte (fp32)
 // reads.  Accumulation is fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -196,6 +198,27 @@ template <typename T, int N> struct RowLoader {
   }
   __device__ inline Raw load(int it, int k) const {
     return *reinterpret_cast<const u32x4 *>(p[it] + k);
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
+    uint4 v = to_uint4(r);
+    pin(v);
+    return keep_if(v, live[it]);
+  }
+};
+
+// Rows of a matrix stored in blocks of BR rows x 32 columns (block after block
+// along K): p is the row's first element in the first block, and column k sits
+// k / 32 blocks further.
+template <typename T, int N, int BR> struct BlockedRowLoader {
+  using Raw = u32x4;
+  const T *p[N];
+  bool live[N];
+  __device__ inline void set(int it, const T *row, bool ok, const T *fallback) {
+    p[it] = ok ? row : fallback;
+    live[it] = ok;
+  }
+  __device__ inline Raw load(int it, int k) const {
+    return *reinterpret_cast<const u32x4 *>(p[it] + (int64_t)(k >> 5) * (BR * 32) + (k & 31));
   }
   __device__ inline uint4 finish(int it, const Raw &r) const {
     uint4 v = to_uint4(r);
@@ -428,10 +451,12 @@ struct DmaLoop {
   using frag = MF::frag;
 
   // rowa(r) / rowb(r): first element of row r of the A / B tile (always a
-  // dereferenceable row); K must be a multiple of BK
+  // dereferenceable row); K must be a multiple of BK.  astep: elements between
+  // consecutive K steps of an A row (BK for a row-major matrix, BM * BK for
+  // one stored in BM x BK blocks)
   template <class RA, class RB>
   __device__ static void run(char *(&st)[NS], const RA &rowa, const RB &rowb, int K,
-                             f32x4 (&acc)[TM][TN]) {
+                             int64_t astep, f32x4 (&acc)[TM][TN]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WGN, wn = w % WGN;
 #pragma unroll
@@ -451,7 +476,8 @@ struct DmaLoop {
 #pragma unroll
       for (int i = 0; i < QW; ++i)
         __builtin_amdgcn_global_load_lds(
-            gp[i] + kt * BK, (__attribute__((address_space(3))) void *)(s + (w * QW + i) * 1024), 16,
+            gp[i] + kt * (w * QW + i < QA ? astep : (int64_t)BK),
+            (__attribute__((address_space(3))) void *)(s + (w * QW + i) * 1024), 16,
             0, 0);
     };
     // fragment of row (16-aligned base) + lane%16, logical chunk lane/16
@@ -504,7 +530,8 @@ struct DmaLoop {
 // over the vocabulary runs mostly inside a lane.
 // ---------------------------------------------------------------------------
 // PF < 0 selects the direct-to-LDS K loop with -PF stages (bf16, BK = 32).
-template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
+// TL: the head is read from its copy in BM x 32 blocks (a.head_tiled).
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool TL = false>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF < 0 ? 1 : PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
@@ -534,21 +561,28 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     char *st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s] = st4[s];
-    auto rowa = [&](int r) { return head + (int64_t)(v0 + r) * d; };
+    const T *ht = static_cast<const T *>(a.head_tiled);
+    auto rowa = [&](int r) {
+      return TL ? ht + (int64_t)v0 * d + r * 32 : head + (int64_t)(v0 + r) * d;
+    };
     auto rowb = [&](int r) {
       const int64_t n = n0 + r;
       int64_t src = -1;
       if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
       return hh + (src >= 0 ? src : 0) * d;
     };
-    D::run(st, rowa, rowb, d, acc);
+    D::run(st, rowa, rowb, d, TL ? (int64_t)BM * 32 : (int64_t)32, acc);
   } else {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
-    RowLoader<T, G::AI> al;
+    static_assert(!TL || (BK == 32 && sizeof(T) == 2), "blocked head: bf16, BK = 32");
+    using AL = typename std::conditional<TL, BlockedRowLoader<T, G::AI, BM>, RowLoader<T, G::AI>>::type;
+    AL al;
+    const T *ht = static_cast<const T *>(a.head_tiled);
 #pragma unroll
     for (int it = 0; it < G::AI; ++it) {
       const int v = v0 + G::a_row(it);
-      al.set(it, head + (int64_t)v * d, v < a.vocab, head);
+      al.set(it, TL ? ht + (int64_t)v0 * d + G::a_row(it) * 32 : head + (int64_t)v * d, v < a.vocab,
+             TL ? ht : head);
     }
     RowLoader<T, G::BI> bl;
 #pragma unroll
@@ -828,10 +862,15 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
     // few rows (slot reads): a 64-row tile keeps the MFMA work proportional to
     // the rows and three workgroups per CU keep the vocabulary stream busy
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
-    hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
+    if (a.head_tiled)
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32, true>), grid, dim3(4 * WAVE), 0, st, a);
+    else
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
   } else if (bf) {
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
-    if (a.d % 32 == 0)
+    if (a.d % 32 == 0 && a.head_tiled)
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, -kLmStages, 32, true>), grid, dim3(8 * WAVE), 0, st, a);
+    else if (a.d % 32 == 0)
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, -kLmStages, 32>), grid, dim3(8 * WAVE), 0, st, a);
     else
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);

@@ -39,6 +39,7 @@ struct OprojArgs {
 
 struct LmheadArgs {
   const void *head;        // [V, d]
+  const void *head_tiled;  // the same in 256 x 32 blocks (bf16), or null
   const void *h;           // [*, d]
   const int32_t *row_index;  // [nrows] rows of h to use (-1 = none) or null (identity)
   const int32_t *active_rows;  // per-group flag (groups of rows_per_flag rows) or null
@@ -130,6 +131,8 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
+// bf16 [rows, cols] -> blocks of 256 rows x 32 columns (rows % 256 == 0, cols % 32 == 0)
+hipError_t launch_tile_lm(const void *src, void *dst, int rows, int cols, hipStream_t st);
 hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,
                             hipStream_t st);
 hipError_t launch_clear_i32(int32_t *p, int64_t n, hipStream_t st);

@@ -175,6 +175,28 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *src, T *dst, in
   }
 }
 
+// [rows, cols] bf16 into blocks of 256 rows x 32 columns, 16 bytes per thread
+__global__ __launch_bounds__(256) void tile_lm_kernel(const uint4 *src, uint4 *dst, int rows,
+                                                      int cols) {
+  const int64_t n = (int64_t)rows * cols / 8;
+  const int cb = cols / 32;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / (cols / 8);
+    const int k = (int)(i % (cols / 8)) * 8;
+    const int64_t o = ((r / 256) * cb + k / 32) * 8192 + (r % 256) * 32 + k % 32;
+    dst[o / 8] = src[i];
+  }
+}
+
+hipError_t launch_tile_lm(const void *src, void *dst, int rows, int cols, hipStream_t st) {
+  if (rows % 256 || cols % 32) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)rows * cols / 8;
+  const unsigned grid = (unsigned)(cdiv64(n, 256) < 65536 ? cdiv64(n, 256) : 65536);
+  hipLaunchKernelGGL(tile_lm_kernel, dim3(grid), dim3(256), 0, st,
+                     static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), rows, cols);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,
                             hipStream_t st) {
   dim3 grid((unsigned)cdiv64(cols, 64), (unsigned)cdiv64(rows, 64));

@@ -23,7 +23,7 @@ def to_device(a, dtype=None, device="cuda"):
 class DeviceProblem:
     """A workload's weights, prompt KV and canvases resident in device memory."""
 
-    def __init__(self, inp, device="cuda", with_embed_t=True):
+    def __init__(self, inp, device="cuda", with_embed_t=True, with_lm_tiled=True):
         dm = inp["dims"]
         self.inp = inp
         self.device = device
@@ -45,6 +45,12 @@ class DeviceProblem:
         if with_embed_t:
             self.embed_t = torch.empty((self.d, self.V), dtype=T, device=device)
             dg.dg_prepare_embed_t(self.dims, self.embed, self.embed_t)
+        # the LM head in 256 x 32 blocks (bf16 only): same results, faster reads
+        self.lm_tiled = None
+        if with_lm_tiled and dm.dtype == "bf16" and self.d % 32 == 0:
+            head = self.lm_head if self.lm_head is not None else self.embed
+            self.lm_tiled = torch.empty((self.V * self.d,), dtype=T, device=device)
+            dg.dg_prepare_lm_tiled(self.dims, head, self.lm_tiled)
         total = int(inp["cu_seqlens"][-1])
         kshape = (max(total, 1),) + inp["prompt_k"].shape[1:]
         self.prompt_k = torch.zeros(kshape, dtype=T, device=device)
@@ -62,7 +68,8 @@ class DeviceProblem:
         self.noise_ids = to_device(inp["noise_ids"].astype(np.int32), None, device)
         self.S = int(inp["slot_pos"].shape[1])
         self.weights = dg.make_weights(self.embed, self.wq, self.wk, self.wv, self.wo,
-                                       embed_t=self.embed_t, lm_head=self.lm_head)
+                                       embed_t=self.embed_t, lm_head=self.lm_head,
+                                       lm_tiled=self.lm_tiled)
         self.kv = dg.make_prompt_kv(self.prompt_k, self.prompt_v, self.cu, self.max_prompt,
                                     total)
         self._ws = {}

@@ -162,3 +162,24 @@ def test_step_deterministic(torch_cuda):
     torch.cuda.synchronize()
     for k in ("conf", "entropy", "argmax", "sc_out", "attn_out", "hidden_out", "logits"):
         assert torch.equal(a[k], b[k]), k
+
+
+def test_blocked_lm_head_matches_row_major(torch_cuda):
+    """The LM head read from its 256 x 32 blocked copy (dg_prepare_lm_tiled) gives
+    bitwise the same step and slot-read outputs as the row-major head: the same
+    MFMAs over the same K order, only the addresses differ.  Covers the 256-row
+    tile (the step) and the few-row tile (the read)."""
+    from slot_readout_amd.runtime import DeviceProblem
+    cfg = config("bf16_step", vocab=4096, mask_id=4095)
+    inp = make_inputs(cfg, prompt_override=("fixed", 200))
+    outs = []
+    for tiled in (True, False):
+        dev = DeviceProblem(inp, with_lm_tiled=tiled)
+        assert (dev.lm_tiled is not None) == tiled
+        st = dev.step(want_sc=True)
+        rd = dev.slot_read()
+        torch_cuda.cuda.synchronize()
+        outs.append({**{"step_" + k: to_np(v) for k, v in st.items()},
+                     **{"read_" + k: to_np(v) for k, v in rd.items()}})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
