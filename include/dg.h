@@ -95,7 +95,8 @@ typedef struct {
 /* Weights, all T, row-major, device.
  *   embed    [vocab, d_model]  token embedding; also the LM head when lm_head is NULL
  *   embed_t  [d_model, vocab]  the same matrix transposed (see dg_prepare_embed_t);
- *                              required when sc_out is requested
+ *                              required when sc_out is requested, unless
+ *                              embed_t_tiled is set
  *   lm_head  [vocab, d_model]  separate LM head, or NULL for a tied head
  *   wq       [n_q_heads*head_dim, d_model]
  *   wk, wv   [n_kv_heads*head_dim, d_model]
@@ -103,11 +104,17 @@ typedef struct {
  *   lm_tiled the LM head (lm_head, else embed) in the blocked layout written by
  *            dg_prepare_lm_tiled, or NULL.  Optional and bf16 only (ignored for
  *            fp32); the results are the same either way, the blocked layout is
- *            read faster.  Appended last, so a struct initialised with the first
- *            seven fields leaves it NULL. */
+ *            read faster.  Appended after the first seven fields, so a struct
+ *            initialised with those seven leaves it NULL.
+ *   embed_t_tiled  embed_t in the blocked layout written by dg_prepare_embed_t_tiled,
+ *            or NULL.  Optional and bf16 only, for d_model a multiple of 256; when
+ *            set, the self-conditioning contraction streams it instead of embed_t
+ *            (same results, contiguous 16 KB reads per K step) and sc_out may be
+ *            requested without embed_t. */
 typedef struct {
     const void *embed, *embed_t, *lm_head, *wq, *wk, *wv, *wo;
     const void *lm_tiled;
+    const void *embed_t_tiled;
 } dg_weights;
 
 /* Cached prompt (encoder-mode) keys and values of every sequence, packed.
@@ -263,6 +270,18 @@ dg_status dg_prepare_embed_t(const dg_dims *dims, const void *embed, void *embed
  * head and lm_tiled are device pointers, 16-byte aligned. */
 dg_status dg_prepare_lm_tiled(const dg_dims *dims, const void *head, void *lm_tiled,
                               void *stream);
+
+/* Writes embed_t_tiled, embed^T [d_model, vocab] (bf16) in blocks of 256 rows of
+ * d_model x 32 vocabulary columns: element (c, v) of embed^T (= embed[v][c]) sits at
+ *   ((c / 256) * (vocab / 32) + v / 32) * 8192 + (c % 256) * 32 + v % 32,
+ * so one K step (32 vocabulary entries) of a 256-wide d tile of the
+ * self-conditioning contraction is 16 KB of contiguous memory.  Reads embed_t
+ * (row-major, from dg_prepare_embed_t); embed_t_tiled holds vocab * d_model
+ * elements.  Requires dtype DG_BF16 and d_model a multiple of 256
+ * (DG_ERR_UNSUPPORTED otherwise).  Weight preparation, done once; both pointers
+ * are device pointers, 16-byte aligned. */
+dg_status dg_prepare_embed_t_tiled(const dg_dims *dims, const void *embed_t,
+                                   void *embed_t_tiled, void *stream);
 
 /* Host-only validation (no HIP calls; usable without a GPU).  Same checks the
  * calls above make before launching anything. */

@@ -87,7 +87,7 @@ dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const
   if (kv->max_len > 0 && (!kv->k || !kv->v))
     return fail(DG_ERR_INVALID_ARG, "prompt_kv.k/v are NULL but max_len > 0");
   const void *ptrs[] = {w->embed, w->embed_t, w->lm_head, w->wq, w->wk, w->wv, w->wo, w->lm_tiled,
-                        kv->k, kv->v};
+                        w->embed_t_tiled, kv->k, kv->v};
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(DG_ERR_INVALID_ARG, "weight / KV pointers must be 16-byte aligned");
   return DG_OK;
@@ -144,7 +144,8 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
   p.part_ml = a.take(p.attn.part_ml);
   p.h = a.take(M * d.d_model * ts);
   p.stats = a.take(M * nvt * sizeof(float4));
-  p.ptilde = a.take(M * d.vocab * ts);
+  // bf16 p~ is stored in blocks of 256 rows: whole row blocks are allocated
+  p.ptilde = a.take((bf ? (M + 255) / 256 * 256 : M) * d.vocab * ts);
   p.shift = a.take(M * nvt * sizeof(int32_t));
   p.inv_z = a.take(M * sizeof(float));
   p.ksplit = dg::sc_ksplit((int64_t)M, d.d_model, d.vocab, bf);
@@ -244,6 +245,10 @@ template <typename P> P *at(void *ws, size_t off) {
 // the blocked copy of the LM head, where the kernels read it (bf16, d % 32 == 0)
 const void *lm_tiled_of(const dg_dims &d, const dg_weights *w) {
   return d.dtype == DG_BF16 && d.d_model % 32 == 0 ? w->lm_tiled : nullptr;
+}
+
+const void *embed_t_tiled_of(const dg_dims &d, const dg_weights *w) {
+  return d.dtype == DG_BF16 && d.d_model % 256 == 0 ? w->embed_t_tiled : nullptr;
 }
 
 // The softmax scale in log2 units rides on q, so attention exponentiates
@@ -426,8 +431,10 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   if (batch == 0) return ok();
   if (!canvas_ids || !conf || !entropy || !argmax)
     return fail(DG_ERR_INVALID_ARG, "canvas_ids, conf, entropy and argmax are required");
-  if (sc_out && !w->embed_t)
-    return fail(DG_ERR_INVALID_ARG, "sc_out requires weights.embed_t (see dg_prepare_embed_t)");
+  const void *et_tiled = embed_t_tiled_of(d, w);
+  if (sc_out && !w->embed_t && !et_tiled)
+    return fail(DG_ERR_INVALID_ARG,
+                "sc_out requires weights.embed_t (see dg_prepare_embed_t) or embed_t_tiled");
   if (!aligned16(sc_in) || !aligned16(sc_out) || !aligned16(workspace))
     return fail(DG_ERR_INVALID_ARG, "sc_in, sc_out and workspace must be 16-byte aligned");
   if (debug && (!aligned16(debug->attn_out) || !aligned16(debug->hidden_out)))
@@ -459,6 +466,7 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
   la.row_scale = row_scale;
   la.stats = at<float4>(workspace, p.stats);
   la.ptilde = sc_out ? at<char>(workspace, p.ptilde) : nullptr;
+  la.ptilde_blocked = bf;
   la.logits = debug ? debug->logits_out : nullptr;
   la.nrows = M;
   la.d = d.d_model;
@@ -487,7 +495,9 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
     sa.ptilde = la.ptilde;
     sa.shift = va.shift;
     sa.inv_z = va.inv_z;
+    sa.ptilde_blocked = la.ptilde_blocked;
     sa.embed_t = w->embed_t;
+    sa.embed_t_tiled = et_tiled;
     sa.part = at<float>(workspace, p.sc_part);
     sa.out = sc_out;
     sa.M = M;
@@ -736,6 +746,23 @@ dg_status dg_prepare_lm_tiled(const dg_dims *dims, const void *head, void *lm_ti
   DG_TRY_HIP(dg::launch_tile_lm(head, lm_tiled, dims->vocab, dims->d_model,
                                 static_cast<hipStream_t>(stream)),
              "LM head tiling launch");
+  return ok();
+}
+
+dg_status dg_prepare_embed_t_tiled(const dg_dims *dims, const void *embed_t,
+                                   void *embed_t_tiled, void *stream) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (!embed_t || !embed_t_tiled)
+    return fail(DG_ERR_INVALID_ARG, "embed_t and embed_t_tiled are required");
+  if (!aligned16(embed_t) || !aligned16(embed_t_tiled))
+    return fail(DG_ERR_INVALID_ARG, "embed_t and embed_t_tiled must be 16-byte aligned");
+  if (dims->dtype != DG_BF16 || dims->d_model % 256)
+    return fail(DG_ERR_UNSUPPORTED, "the blocked embed^T needs bf16 and d_model %% 256 == 0");
+  // embed^T is [d_model, vocab]: blocks of 256 of its rows x 32 of its columns
+  DG_TRY_HIP(dg::launch_tile_lm(embed_t, embed_t_tiled, dims->d_model, dims->vocab,
+                                static_cast<hipStream_t>(stream)),
+             "embed^T tiling launch");
   return ok();
 }
 

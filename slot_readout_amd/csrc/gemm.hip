@@ -272,14 +272,16 @@ __device__ inline uint4 pow2_down(uint4 v, int sh, float) {
   return __builtin_bit_cast(uint4, __builtin_elementwise_sub_sat(x, d));
 }
 
-template <typename T, int N> struct ShiftedRowLoader {
+// BLK: p~ stored in blocks of 256 rows x 32 columns; p is then the row's first
+// element in its first block and column k sits k / 32 blocks further
+template <typename T, int N, bool BLK> struct ShiftedRowLoader {
   struct Raw { u32x4 p; int sh; };
   const T *p[N];
   const int32_t *sh[N];
   bool live[N];
   __device__ inline Raw load(int it, int k) const {
     Raw r;
-    r.p = *reinterpret_cast<const u32x4 *>(p[it] + k);
+    r.p = *reinterpret_cast<const u32x4 *>(p[it] + (BLK ? (int64_t)(k >> 5) * 8192 + (k & 31) : k));
     r.sh = sh[it][k / VTILE];
     return r;
   }
@@ -695,8 +697,14 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
         t += e * x;
         e4[r] = e;
       }
-      // four consecutive vocabulary entries of one row: one 8- (bf16) or 16-byte store
-      if (pt && live) store4<T>(pt + n * a.vocab + vb, e4);
+      // four consecutive vocabulary entries of one row: one 8- (bf16) or 16-byte
+      // store (row-major, or inside one 256 x 32 block)
+      if (pt && live) {
+        const int64_t off = a.ptilde_blocked
+                                ? ((n >> 8) * (a.vocab >> 5) + (vb >> 5)) * 8192 + (n & 255) * 32 + (vb & 31)
+                                : n * a.vocab + vb;
+        store4<T>(pt + off, e4);
+      }
       if (a.logits && live) *reinterpret_cast<f32x4 *>(a.logits + n * a.vocab + vb) = acc[i][j];
     }
     s += __shfl_xor(s, 16);
@@ -736,9 +744,14 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
 // ---------------------------------------------------------------------------
 // S6: sc = p E over a range of the vocabulary (A = p~ scaled, B = E^T rows)
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
+// PB: p~ in 256-row blocks (a.ptilde_blocked); BT: E^T read from its 256 x 32
+// blocked copy (a.embed_t_tiled, d % 256 == 0)
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool PB = false,
+          bool BT = false>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
+  static_assert(!(PB || BT) || (sizeof(T) == 2 && BK % 32 == 0), "blocked operands: bf16, BK % 32 == 0");
+  static_assert(!BT || BN == 256, "blocked E^T: 256-wide d tiles");
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   // group = vocabulary range z; its (row, d) tiles share the p~ slice and run
   // on one XCD
@@ -759,20 +772,26 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
   const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * G::BK;
   const T *ptl = static_cast<const T *>(a.ptilde);
   const T *et = static_cast<const T *>(a.embed_t);
-  ShiftedRowLoader<T, G::AI> al;
+  ShiftedRowLoader<T, G::AI, PB> al;
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
     const bool ok = row < a.M;
-    al.p[it] = ptl + (ok ? row * a.vocab : 0);
-    al.sh[it] = a.shift + (ok ? row * a.nvt : 0);
+    const int64_t r = ok ? row : 0;
+    al.p[it] = ptl + (PB ? (r >> 8) * 256 * (int64_t)a.vocab + (r & 255) * 32 : r * a.vocab);
+    al.sh[it] = a.shift + r * a.nvt;
     al.live[it] = ok;
   }
-  RowLoader<T, G::BI> bl;
+  using BL = typename std::conditional<BT, BlockedRowLoader<T, G::BI, 256>, RowLoader<T, G::BI>>::type;
+  BL bl;
+  const T *ett = static_cast<const T *>(a.embed_t_tiled);
 #pragma unroll
   for (int it = 0; it < G::BI; ++it) {
     const int n = n0 + G::a_row(it);
-    bl.set(it, et + (int64_t)n * a.vocab, n < a.d, et);
+    if constexpr (BT)
+      bl.set(it, ett + (int64_t)(n >> 8) * 256 * a.vocab + (n & 255) * 32, n < a.d, ett);
+    else
+      bl.set(it, et + (int64_t)n * a.vocab, n < a.d, et);
   }
   f32x4 acc[G::TM][G::TN];
   G::run(smem, al, bl, kbeg, kend, acc);
@@ -898,7 +917,12 @@ hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
   if (bf) {
     const dim3 grid = kScGroup ? xcd_grid(a.ksplit, cdiv64(a.d, kScTileD) * cdiv64(a.M, 256))
                                : dim3((unsigned)(a.ksplit * cdiv64(a.d, kScTileD) * cdiv64(a.M, 256)));
-    hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
+    if (a.ptilde_blocked && a.embed_t_tiled)
+      hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64, true, true>), grid, dim3(8 * WAVE), 0, st, a);
+    else if (a.ptilde_blocked)
+      hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64, true>), grid, dim3(8 * WAVE), 0, st, a);
+    else
+      hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64>), grid, dim3(8 * WAVE), 0, st, a);
   } else {
     const int64_t nt = cdiv64(a.d, 64) * cdiv64(a.M, 64);
     const dim3 grid = kScGroup ? xcd_grid(a.ksplit, nt) : dim3((unsigned)(a.ksplit * nt));

@@ -49,7 +49,10 @@ struct LmheadArgs {
   // per (row, tile): (m = max l, sum e, sum e*(l - r ln2), argmax bits) with
   // e = e^(l - r ln2), r = tile_ref(m)
   float4 *stats;           // [nrows, nvt]
-  void *ptilde;            // [nrows, V] T or null: e^(l - r ln2) of the row's tile
+  void *ptilde;            // T or null: e^(l - r ln2) of the row's tile, [nrows, V]
+  // row-major, or (ptilde_blocked) in blocks of 256 rows x 32 vocabulary
+  // entries: (n, v) at ((n / 256) * (V / 32) + v / 32) * 8192 + (n % 256) * 32 + v % 32
+  int ptilde_blocked;
   float *logits;           // [nrows, V] or null
   // label logits of slot rows (optional): row n belongs to slot
   // bs = (n / lab_span) * lab_S + n % lab_S, whose lab_n[bs] label ids are
@@ -63,7 +66,9 @@ struct LmheadArgs {
 };
 
 struct ScArgs {
-  const void *ptilde;      // [M, V]
+  const void *ptilde;      // [M, V], row-major or blocked as in LmheadArgs
+  int ptilde_blocked;
+  const void *embed_t_tiled;  // E^T in 256 x 32 blocks (d % 256 == 0), or null
   const int32_t *shift;    // [M, nvt] p = p~ * 2^-shift / Z
   const float *inv_z;      // [M] 1/Z
   const void *embed_t;     // [d, V]

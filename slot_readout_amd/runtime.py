@@ -23,7 +23,8 @@ def to_device(a, dtype=None, device="cuda"):
 class DeviceProblem:
     """A workload's weights, prompt KV and canvases resident in device memory."""
 
-    def __init__(self, inp, device="cuda", with_embed_t=True, with_lm_tiled=True):
+    def __init__(self, inp, device="cuda", with_embed_t=True, with_lm_tiled=True,
+                 with_embed_t_tiled=True):
         dm = inp["dims"]
         self.inp = inp
         self.device = device
@@ -51,6 +52,12 @@ class DeviceProblem:
             head = self.lm_head if self.lm_head is not None else self.embed
             self.lm_tiled = torch.empty((self.V * self.d,), dtype=T, device=device)
             dg.dg_prepare_lm_tiled(self.dims, head, self.lm_tiled)
+        # embed^T in 256 x 32 blocks (bf16, d % 256 == 0) for the p.E contraction
+        self.embed_t_tiled = None
+        if (with_embed_t_tiled and self.embed_t is not None and dm.dtype == "bf16"
+                and self.d % 256 == 0):
+            self.embed_t_tiled = torch.empty((self.V * self.d,), dtype=T, device=device)
+            dg.dg_prepare_embed_t_tiled(self.dims, self.embed_t, self.embed_t_tiled)
         total = int(inp["cu_seqlens"][-1])
         kshape = (max(total, 1),) + inp["prompt_k"].shape[1:]
         self.prompt_k = torch.zeros(kshape, dtype=T, device=device)
@@ -69,7 +76,8 @@ class DeviceProblem:
         self.S = int(inp["slot_pos"].shape[1])
         self.weights = dg.make_weights(self.embed, self.wq, self.wk, self.wv, self.wo,
                                        embed_t=self.embed_t, lm_head=self.lm_head,
-                                       lm_tiled=self.lm_tiled)
+                                       lm_tiled=self.lm_tiled,
+                                       embed_t_tiled=self.embed_t_tiled)
         self.kv = dg.make_prompt_kv(self.prompt_k, self.prompt_v, self.cu, self.max_prompt,
                                     total)
         self._ws = {}

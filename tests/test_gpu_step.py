@@ -183,3 +183,34 @@ def test_blocked_lm_head_matches_row_major(torch_cuda):
                      **{"read_" + k: to_np(v) for k, v in rd.items()}})
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_blocked_self_conditioning_matches_row_major(torch_cuda):
+    """p.E read from the 256 x 32 blocked embed^T (dg_prepare_embed_t_tiled) gives
+    bitwise the same sc_out as the row-major embed^T: the same MFMAs in the same
+    K order, only the addresses differ."""
+    from slot_readout_amd.runtime import DeviceProblem
+    cfg = config("bf16_step", vocab=4096, mask_id=4095)
+    inp = make_inputs(cfg, prompt_override=("fixed", 200))
+    outs = []
+    for tiled in (True, False):
+        dev = DeviceProblem(inp, with_embed_t_tiled=tiled)
+        assert (dev.embed_t_tiled is not None) == tiled
+        st = dev.step(want_sc=True)
+        torch_cuda.cuda.synchronize()
+        outs.append({k: to_np(v) for k, v in st.items()})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_step_bf16_partial_row_block(torch_cuda):
+    """bf16 canvases whose rows do not fill the last 256-row block of p~
+    (2 x 200 rows): every output, sc_out included, against the oracle."""
+    inp = make_inputs(config("ragged32", batch=2, canvas=200),
+                      prompt_override=("uniform", 100, 300))
+    dev = _problem(inp)
+    assert dev.embed_t_tiled is not None
+    out = dev.step(debug=True)
+    torch_cuda.cuda.synchronize()
+    refs = oracle.denoise_step(inp, need_logits=True)
+    _check_step(inp, out, refs, "bf16", label="ragged 2x200")
