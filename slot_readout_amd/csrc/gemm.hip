@@ -453,12 +453,13 @@ struct DmaLoop {
   using frag = MF::frag;
 
   // rowa(r) / rowb(r): first element of row r of the A / B tile (always a
-  // dereferenceable row); K must be a multiple of BK.  astep: elements between
-  // consecutive K steps of an A row (BK for a row-major matrix, BM * BK for
-  // one stored in BM x BK blocks)
-  template <class RA, class RB>
+  // dereferenceable row); K must be a multiple of BK.  astep / bstep: elements
+  // between consecutive K steps of an A / B row (BK for a row-major matrix,
+  // BM * BK for one stored in BM x BK blocks).  afix(kt, a) may transform the
+  // A fragments of step kt after they are read from LDS.
+  template <class RA, class RB, class AF>
   __device__ static void run(char *(&st)[NS], const RA &rowa, const RB &rowb, int K,
-                             int64_t astep, f32x4 (&acc)[TM][TN]) {
+                             int64_t astep, int64_t bstep, f32x4 (&acc)[TM][TN], const AF &afix) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WGN, wn = w % WGN;
 #pragma unroll
@@ -478,17 +479,18 @@ struct DmaLoop {
 #pragma unroll
       for (int i = 0; i < QW; ++i)
         __builtin_amdgcn_global_load_lds(
-            gp[i] + kt * (w * QW + i < QA ? astep : (int64_t)BK),
+            gp[i] + kt * (w * QW + i < QA ? astep : bstep),
             (__attribute__((address_space(3))) void *)(s + (w * QW + i) * 1024), 16,
             0, 0);
     };
     // fragment of row (16-aligned base) + lane%16, logical chunk lane/16
     const int pc = 16 * ((lane >> 4) ^ ((lane >> 2) & 3)) + 64 * (lane & 15);
-    auto compute = [&](const char *s) {
+    auto compute = [&](const char *s, int kt) {
       frag a[TM], b[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         a[i] = *reinterpret_cast<const frag *>(s + (wm * WM + i * 16) * 64 + pc);
+      afix(kt, a);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         b[j] = *reinterpret_cast<const frag *>(s + (BM + wn * WN + j * 16) * 64 + pc);
@@ -508,7 +510,7 @@ struct DmaLoop {
       __builtin_amdgcn_s_waitcnt(WAIT);
       __builtin_amdgcn_s_barrier();
       dma(kt + NS - 1 < nk ? kt + NS - 1 : nk - 1, st[(j + NS - 1) % NS]);
-      compute(st[j]);
+      compute(st[j], kt);
     };
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) dma(s < nk ? s : nk - 1, st[s]);
@@ -573,7 +575,8 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
       if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
       return hh + (src >= 0 ? src : 0) * d;
     };
-    D::run(st, rowa, rowb, d, TL ? (int64_t)BM * 32 : (int64_t)32, acc);
+    D::run(st, rowa, rowb, d, TL ? (int64_t)BM * 32 : (int64_t)32, (int64_t)32, acc,
+           [](int, typename D::frag(&)[D::TM]) {});
   } else {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
     static_assert(!TL || (BK == 32 && sizeof(T) == 2), "blocked head: bf16, BK = 32");
@@ -815,6 +818,84 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
     }
 }
 
+// S6 with the direct-to-LDS K loop: p~ (256-row blocks) and E^T (256 x 32
+// blocks) stream into four LDS stages without passing through registers, and
+// the power-of-two rescale of p~ is applied to the A fragments after they are
+// read from LDS.  The shifts of the workgroup's rows and vocabulary tiles are
+// staged in LDS once, as bytes (a shift >= 255 already flushes a bf16 to 0),
+// laid out so that a lane fetches the shifts of its four fragment rows with one
+// 4-byte read.  Requires d % 256 == 0 and at most kScDmaTiles vocabulary tiles
+// per split.
+constexpr int kScDmaTiles = 64;
+
+template <int WGM, int WGN>
+__global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_dma_kernel(ScArgs a) {
+  constexpr int BM = 256, BN = 256, NS = 4;
+  using D = DmaLoop<BM, BN, WGM, WGN, NS>;
+  static_assert(D::TM == 4, "one 4-byte shift read covers a wave's four fragment rows");
+  __shared__ __attribute__((aligned(1024))) char s0[D::STAGE], s1[D::STAGE], s2[D::STAGE],
+      s3[D::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char shl[kScDmaTiles * BM];
+  char *st[NS] = {s0, s1, s2, s3};
+  const int ntn = a.d / BN;
+  const int nt = ntn * (int)cdiv64(a.M, BM);
+  if ((int)blockIdx.x >= a.ksplit * nt) return;
+  const int z = blockIdx.x / nt, t = blockIdx.x % nt;
+  const int n0 = (t % ntn) * BN;
+  const int64_t m0 = (int64_t)(t / ntn) * BM;
+  const int nk = a.vocab / 64;   // split boundaries on 64-entry steps
+  const int kbeg = (int)((int64_t)z * nk / a.ksplit) * 64;
+  const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * 64;
+  const int t0 = kbeg / VTILE;
+  const int ntl = kend > kbeg ? (kend - 1) / VTILE - t0 + 1 : 0;
+  // shift of (row m, tile t) at byte t*256 + (m/64)*64 + (m%16)*4 + (m%64)/16
+  for (int i = threadIdx.x; i < ntl * BM; i += WGM * WGN * WAVE) {
+    const int tl = i / BM, m = i % BM;
+    const int64_t row = m0 + m;
+    int sh = row < a.M ? a.shift[row * a.nvt + t0 + tl] : 255;
+    sh = sh < 0 ? 0 : (sh > 255 ? 255 : sh);
+    shl[tl * BM + (m >> 6) * 64 + (m & 15) * 4 + ((m >> 4) & 3)] = (unsigned char)sh;
+  }
+  __syncthreads();
+  const bf16 *ptl = static_cast<const bf16 *>(a.ptilde);
+  const bf16 *ett = static_cast<const bf16 *>(a.embed_t_tiled);
+  const int64_t kb = (int64_t)(kbeg >> 5) * 8192;
+  // rows of the last row block past M hold stale p~: their outputs are never stored
+  const bf16 *pa = ptl + (m0 >> 8) * 256 * (int64_t)a.vocab + kb;
+  const bf16 *pb = ett + (int64_t)(n0 >> 8) * 256 * a.vocab + kb;
+  auto rowa = [&](int r) { return pa + r * 32; };
+  auto rowb = [&](int r) { return pb + r * 32; };
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const unsigned char *shw = shl + wm * 64 + (lane & 15) * 4;
+  auto afix = [&](int kt, typename D::frag (&af)[D::TM]) {
+    const int tl = ((kbeg + kt * 32) >> 8) - t0;
+    const unsigned sh4 = *reinterpret_cast<const unsigned *>(shw + tl * BM);
+#pragma unroll
+    for (int i = 0; i < D::TM; ++i) {
+      const uint4 v = __builtin_bit_cast(uint4, af[i]);
+      af[i] = __builtin_bit_cast(typename D::frag, pow2_down(v, (int)((sh4 >> (8 * i)) & 255), bf16{}));
+    }
+  };
+  f32x4 acc[D::TM][D::TN];
+  D::run(st, rowa, rowb, kend - kbeg, (int64_t)8192, (int64_t)8192, acc, afix);
+#pragma unroll
+  for (int i = 0; i < D::TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + wm * D::WM + i * 16 + 4 * (lane >> 4) + r;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < D::TN; ++j) {
+        const int col = n0 + wn * D::WN + j * 16 + (lane & 15);
+        if (a.ksplit == 1)
+          static_cast<bf16 *>(a.out)[row * a.d + col] = from_f<bf16>(acc[i][j][r] * a.inv_z[row]);
+        else
+          a.part[((int64_t)z * a.M + row) * a.d + col] = acc[i][j][r];
+      }
+    }
+}
+
 // fixed-order sum of the split-K partials
 template <typename T>
 __global__ __launch_bounds__(256) void sc_reduce_kernel(const float *part, const float *inv_z,
@@ -917,7 +998,11 @@ hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
   if (bf) {
     const dim3 grid = kScGroup ? xcd_grid(a.ksplit, cdiv64(a.d, kScTileD) * cdiv64(a.M, 256))
                                : dim3((unsigned)(a.ksplit * cdiv64(a.d, kScTileD) * cdiv64(a.M, 256)));
-    if (a.ptilde_blocked && a.embed_t_tiled)
+    // vocabulary tiles a split can span: its 64-entry steps, rounded up, plus one
+    const int64_t tiles = (int64_t)(a.vocab / 64 + a.ksplit - 1) / a.ksplit * 64 / VTILE + 2;
+    if (a.ptilde_blocked && a.embed_t_tiled && a.d % 256 == 0 && tiles <= kScDmaTiles)
+      hipLaunchKernelGGL((scgemm_dma_kernel<4, 2>), grid, dim3(8 * WAVE), 0, st, a);
+    else if (a.ptilde_blocked && a.embed_t_tiled)
       hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64, true, true>), grid, dim3(8 * WAVE), 0, st, a);
     else if (a.ptilde_blocked)
       hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64, true>), grid, dim3(8 * WAVE), 0, st, a);
