@@ -244,7 +244,7 @@ def main():
             "selfcond": (stages["selfcond"], sc_bytes, sc_flops),
             "attention": (stages["attention"], at_bytes, at_flops)}
     names = {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
-             "selfcond": "scgemm_kernel + sc_reduce_kernel (S6)",
+             "selfcond": "scgemm_dma_kernel + sc_reduce_kernel (S6)",
              "attention": "attn_kernel + attn_merge_kernel (S2)"}
     dom = max(cand, key=lambda k: cand[k][0])
     t_ms, nbytes, flops = cand[dom]

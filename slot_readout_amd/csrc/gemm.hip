@@ -435,8 +435,11 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
 // instruction moves a block of 16 rows x 64 bytes (BK = 32) from global memory
 // straight into LDS.  NS stages give NS-1 steps of loads in flight without
 // holding staged tiles in registers.  The four 16-byte chunks of a 64-byte row
-// sit XOR-swizzled by (row >> 2) & 3, which keeps the 16-row fragment reads
-// free of bank conflicts; the swizzle is applied on the global side (each lane
+// sit XOR-swizzled by (row >> 1) & 3.  A 16-byte LDS read is served eight
+// lanes at a time over 128 bytes of banks; with this swizzle the eight rows a
+// pass reads (rows 8q .. 8q+7 of one logical chunk) land on eight distinct
+// 16-byte bank groups (SQ_LDS_BANK_CONFLICT 0; a (row >> 2) & 3 swizzle costs
+// 2x on half the passes).  The swizzle is applied on the global side (each lane
 // fetches the chunk that belongs at its LDS slot).  Stages live in separate
 // LDS arrays, so the compiler can tell a stage being read from the stages
 // still being filled and waits only for the loads a read depends on.
@@ -468,7 +471,7 @@ struct DmaLoop {
       for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
     const int nk = K / BK;
     // lane l fills slot (row l/4, chunk l%4) of each 16-row block it loads
-    const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+    const int lc = (lane & 3) ^ ((lane >> 3) & 3);
     const bf16 *gp[QW];
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
@@ -484,7 +487,7 @@ struct DmaLoop {
             0, 0);
     };
     // fragment of row (16-aligned base) + lane%16, logical chunk lane/16
-    const int pc = 16 * ((lane >> 4) ^ ((lane >> 2) & 3)) + 64 * (lane & 15);
+    const int pc = 16 * ((lane >> 4) ^ ((lane >> 1) & 3)) + 64 * (lane & 15);
     auto compute = [&](const char *s, int kt) {
       frag a[TM], b[TN];
 #pragma unroll
