@@ -84,10 +84,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, launch_rows):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "counters_bf16_step.json")
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of the
+    workload, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -252,7 +252,7 @@ def main():
     roofline = {"kernel": names[dom],
                 "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, M),
+                "traffic": measured_traffic(dom, workload),
                 "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(t_ms, 4),
                 "mfma_tflops": round(flops / (t_ms * 1e-3) / 1e12, 1),
                 "mfma_frac": round(flops / (t_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
