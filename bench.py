@@ -123,12 +123,39 @@ def cpu_baseline(inp):
     }
 
 
+def loop_leg(dev, inp, stream, runs=3, check_every=16):
+    """The multi-step loop (dg_denoise_loop: step, commit, p.E feedback until no
+    mask id remains) from the workload's canvas, timed after the step bench; it
+    synchronises the host every check_every steps.  Committed canvas tokens per
+    second of wall time, median of `runs` complete loops."""
+    import numpy as np
+    import torch
+    mask_id = inp["dims"].mask_id
+    n_masked = int((inp["canvas_ids"] == mask_id).sum())
+    times, out = [], None
+    for _ in range(runs + 1):          # the first run warms up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = dev.loop(tau=inp["tau"], check_every=check_every, stream=stream)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times[1:]))
+    steps = int(out["steps"].max().item())
+    left = int((out["ids"] == mask_id).sum().item())
+    return {"committed_tokens": n_masked - left, "steps": steps, "steps_launched": out["launched"],
+            "ms": round(t * 1e3, 3), "ms_per_step": round(t * 1e3 / max(steps, 1), 4),
+            "committed_tokens_per_s": round((n_masked - left) / t, 1), "check_every": check_every,
+            "tau": inp["tau"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-loop", action="store_true",
+                    help="skip the multi-step generation loop leg (measured after the timed steps)")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["bf16_step", "long_read", "ragged32"],
                     help="bf16_step (default) times step + commit + slot read; long_read and "
@@ -292,6 +319,8 @@ def main():
         "host_wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
     }
     marks.destroy()
+    if not args.no_loop and workload == WORKLOAD:
+        line["loop"] = loop_leg(dev, inp, stream)
     stage_ev.destroy()
     if not args.no_cpu_baseline and workload == WORKLOAD:
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -198,6 +198,49 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
                           const dg_debug *debug, int32_t *dev_flags,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/* Repeated denoise steps until no canvas holds a mask id: the generation loop
+ * of 24-ai.news, "How is diffusion text generation different?" (the canvas is
+ * refined over several steps) and "Mechanism for deciding completed tokens"
+ * (each step commits the most confident positions until the cumulative
+ * entropy exceeds the threshold, and the step's self-conditioning vector
+ * p.E is an additional input of the next step).
+ * Step t runs dg_denoise_step on the current canvas with sc_in = the previous
+ * step's sc_out (the caller's sc_in, or none, at t = 0), then dg_commit with
+ * threshold_nats, and writes the committed ids into the canvas.  In the loop
+ * the mask id is removed from the vocabulary softmax (its logit is -inf), so
+ * confidence, entropy, argmax and p.E cover the other ids and every commit
+ * writes a real token: committing the mask id would leave the position
+ * undecided and could stall the loop.  A canvas with no mask id left is
+ * finished: later steps skip it.
+ *   canvas_ids    [batch, canvas] int32, device, in/out: the start canvas; on
+ *                 return the final canvas
+ *   sc_in         [batch, canvas, d_model] T or NULL (first step only)
+ *   logit_scale, row_scale  as in dg_denoise_step (row_scale applies at every step)
+ *   threshold_nats  commit threshold, >= 0 (DG_ERR_INVALID_ARG otherwise: the
+ *                 loop progresses only if every step commits)
+ *   max_steps     at most this many steps (>= 0)
+ *   check_every   the host reads back the number of unfinished canvases
+ *                 every check_every steps (>= 1) and stops at 0; steps launched
+ *                 after the last canvas finished change nothing
+ *   commit_step   [batch, canvas] int32, device, out: the step at which each
+ *                 position was committed, -1 for positions never committed
+ *   steps_taken   [batch] int32, device, out: steps until the canvas finished
+ *                 (or max_steps)
+ *   steps_launched  host int32 out (may be NULL): steps the call launched
+ *   dev_flags     as in dg_denoise_step, accumulated over the steps (may be NULL)
+ * Requires weights.embed_t or embed_t_tiled.  The workspace holds a step's
+ * workspace plus the loop state; size it with dg_denoise_loop_workspace.
+ * The call synchronises the stream every check_every steps (the only host
+ * synchronisation of the library); it allocates nothing.
+ * Errors: as dg_denoise_step and dg_commit. */
+size_t dg_denoise_loop_workspace(const dg_dims *dims, int32_t batch, int32_t max_prompt);
+dg_status dg_denoise_loop(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                          int32_t batch, int32_t *canvas_ids, const void *sc_in,
+                          float logit_scale, const float *row_scale, float threshold_nats,
+                          int32_t max_steps, int32_t check_every, int32_t *commit_step,
+                          int32_t *steps_taken, int32_t *steps_launched, int32_t *dev_flags,
+                          void *workspace, size_t ws_bytes, void *stream);
+
 /* Entropy-bounded commit of `batch` canvases of `canvas` positions each
  * (1 <= canvas <= DG_MAX_CANVAS).  Candidates are positions whose id equals
  * mask_id; they are ranked by (conf descending, position ascending); the

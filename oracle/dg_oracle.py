@@ -197,7 +197,9 @@ def vocab_softmax(l):
     e = np.exp(l - m[:, None])
     Z = e.sum(axis=1)
     p = e / Z[:, None]
-    H = np.log(Z) - (p * (l - m[:, None])).sum(axis=1)
+    # an entry with p = 0 adds 0 (0 ln 0 = 0), also where its logit is -inf
+    with np.errstate(invalid="ignore"):
+        H = np.log(Z) - np.where(p > 0, p * (l - m[:, None]), 0.0).sum(axis=1)
     am = np.argmax(l, axis=1)          # numpy returns the first maximum
     return VocabStats(m=m, Z=Z, p=p, conf=1.0 / Z, entropy=H, argmax=am.astype(np.int64),
                       lse=m + np.log(Z))
@@ -222,13 +224,15 @@ def self_condition(p, E):
 # --------------------------------------------------------------------------
 def denoise_canvas(E, Wq, Wk, Wv, Wo, Kp, Vp, ids, dims, sc_in=None, lm_head=None,
                    logit_scale=1.0, row_scale=None, rows=None, need_sc=True,
-                   need_logits=False):
+                   need_logits=False, exclude_id=None):
     """One decoder-mode denoise step over one canvas (24-ai.news, "How is
     diffusion text generation different?": every canvas position is refined
     in parallel in one forward pass).
 
     ``rows`` restricts S2..S6 to those positions (S0/S1 keys and values are
-    always computed for the whole canvas).  Returns a dict of float64 arrays.
+    always computed for the whole canvas).  ``exclude_id`` removes one id from
+    the vocabulary softmax (its logit becomes -inf): the multi-step loop
+    removes the mask id.  Returns a dict of float64 arrays.
     """
     x = embed_input(E, ids, sc_in)
     q, k, v = qkv_project(x, Wq, Wk, Wv, dims.n_q_heads, dims.n_kv_heads, dims.head_dim)
@@ -239,6 +243,8 @@ def denoise_canvas(E, Wq, Wk, Wv, Wo, Kp, Vp, ids, dims, sc_in=None, lm_head=Non
     s = logit_scale if row_scale is None else logit_scale * np.asarray(row_scale, F64)[rows]
     head = E if lm_head is None else lm_head
     l = lm_logits(h, head, s)
+    if exclude_id is not None:
+        l[:, exclude_id] = -np.inf
     st = vocab_softmax(l)
     out = {"rows": rows, "x": x[rows], "attn_out": o.reshape(len(rows), -1),
            "hidden_out": h, "conf": st.conf, "entropy": st.entropy,
@@ -312,6 +318,67 @@ def commit(ids, conf, entropy, argmax, mask_id, tau):
         outs.append(o)
         ns.append(n)
     return np.stack(masks), np.stack(outs), np.array(ns, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Multi-step loop: denoise, commit, self-conditioning feedback
+# --------------------------------------------------------------------------
+def denoise_loop(inp, tau, max_steps=None, row_scale=None, sc_in=None, tie_eps=None):
+    """Repeat denoise step + commit on each canvas until it holds no mask id.
+
+    24-ai.news, "How is diffusion text generation different?": the canvas is
+    refined over several steps; "Mechanism for deciding completed tokens":
+    each step commits the most confident positions until the cumulative
+    entropy exceeds the threshold, and the self-conditioning vector of a step
+    is an additional input of the next one.  Readings: step t of a canvas uses
+    sc_in = sc_out of step t-1 (the given sc_in, or none, at t = 0); the mask
+    id is removed from the vocabulary softmax of every loop step (committing
+    the mask token would leave the position undecided, and with tied
+    embeddings a masked position's own input makes the mask id its argmax, so
+    the loop would stall); a canvas with no mask id left takes no more steps;
+    at most max_steps steps (default: the canvas length, enough for any
+    tau >= 0 since each step then commits at least one real token).
+
+    With tie_eps, the first step at which the oracle itself declares a near-tie
+    (commit_near_ties on the step's candidates, or argmax_near_ties on a
+    position it commits) is recorded per canvas (-1: none): trajectories that
+    differ only by rounding can part there.
+
+    Returns ids [B, C] (final canvas), commit_step [B, C] (step at which each
+    position was committed, -1 if never), steps [B], first_tie [B].
+    """
+    dims = inp["dims"]
+    B, C, mask_id = inp["batch"], dims.canvas, dims.mask_id
+    cu = inp["cu_seqlens"]
+    max_steps = C if max_steps is None else max_steps
+    ids = np.asarray(inp["canvas_ids"]).astype(np.int64).copy()
+    commit_step = np.full((B, C), -1, dtype=np.int64)
+    steps = np.zeros(B, dtype=np.int64)
+    first_tie = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        p0, p1 = int(cu[b]), int(cu[b + 1])
+        sc = None if sc_in is None else sc_in[b]
+        for t in range(max_steps):
+            if not (ids[b] == mask_id).any():
+                break
+            st = denoise_canvas(
+                inp["embed"], inp["wq"], inp["wk"], inp["wv"], inp["wo"],
+                inp["prompt_k"][p0:p1], inp["prompt_v"][p0:p1], ids[b], dims, sc_in=sc,
+                lm_head=inp.get("lm_head"), logit_scale=inp["logit_scale"],
+                row_scale=None if row_scale is None else row_scale[b],
+                need_sc=True, need_logits=tie_eps is not None, exclude_id=mask_id)
+            mask, out, _ = commit_canvas(ids[b], st["conf"], st["entropy"], st["argmax"],
+                                         mask_id, tau)
+            if tie_eps is not None and first_tie[b] < 0:
+                near = commit_near_ties(ids[b], st["conf"], st["entropy"], mask_id, tau, tie_eps)
+                am = argmax_near_ties(st["logits"], tie_eps).mask
+                if near.any() or (am & (mask == 1)).any():
+                    first_tie[b] = t
+            commit_step[b][mask == 1] = t
+            ids[b] = out
+            sc = st["sc_out"]
+            steps[b] = t + 1
+    return {"ids": ids, "commit_step": commit_step, "steps": steps, "first_tie": first_tie}
 
 
 # --------------------------------------------------------------------------

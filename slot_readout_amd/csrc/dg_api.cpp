@@ -1,6 +1,7 @@
 // C-ABI entry points: host-side validation, workspace planning and the launch
-// sequence of each call.  Nothing here allocates device memory or
-// synchronises the host.
+// sequence of each call.  Nothing here allocates device memory; only the
+// multi-step loop synchronises the host (every check_every steps, to stop once
+// no canvas holds a mask id).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -150,6 +151,32 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
   p.inv_z = a.take(M * sizeof(float));
   p.ksplit = dg::sc_ksplit((int64_t)M, d.d_model, d.vocab, bf);
   p.sc_part = a.take(p.ksplit > 1 ? (size_t)p.ksplit * M * d.d_model * sizeof(float) : 0);
+  p.total = a.off;
+  return p;
+}
+
+// Workspace of the multi-step loop: a step's workspace, then the loop state.
+struct LoopPlan {
+  StepPlan step;
+  size_t conf, entropy, argmax, sc0, sc1, cmask, out_ids, n_commit, active, n_active, total;
+};
+
+LoopPlan plan_loop(const dg_dims &d, int B, int max_prompt) {
+  LoopPlan p{};
+  p.step = plan_step(d, B, max_prompt);
+  const size_t M = (size_t)B * d.canvas;
+  Arena a;
+  a.off = (p.step.total + 255) & ~size_t(255);
+  p.conf = a.take(M * sizeof(float));
+  p.entropy = a.take(M * sizeof(float));
+  p.argmax = a.take(M * sizeof(int32_t));
+  p.sc0 = a.take(M * d.d_model * tsize(d));
+  p.sc1 = a.take(M * d.d_model * tsize(d));
+  p.cmask = a.take(M);
+  p.out_ids = a.take(M * sizeof(int32_t));
+  p.n_commit = a.take((size_t)B * sizeof(int32_t));
+  p.active = a.take((size_t)B * sizeof(int32_t));
+  p.n_active = a.take(sizeof(int32_t));
   p.total = a.off;
   return p;
 }
@@ -364,6 +391,110 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   return DG_OK;
 }
 
+// Argument checks of a denoise step (no HIP calls).
+dg_status check_step_args(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                          int32_t batch, const int32_t *canvas_ids, const void *sc_in,
+                          const float *conf, const float *entropy, const int32_t *argmax,
+                          const void *sc_out, const dg_debug *debug) {
+  dg_status s = check_model(dims, batch, kv ? kv->max_len : 0, w, kv);
+  if (s != DG_OK) return s;
+  const dg_dims &d = *dims;
+  if (batch == 0) return ok();
+  if (!canvas_ids || !conf || !entropy || !argmax)
+    return fail(DG_ERR_INVALID_ARG, "canvas_ids, conf, entropy and argmax are required");
+  const void *et_tiled = embed_t_tiled_of(d, w);
+  if (sc_out && !w->embed_t && !et_tiled)
+    return fail(DG_ERR_INVALID_ARG,
+                "sc_out requires weights.embed_t (see dg_prepare_embed_t) or embed_t_tiled");
+  if (!aligned16(sc_in) || !aligned16(sc_out))
+    return fail(DG_ERR_INVALID_ARG, "sc_in and sc_out must be 16-byte aligned");
+  if (debug && (!aligned16(debug->attn_out) || !aligned16(debug->hidden_out)))
+    return fail(DG_ERR_INVALID_ARG, "debug outputs must be 16-byte aligned");
+  return DG_OK;
+}
+
+// One denoise step on a validated call with a planned workspace (no flag
+// clear).  active: per-canvas flags or null; canvases whose flag is 0 are
+// skipped by the projections, attention, the LM head and p.E, and their
+// outputs are left unspecified.  exclude_id >= 0 removes that id from the
+// vocabulary softmax (the multi-step loop removes the mask id).
+dg_status step_core(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *kv, int batch,
+                    const int32_t *canvas_ids, const void *sc_in, float logit_scale,
+                    const float *row_scale, float *conf, float *entropy, int32_t *argmax,
+                    void *sc_out, const dg_debug *debug, int32_t *dev_flags,
+                    const int32_t *active, void *workspace, const StepPlan &p, hipStream_t st,
+                    int exclude_id = -1) {
+  const bool bf = d.dtype == DG_BF16;
+  const int64_t M = (int64_t)batch * d.canvas;
+  const int nvt = d.vocab / dg::VTILE;
+  void *o = (debug && debug->attn_out) ? debug->attn_out : at<char>(workspace, p.o);
+  void *h = (debug && debug->hidden_out) ? debug->hidden_out : at<char>(workspace, p.h);
+  Stages sg;
+  sg.ev = debug ? debug->stage_events : nullptr;
+  sg.st = st;
+  dg_status s = run_block(d, w, kv, batch, 1, canvas_ids, sc_in, active, dev_flags, at<char>(workspace, p.q),
+                at<char>(workspace, p.k), at<char>(workspace, p.v), o, p.attn,
+                at<char>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st, sg);
+  if (s != DG_OK) return s;
+
+  dg::LmheadArgs la{};
+  la.head = w->lm_head ? w->lm_head : w->embed;
+  la.head_tiled = lm_tiled_of(d, w);
+  la.h = h;
+  la.logit_scale = logit_scale;
+  la.row_scale = row_scale;
+  la.stats = at<float4>(workspace, p.stats);
+  la.ptilde = sc_out ? at<char>(workspace, p.ptilde) : nullptr;
+  la.ptilde_blocked = bf;
+  la.logits = debug ? debug->logits_out : nullptr;
+  la.nrows = M;
+  la.active_rows = active;
+  la.rows_per_flag = d.canvas;
+  la.exclude_id1 = exclude_id + 1;
+  la.d = d.d_model;
+  la.vocab = d.vocab;
+  la.nvt = nvt;
+  DG_MARK(sg, DG_STAGE_LMHEAD, 0);
+  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "LM head launch");
+  DG_MARK(sg, DG_STAGE_LMHEAD, 1);
+
+  dg::VocabMergeArgs va{};
+  va.stats = la.stats;
+  va.nrows = M;
+  va.nvt = nvt;
+  va.conf = conf;
+  va.entropy = entropy;
+  va.argmax = argmax;
+  va.shift = sc_out ? at<int32_t>(workspace, p.shift) : nullptr;
+  va.inv_z = sc_out ? at<float>(workspace, p.inv_z) : nullptr;
+  DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 0);
+  DG_TRY_HIP(dg::launch_vocab_merge(va, st), "vocabulary merge launch");
+  DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 1);
+
+  DG_MARK(sg, DG_STAGE_SELFCOND, 0);
+  if (sc_out) {
+    dg::ScArgs sa{};
+    sa.ptilde = la.ptilde;
+    sa.shift = va.shift;
+    sa.inv_z = va.inv_z;
+    sa.ptilde_blocked = la.ptilde_blocked;
+    sa.embed_t = w->embed_t;
+    sa.embed_t_tiled = embed_t_tiled_of(d, w);
+    sa.part = at<float>(workspace, p.sc_part);
+    sa.out = sc_out;
+    sa.M = M;
+    sa.d = d.d_model;
+    sa.vocab = d.vocab;
+    sa.nvt = nvt;
+    sa.ksplit = p.ksplit;
+    sa.active = active;
+    sa.C = d.canvas;
+    DG_TRY_HIP(dg::launch_scgemm(sa, bf, st), "self-conditioning launch");
+  }
+  DG_MARK(sg, DG_STAGE_SELFCOND, 1);
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -425,89 +556,103 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
                           float logit_scale, const float *row_scale, float *conf, float *entropy,
                           int32_t *argmax, void *sc_out, const dg_debug *debug,
                           int32_t *dev_flags, void *workspace, size_t ws_bytes, void *stream) {
-  dg_status s = check_model(dims, batch, kv ? kv->max_len : 0, w, kv);
-  if (s != DG_OK) return s;
-  const dg_dims &d = *dims;
-  if (batch == 0) return ok();
-  if (!canvas_ids || !conf || !entropy || !argmax)
-    return fail(DG_ERR_INVALID_ARG, "canvas_ids, conf, entropy and argmax are required");
-  const void *et_tiled = embed_t_tiled_of(d, w);
-  if (sc_out && !w->embed_t && !et_tiled)
-    return fail(DG_ERR_INVALID_ARG,
-                "sc_out requires weights.embed_t (see dg_prepare_embed_t) or embed_t_tiled");
-  if (!aligned16(sc_in) || !aligned16(sc_out) || !aligned16(workspace))
-    return fail(DG_ERR_INVALID_ARG, "sc_in, sc_out and workspace must be 16-byte aligned");
-  if (debug && (!aligned16(debug->attn_out) || !aligned16(debug->hidden_out)))
-    return fail(DG_ERR_INVALID_ARG, "debug outputs must be 16-byte aligned");
-  const StepPlan p = plan_step(d, batch, kv->max_len);
+  dg_status s = check_step_args(dims, w, kv, batch, canvas_ids, sc_in, conf, entropy, argmax,
+                                sc_out, debug);
+  if (s != DG_OK || batch == 0) return s;
+  if (!aligned16(workspace)) return fail(DG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const StepPlan p = plan_step(*dims, batch, kv->max_len);
   if (!workspace || ws_bytes < p.total)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 ws_bytes, p.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf = d.dtype == DG_BF16;
-  const int64_t M = (int64_t)batch * d.canvas;
-  const int nvt = d.vocab / dg::VTILE;
-  void *o = (debug && debug->attn_out) ? debug->attn_out : at<char>(workspace, p.o);
-  void *h = (debug && debug->hidden_out) ? debug->hidden_out : at<char>(workspace, p.h);
-  Stages sg;
-  sg.ev = debug ? debug->stage_events : nullptr;
-  sg.st = st;
   if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
-  s = run_block(d, w, kv, batch, 1, canvas_ids, sc_in, nullptr, dev_flags, at<char>(workspace, p.q),
-                at<char>(workspace, p.k), at<char>(workspace, p.v), o, p.attn,
-                at<char>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st, sg);
+  s = step_core(*dims, w, kv, batch, canvas_ids, sc_in, logit_scale, row_scale, conf, entropy,
+                argmax, sc_out, debug, dev_flags, nullptr, workspace, p, st);
+  return s != DG_OK ? s : ok();
+}
+
+size_t dg_denoise_loop_workspace(const dg_dims *dims, int32_t batch, int32_t max_prompt) {
+  if (check_dims(dims) != DG_OK || batch < 0 || max_prompt < 0) return 0;
+  return plan_loop(*dims, batch, max_prompt).total;
+}
+
+dg_status dg_denoise_loop(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                          int32_t batch, int32_t *canvas_ids, const void *sc_in,
+                          float logit_scale, const float *row_scale, float threshold_nats,
+                          int32_t max_steps, int32_t check_every, int32_t *commit_step,
+                          int32_t *steps_taken, int32_t *steps_launched, int32_t *dev_flags,
+                          void *workspace, size_t ws_bytes, void *stream) {
+  if (steps_launched) *steps_launched = 0;
+  // the loop makes progress only when every step commits: tau >= 0 accepts
+  // the most confident candidate at least
+  if (!(threshold_nats >= 0.f))
+    return fail(DG_ERR_INVALID_ARG, "threshold %g: the loop needs a threshold >= 0", threshold_nats);
+  if (max_steps < 0 || check_every < 1)
+    return fail(DG_ERR_INVALID_ARG, "max_steps %d must be >= 0 and check_every %d >= 1", max_steps,
+                check_every);
+  if (!commit_step || !steps_taken)
+    return fail(DG_ERR_INVALID_ARG, "commit_step and steps_taken are required");
+  // the step's own checks, with stand-in outputs (they live in the workspace)
+  static const float f_dummy[4] = {0, 0, 0, 0};
+  static const int32_t i_dummy[4] = {0, 0, 0, 0};
+  dg_status s = check_step_args(dims, w, kv, batch, canvas_ids, sc_in, f_dummy, f_dummy, i_dummy,
+                                f_dummy, nullptr);
+  if (s != DG_OK || batch == 0) return s;
+  if (!w->embed_t && !embed_t_tiled_of(*dims, w))
+    return fail(DG_ERR_INVALID_ARG, "the loop feeds p.E back: weights.embed_t or embed_t_tiled is required");
+  s = dg_commit_validate(batch, dims->canvas);
   if (s != DG_OK) return s;
-
-  dg::LmheadArgs la{};
-  la.head = w->lm_head ? w->lm_head : w->embed;
-  la.head_tiled = lm_tiled_of(d, w);
-  la.h = h;
-  la.logit_scale = logit_scale;
-  la.row_scale = row_scale;
-  la.stats = at<float4>(workspace, p.stats);
-  la.ptilde = sc_out ? at<char>(workspace, p.ptilde) : nullptr;
-  la.ptilde_blocked = bf;
-  la.logits = debug ? debug->logits_out : nullptr;
-  la.nrows = M;
-  la.d = d.d_model;
-  la.vocab = d.vocab;
-  la.nvt = nvt;
-  DG_MARK(sg, DG_STAGE_LMHEAD, 0);
-  DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "LM head launch");
-  DG_MARK(sg, DG_STAGE_LMHEAD, 1);
-
-  dg::VocabMergeArgs va{};
-  va.stats = la.stats;
-  va.nrows = M;
-  va.nvt = nvt;
-  va.conf = conf;
-  va.entropy = entropy;
-  va.argmax = argmax;
-  va.shift = sc_out ? at<int32_t>(workspace, p.shift) : nullptr;
-  va.inv_z = sc_out ? at<float>(workspace, p.inv_z) : nullptr;
-  DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 0);
-  DG_TRY_HIP(dg::launch_vocab_merge(va, st), "vocabulary merge launch");
-  DG_MARK(sg, DG_STAGE_VOCAB_MERGE, 1);
-
-  DG_MARK(sg, DG_STAGE_SELFCOND, 0);
-  if (sc_out) {
-    dg::ScArgs sa{};
-    sa.ptilde = la.ptilde;
-    sa.shift = va.shift;
-    sa.inv_z = va.inv_z;
-    sa.ptilde_blocked = la.ptilde_blocked;
-    sa.embed_t = w->embed_t;
-    sa.embed_t_tiled = et_tiled;
-    sa.part = at<float>(workspace, p.sc_part);
-    sa.out = sc_out;
-    sa.M = M;
-    sa.d = d.d_model;
-    sa.vocab = d.vocab;
-    sa.nvt = nvt;
-    sa.ksplit = p.ksplit;
-    DG_TRY_HIP(dg::launch_scgemm(sa, bf, st), "self-conditioning launch");
+  if (!aligned16(workspace)) return fail(DG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const dg_dims &d = *dims;
+  const LoopPlan p = plan_loop(d, batch, kv->max_len);
+  if (!workspace || ws_bytes < p.total)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                ws_bytes, p.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float *conf = at<float>(workspace, p.conf), *ent = at<float>(workspace, p.entropy);
+  int32_t *am = at<int32_t>(workspace, p.argmax);
+  void *sc[2] = {at<char>(workspace, p.sc0), at<char>(workspace, p.sc1)};
+  uint8_t *cmask = at<uint8_t>(workspace, p.cmask);
+  int32_t *out_ids = at<int32_t>(workspace, p.out_ids);
+  int32_t *ncommit = at<int32_t>(workspace, p.n_commit);
+  int32_t *active = at<int32_t>(workspace, p.active);
+  int32_t *n_active = at<int32_t>(workspace, p.n_active);
+  if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
+  DG_TRY_HIP(dg::launch_loop_init(canvas_ids, batch, d.canvas, d.mask_id, commit_step, steps_taken,
+                                  active, st),
+             "loop init launch");
+  dg::CommitArgs ca{};
+  ca.ids = canvas_ids;
+  ca.conf = conf;
+  ca.entropy = ent;
+  ca.argmax = am;
+  ca.mask = cmask;
+  ca.out_ids = out_ids;
+  ca.n_committed = ncommit;
+  ca.B = batch;
+  ca.C = d.canvas;
+  ca.mask_id = d.mask_id;
+  ca.tau = threshold_nats;
+  for (int t = 0; t < max_steps; ++t) {
+    // step t reads the canvas and the previous step's p.E, and writes its own
+    const void *sc_t = t == 0 ? sc_in : sc[(t + 1) & 1];
+    s = step_core(d, w, kv, batch, canvas_ids, sc_t, logit_scale, row_scale, conf, ent, am,
+                  sc[t & 1], nullptr, dev_flags, active, workspace, p.step, st, d.mask_id);
+    if (s != DG_OK) return s;
+    DG_TRY_HIP(dg::launch_commit(ca, st), "commit launch");
+    DG_TRY_HIP(dg::launch_clear_i32(n_active, 1, st), "counter clear launch");
+    DG_TRY_HIP(dg::launch_loop_update(canvas_ids, out_ids, cmask, batch, d.canvas, d.mask_id, t,
+                                      commit_step, steps_taken, active, n_active, st),
+               "loop update launch");
+    if (steps_launched) *steps_launched = t + 1;
+    if ((t + 1) % check_every == 0 && t + 1 < max_steps) {
+      int32_t left = 0;
+      DG_TRY_HIP(hipMemcpyAsync(&left, n_active, sizeof left, hipMemcpyDeviceToHost, st),
+                 "active-count read-back");
+      DG_TRY_HIP(hipStreamSynchronize(st), "loop check synchronisation");
+      if (left == 0) break;
+    }
   }
-  DG_MARK(sg, DG_STAGE_SELFCOND, 1);
   return ok();
 }
 

@@ -619,9 +619,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     for (int i = 0; i < G::TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float l = acc[i][j][r] * s;
-        acc[i][j][r] = l;
         const int v = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
+        const float l = v + 1 == a.exclude_id1 ? -INFINITY : acc[i][j][r] * s;
+        acc[i][j][r] = l;
         if (l > m) { m = l; id = v; }
       }
     // across the four lane groups: larger value, then lower id
@@ -696,7 +696,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
       f32x4 e4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = fmaf(acc[i][j][r], kLog2e, -rj);
+        // clamped below: e = 2^x is 0 below -149 either way, and an excluded
+        // id (l = -inf) then adds 0 to s and t instead of 0 * -inf
+        const float x = fmaxf(fmaf(acc[i][j][r], kLog2e, -rj), -256.f);
         // raw v_exp_f32: x <= 0 (r >= m log2 e)
         const float e = __builtin_amdgcn_exp2f(x);
         s += e;
@@ -773,6 +775,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_kernel(ScArgs a) {
   }
   const int n0 = (t % ntn) * BN;
   const int64_t m0 = (int64_t)(t / ntn) * BM;
+  if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const int nk = a.vocab / G::BK;
   const int kbeg = (int)((int64_t)z * nk / a.ksplit) * G::BK;
   const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * G::BK;
@@ -846,6 +849,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_dma_kernel(ScArgs a) {
   const int z = blockIdx.x / nt, t = blockIdx.x % nt;
   const int n0 = (t % ntn) * BN;
   const int64_t m0 = (int64_t)(t / ntn) * BM;
+  if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const int nk = a.vocab / 64;   // split boundaries on 64-entry steps
   const int kbeg = (int)((int64_t)z * nk / a.ksplit) * 64;
   const int kend = (int)((int64_t)(z + 1) * nk / a.ksplit) * 64;

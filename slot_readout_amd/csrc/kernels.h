@@ -63,6 +63,8 @@ struct LmheadArgs {
   int lab_span, lab_S;
   int64_t nrows;
   int d, vocab, nvt;
+  // 1 + an id removed from the softmax (its logit is -inf), or 0 for none
+  int exclude_id1;
 };
 
 struct ScArgs {
@@ -74,8 +76,9 @@ struct ScArgs {
   const void *embed_t;     // [d, V]
   float *part;             // [ksplit, M, d]
   void *out;               // [M, d] T
+  const int32_t *active;   // per-canvas flag (canvases of C rows) or null
   int64_t M;
-  int d, vocab, nvt, ksplit;
+  int d, vocab, nvt, ksplit, C;
 };
 
 struct VocabMergeArgs {
@@ -136,6 +139,17 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
+// Multi-step loop bookkeeping (one workgroup per canvas).  loop_init: commit
+// step -1 everywhere, steps 0, active = the canvas holds a mask id.
+// loop_update after the commit of step t: for each active canvas, the
+// committed positions take their new ids and commit step t, its step count
+// becomes t + 1, it stays active while a mask id remains, and *n_active
+// counts the canvases still active (cleared by the caller first).
+hipError_t launch_loop_init(const int32_t *ids, int B, int C, int mask_id, int32_t *commit_step,
+                            int32_t *steps, int32_t *active, hipStream_t st);
+hipError_t launch_loop_update(int32_t *ids, const int32_t *out_ids, const uint8_t *mask, int B,
+                              int C, int mask_id, int t, int32_t *commit_step, int32_t *steps,
+                              int32_t *active, int32_t *n_active, hipStream_t st);
 // bf16 [rows, cols] -> blocks of 256 rows x 32 columns (rows % 256 == 0, cols % 32 == 0)
 hipError_t launch_tile_lm(const void *src, void *dst, int rows, int cols, hipStream_t st);
 hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,

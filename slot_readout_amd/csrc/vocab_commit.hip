@@ -221,4 +221,75 @@ hipError_t launch_clear_i32(int32_t *p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Multi-step loop bookkeeping: one workgroup of 256 threads per canvas.
+// ---------------------------------------------------------------------------
+__device__ inline bool block_any(bool v) {
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  if (v) any = 1;   // every writer stores the same value
+  __syncthreads();
+  return any != 0;
+}
+
+__global__ __launch_bounds__(256) void loop_init_kernel(const int32_t *ids, int C, int mask_id,
+                                                        int32_t *commit_step, int32_t *steps,
+                                                        int32_t *active) {
+  const int64_t base = (int64_t)blockIdx.x * C;
+  bool has = false;
+  for (int i = threadIdx.x; i < C; i += blockDim.x) {
+    commit_step[base + i] = -1;
+    has |= ids[base + i] == mask_id;
+  }
+  const bool a = block_any(has);
+  if (threadIdx.x == 0) {
+    steps[blockIdx.x] = 0;
+    active[blockIdx.x] = a ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void loop_update_kernel(int32_t *ids, const int32_t *out_ids,
+                                                          const uint8_t *mask, int C, int mask_id,
+                                                          int t, int32_t *commit_step,
+                                                          int32_t *steps, int32_t *active,
+                                                          int32_t *n_active) {
+  const int b = blockIdx.x;
+  if (!active[b]) return;   // uniform per workgroup
+  const int64_t base = (int64_t)b * C;
+  bool has = false;
+  for (int i = threadIdx.x; i < C; i += blockDim.x) {
+    int id = ids[base + i];
+    if (mask[base + i]) {
+      id = out_ids[base + i];
+      ids[base + i] = id;
+      commit_step[base + i] = t;
+    }
+    has |= id == mask_id;
+  }
+  const bool a = block_any(has);
+  if (threadIdx.x == 0) {
+    steps[b] = t + 1;
+    active[b] = a ? 1 : 0;
+    if (a) atomicAdd(n_active, 1);
+  }
+}
+
+hipError_t launch_loop_init(const int32_t *ids, int B, int C, int mask_id, int32_t *commit_step,
+                            int32_t *steps, int32_t *active, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(loop_init_kernel, dim3(B), dim3(256), 0, st, ids, C, mask_id, commit_step,
+                     steps, active);
+  return hipGetLastError();
+}
+
+hipError_t launch_loop_update(int32_t *ids, const int32_t *out_ids, const uint8_t *mask, int B,
+                              int C, int mask_id, int t, int32_t *commit_step, int32_t *steps,
+                              int32_t *active, int32_t *n_active, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(loop_update_kernel, dim3(B), dim3(256), 0, st, ids, out_ids, mask, C,
+                     mask_id, t, commit_step, steps, active, n_active);
+  return hipGetLastError();
+}
+
 }  // namespace dg

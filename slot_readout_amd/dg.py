@@ -65,6 +65,10 @@ _SIGS = {
                                _I32, _P, _P, _F, _P, _P, _P, _P, _P, ctypes.POINTER(Debug), _P,
                                _P, _SZ, _P]),
     "dg_commit": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _F, _P, _P, _P, _P]),
+    "dg_denoise_loop_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32]),
+    "dg_denoise_loop": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
+                               _I32, _P, _P, _F, _P, _F, _I32, _I32, _P, _P,
+                               ctypes.POINTER(_I32), _P, _P, _SZ, _P]),
     "dg_slot_read_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32, _I32, _I32]),
     "dg_slot_read": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                             _I32, _P, _I32, _P, _P, _P, _P, _F, _P, _F, _I32,
@@ -168,6 +172,24 @@ def dg_commit(batch, canvas, mask_id, canvas_ids, conf, entropy, argmax, thresho
     _check(lib().dg_commit(batch, canvas, mask_id, _ptr(canvas_ids), _ptr(conf), _ptr(entropy),
                            _ptr(argmax), float(threshold_nats), _ptr(commit_mask), _ptr(out_ids),
                            _ptr(n_committed), _stream(stream)))
+
+
+def dg_denoise_loop_workspace(dims, batch, max_prompt):
+    return lib().dg_denoise_loop_workspace(ctypes.byref(dims), batch, max_prompt)
+
+
+def dg_denoise_loop(dims, weights, kv, batch, canvas_ids, sc_in, logit_scale, row_scale,
+                    threshold_nats, max_steps, check_every, commit_step, steps_taken, dev_flags,
+                    workspace, stream=None):
+    """Runs the loop; returns the number of steps launched."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    launched = _I32(0)
+    _check(lib().dg_denoise_loop(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(kv), batch, _ptr(canvas_ids),
+        _ptr(sc_in), float(logit_scale), _ptr(row_scale), float(threshold_nats), int(max_steps),
+        int(check_every), _ptr(commit_step), _ptr(steps_taken), ctypes.byref(launched),
+        _ptr(dev_flags), _ptr(workspace), ws_bytes, _stream(stream)))
+    return int(launched.value)
 
 
 def dg_slot_read_workspace(dims, batch, n_slots, max_prompt, n_draws):

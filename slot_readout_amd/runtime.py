@@ -138,6 +138,24 @@ class DeviceProblem:
                      stream)
         return out
 
+    # ---------------------------------------------------------------- loop --
+    def loop(self, tau=None, max_steps=None, check_every=8, sc_in=None, row_scale=None,
+             canvas_ids=None, stream=None):
+        """dg_denoise_loop from the problem's canvas (or canvas_ids, which is left
+        untouched): returns the final canvas, commit steps, steps per canvas, the
+        steps launched and the device flag word."""
+        ids = (self.canvas_ids if canvas_ids is None else canvas_ids).clone()
+        cs = torch.empty((self.B, self.C), dtype=torch.int32, device=self.device)
+        steps = torch.empty((self.B,), dtype=torch.int32, device=self.device)
+        flags = torch.zeros(1, dtype=torch.int32, device=self.device)
+        ws = self.workspace("loop", dg.dg_denoise_loop_workspace(self.dims, self.B, self.max_prompt))
+        n = dg.dg_denoise_loop(self.dims, self.weights, self.kv, self.B, ids, sc_in,
+                               self.inp["logit_scale"], row_scale,
+                               self.inp["tau"] if tau is None else tau,
+                               self.C if max_steps is None else max_steps, check_every, cs, steps,
+                               flags, ws, stream)
+        return {"ids": ids, "commit_step": cs, "steps": steps, "launched": n, "flags": flags}
+
     # ----------------------------------------------------------- slot read --
     def slot_outputs(self):
         B, S = self.B, self.S
