@@ -128,3 +128,34 @@ def test_label_count_rule():
     with pytest.raises(ValueError, match="question 'intent': at most 26 alternatives"):
         dg.check_alternatives("intent", [f"i{k}" for k in range(77)])
     dg.check_alternatives("urgent", ["yes", "no"])
+
+
+def test_loop_rejects_bad_arguments_before_any_launch():
+    """dg_denoise_loop checks its threshold (>= 0: the loop must progress), step
+    counts, outputs, the p.E weights and the workspace size on the host; these
+    calls carry fake device addresses and return before touching a device."""
+    import ctypes
+    dg = _lib_or_skip()
+    L = dg.lib()
+    d = _dims(dg)
+    w_t = dg.make_weights(256, 256, 256, 256, 256, embed_t=256)
+    launched = ctypes.c_int32(-1)
+
+    def call(w=w_t, tau=1.0, max_steps=16, check_every=4, cs=2048, steps=4096, ws=8192,
+             ws_bytes=1 << 40):
+        return L.dg_denoise_loop(ctypes.byref(d), ctypes.byref(w), ctypes.byref(_kv(dg)), 1, 1024,
+                                 None, 8.0, None, tau, max_steps, check_every, cs, steps,
+                                 ctypes.byref(launched), None, ws, ws_bytes, None)
+
+    assert call(tau=-0.5) == dg.DG_ERR_INVALID_ARG
+    assert call(tau=float("nan")) == dg.DG_ERR_INVALID_ARG
+    assert launched.value == 0
+    assert call(max_steps=-1) == dg.DG_ERR_INVALID_ARG
+    assert call(check_every=0) == dg.DG_ERR_INVALID_ARG
+    assert call(cs=None) == dg.DG_ERR_INVALID_ARG
+    assert call(steps=None) == dg.DG_ERR_INVALID_ARG
+    assert call(w=_weights(dg)) == dg.DG_ERR_INVALID_ARG          # no embed_t for p.E
+    need = dg.dg_denoise_loop_workspace(d, 1, 128)
+    assert need > dg.dg_denoise_step_workspace(d, 1, 128) > 0
+    assert call(ws_bytes=need - 1) == dg.DG_ERR_WORKSPACE
+    assert "workspace" in dg.lib().dg_last_error().decode()
