@@ -79,7 +79,7 @@ typedef enum {
 typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
 
 /* Model and canvas dimensions.
- *   d_model    multiple of 32
+ *   d_model    multiple of 32 (of 64 with bf16 storage)
  *   head_dim   64 or 512
  *   n_q_heads  multiple of n_kv_heads (GQA group G = n_q_heads / n_kv_heads)
  *   vocab      multiple of 256

@@ -56,6 +56,9 @@ dg_status check_dims(const dg_dims *d) {
     return fail(DG_ERR_UNSUPPORTED, "head_dim 512 is supported with bf16 storage only");
   if (d->d_model <= 0 || d->d_model % 32 != 0)
     return fail(DG_ERR_INVALID_ARG, "d_model %d must be a positive multiple of 32", d->d_model);
+  // bf16 projections step through d_model 64 columns at a time
+  if (d->dtype == DG_BF16 && d->d_model % 64 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "bf16 storage needs d_model %d to be a multiple of 64", d->d_model);
   if (d->n_kv_heads <= 0 || d->n_q_heads <= 0 || d->n_q_heads % d->n_kv_heads != 0)
     return fail(DG_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
                 d->n_q_heads, d->n_kv_heads);

@@ -67,6 +67,7 @@ def test_validation_accepts_the_workload_dims():
     (dict(head_dim=512, dtype="f32"), "DG_ERR_UNSUPPORTED"),
     (dict(dtype=7), "DG_ERR_UNSUPPORTED"),
     (dict(d_model=250), "DG_ERR_INVALID_ARG"),
+    (dict(d_model=96, dtype="bf16"), "DG_ERR_UNSUPPORTED"),   # bf16 steps d_model by 64
     (dict(n_q_heads=6, n_kv_heads=4), "DG_ERR_INVALID_ARG"),
     (dict(vocab=2000), "DG_ERR_INVALID_ARG"),
     (dict(canvas=0), "DG_ERR_INVALID_ARG"),
