@@ -79,8 +79,12 @@ def attention_work(inp):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources (the .hip files and their headers; the host-side
+    C-ABI layer does not change what a kernel moves)."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "slot_readout_amd", "csrc"))):
+        if not f.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(ROOT, "slot_readout_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -148,6 +152,34 @@ def loop_leg(dev, inp, stream, runs=3, check_every=16):
             "ms": round(t * 1e3, 3), "ms_per_step": round(t * 1e3 / max(steps, 1), 4),
             "committed_tokens_per_s": round((n_masked - left) / t, 1), "check_every": check_every,
             "tau": inp["tau"]}
+
+
+def prefill_leg(dev, inp, stream, runs=5):
+    """dg_prefill_kv of the workload's prompt tokens (seeded ids) into a scratch
+    cache of the same shape, timed with HIP events after the step bench;
+    median of `runs` calls after one warm-up call."""
+    import numpy as np
+    import torch
+    from slot_readout_amd import dg
+    dm = inp["dims"]
+    n = int(inp["cu_seqlens"][-1])
+    if n == 0:
+        return None
+    ids = torch.from_numpy(np.random.default_rng(7).integers(0, dm.vocab - 1, size=n)
+                           .astype(np.int32)).cuda()
+    k = torch.empty((n, dm.n_kv_heads, dm.head_dim), dtype=dev.tdt, device="cuda")
+    v = torch.empty_like(k)
+    ts = []
+    for i in range(runs + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dg.dg_prefill_kv(dev.dims, dev.weights, n, ids, k, v, None, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    t = float(np.median(ts))
+    return {"tokens": n, "ms": round(t, 4), "tokens_per_s": round(n / (t * 1e-3), 1)}
 
 
 def main():
@@ -333,6 +365,8 @@ def main():
     span.destroy()
     if not args.no_loop and workload == WORKLOAD:
         line["loop"] = loop_leg(dev, inp, stream)
+    if workload in ("bf16_step", "long_read"):
+        line["prefill"] = prefill_leg(dev, inp, stream)
     stage_ev.destroy()
     if not args.no_cpu_baseline and workload == WORKLOAD:
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -241,6 +241,25 @@ dg_status dg_denoise_loop(const dg_dims *dims, const dg_weights *w, const dg_pro
                           int32_t *steps_taken, int32_t *steps_launched, int32_t *dev_flags,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/* Encoder-mode prefill of the cached prompt keys and values: the encoder mode
+ * fills the KV cache that the decoder-mode denoise step reads (thakicloud,
+ * "What is DiffusionGemma"; prefill is a stage of its own in 24-ai.news,
+ * "Integration into vLLM infrastructure").  With the single attention block
+ * that stands in for the backbone, the cache entry of prompt token t is that
+ * block's key and value projection of its embedding:
+ *   k_t = E[id_t] Wk^T,  v_t = E[id_t] Wv^T  (no self-conditioning input)
+ *   n_tokens    tokens to prefill (>= 0)
+ *   prompt_ids  [n_tokens] int32, device; ids outside [0, vocab) embed as zero
+ *               rows and set DG_FLAG_BAD_TOKEN in *dev_flags
+ *   k_out, v_out  [n_tokens, n_kv_heads, head_dim] T, device (e.g. rows
+ *               cu[b] .. cu[b+1]-1 of a packed dg_prompt_kv cache)
+ *   dev_flags   device int32 or NULL: cleared, then set as described
+ * Uses weights.embed, wk, wv.  Allocates nothing; asynchronous on stream.
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+dg_status dg_prefill_kv(const dg_dims *dims, const dg_weights *w, int64_t n_tokens,
+                        const int32_t *prompt_ids, void *k_out, void *v_out,
+                        int32_t *dev_flags, void *stream);
+
 /* Entropy-bounded commit of `batch` canvases of `canvas` positions each
  * (1 <= canvas <= DG_MAX_CANVAS).  Candidates are positions whose id equals
  * mask_id; they are ranked by (conf descending, position ascending); the

@@ -97,6 +97,24 @@ def qkv_project(x, Wq, Wk, Wv, n_q_heads, n_kv_heads, head_dim):
             v.reshape(n, n_kv_heads, head_dim))
 
 
+def prefill_kv(E, Wk, Wv, ids, n_kv_heads, head_dim):
+    """Encoder-mode prefill of the prompt KV cache (thakicloud, "What is
+    DiffusionGemma": the encoder mode writes the KV cache the decoder reads).
+    With one attention block standing in for the backbone, prompt token t's
+    cache entry is that block's key/value projection of its embedding:
+    k_t = E[id_t] Wk^T, v_t = E[id_t] Wv^T, shaped [n, n_kv_heads, head_dim].
+    Ids outside [0, V) embed as zero rows.
+    """
+    ids = np.asarray(ids)
+    ok = (ids >= 0) & (ids < E.shape[0])
+    x = np.zeros((len(ids), E.shape[1]), dtype=F64)
+    x[ok] = embed_input(E, ids[ok])
+    k = x @ np.asarray(Wk, F64).T
+    v = x @ np.asarray(Wv, F64).T
+    n = x.shape[0]
+    return k.reshape(n, n_kv_heads, head_dim), v.reshape(n, n_kv_heads, head_dim)
+
+
 def block_output(x, o, Wo):
     """h = x + concat_heads(o) Wo^T  (residual around the attention block)."""
     n = o.shape[0]

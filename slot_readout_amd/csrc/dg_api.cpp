@@ -659,6 +659,45 @@ dg_status dg_denoise_loop(const dg_dims *dims, const dg_weights *w, const dg_pro
   return ok();
 }
 
+dg_status dg_prefill_kv(const dg_dims *dims, const dg_weights *w, int64_t n_tokens,
+                        const int32_t *prompt_ids, void *k_out, void *v_out,
+                        int32_t *dev_flags, void *stream) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (!w || !w->embed || !w->wk || !w->wv)
+    return fail(DG_ERR_INVALID_ARG, "prefill needs weights.embed, wk and wv");
+  if (n_tokens < 0) return fail(DG_ERR_INVALID_ARG, "n_tokens %lld < 0", (long long)n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!prompt_ids || !k_out || !v_out)
+    return fail(DG_ERR_INVALID_ARG, "prompt_ids, k_out and v_out are required");
+  if (!aligned16(w->embed) || !aligned16(w->wk) || !aligned16(w->wv) || !aligned16(k_out) ||
+      !aligned16(v_out))
+    return fail(DG_ERR_INVALID_ARG, "weights and the k/v outputs must be 16-byte aligned");
+  const dg_dims &d = *dims;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
+  dg::QkvArgs qa{};
+  qa.ids = prompt_ids;
+  qa.embed = w->embed;
+  qa.wq = w->wk;   // no q column is computed; any valid matrix pointer
+  qa.wk = w->wk;
+  qa.wv = w->wv;
+  qa.k = k_out;
+  qa.v = v_out;
+  qa.flags = dev_flags;
+  qa.M = n_tokens;
+  qa.d = d.d_model;
+  qa.nq = d.n_q_heads * d.head_dim;
+  qa.nkv = d.n_kv_heads * d.head_dim;
+  qa.vocab = d.vocab;
+  qa.C = d.canvas;
+  qa.q_scale = 1.f;
+  qa.col0 = qa.nq;                 // the k and v columns of [q | k | v]
+  qa.col1 = qa.nq + 2 * qa.nkv;
+  DG_TRY_HIP(dg::launch_qkv(qa, d.dtype == DG_BF16, st), "prefill projection launch");
+  return ok();
+}
+
 dg_status dg_commit(int32_t batch, int32_t canvas, int32_t mask_id, const int32_t *canvas_ids,
                     const float *conf, const float *entropy, const int32_t *argmax,
                     float threshold_nats, uint8_t *commit_mask, int32_t *out_ids,

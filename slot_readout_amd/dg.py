@@ -65,6 +65,8 @@ _SIGS = {
                                _I32, _P, _P, _F, _P, _P, _P, _P, _P, ctypes.POINTER(Debug), _P,
                                _P, _SZ, _P]),
     "dg_commit": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _F, _P, _P, _P, _P]),
+    "dg_prefill_kv": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.c_int64, _P, _P,
+                             _P, _P, _P]),
     "dg_denoise_loop_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32]),
     "dg_denoise_loop": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                                _I32, _P, _P, _F, _P, _F, _I32, _I32, _P, _P,
@@ -172,6 +174,12 @@ def dg_commit(batch, canvas, mask_id, canvas_ids, conf, entropy, argmax, thresho
     _check(lib().dg_commit(batch, canvas, mask_id, _ptr(canvas_ids), _ptr(conf), _ptr(entropy),
                            _ptr(argmax), float(threshold_nats), _ptr(commit_mask), _ptr(out_ids),
                            _ptr(n_committed), _stream(stream)))
+
+
+def dg_prefill_kv(dims, weights, n_tokens, prompt_ids, k_out, v_out, dev_flags=None, stream=None):
+    _check(lib().dg_prefill_kv(ctypes.byref(dims), ctypes.byref(weights), int(n_tokens),
+                               _ptr(prompt_ids), _ptr(k_out), _ptr(v_out), _ptr(dev_flags),
+                               _stream(stream)))
 
 
 def dg_denoise_loop_workspace(dims, batch, max_prompt):
