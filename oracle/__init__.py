@@ -9,5 +9,6 @@ from .dg_oracle import (  # noqa: F401
     vocab_softmax, self_condition, denoise_canvas, denoise_step, commit_canvas,
     commit, denoise_loop, label_read, slot_read_canvas, slot_read, NearTies, argmax_near_ties,
     commit_near_ties, best_near_ties, SLOT_OK, SLOT_BAD_POS, SLOT_BAD_COUNT,
-    SLOT_BAD_LABEL, SLOT_BAD_NOISE, MAX_LABELS,
+    SLOT_BAD_LABEL, SLOT_BAD_NOISE, MAX_LABELS, E4M3_MAX, e4m3_row_exponent, e4m3_encode,
+    e4m3_decode, quantize_head_e4m3, dequantize_head_e4m3,
 )

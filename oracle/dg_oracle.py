@@ -189,6 +189,75 @@ def lm_logits(h, head, scale, chunk=32768):
 
 
 # --------------------------------------------------------------------------
+# FP8 (e4m3) copy of the LM head: weight-only FP8, bf16 activations
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0   # largest finite e4m3 value (OCP 8-bit float, 4 exponent bits, bias 7)
+
+
+def e4m3_row_exponent(amax):
+    """Smallest integer e with amax <= 448 * 2^e (0 for an all-zero row).
+
+    With amax = m 2^E, 1 <= m < 2, and 448 = 1.75 2^8: e = E - 8, plus 1 when
+    m > 1.75.  Exact (no division).
+    """
+    amax = np.asarray(amax, dtype=np.float32)
+    f, x = np.frexp(amax)                  # amax = f 2^x, 0.5 <= f < 1
+    m = 2.0 * f.astype(np.float64)         # 1 <= m < 2, E = x - 1
+    e = (x - 1) - 8 + (m > 1.75)
+    return np.where(amax > 0, e, 0).astype(np.int64)
+
+
+def e4m3_encode(q):
+    """Round-to-nearest-even to e4m3 codes (uint8) of values |q| <= 448, taken
+    in float32: subnormals (|q| < 2^-6) are multiples of 2^-9, normals have a
+    3-bit mantissa; a mantissa that rounds up to 8 carries into the exponent
+    (for subnormals that carry is the code of 2^-6 itself)."""
+    q = np.asarray(q, dtype=np.float32)
+    a = np.abs(q)
+    sign = (np.signbit(q)).astype(np.uint8) << 7
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < np.float32(2.0 ** -6)
+    code[sub] = np.rint(a[sub] * np.float32(512.0)).astype(np.int64)
+    nrm = ~sub
+    if nrm.any():
+        _, x = np.frexp(a[nrm])
+        E = x - 1                                           # a = (1 + f) 2^E
+        frac = (a[nrm] / np.ldexp(np.float32(1.0), E).astype(np.float32)) - np.float32(1.0)
+        m3 = np.rint(frac * np.float32(8.0)).astype(np.int64)
+        carry = m3 == 8
+        E = E + carry
+        m3 = np.where(carry, 0, m3)
+        code[nrm] = ((E + 7) << 3) | m3
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(codes):
+    """Value of each e4m3 code: (-1)^s (1 + m/8) 2^(e-7), or (-1)^s m 2^-9 for
+    e = 0.  (Code 0x7F / 0xFF, not a number, is never produced.)"""
+    c = np.asarray(codes, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return s * val
+
+
+def quantize_head_e4m3(head):
+    """Per vocabulary row: exponent e (e4m3_row_exponent of the row's largest
+    magnitude) and codes of head / 2^e.  The head is read as stored (bf16 values
+    are exact in float32).  Returns (codes uint8 [V, d], exps int64 [V])."""
+    h = np.asarray(head, dtype=np.float32)
+    e = e4m3_row_exponent(np.abs(h).max(axis=1))
+    q = h * np.ldexp(np.float32(1.0), -e).astype(np.float32)[:, None]   # exact: power of two
+    return e4m3_encode(q), e
+
+
+def dequantize_head_e4m3(codes, exps):
+    """The head the FP8 LM head computes with: decode(code) 2^e, float64."""
+    return e4m3_decode(codes) * np.exp2(np.asarray(exps, dtype=np.float64))[:, None]
+
+
+# --------------------------------------------------------------------------
 # S5  vocabulary softmax: confidence, entropy, argmax
 # --------------------------------------------------------------------------
 @dataclass
