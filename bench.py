@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lm-fp8", action="store_true",
+                    help="LM head from its e4m3 copy (weight-only FP8, bf16 activations)")
     ap.add_argument("--no-loop", action="store_true",
                     help="skip the multi-step generation loop leg (measured after the timed steps)")
     ap.add_argument("--workload", default=WORKLOAD,
@@ -222,7 +224,7 @@ def main():
     cfg = config(workload)
     t_in = time.perf_counter()
     inp = make_inputs(cfg)
-    dev = DeviceProblem(inp, device="cuda:0")
+    dev = DeviceProblem(inp, device="cuda:0", with_lm_fp8=args.lm_fp8)
     dm = inp["dims"]
     B, C, S, V, d = dev.B, dev.C, dev.S, dm.vocab, dm.d_model
     stream = torch.cuda.current_stream().cuda_stream
@@ -304,7 +306,8 @@ def main():
     M = B * C
     nvt = V // 256
     # algorithmic work per launch of the two vocabulary-sized kernels
-    lm_bytes = V * d * 2 + M * d * 2 + M * V * 2 + M * nvt * 16
+    head_bytes = V * d + V * 4 if args.lm_fp8 else V * d * 2      # e4m3 codes + exponents
+    lm_bytes = head_bytes + M * d * 2 + M * V * 2 + M * nvt * 16
     lm_flops = 2.0 * M * V * d
     sc_bytes = d * V * 2 + M * V * 2 + M * nvt * 4 + M * d * 2
     sc_flops = 2.0 * M * V * d
@@ -348,7 +351,9 @@ def main():
         "data": "synthetic (seeded; weights N(0,0.02), prompt K/V N(0,1))",
         "config": {"workload": wl_desc, "batch": B, "canvas": C,
                    "prompt": int(inp["max_prompt"]), "slots": S if with_read else 0,
-                   "cold_cache": bool(cold)},
+                   "cold_cache": bool(cold),
+                   "lm_head": "e4m3 codes, per-row power-of-two scales (weight-only FP8)"
+                   if args.lm_fp8 else "bf16"},
         "slot_reads_per_s": round(B * S / (ms_per_step * 1e-3), 1) if with_read else None,
         "breakdown_ms": {"pass": "K further steps with per-stage HIP events, after the timed steps",
                          "denoise_step": round(step_ms, 4), "commit": round(commit_ms, 4),
@@ -363,6 +368,8 @@ def main():
     }
     marks.destroy()
     span.destroy()
+    if args.lm_fp8:   # counters were taken with the bf16 head
+        line["roofline"]["traffic"] = None
     if not args.no_loop and workload == WORKLOAD:
         line["loop"] = loop_leg(dev, inp, stream)
     if workload in ("bf16_step", "long_read"):

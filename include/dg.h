@@ -110,11 +110,20 @@ typedef struct {
  *            or NULL.  Optional and bf16 only, for d_model a multiple of 256; when
  *            set, the self-conditioning contraction streams it instead of embed_t
  *            (same results, contiguous 16 KB reads per K step) and sc_out may be
- *            requested without embed_t. */
+ *            requested without embed_t.
+ *   lm_fp8, lm_fp8_exp  an FP8 copy of the LM head written by dg_prepare_lm_fp8, or
+ *            NULL: codes [vocab, d_model] uint8 (e4m3) and per-row exponents [vocab]
+ *            int32; head row v = decode(codes[v]) * 2^lm_fp8_exp[v].  bf16 only;
+ *            when set, every LM-head pass (denoise step, slot read, loop) uses this
+ *            head instead of lm_head / embed, with bf16 activations and fp32
+ *            accumulation (weight-only FP8: half the bytes per vocabulary pass).
+ *            The embedding and p.E keep the bf16 embed. */
 typedef struct {
     const void *embed, *embed_t, *lm_head, *wq, *wk, *wv, *wo;
     const void *lm_tiled;
     const void *embed_t_tiled;
+    const void *lm_fp8;
+    const int32_t *lm_fp8_exp;
 } dg_weights;
 
 /* Cached prompt (encoder-mode) keys and values of every sequence, packed.
@@ -344,6 +353,18 @@ dg_status dg_prepare_lm_tiled(const dg_dims *dims, const void *head, void *lm_ti
  * are device pointers, 16-byte aligned. */
 dg_status dg_prepare_embed_t_tiled(const dg_dims *dims, const void *embed_t,
                                    void *embed_t_tiled, void *stream);
+
+/* Writes the FP8 (e4m3) copy of the LM head [vocab, d_model] (bf16): for each
+ * vocabulary row v, exps[v] = the smallest integer e with max_k |head[v][k]| <=
+ * 448 * 2^e (0 for a zero row), and codes[v][k] = head[v][k] / 2^e rounded to the
+ * nearest e4m3 value, ties to even (e4m3: sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, subnormals, largest finite 448).  The FP8 variant of the
+ * checkpoints the pages measure (24-ai.news, performance section), here as a
+ * weight-only format.  codes holds vocab * d_model bytes, exps vocab int32; all
+ * device pointers, 16-byte aligned.  Requires dtype DG_BF16 (DG_ERR_UNSUPPORTED
+ * otherwise).  Weight preparation, done once. */
+dg_status dg_prepare_lm_fp8(const dg_dims *dims, const void *head, void *codes, int32_t *exps,
+                            void *stream);
 
 /* Host-only validation (no HIP calls; usable without a GPU).  Same checks the
  * calls above make before launching anything. */

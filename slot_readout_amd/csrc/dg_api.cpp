@@ -91,9 +91,13 @@ dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const
   if (kv->max_len > 0 && (!kv->k || !kv->v))
     return fail(DG_ERR_INVALID_ARG, "prompt_kv.k/v are NULL but max_len > 0");
   const void *ptrs[] = {w->embed, w->embed_t, w->lm_head, w->wq, w->wk, w->wv, w->wo, w->lm_tiled,
-                        w->embed_t_tiled, kv->k, kv->v};
+                        w->embed_t_tiled, w->lm_fp8, w->lm_fp8_exp, kv->k, kv->v};
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(DG_ERR_INVALID_ARG, "weight / KV pointers must be 16-byte aligned");
+  if (w->lm_fp8 && d->dtype != DG_BF16)
+    return fail(DG_ERR_UNSUPPORTED, "the e4m3 LM head (weights.lm_fp8) needs bf16 storage");
+  if (!w->lm_fp8 != !w->lm_fp8_exp)
+    return fail(DG_ERR_INVALID_ARG, "weights.lm_fp8 and lm_fp8_exp go together");
   return DG_OK;
 }
 
@@ -443,6 +447,8 @@ dg_status step_core(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   dg::LmheadArgs la{};
   la.head = w->lm_head ? w->lm_head : w->embed;
   la.head_tiled = lm_tiled_of(d, w);
+  la.head_fp8 = static_cast<const uint8_t *>(w->lm_fp8);
+  la.head_exp = w->lm_fp8_exp;
   la.h = h;
   la.logit_scale = logit_scale;
   la.row_scale = row_scale;
@@ -803,6 +809,8 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   dg::LmheadArgs la{};
   la.head = w->lm_head ? w->lm_head : w->embed;
   la.head_tiled = lm_tiled_of(d, w);
+  la.head_fp8 = static_cast<const uint8_t *>(w->lm_fp8);
+  la.head_exp = w->lm_fp8_exp;
   la.h = h;
   la.row_index = sa.rows;
   la.logit_scale = logit_scale;
@@ -933,6 +941,21 @@ dg_status dg_prepare_lm_tiled(const dg_dims *dims, const void *head, void *lm_ti
   DG_TRY_HIP(dg::launch_tile_lm(head, lm_tiled, dims->vocab, dims->d_model,
                                 static_cast<hipStream_t>(stream)),
              "LM head tiling launch");
+  return ok();
+}
+
+dg_status dg_prepare_lm_fp8(const dg_dims *dims, const void *head, void *codes, int32_t *exps,
+                            void *stream) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (!head || !codes || !exps) return fail(DG_ERR_INVALID_ARG, "head, codes and exps are required");
+  if (!aligned16(head) || !aligned16(codes) || !aligned16(exps))
+    return fail(DG_ERR_INVALID_ARG, "head, codes and exps must be 16-byte aligned");
+  if (dims->dtype != DG_BF16)
+    return fail(DG_ERR_UNSUPPORTED, "the e4m3 LM head is made from a bf16 head");
+  DG_TRY_HIP(dg::launch_quantize_e4m3(head, static_cast<uint8_t *>(codes), exps, dims->vocab,
+                                      dims->d_model, static_cast<hipStream_t>(stream)),
+             "e4m3 quantisation launch");
   return ok();
 }
 

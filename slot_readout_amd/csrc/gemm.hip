@@ -227,6 +227,32 @@ template <typename T, int N, int BR> struct BlockedRowLoader {
   }
 };
 
+// Rows of an e4m3 (FP8) matrix: each 8-byte load holds the 8 codes of a chunk,
+// decoded to bf16 (exactly: every e4m3 value is a bf16 value) at the LDS store.
+// The per-row power-of-two scale is applied to the GEMM result.
+template <int N> struct Fp8RowLoader {
+  using Raw = uint2;
+  const uint8_t *p[N];
+  bool live[N];
+  __device__ inline void set(int it, const uint8_t *row, bool ok, const uint8_t *fallback) {
+    p[it] = ok ? row : fallback;
+    live[it] = ok;
+  }
+  __device__ inline Raw load(int it, int k) const {
+    return *reinterpret_cast<const uint2 *>(p[it] + k);
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
+    uint2 c = r;
+    asm volatile("" : "+v"(c.x), "+v"(c.y));
+    uint4 v;
+    v.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.f, false));
+    v.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.f, true));
+    v.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.f, false));
+    v.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.f, true));
+    return keep_if(v, live[it]);
+  }
+};
+
 // x = E[id] + sc_in, rounded to T (SC: sc_in present for the whole launch; a
 // compile-time switch, so no load sits behind a branch)
 template <typename T, int N, bool SC> struct GatherLoader {
@@ -538,7 +564,8 @@ struct DmaLoop {
 // ---------------------------------------------------------------------------
 // PF < 0 selects the direct-to-LDS K loop with -PF stages (bf16, BK = 32).
 // TL: the head is read from its copy in BM x 32 blocks (a.head_tiled).
-template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool TL = false>
+// F8: the head is read from its e4m3 copy (a.head_fp8, a.head_exp; register K loop)
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool TL = false, bool F8 = false>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF < 0 ? 1 : PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
@@ -583,14 +610,20 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   } else {
     __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
     static_assert(!TL || (BK == 32 && sizeof(T) == 2), "blocked head: bf16, BK = 32");
-    using AL = typename std::conditional<TL, BlockedRowLoader<T, G::AI, BM>, RowLoader<T, G::AI>>::type;
+    static_assert(!F8 || (!TL && sizeof(T) == 2), "e4m3 head: bf16 activations, row-major codes");
+    using AL = typename std::conditional<
+        F8, Fp8RowLoader<G::AI>,
+        typename std::conditional<TL, BlockedRowLoader<T, G::AI, BM>, RowLoader<T, G::AI>>::type>::type;
     AL al;
     const T *ht = static_cast<const T *>(a.head_tiled);
 #pragma unroll
     for (int it = 0; it < G::AI; ++it) {
       const int v = v0 + G::a_row(it);
-      al.set(it, TL ? ht + (int64_t)v0 * d + G::a_row(it) * 32 : head + (int64_t)v * d, v < a.vocab,
-             TL ? ht : head);
+      if constexpr (F8)
+        al.set(it, a.head_fp8 + (int64_t)v * d, v < a.vocab, a.head_fp8);
+      else
+        al.set(it, TL ? ht + (int64_t)v0 * d + G::a_row(it) * 32 : head + (int64_t)v * d, v < a.vocab,
+               TL ? ht : head);
     }
     RowLoader<T, G::BI> bl;
 #pragma unroll
@@ -620,7 +653,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
-        const float l = v + 1 == a.exclude_id1 ? -INFINITY : acc[i][j][r] * s;
+        float sv = s;
+        if constexpr (F8) sv = ldexpf(s, a.head_exp[v]);   // exact: a power of two
+        const float l = v + 1 == a.exclude_id1 ? -INFINITY : acc[i][j][r] * sv;
         acc[i][j][r] = l;
         if (l > m) { m = l; id = v; }
       }
@@ -965,7 +1000,16 @@ constexpr int64_t kLmFewRows = 64;
 constexpr int kLmStages = 4;
 
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
-  if (bf && a.nrows <= kLmFewRows) {
+  if (bf && a.head_fp8) {
+    // e4m3 head: register K loop (the codes are decoded on their way into LDS)
+    if (a.nrows <= kLmFewRows) {
+      const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32, false, true>), grid, dim3(4 * WAVE), 0, st, a);
+    } else {
+      const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64, false, true>), grid, dim3(8 * WAVE), 0, st, a);
+    }
+  } else if (bf && a.nrows <= kLmFewRows) {
     // few rows (slot reads): a 64-row tile keeps the MFMA work proportional to
     // the rows and three workgroups per CU keep the vocabulary stream busy
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));

@@ -40,6 +40,8 @@ struct OprojArgs {
 struct LmheadArgs {
   const void *head;        // [V, d]
   const void *head_tiled;  // the same in 256 x 32 blocks (bf16), or null
+  const uint8_t *head_fp8;  // e4m3 codes [V, d] (bf16 storage only), or null
+  const int32_t *head_exp;  // [V]: head row v = decode(codes[v]) * 2^head_exp[v]
   const void *h;           // [*, d]
   const int32_t *row_index;  // [nrows] rows of h to use (-1 = none) or null (identity)
   const int32_t *active_rows;  // per-group flag (groups of rows_per_flag rows) or null
@@ -152,6 +154,9 @@ hipError_t launch_loop_update(int32_t *ids, const int32_t *out_ids, const uint8_
                               int32_t *active, int32_t *n_active, hipStream_t st);
 // bf16 [rows, cols] -> blocks of 256 rows x 32 columns (rows % 256 == 0, cols % 32 == 0)
 hipError_t launch_tile_lm(const void *src, void *dst, int rows, int cols, hipStream_t st);
+// e4m3 copy of a bf16 [rows, cols] head: per-row exponents and codes
+hipError_t launch_quantize_e4m3(const void *head, uint8_t *codes, int32_t *exps, int rows, int cols,
+                                hipStream_t st);
 hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,
                             hipStream_t st);
 hipError_t launch_clear_i32(int32_t *p, int64_t n, hipStream_t st);

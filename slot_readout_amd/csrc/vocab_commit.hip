@@ -292,4 +292,58 @@ hipError_t launch_loop_update(int32_t *ids, const int32_t *out_ids, const uint8_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// e4m3 (FP8) copy of the LM head: one workgroup per row.  The exponent e is the
+// smallest integer with amax <= 448 * 2^e: with amax = m 2^E (1 <= m < 2) and
+// 448 = 1.75 * 2^8, e = E - 8, plus 1 when m > 1.75.  Each value q = x * 2^-e
+// (exact) is rounded to nearest, ties to even, in float32: below 2^-6 to a
+// multiple of 2^-9 (a subnormal code; 8 * 2^-9 is the code of 2^-6 itself),
+// otherwise to a 3-bit mantissa whose carry moves into the exponent field.
+// ---------------------------------------------------------------------------
+__device__ inline unsigned encode_e4m3(float q) {
+  const unsigned sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  if (a < 0.015625f) return sign | (unsigned)rintf(a * 512.f);
+  int x;
+  frexpf(a, &x);                                   // a = f 2^x, 0.5 <= f < 1
+  const int E = x - 1;
+  const float frac = ldexpf(a, -E) - 1.f;          // exact
+  int m3 = (int)rintf(frac * 8.f);
+  int e = E;
+  if (m3 == 8) { m3 = 0; e += 1; }
+  return sign | (unsigned)(((e + 7) << 3) | m3);
+}
+
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const bf16 *head, uint8_t *codes,
+                                                            int32_t *exps, int cols) {
+  const int64_t base = (int64_t)blockIdx.x * cols;
+  __shared__ float red[256];
+  float amax = 0.f;
+  for (int k = threadIdx.x; k < cols; k += 256) amax = fmaxf(amax, fabsf(to_f(head[base + k])));
+  red[threadIdx.x] = amax;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  amax = red[0];
+  int e = 0;
+  if (amax > 0.f) {
+    int x;
+    const float f = frexpf(amax, &x);
+    e = (x - 1) - 8 + (2.f * f > 1.75f ? 1 : 0);
+  }
+  if (threadIdx.x == 0) exps[blockIdx.x] = e;
+  for (int k = threadIdx.x; k < cols; k += 256)
+    codes[base + k] = (uint8_t)encode_e4m3(ldexpf(to_f(head[base + k]), -e));
+}
+
+hipError_t launch_quantize_e4m3(const void *head, uint8_t *codes, int32_t *exps, int rows, int cols,
+                                hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_e4m3_kernel, dim3(rows), dim3(256), 0, st,
+                     static_cast<const bf16 *>(head), codes, exps, cols);
+  return hipGetLastError();
+}
+
 }  // namespace dg

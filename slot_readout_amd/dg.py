@@ -35,7 +35,7 @@ class Dims(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("embed", "embed_t", "lm_head", "wq", "wk", "wv", "wo", "lm_tiled",
-                 "embed_t_tiled")]
+                 "embed_t_tiled", "lm_fp8", "lm_fp8_exp")]
 
 
 class PromptKV(ctypes.Structure):
@@ -78,6 +78,7 @@ _SIGS = {
     "dg_prepare_embed_t": (_I32, [ctypes.POINTER(Dims), _P, _P, _P]),
     "dg_prepare_lm_tiled": (_I32, [ctypes.POINTER(Dims), _P, _P, _P]),
     "dg_prepare_embed_t_tiled": (_I32, [ctypes.POINTER(Dims), _P, _P, _P]),
+    "dg_prepare_lm_fp8": (_I32, [ctypes.POINTER(Dims), _P, _P, _P, _P]),
     "dg_denoise_step_validate": (_I32, [ctypes.POINTER(Dims), _I32, _I32, ctypes.POINTER(Weights),
                                         ctypes.POINTER(PromptKV)]),
     "dg_slot_read_validate": (_I32, [ctypes.POINTER(Dims), _I32, _I32, _I32, _F]),
@@ -139,9 +140,9 @@ def make_dims(d_model, n_q_heads, n_kv_heads, head_dim, vocab, canvas, window, m
 
 
 def make_weights(embed, wq, wk, wv, wo, embed_t=None, lm_head=None, lm_tiled=None,
-                 embed_t_tiled=None):
+                 embed_t_tiled=None, lm_fp8=None, lm_fp8_exp=None):
     return Weights(_ptr(embed), _ptr(embed_t), _ptr(lm_head), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
-                   _ptr(lm_tiled), _ptr(embed_t_tiled))
+                   _ptr(lm_tiled), _ptr(embed_t_tiled), _ptr(lm_fp8), _ptr(lm_fp8_exp))
 
 
 def make_prompt_kv(k, v, cu_seqlens, max_len, total_len):
@@ -222,6 +223,11 @@ def dg_prepare_embed_t(dims, embed, embed_t, stream=None):
 
 def dg_prepare_lm_tiled(dims, head, lm_tiled, stream=None):
     _check(lib().dg_prepare_lm_tiled(ctypes.byref(dims), _ptr(head), _ptr(lm_tiled), _stream(stream)))
+
+
+def dg_prepare_lm_fp8(dims, head, codes, exps, stream=None):
+    _check(lib().dg_prepare_lm_fp8(ctypes.byref(dims), _ptr(head), _ptr(codes), _ptr(exps),
+                                   _stream(stream)))
 
 
 def dg_prepare_embed_t_tiled(dims, embed_t, embed_t_tiled, stream=None):

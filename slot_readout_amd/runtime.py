@@ -24,7 +24,7 @@ class DeviceProblem:
     """A workload's weights, prompt KV and canvases resident in device memory."""
 
     def __init__(self, inp, device="cuda", with_embed_t=True, with_lm_tiled=True,
-                 with_embed_t_tiled=True):
+                 with_embed_t_tiled=True, with_lm_fp8=False):
         dm = inp["dims"]
         self.inp = inp
         self.device = device
@@ -58,6 +58,13 @@ class DeviceProblem:
                 and self.d % 256 == 0):
             self.embed_t_tiled = torch.empty((self.V * self.d,), dtype=T, device=device)
             dg.dg_prepare_embed_t_tiled(self.dims, self.embed_t, self.embed_t_tiled)
+        # opt-in e4m3 copy of the LM head (bf16 only): every LM-head pass uses it
+        self.lm_fp8 = self.lm_fp8_exp = None
+        if with_lm_fp8:
+            head = self.lm_head if self.lm_head is not None else self.embed
+            self.lm_fp8 = torch.empty((self.V, self.d), dtype=torch.uint8, device=device)
+            self.lm_fp8_exp = torch.empty((self.V,), dtype=torch.int32, device=device)
+            dg.dg_prepare_lm_fp8(self.dims, head, self.lm_fp8, self.lm_fp8_exp)
         total = int(inp["cu_seqlens"][-1])
         kshape = (max(total, 1),) + inp["prompt_k"].shape[1:]
         self.prompt_k = torch.zeros(kshape, dtype=T, device=device)
@@ -77,7 +84,8 @@ class DeviceProblem:
         self.weights = dg.make_weights(self.embed, self.wq, self.wk, self.wv, self.wo,
                                        embed_t=self.embed_t, lm_head=self.lm_head,
                                        lm_tiled=self.lm_tiled,
-                                       embed_t_tiled=self.embed_t_tiled)
+                                       embed_t_tiled=self.embed_t_tiled,
+                                       lm_fp8=self.lm_fp8, lm_fp8_exp=self.lm_fp8_exp)
         self.kv = dg.make_prompt_kv(self.prompt_k, self.prompt_v, self.cu, self.max_prompt,
                                     total)
         self._ws = {}

@@ -20,7 +20,7 @@ def _lib_or_skip():
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_three_calls():
