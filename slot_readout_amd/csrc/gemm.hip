@@ -1001,10 +1001,11 @@ constexpr int kLmStages = 4;
 
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
   if (bf && a.head_fp8) {
-    // e4m3 head: register K loop (the codes are decoded on their way into LDS)
+    // e4m3 head: register K loop (the codes are decoded on their way into LDS);
+    // with half the bytes per step, the few-row tile keeps two steps in flight
     if (a.nrows <= kLmFewRows) {
       const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
-      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32, false, true>), grid, dim3(4 * WAVE), 0, st, a);
+      hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 2, 32, false, true>), grid, dim3(4 * WAVE), 0, st, a);
     } else {
       const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64, false, true>), grid, dim3(8 * WAVE), 0, st, a);
