@@ -62,6 +62,7 @@ SLOT_BAD_POS = 1           # slot position outside [0, C)
 SLOT_BAD_COUNT = 2         # label count outside [1, 26]
 SLOT_BAD_LABEL = 3         # a label id outside [0, V)
 SLOT_BAD_NOISE = 4         # a noise-draw token id outside [0, V) (replaced by the mask id)
+SLOT_NOT_ASKED = 5         # staged read: the slot's ask_if condition did not hold
 
 
 # --------------------------------------------------------------------------
@@ -605,6 +606,75 @@ def slot_read(inp, row_scale=None, canvases=None, n_draws=None):
             row_scale=None if row_scale is None else row_scale[b],
             entropy_threshold=inp["entropy_threshold"], n_draws=nd,
             lm_head=inp.get("lm_head")))
+    return {k: np.stack([o[k] for o in outs]) for k in outs[0]}
+
+
+def slot_read_staged(inp, stage, ask_if_slot, ask_if_label, row_scale=None, n_draws=None):
+    """Two-stage structured read of every canvas.
+
+    sotaaz, "The server takes at most 26 alternatives": a question with ask_if
+    is read only when the answer of an earlier question meets the condition,
+    the entropy-triggered draws are taken per stage (two stages: up to 8
+    reads), and the server writes the first answer back into the canvas before
+    the second read.  Readings: stage[s] is 0 or 1; stage-0 slots are read
+    first (their draws put noise at the stage-0 slots only; stage-1 slots keep
+    the mask id); the best label of each stage-0 slot read without error is
+    then pinned into the canvas at its position; stage-1 slots are read on that
+    canvas (draws put noise at every stage-1 slot).  A stage-1 slot with
+    ask_if_slot[s] = c >= 0 is asked only if slot c was read without error and
+    its best label index equals ask_if_label[s]; otherwise its outputs are the
+    zeros of a skipped slot with status SLOT_NOT_ASKED.  A slot not asked
+    still holds the mask id and takes noise in the draws, but it is read with
+    its first label only, so it never asks for draws itself.
+    """
+    dims = inp["dims"]
+    cu = inp["cu_seqlens"]
+    B = inp["batch"]
+    nd = inp["n_draws"] if n_draws is None else n_draws
+    stage = np.asarray(stage)
+    ask_if_slot = np.asarray(ask_if_slot)
+    ask_if_label = np.asarray(ask_if_label)
+    S0 = np.nonzero(stage == 0)[0]
+    S1 = np.nonzero(stage == 1)[0]
+    outs = []
+    for b in range(B):
+        p0, p1 = int(cu[b]), int(cu[b + 1])
+        args = (inp["embed"], inp["wq"], inp["wk"], inp["wv"], inp["wo"],
+                inp["prompt_k"][p0:p1], inp["prompt_v"][p0:p1])
+        kw = dict(logit_scale=inp["logit_scale"], entropy_threshold=inp["entropy_threshold"],
+                  n_draws=nd, lm_head=inp.get("lm_head"))
+        rs = None if row_scale is None else np.asarray(row_scale)[b]
+        pos, labs, nlab = inp["slot_pos"][b], inp["label_ids"][b], inp["n_labels"][b]
+        noise = inp["noise_ids"][:, b, :]
+        S = len(pos)
+        out = {"logprobs": np.zeros((S, MAX_LABELS)), "probs": np.zeros((S, MAX_LABELS)),
+               "entropy": np.zeros(S), "first_entropy": np.zeros(S),
+               "best": np.full(S, -1, dtype=np.int64), "draws_used": np.zeros(S, dtype=np.int64),
+               "status": np.zeros(S, dtype=np.int64)}
+        ids = np.asarray(inp["canvas_ids"][b]).copy()
+        if len(S0):
+            r0 = slot_read_canvas(*args, ids, dims, pos[S0], labs[S0], nlab[S0], noise[:, S0],
+                                  row_scale=None if rs is None else rs[S0], **kw)
+            for j, s in enumerate(S0):
+                for k in out:
+                    out[k][s] = r0[k][j]
+            for j, s in enumerate(S0):
+                if r0["status"][j] == SLOT_OK:
+                    ids[int(pos[s])] = int(labs[s][int(r0["best"][j])])
+        if len(S1):
+            asked = np.array([ask_if_slot[s] < 0 or
+                              (out["status"][ask_if_slot[s]] == SLOT_OK and
+                               out["best"][ask_if_slot[s]] == ask_if_label[s]) for s in S1])
+            n1 = np.where(asked, nlab[S1], 1)
+            r1 = slot_read_canvas(*args, ids, dims, pos[S1], labs[S1], n1, noise[:, S1],
+                                  row_scale=None if rs is None else rs[S1], **kw)
+            for j, s in enumerate(S1):
+                if asked[j]:
+                    for k in out:
+                        out[k][s] = r1[k][j]
+                else:
+                    out["status"][s] = SLOT_NOT_ASKED
+        outs.append(out)
     return {k: np.stack([o[k] for o in outs]) for k in outs[0]}
 
 
