@@ -179,6 +179,8 @@ typedef struct {
 #define DG_SLOT_BAD_COUNT 2  /* n_labels outside [1, 26]: slot skipped */
 #define DG_SLOT_BAD_LABEL 3  /* a label id outside [0, vocab): slot skipped */
 #define DG_SLOT_BAD_NOISE 4  /* a noise id outside [0, vocab): the mask id was used instead */
+#define DG_SLOT_NOT_ASKED 5  /* dg_slot_read_staged: the slot's ask_if condition did not hold */
+#define DG_MAX_STAGED_SLOTS 64 /* slots of one dg_slot_read_staged call */
 
 /* Bytes of workspace dg_denoise_step needs for `batch` sequences whose prompts
  * are at most `max_prompt` long.  Returns 0 for invalid dims. */
@@ -326,6 +328,40 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
                        float *logprobs, float *probs, float *entropy, float *first_entropy,
                        int32_t *best, int32_t *draws_used, int32_t *status,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/* Two-stage structured read (sotaaz, "The server takes at most 26
+ * alternatives per question": a question with ask_if is read only when the
+ * answer of an earlier question meets the condition, the draws are taken per
+ * stage, and the first answer is written back into the canvas before the
+ * second read).  Arguments as dg_slot_read, plus three host arrays of n_slots
+ * entries (n_slots <= DG_MAX_STAGED_SLOTS):
+ *   slot_stage    0 or 1: the stage that reads the slot
+ *   ask_if_slot   -1, or a stage-0 slot c: this stage-1 slot is asked only if
+ *                 slot c was read without error (DG_SLOT_OK) with best label
+ *                 index ask_if_label[s]
+ *   ask_if_label  label index in [0, 26) (used when ask_if_slot >= 0)
+ * Stage 0 reads its slots with dg_slot_read (draws put noise at stage-0 slots;
+ * stage-1 slots keep the mask id).  The best label of every stage-0 slot read
+ * without error is then written at its position in a copy of the canvas, in
+ * slot order, and stage 1 reads its slots on that copy (draws put noise at
+ * every stage-1 slot).  A slot not asked is read with its first label only (it
+ * never asks for draws) and reports zeros, best -1, draws_used 0 and status
+ * DG_SLOT_NOT_ASKED.  canvas_ids is never modified.  The workspace holds
+ * dg_slot_read's for n_slots slots plus the stage copies; size it with
+ * dg_slot_read_staged_workspace.
+ * Errors: as dg_slot_read; DG_ERR_INVALID_ARG for a bad stage array. */
+size_t dg_slot_read_staged_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                                     int32_t max_prompt, int32_t n_draws);
+dg_status dg_slot_read_staged(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                              int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                              const int32_t *slot_pos, const int32_t *label_ids,
+                              const int32_t *n_labels, const int32_t *noise_ids,
+                              const int32_t *slot_stage, const int32_t *ask_if_slot,
+                              const int32_t *ask_if_label, float logit_scale,
+                              const float *row_scale, float entropy_threshold, int32_t n_draws,
+                              float *logprobs, float *probs, float *entropy, float *first_entropy,
+                              int32_t *best, int32_t *draws_used, int32_t *status,
+                              void *workspace, size_t ws_bytes, void *stream);
 
 /* Writes embed_t = embed^T ([d_model, vocab] from [vocab, d_model]), the layout
  * the self-conditioning contraction streams.  Weight preparation, done once. */

@@ -919,6 +919,155 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+// Workspace of a two-stage read: the stage copies, then dg_slot_read's.
+struct StagedPlan {
+  size_t pos, lab, nlab, noise, rs, lp, pr, ent, fent, best, draws, status, pinned, inner,
+      inner_bytes, total;
+};
+
+StagedPlan plan_staged(const dg_dims &d, int B, int S, int max_prompt, int nd) {
+  StagedPlan p{};
+  const size_t BS = (size_t)B * S;
+  Arena a;
+  p.pos = a.take(BS * 4);
+  p.lab = a.take(BS * DG_MAX_LABELS * 4);
+  p.nlab = a.take(BS * 4);
+  p.noise = a.take((size_t)(nd > 1 ? nd : 1) * BS * 4);
+  p.rs = a.take(BS * 4);
+  p.lp = a.take(BS * DG_MAX_LABELS * 4);
+  p.pr = a.take(BS * DG_MAX_LABELS * 4);
+  p.ent = a.take(BS * 4);
+  p.fent = a.take(BS * 4);
+  p.best = a.take(BS * 4);
+  p.draws = a.take(BS * 4);
+  p.status = a.take(BS * 4);
+  p.pinned = a.take((size_t)B * d.canvas * 4);
+  p.inner_bytes = plan_slot(d, B, S, max_prompt, nd).total;
+  p.inner = a.take(p.inner_bytes);
+  p.total = a.off;
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+size_t dg_slot_read_staged_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                                     int32_t max_prompt, int32_t n_draws) {
+  if (dg_slot_read_validate(dims, batch, n_slots, n_draws, 0.1f) != DG_OK || max_prompt < 0)
+    return 0;
+  return plan_staged(*dims, batch, n_slots, max_prompt, n_draws).total;
+}
+
+dg_status dg_slot_read_staged(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                              int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                              const int32_t *slot_pos, const int32_t *label_ids,
+                              const int32_t *n_labels, const int32_t *noise_ids,
+                              const int32_t *slot_stage, const int32_t *ask_if_slot,
+                              const int32_t *ask_if_label, float logit_scale,
+                              const float *row_scale, float entropy_threshold, int32_t n_draws,
+                              float *logprobs, float *probs, float *entropy, float *first_entropy,
+                              int32_t *best, int32_t *draws_used, int32_t *status,
+                              void *workspace, size_t ws_bytes, void *stream) {
+  dg_status s = dg_slot_read_validate(dims, batch, n_slots, n_draws, entropy_threshold);
+  if (s != DG_OK) return s;
+  if (n_slots > DG_MAX_STAGED_SLOTS)
+    return fail(DG_ERR_INVALID_ARG, "n_slots %d exceeds %d for a staged read", n_slots,
+                DG_MAX_STAGED_SLOTS);
+  if (n_slots > 0 && (!slot_stage || !ask_if_slot || !ask_if_label))
+    return fail(DG_ERR_INVALID_ARG, "slot_stage, ask_if_slot and ask_if_label are required");
+  dg::StagedArgs st0{}, st1{};
+  for (int q = 0; q < n_slots; ++q) {
+    if (slot_stage[q] != 0 && slot_stage[q] != 1)
+      return fail(DG_ERR_INVALID_ARG, "slot %d: stage %d is neither 0 nor 1", q, slot_stage[q]);
+    const int c = ask_if_slot[q];
+    if (c != -1) {
+      if (slot_stage[q] != 1 || c < 0 || c >= n_slots || slot_stage[c] != 0)
+        return fail(DG_ERR_INVALID_ARG, "slot %d: ask_if_slot %d must name a stage-0 slot of a "
+                    "stage-1 question", q, c);
+      if (ask_if_label[q] < 0 || ask_if_label[q] >= DG_MAX_LABELS)
+        return fail(DG_ERR_INVALID_ARG, "slot %d: ask_if_label %d outside [0, %d)", q,
+                    ask_if_label[q], DG_MAX_LABELS);
+    }
+    dg::StagedArgs &g = slot_stage[q] == 0 ? st0 : st1;
+    g.idx[g.n] = q;
+    g.ask_slot[g.n] = c;
+    g.ask_label[g.n] = c >= 0 ? ask_if_label[q] : 0;
+    ++g.n;
+  }
+  s = check_model(dims, batch, kv ? kv->max_len : 0, w, kv);
+  if (s != DG_OK) return s;
+  if (batch == 0 || n_slots == 0) return ok();
+  if (!canvas_ids || !slot_pos || !label_ids || !n_labels || !logprobs || !probs || !entropy ||
+      !first_entropy || !best || !draws_used || !status)
+    return fail(DG_ERR_INVALID_ARG, "slot-read input and output arrays must not be NULL");
+  if (n_draws > 1 && !noise_ids) return fail(DG_ERR_INVALID_ARG, "noise_ids is required when n_draws > 1");
+  if (!aligned16(workspace)) return fail(DG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const dg_dims &d = *dims;
+  const StagedPlan p = plan_staged(d, batch, n_slots, kv->max_len, n_draws);
+  if (!workspace || ws_bytes < p.total)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                ws_bytes, p.total);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (dg::StagedArgs *g : {&st0, &st1}) {
+    g->S = n_slots;
+    g->B = batch;
+    g->C = d.canvas;
+    g->nd = n_draws;
+    g->slot_pos = slot_pos;
+    g->label_ids = label_ids;
+    g->n_labels = n_labels;
+    g->noise_ids = n_draws > 1 ? noise_ids : nullptr;
+    g->row_scale = row_scale;
+    g->pos_s = at<int32_t>(workspace, p.pos);
+    g->lab_s = at<int32_t>(workspace, p.lab);
+    g->nlab_s = at<int32_t>(workspace, p.nlab);
+    g->noise_s = at<int32_t>(workspace, p.noise);
+    g->rs_s = at<float>(workspace, p.rs);
+    g->lp_s = at<float>(workspace, p.lp);
+    g->pr_s = at<float>(workspace, p.pr);
+    g->ent_s = at<float>(workspace, p.ent);
+    g->fent_s = at<float>(workspace, p.fent);
+    g->best_s = at<int32_t>(workspace, p.best);
+    g->draws_s = at<int32_t>(workspace, p.draws);
+    g->status_s = at<int32_t>(workspace, p.status);
+    g->logprobs = logprobs;
+    g->probs = probs;
+    g->entropy = entropy;
+    g->first_entropy = first_entropy;
+    g->best = best;
+    g->draws_used = draws_used;
+    g->status = status;
+    g->canvas = canvas_ids;
+    g->pinned = at<int32_t>(workspace, p.pinned);
+  }
+  void *inner = at<char>(workspace, p.inner);
+  auto read_stage = [&](const dg::StagedArgs &g, const int32_t *ids) -> dg_status {
+    if (g.n == 0) return DG_OK;
+    DG_TRY_HIP(dg::launch_staged_gather(g, hs), "stage gather launch");
+    dg_status r = dg_slot_read(dims, w, kv, batch, ids, g.n, g.pos_s, g.lab_s, g.nlab_s,
+                               g.noise_ids ? g.noise_s : nullptr, logit_scale,
+                               row_scale ? g.rs_s : nullptr, entropy_threshold, n_draws,
+                               const_cast<float *>(g.lp_s), const_cast<float *>(g.pr_s),
+                               const_cast<float *>(g.ent_s), const_cast<float *>(g.fent_s),
+                               const_cast<int32_t *>(g.best_s), const_cast<int32_t *>(g.draws_s),
+                               const_cast<int32_t *>(g.status_s), inner, p.inner_bytes, stream);
+    if (r != DG_OK) return r;
+    DG_TRY_HIP(dg::launch_staged_scatter(g, hs), "stage scatter launch");
+    return DG_OK;
+  };
+  s = read_stage(st0, canvas_ids);
+  if (s != DG_OK) return s;
+  if (st1.n > 0) {
+    DG_TRY_HIP(dg::launch_staged_pin(st0, hs), "answer pinning launch");
+    s = read_stage(st1, st0.pinned);
+    if (s != DG_OK) return s;
+  }
+  return ok();
+}
+
 dg_status dg_prepare_embed_t(const dg_dims *dims, const void *embed, void *embed_t, void *stream) {
   dg_status s = check_dims(dims);
   if (s != DG_OK) return s;

@@ -206,6 +206,32 @@ hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hi
 // the rest of a one-pass read, one workgroup per canvas: first read, re-read
 // flags, noise-id status and draw average
 hipError_t launch_slot_finish(const SlotArgs &a, hipStream_t st);
+// Two-stage reads: the slots of one stage (idx, by value), gathered from and
+// scattered back to the [B, S] arrays of the call.
+constexpr int kMaxStagedSlots = 64;
+struct StagedArgs {
+  int idx[kMaxStagedSlots];        // the stage's slots, in order
+  int ask_slot[kMaxStagedSlots];   // per stage slot: condition slot (-1: none)
+  int ask_label[kMaxStagedSlots];  // per stage slot: required best label index
+  int n, S, B, C, nd;
+  const int32_t *slot_pos, *label_ids, *n_labels, *noise_ids;   // [B,S], [B,S,26], [B,S], [nd,B,S]
+  const float *row_scale;                                        // [B,S] or null
+  int32_t *pos_s, *lab_s, *nlab_s, *noise_s;                     // the stage's copies, n slots
+  float *rs_s;
+  const float *lp_s, *pr_s, *ent_s, *fent_s;                     // the stage's outputs
+  const int32_t *best_s, *draws_s, *status_s;
+  float *logprobs, *probs, *entropy, *first_entropy;             // the call's outputs
+  int32_t *best, *draws_used, *status;
+  const int32_t *canvas;                                         // [B,C]
+  int32_t *pinned;                                               // [B,C]
+};
+// stage copies of slot arrays; slots whose ask_if fails get one label
+hipError_t launch_staged_gather(const StagedArgs &a, hipStream_t st);
+// stage outputs into the call's outputs; slots whose ask_if fails: not asked
+hipError_t launch_staged_scatter(const StagedArgs &a, hipStream_t st);
+// pinned = canvas with each stage slot read without error holding its best label
+hipError_t launch_staged_pin(const StagedArgs &a, hipStream_t st);
+
 // copies k and v of canvas g*G (every position) into canvases g*G + 1 .. g*G + G-1
 hipError_t launch_kv_replicate(void *k, void *v, int groups, int G, int C, int nkv, int elem_bytes,
                                hipStream_t st);

@@ -368,4 +368,78 @@ hipError_t launch_slot_average(const SlotArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Two-stage reads (one workgroup per canvas, one thread per stage slot)
+// ---------------------------------------------------------------------------
+__device__ inline bool staged_asked(const StagedArgs &a, int b, int j) {
+  const int c = a.ask_slot[j];
+  if (c < 0) return true;
+  const int64_t bc = (int64_t)b * a.S + c;
+  return a.status[bc] == DG_SLOT_OK && a.best[bc] == a.ask_label[j];
+}
+
+__global__ __launch_bounds__(64) void staged_gather_kernel(StagedArgs a) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  if (j >= a.n) return;
+  const int s = a.idx[j];
+  const int64_t from = (int64_t)b * a.S + s, to = (int64_t)b * a.n + j;
+  a.pos_s[to] = a.slot_pos[from];
+  a.nlab_s[to] = staged_asked(a, b, j) ? a.n_labels[from] : 1;
+  for (int q = 0; q < DG_MAX_LABELS; ++q)
+    a.lab_s[to * DG_MAX_LABELS + q] = a.label_ids[from * DG_MAX_LABELS + q];
+  if (a.noise_ids)
+    for (int d = 0; d < a.nd; ++d)
+      a.noise_s[((int64_t)d * a.B + b) * a.n + j] = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
+  if (a.row_scale) a.rs_s[to] = a.row_scale[from];
+}
+
+__global__ __launch_bounds__(64) void staged_scatter_kernel(StagedArgs a) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  if (j >= a.n) return;
+  const int s = a.idx[j];
+  const int64_t to = (int64_t)b * a.S + s, from = (int64_t)b * a.n + j;
+  const bool asked = staged_asked(a, b, j);
+  for (int q = 0; q < DG_MAX_LABELS; ++q) {
+    a.logprobs[to * DG_MAX_LABELS + q] = asked ? a.lp_s[from * DG_MAX_LABELS + q] : 0.f;
+    a.probs[to * DG_MAX_LABELS + q] = asked ? a.pr_s[from * DG_MAX_LABELS + q] : 0.f;
+  }
+  a.entropy[to] = asked ? a.ent_s[from] : 0.f;
+  a.first_entropy[to] = asked ? a.fent_s[from] : 0.f;
+  a.best[to] = asked ? a.best_s[from] : -1;
+  a.draws_used[to] = asked ? a.draws_s[from] : 0;
+  a.status[to] = asked ? a.status_s[from] : DG_SLOT_NOT_ASKED;
+}
+
+__global__ __launch_bounds__(256) void staged_pin_kernel(StagedArgs a) {
+  const int b = blockIdx.x;
+  const int64_t base = (int64_t)b * a.C;
+  for (int i = threadIdx.x; i < a.C; i += 256) a.pinned[base + i] = a.canvas[base + i];
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  // in slot order, so a later slot at the same position wins
+  for (int j = 0; j < a.n; ++j) {
+    const int64_t bs = (int64_t)b * a.S + a.idx[j];
+    if (a.status[bs] != DG_SLOT_OK) continue;
+    const int pos = a.slot_pos[bs], k = a.best[bs];
+    if (pos < 0 || pos >= a.C || k < 0 || k >= DG_MAX_LABELS) continue;
+    a.pinned[base + pos] = a.label_ids[bs * DG_MAX_LABELS + k];
+  }
+}
+
+hipError_t launch_staged_gather(const StagedArgs &a, hipStream_t st) {
+  if (a.B <= 0 || a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(staged_gather_kernel, dim3(a.B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_staged_scatter(const StagedArgs &a, hipStream_t st) {
+  if (a.B <= 0 || a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(staged_scatter_kernel, dim3(a.B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_staged_pin(const StagedArgs &a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(staged_pin_kernel, dim3(a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace dg

@@ -146,6 +146,24 @@ class DeviceProblem:
                      stream)
         return out
 
+    def slot_read_staged(self, stage, ask_if_slot, ask_if_label, row_scale=None, n_draws=None,
+                         threshold=None, out=None, stream=None):
+        """dg_slot_read_staged over the problem's slots (stage arrays are host lists)."""
+        nd = self.inp["n_draws"] if n_draws is None else n_draws
+        th = self.inp["entropy_threshold"] if threshold is None else threshold
+        if out is None:
+            out = self.slot_outputs()
+        ws = self.workspace("staged", dg.dg_slot_read_staged_workspace(self.dims, self.B, self.S,
+                                                                       self.max_prompt, nd))
+        dg.dg_slot_read_staged(self.dims, self.weights, self.kv, self.B, self.canvas_ids, self.S,
+                               self.slot_pos, self.label_ids, self.n_labels, self.noise_ids,
+                               [int(x) for x in stage], [int(x) for x in ask_if_slot],
+                               [int(x) for x in ask_if_label], self.inp["logit_scale"], row_scale,
+                               th, nd, out["logprobs"], out["probs"], out["entropy"],
+                               out["first_entropy"], out["best"], out["draws_used"], out["status"],
+                               ws, stream)
+        return out
+
     # ---------------------------------------------------------------- loop --
     def loop(self, tau=None, max_steps=None, check_every=8, sc_in=None, row_scale=None,
              canvas_ids=None, stream=None):

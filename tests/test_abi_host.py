@@ -160,3 +160,33 @@ def test_loop_rejects_bad_arguments_before_any_launch():
     assert need > dg.dg_denoise_step_workspace(d, 1, 128) > 0
     assert call(ws_bytes=need - 1) == dg.DG_ERR_WORKSPACE
     assert "workspace" in dg.lib().dg_last_error().decode()
+
+
+def test_staged_read_rejects_bad_stage_arrays_before_any_launch():
+    """dg_slot_read_staged checks its host stage arrays first: stages 0/1 only,
+    ask_if naming a stage-0 slot from a stage-1 slot, labels in [0, 26), at most
+    DG_MAX_STAGED_SLOTS slots.  Fake device addresses: nothing is launched."""
+    import ctypes
+    dg = _lib_or_skip()
+    L = dg.lib()
+    d = _dims(dg)
+
+    def call(stage, ask, lab, n=None):
+        n = len(stage) if n is None else n
+        arr = ctypes.c_int32 * max(len(stage), 1)
+        st, ak, al = arr(*stage), arr(*ask), arr(*lab)     # alive for the whole call
+        w, kv = _weights(dg), _kv(dg)
+        return L.dg_slot_read_staged(ctypes.byref(d), ctypes.byref(w), ctypes.byref(kv), 1, 1024, n,
+                                     2048, 4096, 6144, 8192, ctypes.addressof(st),
+                                     ctypes.addressof(ak), ctypes.addressof(al), 8.0, None, 0.1, 4,
+                                     *([1 << 20] * 7), 1 << 21, 16, None)
+
+    I = dg.DG_ERR_INVALID_ARG
+    assert call([0, 2], [-1, -1], [0, 0]) == I                # stage 2
+    assert call([0, 1], [-1, 1], [0, 0]) == I                 # ask_if naming a stage-1 slot
+    assert call([0, 1], [1, -1], [0, 0]) == I                 # ask_if on a stage-0 slot
+    assert call([0, 1], [-1, 0], [0, 26]) == I                # label out of range
+    assert call([0, 1], [-1, 5], [0, 0]) == I                 # slot out of range
+    assert call([0] * 65, [-1] * 65, [0] * 65) == I           # too many slots
+    # a valid schema gets past these checks (and fails on the tiny workspace)
+    assert call([0, 1], [-1, 0], [0, 3]) == dg.DG_ERR_WORKSPACE
