@@ -182,6 +182,70 @@ def prefill_leg(dev, inp, stream, runs=5):
     return {"tokens": n, "ms": round(t, 4), "tokens_per_s": round(n / (t * 1e-3), 1)}
 
 
+def staged_leg(dev, inp, stream, runs=5):
+    """dg_slot_read_staged of the workload's slots: the first half in stage 0, the
+    second half in stage 1, whose first slot is asked only if stage-0 slot 0
+    answers label 0; median of `runs` calls after one warm-up call."""
+    import numpy as np
+    import torch
+    S = dev.S
+    stage = [0] * (S // 2) + [1] * (S - S // 2)
+    ask, lab = [-1] * S, [0] * S
+    if S >= 2:
+        ask[S // 2] = 0
+    out = dev.slot_outputs()
+    ts = []
+    for i in range(runs + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dev.slot_read_staged(stage, ask, lab, out=out, stream=stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    t = float(np.median(ts))
+    return {"slots": S, "stages": 2, "ms": round(t, 4), "slot_reads_per_s": round(dev.B * S / (t * 1e-3), 1),
+            "reads_per_slot": int(out["draws_used"].max().item()) + 1}
+
+
+def fp8_leg(inp, stream, K=20, W=3):
+    """The same step (step + commit + read) with the e4m3 copy of the LM head."""
+    import numpy as np
+    import torch
+    from slot_readout_amd import dg
+    from slot_readout_amd.runtime import DeviceProblem
+    dev = DeviceProblem(inp, device="cuda:0", with_lm_fp8=True)
+    dm = inp["dims"]
+    so, co, ro = dev.step_outputs(want_sc=True), dev.commit_outputs(), dev.slot_outputs()
+    ws = dev.workspace("step", dg.dg_denoise_step_workspace(dev.dims, dev.B, dev.max_prompt))
+
+    def step():
+        dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, dev.B, dev.canvas_ids, None,
+                           inp["logit_scale"], None, so["conf"], so["entropy"], so["argmax"],
+                           so["sc_out"], None, so["flags"], ws, stream)
+        dg.dg_commit(dev.B, dev.C, dm.mask_id, dev.canvas_ids, so["conf"], so["entropy"],
+                     so["argmax"], inp["tau"], co["mask"], co["out_ids"], co["n"], stream)
+        dev.slot_read(out=ro, stream=stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    del dev
+    return {"lm_head": "e4m3 codes, per-row power-of-two scales", "ms_per_step": round(ms, 4),
+            "canvas_tokens_per_s": round(dev_tokens(inp) / (ms * 1e-3), 1)}
+
+
+def dev_tokens(inp):
+    return inp["batch"] * inp["dims"].canvas
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -374,6 +438,10 @@ def main():
         line["loop"] = loop_leg(dev, inp, stream)
     if workload in ("bf16_step", "long_read"):
         line["prefill"] = prefill_leg(dev, inp, stream)
+    if workload == WORKLOAD:
+        line["staged_read"] = staged_leg(dev, inp, stream)
+        if not args.lm_fp8:
+            line["fp8_head_step"] = fp8_leg(inp, stream)
     stage_ev.destroy()
     if not args.no_cpu_baseline and workload == WORKLOAD:
         line["cpu_baseline"] = cpu_baseline(inp)
