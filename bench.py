@@ -269,8 +269,9 @@ def main():
                          "for long_read, whose prompt KV would otherwise sit in the 256 MB MALL")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build is a single-GPU hot path "
-              "(see the sharding notes in the design document); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the hot path runs on a single GPU "
+              "(the design document describes how it would shard); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

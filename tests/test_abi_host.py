@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "dg.h")
 def _lib_or_skip():
     from slot_readout_amd import dg
     if not os.path.exists(dg.LIB_PATH):
-        pytest.skip("libdg.so not built (run __graft_entry__.build())")
+        pytest.skip("libdg.so not built (run python -m slot_readout_amd.build)")
     return dg
 
 
