@@ -246,6 +246,36 @@ def dev_tokens(inp):
     return inp["batch"] * inp["dims"].canvas
 
 
+def achievable_peaks():
+    """Measured ceilings on this GPU, beside the vendor peaks: a 1 GiB device-to-device
+    copy (bytes read + written per second) and a bf16 8192^3 matrix product
+    (contiguous operands).  Taken after the timed steps."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda:0")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda:0")
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    t_copy = timed(lambda: y.copy_(x), 10)
+    t_mm = timed(lambda: torch.matmul(a, b), 10)
+    out = {"copy_GBs": round(2 * x.numel() * 4 / (t_copy * 1e-3) / 1e9, 1),
+           "matmul_bf16_TFLOPs": round(2 * 8192 ** 3 / (t_mm * 1e-3) / 1e12, 1)}
+    del x, y, a, b
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +465,10 @@ def main():
     span.destroy()
     if args.lm_fp8:   # counters were taken with the bf16 head
         line["roofline"]["traffic"] = None
+    peaks = achievable_peaks()
+    roof = line["roofline"]
+    roof["achievable"] = dict(peaks, frac_of_copy=round(roof["achieved"] / peaks["copy_GBs"], 4),
+                              mfma_frac_of_matmul=round(roof["mfma_tflops"] / peaks["matmul_bf16_TFLOPs"], 4))
     if not args.no_loop and workload == WORKLOAD:
         line["loop"] = loop_leg(dev, inp, stream)
     if workload in ("bf16_step", "long_read"):
