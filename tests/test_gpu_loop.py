@@ -122,3 +122,17 @@ def test_loop_check_interval_changes_nothing(torch_cuda):
     for k in ("ids", "commit_step", "steps"):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     assert a["launched"] == int(a["steps"].max()) and b["launched"] == 64
+
+
+def test_loop_deterministic(torch_cuda):
+    """Two runs of the loop (fixed-order reductions, no float atomics) give bitwise
+    the same canvases, commit steps and step counts."""
+    from slot_readout_amd.runtime import DeviceProblem
+    import torch
+    inp = make_inputs(config("ragged32", batch=3, canvas=96), prompt_override=("uniform", 50, 300))
+    rs = torch.from_numpy(companion_row_scale(inp, (3, 96))).cuda()
+    dev = DeviceProblem(inp)
+    a = _run(dev, tau=2.0, row_scale=rs, check_every=2)
+    b = _run(dev, tau=2.0, row_scale=rs, check_every=5)
+    for k in ("ids", "commit_step", "steps"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)

@@ -82,3 +82,17 @@ def test_staged_read_without_second_stage_is_the_plain_read(torch_cuda):
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_staged_read_deterministic(torch_cuda):
+    import torch
+    from slot_readout_amd.runtime import DeviceProblem
+    inp = make_inputs(config("reads512"), batch=6, prompt_override=("fixed", 80))
+    S = inp["slot_pos"].shape[1]
+    stage, ask, lab = [0, 0, 1, 1][:S], [-1, -1, 0, -1][:S], [0, 0, 1, 0][:S]
+    dev = DeviceProblem(inp, with_embed_t=False)
+    a = {k: v.clone() for k, v in dev.slot_read_staged(stage, ask, lab).items()}
+    b = dev.slot_read_staged(stage, ask, lab)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
