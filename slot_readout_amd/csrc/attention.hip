@@ -132,10 +132,13 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const int QN = a.qpos ? a.qn : a.C;   // queries per canvas
   const int nqt = (QN + NQ - 1) / NQ;
   int grpi, tile;
-  if (!xcd_group_tile(a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * nqt, &grpi, &tile)) return;
+  if (!xcd_group_tile(a.nc * a.Hkv * a.nsplit, a.packed ? 1 : (a.Hq / a.Hkv) * nqt, &grpi, &tile))
+    return;
   const int s = grpi % a.nsplit;
   const int cb = grpi / a.nsplit / a.Hkv;
-  const int h = (grpi / a.nsplit % a.Hkv) * (a.Hq / a.Hkv) + tile / nqt, qt = tile % nqt;
+  // packed: h is the kv group's first query head and every column names its own
+  const int h = (grpi / a.nsplit % a.Hkv) * (a.Hq / a.Hkv) + (a.packed ? 0 : tile / nqt);
+  const int qt = a.packed ? 0 : tile % nqt;
   if (a.active && !a.active[cb]) return;
   const int G = a.Hq / a.Hkv, g = h / G;
   const int C = a.C, W = a.W;
@@ -166,6 +169,14 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   // q rows: canvas positions, or the compact rows of gathered queries
   const T *qbase = static_cast<const T *>(a.q) + (int64_t)cb * (a.qpos ? QN : C) * q_stride +
                    (int64_t)h * HD;
+  // query index and head of each of the lane's columns (packed: c -> (c / QN, c % QN))
+  int cq[QB], chd[QB];
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) {
+    const int c = i0 + w * QB * 16 + jb * 16 + col;
+    cq[jb] = a.packed ? (c < G * QN ? c % QN : QN) : c;
+    chd[jb] = a.packed ? (c < G * QN ? c / QN : 0) : 0;
+  }
   const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
   const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
   const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
@@ -178,7 +189,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   int qp[QB];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
-    const int qi = i0 + w * QB * 16 + jb * 16 + col;
+    const int qi = cq[jb];
     int p = qi;
     if (a.qpos) p = qi < QN ? a.qpos[(int64_t)cb * QN + qi] : -1;
     qp[jb] = p >= 0 && p < C ? p : -(1 << 20);
@@ -192,11 +203,12 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   frag qf[QB][KS];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
-    const int qrow = a.qpos ? i0 + w * QB * 16 + jb * 16 + col : qp[jb];
+    const int qrow = a.qpos ? cq[jb] : qp[jb];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qp[jb] >= 0)
-        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qrow * q_stride + ks * MF::KI +
+        qf[jb][ks] = *reinterpret_cast<const frag *>(qbase + (int64_t)qrow * q_stride +
+                                                      (int64_t)chd[jb] * HD + ks * MF::KI +
                                                       grp * MF::KPL);
       else
         qf[jb][ks] = frag{};
@@ -480,18 +492,18 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
-    const int qi = i0 + w * QB * 16 + jb * 16 + col;
+    const int qi = cq[jb], hq = h + chd[jb];
     const float L = group4_sum(grp == 0 ? oacc[HD / 16][jb][0] : 0.f);
     if (qi >= QN) continue;
     if (a.nsplit == 1) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      T *o = static_cast<T *>(a.o) + (((int64_t)cb * QN + qi) * a.Hq + h) * HD;
+      T *o = static_cast<T *>(a.o) + (((int64_t)cb * QN + qi) * a.Hq + hq) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<T>(oacc[rb][jb][r] * inv);
     } else {
-      const int64_t row = ((int64_t)cb * a.Hq + h) * QN + qi;
+      const int64_t row = ((int64_t)cb * a.Hq + hq) * QN + qi;
       T *po = static_cast<T *>(a.part_o) + ((int64_t)s * R + row) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb) store4v<T>(po + rb * 16 + grp * 4, oacc[rb][jb]);
@@ -584,6 +596,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 }
 
 int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 128; }
+
+bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim) {
+  return gathered && Hq > Hkv && (int64_t)(Hq / Hkv) * qn <= attn_query_tile(head_dim);
+}
 static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               AttnShape<float, 64>::NW * AttnShape<float, 64>::QB * 16 == 128 &&
               AttnShape<bf16, 512>::NW * AttnShape<bf16, 512>::QB * 16 == 64,
@@ -593,7 +609,9 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
                int max_len, int *nsplit, int *chunk) {
   const int nq = attn_query_tile(head_dim);
   const int nk = head_dim == 512 ? 32 : 64;
-  const int64_t base = (int64_t)nc * Hq * cdiv64(qn, nq);
+  const int64_t base = attn_packed(qn, gathered, Hq, Hkv, head_dim)
+                           ? (int64_t)nc * Hkv
+                           : (int64_t)nc * Hq * cdiv64(qn, nq);
   // most keys one query tile can see: the prompt plus its window span
   const int64_t win = gathered ? C : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
   const int64_t span = (int64_t)max_len + win;
@@ -619,8 +637,10 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
   const int QN = a.qpos ? a.qn : a.C;
   if (QN <= 0) return hipSuccess;
-  const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, (a.Hq / a.Hkv) * cdiv64(QN, NQ));
-  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(64 * NW), 0, st, a);
+  AttnArgs b = a;
+  b.packed = attn_packed(QN, a.qpos != nullptr, a.Hq, a.Hkv, HD) ? 1 : 0;
+  const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, b.packed ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
+  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(64 * NW), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * QN;

@@ -111,6 +111,9 @@ struct AttnArgs {
   float2 *part_ml;             // [nsplit, nc*Hq*qn]
   int64_t total_len;
   int nc, C, Hq, Hkv, W, max_len, nsplit, chunk, canvas_per_prompt;
+  // gathered queries only: one workgroup serves every query head of its kv head
+  // (query column c: head kv*G + c / qn, query c % qn); set by the launcher
+  int packed;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
 };
 
@@ -134,6 +137,8 @@ hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st);
 
 // attention: query rows per workgroup, split-KV planning, launch (+ merge)
 int attn_query_tile(int head_dim);
+// whether gathered queries pack the G query heads of a kv head into one tile
+bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim);
 // qn queries per canvas; gathered: queries at arbitrary positions (every
 // canvas key is a candidate) instead of consecutive ones
 void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
