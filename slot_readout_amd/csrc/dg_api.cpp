@@ -2,6 +2,7 @@
 // sequence of each call.  Nothing here allocates device memory; only the
 // multi-step loop synchronises the host (every check_every steps, to stop once
 // no canvas holds a mask id).
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -130,8 +131,14 @@ AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1) {
   return p;
 }
 
+// fp32 split-K partials of a projection of M rows x ncols outputs over K (0: unsplit)
+size_t proj_part_bytes(const dg_dims &d, int64_t M, int64_t ncols, int K) {
+  const int ks = dg::proj_ksplit(M, ncols, K, d.dtype == DG_BF16);
+  return ks > 1 ? (size_t)ks * M * ncols * sizeof(float) : 0;
+}
+
 struct StepPlan {
-  size_t q, k, v, o, part_o, part_ml, h, stats, ptilde, shift, inv_z, sc_part, total;
+  size_t q, k, v, o, part_o, part_ml, proj_part, h, stats, ptilde, shift, inv_z, sc_part, total;
   AttnPlan attn;
   int ksplit;
 };
@@ -150,6 +157,8 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
   p.attn = plan_attention(d, B, max_prompt);
   p.part_o = a.take(p.attn.part_o);
   p.part_ml = a.take(p.attn.part_ml);
+  p.proj_part = a.take(std::max(proj_part_bytes(d, M, nq + 2 * nkv, d.d_model),
+                                proj_part_bytes(d, M, d.d_model, (int)nq)));
   p.h = a.take(M * d.d_model * ts);
   p.stats = a.take(M * nvt * sizeof(float4));
   // bf16 p~ is stored in blocks of 256 rows: whole row blocks are allocated
@@ -189,7 +198,7 @@ LoopPlan plan_loop(const dg_dims &d, int B, int max_prompt) {
 }
 
 struct SlotPlan {
-  size_t q, k, v, o, part_o, part_ml, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
+  size_t q, k, v, o, part_o, part_ml, proj_part, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
       rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, total;
   AttnPlan first, draws;
   bool spec;
@@ -237,6 +246,21 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
   p.part_o = a.take(po);
   p.part_ml = a.take(pm);
+  {
+    // every projection a read launches: k/v of whole canvases, q (or, for the
+    // speculated draws, q/k/v) of slot rows, the output projection of slot rows
+    size_t pp = 0;
+    const int64_t C = d.canvas, Bs = (int64_t)B * S;
+    const int64_t kv_rows[] = {B * C, (nd > 1 ? (int64_t)nd : 1) * B * C};
+    const int64_t q_rows[] = {Bs, (nd > 1 ? (int64_t)nd : 1) * Bs, (int64_t)(nd + 1) * Bs};
+    for (int64_t m : kv_rows) pp = std::max(pp, proj_part_bytes(d, m, 2 * nkv, d.d_model));
+    for (int64_t m : q_rows) {
+      pp = std::max(pp, proj_part_bytes(d, m, nq, d.d_model));
+      pp = std::max(pp, proj_part_bytes(d, m, nq + 2 * nkv, d.d_model));
+      pp = std::max(pp, proj_part_bytes(d, m, d.d_model, (int)nq));
+    }
+    p.proj_part = a.take(pp);
+  }
   p.h = a.take(nrows * d.d_model * ts);
   p.rows = a.take(nrows * sizeof(int32_t));
   p.qpos = a.take(nrows * sizeof(int32_t));
@@ -304,8 +328,8 @@ struct Gather {
 dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *kv, int nc,
                     int canvas_per_prompt, const int32_t *ids, const void *sc_in,
                     const int32_t *active, int32_t *flags, void *q, void *k, void *v, void *o,
-                    const AttnPlan &ap, void *part_o, float2 *part_ml, void *h, hipStream_t st,
-                    const Stages &sg = Stages(), const Gather &gq = Gather()) {
+                    const AttnPlan &ap, void *part_o, float2 *part_ml, float *proj_part, void *h,
+                    hipStream_t st, const Stages &sg = Stages(), const Gather &gq = Gather()) {
   const bool bf = d.dtype == DG_BF16;
   const int64_t M = (int64_t)nc * d.canvas;
   dg::QkvArgs qa{};
@@ -330,6 +354,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   qa.col0 = 0;
   qa.col1 = qa.nq + 2 * qa.nkv;
   qa.kv_row = nullptr;
+  qa.part = proj_part;
   DG_MARK(sg, DG_STAGE_QKV, 0);
   if (gq.qpos && !gq.qkv_done) {
     // k, v of every canvas row; q of the gathered rows only (compact).  A
@@ -392,6 +417,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   oa.kdim = d.n_q_heads * d.head_dim;
   oa.vocab = d.vocab;
   oa.C = gq.qpos ? gq.qn : d.canvas;
+  oa.part = proj_part;
   DG_MARK(sg, DG_STAGE_OPROJ, 0);
   DG_TRY_HIP(dg::launch_oproj(oa, bf, st), "output projection launch");
   DG_MARK(sg, DG_STAGE_OPROJ, 1);
@@ -441,7 +467,8 @@ dg_status step_core(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   sg.st = st;
   dg_status s = run_block(d, w, kv, batch, 1, canvas_ids, sc_in, active, dev_flags, at<char>(workspace, p.q),
                 at<char>(workspace, p.k), at<char>(workspace, p.v), o, p.attn,
-                at<char>(workspace, p.part_o), at<float2>(workspace, p.part_ml), h, st, sg);
+                at<char>(workspace, p.part_o), at<float2>(workspace, p.part_ml),
+                at<float>(workspace, p.proj_part), h, st, sg);
   if (s != DG_OK) return s;
 
   dg::LmheadArgs la{};
@@ -767,6 +794,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   void *o = at<char>(workspace, p.o), *h = at<char>(workspace, p.h);
   void *part_o = at<char>(workspace, p.part_o);
   float2 *part_ml = at<float2>(workspace, p.part_ml);
+  float *proj_part = at<float>(workspace, p.proj_part);
 
   dg::SlotArgs sa{};
   sa.slot_pos = slot_pos;
@@ -858,6 +886,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     qa.col0 = qa.nq;
     qa.col1 = qa.nq + 2 * qa.nkv;
     qa.kv_row = sa.kv_row_base;
+    qa.part = proj_part;
     DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "k/v projection launch");
     DG_TRY_HIP(dg::launch_kv_replicate(k, v, batch, G, d.canvas, qa.nkv, (int)tsize(d), st),
                "k/v copy launch");
@@ -871,7 +900,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     Gather gd = gq;
     gd.qkv_done = true;
     s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
-                  p.draws, part_o, part_ml, h, st, Stages(), gd);
+                  p.draws, part_o, part_ml, proj_part, h, st, Stages(), gd);
     if (s != DG_OK) return s;
     la.nrows = (int64_t)batch * G * n_slots;
     la.row_scale = rs_draw;
@@ -889,7 +918,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.off_draw = 0;
   DG_TRY_HIP(dg::launch_slot_rows(sa, st), "slot row launch");
   s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
-                part_o, part_ml, h, st, Stages(), gq);
+                part_o, part_ml, proj_part, h, st, Stages(), gq);
   if (s != DG_OK) return s;
   la.nrows = (int64_t)batch * n_slots;
   la.row_scale = row_scale;
@@ -905,7 +934,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   int32_t *row_active = at<int32_t>(workspace, p.row_active);
   DG_TRY_HIP(dg::launch_slot_draw_rows2(sa, row_active, rs_draw, st), "draw row launch");
   s = run_block(d, w, kv, batch * n_draws, n_draws, sa.draw_ids, nullptr, sa.draw_active, nullptr,
-                q, k, v, o, p.draws, part_o, part_ml, h, st, Stages(), gq);
+                q, k, v, o, p.draws, part_o, part_ml, proj_part, h, st, Stages(), gq);
   if (s != DG_OK) return s;
   la.nrows = (int64_t)batch * n_draws * n_slots;
   la.active_rows = row_active;
@@ -945,7 +974,12 @@ StagedPlan plan_staged(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   p.draws = a.take(BS * 4);
   p.status = a.take(BS * 4);
   p.pinned = a.take((size_t)B * d.canvas * 4);
+  // a stage reads any number of the slots, and the read's workspace is not
+  // monotone in the slot count (speculated draws, split-K partials): take the
+  // largest over 1..S
   p.inner_bytes = plan_slot(d, B, S, max_prompt, nd).total;
+  for (int n = 1; n < S; ++n)
+    p.inner_bytes = std::max(p.inner_bytes, plan_slot(d, B, n, max_prompt, nd).total);
   p.inner = a.take(p.inner_bytes);
   p.total = a.off;
   return p;

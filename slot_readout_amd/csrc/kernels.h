@@ -24,6 +24,9 @@ struct QkvArgs {
   int col0, col1;          // output columns [col0, col1) of [q | k | v]
   // row of k and v that input row m writes (-1: none), or null (row m)
   const int32_t *kv_row;
+  // split-K partials [proj_ksplit][M][col1 - col0] fp32, or null (no split)
+  float *part;
+  int ksplit, kchunk;      // set by the launcher
 };
 
 struct OprojArgs {
@@ -35,6 +38,9 @@ struct OprojArgs {
   const int32_t *active;
   int64_t M;
   int d, kdim, vocab, C;
+  // split-K partials [proj_ksplit][M][d] fp32, or null (no split)
+  float *part;
+  int ksplit, kchunk;      // set by the launcher
 };
 
 struct LmheadArgs {
@@ -128,6 +134,9 @@ struct CommitArgs {
   float tau;
 };
 
+// K splits of a projection of M rows x ncols outputs over K (1: none); the
+// partial buffer of a split launch holds ksplit * M * ncols floats
+int proj_ksplit(int64_t M, int64_t ncols, int K, bool bf);
 hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st);
 hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st);
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st);
