@@ -117,13 +117,13 @@ __device__ bool slot_first_one(const SlotArgs &a, int b, int s, int lane) {
 }
 
 // first read: one wave per slot; also decides which canvases need draws
-__global__ __launch_bounds__(256) void slot_first_kernel(SlotArgs a) {
+__global__ __launch_bounds__(1024) void slot_first_kernel(SlotArgs a) {
   __shared__ int any_flag;
   const int b = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   if (threadIdx.x == 0) any_flag = 0;
   __syncthreads();
-  for (int s = w; s < a.S; s += 4)
+  for (int s = w; s < a.S; s += nw)
     if (slot_first_one(a, b, s, lane) && lane == 0) any_flag = 1;
   __syncthreads();
   if (threadIdx.x == 0) a.canvas_flag[b] = any_flag;
@@ -186,14 +186,27 @@ __device__ void slot_average_one(const SlotArgs &a, int64_t bs, int lane) {
   // r is averaged directly; ln mean_d e^(lp_d) is kept as an online log-sum-exp
   // (lp can sit far below the fp32 range of e^x)
   float racc = 0.f, lm = -INFINITY, ls = 0.f;
-  for (int d = 0; d < a.n_draws; ++d) {
-    const float lp = label_logprob(a, (b * a.grp_draw + a.off_draw + d) * a.S + s, k, lane);
-    const LabelDist dd = renormalise(lp, k, lane);
-    racc += dd.r;
-    if (lane < k) {
-      const float mn = fmaxf(lm, lp);
-      ls = ls * __expf(lm - mn) + __expf(lp - mn);
-      lm = mn;
+  // the label logprobs of up to 8 draws are loaded before their reductions
+  // (one memory wait per 8 draws); the draws are still summed in order
+  constexpr int PD = 8;
+  for (int d0 = 0; d0 < a.n_draws; d0 += PD) {
+    float lpv[PD];
+#pragma unroll
+    for (int j = 0; j < PD; ++j)
+      lpv[j] = d0 + j < a.n_draws
+                   ? label_logprob(a, (b * a.grp_draw + a.off_draw + d0 + j) * a.S + s, k, lane)
+                   : 0.f;
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      if (d0 + j >= a.n_draws) break;
+      const float lp = lpv[j];
+      const LabelDist dd = renormalise(lp, k, lane);
+      racc += dd.r;
+      if (lane < k) {
+        const float mn = fmaxf(lm, lp);
+        ls = ls * __expf(lm - mn) + __expf(lp - mn);
+        lm = mn;
+      }
     }
   }
   LabelDist fin;
@@ -221,19 +234,19 @@ __global__ __launch_bounds__(256) void slot_average_kernel(SlotArgs a) {
 // The rest of a one-pass read for canvas b in one workgroup: first read of
 // every slot, the canvas's re-read flag, the status of slots whose noise id is
 // out of range (re-read canvases only), and the average of the flagged slots.
-__global__ __launch_bounds__(256) void slot_finish_kernel(SlotArgs a) {
+__global__ __launch_bounds__(1024) void slot_finish_kernel(SlotArgs a) {
   __shared__ int any_flag;
   const int b = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   if (threadIdx.x == 0) any_flag = 0;
   __syncthreads();
-  for (int s = w; s < a.S; s += 4)
+  for (int s = w; s < a.S; s += nw)
     if (slot_first_one(a, b, s, lane) && lane == 0) any_flag = 1;
   __syncthreads();
   const bool flagged = any_flag != 0;
   if (threadIdx.x == 0) a.canvas_flag[b] = flagged ? 1 : 0;
   if (!flagged) return;
-  for (int s = threadIdx.x; s < a.S; s += 256) {
+  for (int s = threadIdx.x; s < a.S; s += blockDim.x) {
     const int64_t bs = (int64_t)b * a.S + s;
     if (a.status[bs] != DG_SLOT_OK) continue;
     for (int d = 0; d < a.n_draws; ++d) {
@@ -241,7 +254,7 @@ __global__ __launch_bounds__(256) void slot_finish_kernel(SlotArgs a) {
       if (nid < 0 || nid >= a.V) { a.status[bs] = DG_SLOT_BAD_NOISE; break; }
     }
   }
-  for (int s = w; s < a.S; s += 4) {
+  for (int s = w; s < a.S; s += nw) {
     const int64_t bs = (int64_t)b * a.S + s;
     if (a.canvas_flag[a.B + bs]) slot_average_one(a, bs, lane);
   }
@@ -328,9 +341,12 @@ hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hi
   return hipGetLastError();
 }
 
+// one wave per slot of a canvas, 1 to 16 waves
+static unsigned slot_wave_threads(int S) { return 64u * (unsigned)(S < 1 ? 1 : S > 16 ? 16 : S); }
+
 hipError_t launch_slot_finish(const SlotArgs &a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(slot_finish_kernel, dim3((unsigned)a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(slot_finish_kernel, dim3((unsigned)a.B), dim3(slot_wave_threads(a.S)), 0, st, a);
   return hipGetLastError();
 }
 
@@ -343,7 +359,7 @@ hipError_t launch_slot_rows(const SlotArgs &a, hipStream_t st) {
 
 hipError_t launch_slot_first(const SlotArgs &a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(slot_first_kernel, dim3((unsigned)a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(slot_first_kernel, dim3((unsigned)a.B), dim3(slot_wave_threads(a.S)), 0, st, a);
   return hipGetLastError();
 }
 
