@@ -190,3 +190,25 @@ def test_staged_read_rejects_bad_stage_arrays_before_any_launch():
     assert call([0] * 65, [-1] * 65, [0] * 65) == I           # too many slots
     # a valid schema gets past these checks (and fails on the tiny workspace)
     assert call([0, 1], [-1, 0], [0, 3]) == dg.DG_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("dtype_name", ["DG_BF16", "DG_F32"])
+def test_staged_workspace_covers_every_stage_size(dtype_name):
+    """A two-stage read calls the one-pass read once per stage with that stage's
+    slot count, inside its own workspace.  The one-pass read's workspace is not
+    monotone in the slot count (speculated draws, split-K partials of the
+    projections), so the staged workspace must hold the largest of 1..S."""
+    dg = _lib_or_skip()
+    dt = getattr(dg, dtype_name)
+    cases = [
+        dg.make_dims(2816, 8, 2, 512, 262144, 256, 128, 262143, dt),   # the headline model
+        dg.make_dims(2816, 8, 2, 512, 4096, 256, 128, 4095, dt),       # wide heads, small vocabulary
+        dg.make_dims(256, 4, 4, 64, 2048, 256, 16, 2047, dt),
+    ]
+    if dt == dg.DG_F32:
+        cases = cases[2:]   # 512-wide heads are bf16 only
+    for d in cases:
+        for B, S, P, nd in [(1, 8, 2048, 4), (4, 12, 512, 3), (2, 26, 4096, 5)]:
+            staged = dg.dg_slot_read_staged_workspace(d, B, S, P, nd)
+            one = max(dg.dg_slot_read_workspace(d, B, n, P, nd) for n in range(1, S + 1))
+            assert staged > one > 0, (B, S, P, nd)
