@@ -200,3 +200,33 @@ def test_slot_read_many_slots_one_pass(torch_cuda):
     ref = oracle.slot_read(inp, row_scale=rs)
     assert ref["status"][0, 7] == oracle.SLOT_BAD_POS
     _check_slots(g, ref, inp, "f32", "many slots one pass")
+
+
+def test_slot_read_wide_heads_mixed_rereads(torch_cuda):
+    """Three canvases at d 2816 with 512-wide heads, read in two passes, where
+    only canvas 0 re-reads: its slots offer 26 labels (first-read entropy near
+    ln 26) and the others' offer 2 (near ln 2), with the threshold between.  The
+    draw pass then projects 3 x n_draws x 8 slot rows, so its q and output
+    projections split K, and the per-canvas draw flags skip the rows of the
+    canvases that do not re-read in both the split GEMMs and their reduces."""
+    cfg = config("bf16_step", vocab=4096, mask_id=4095)
+    inp = make_inputs(cfg, batch=3, prompt_override=("fixed", 200))
+    S = inp["slot_pos"].shape[1]
+    assert not _one_pass_draws(inp["dims"], 3, S, inp["n_draws"], int(inp["max_prompt"]))
+    rng = np.random.default_rng(11)
+    lab = np.full_like(inp["label_ids"], -1)
+    for s in range(S):
+        lab[0, s] = rng.choice(4095, size=26, replace=False)
+    lab[1:, :, :2] = inp["label_ids"][1:, :, :2]
+    nl = np.full_like(inp["n_labels"], 2)
+    nl[0] = 26
+    inp["label_ids"], inp["n_labels"] = lab, nl
+    inp["entropy_threshold"] = 2.0
+    ref = oracle.slot_read(inp)
+    ok = ref["status"] == oracle.SLOT_OK
+    assert ok.all()
+    fe = ref["first_entropy"]
+    assert fe[0].min() > 2.5 and fe[1:].max() < 1.0, fe
+    assert (ref["draws_used"][0] == inp["n_draws"]).all() and (ref["draws_used"][1:] == 1).all()
+    g = _read(inp)
+    _check_slots(g, ref, inp, "bf16", "wide heads mixed re-reads")
