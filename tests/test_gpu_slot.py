@@ -230,3 +230,22 @@ def test_slot_read_wide_heads_mixed_rereads(torch_cuda):
     assert (ref["draws_used"][0] == inp["n_draws"]).all() and (ref["draws_used"][1:] == 1).all()
     g = _read(inp)
     _check_slots(g, ref, inp, "bf16", "wide heads mixed re-reads")
+
+
+@pytest.mark.parametrize("name,n_kv,n_slots,batch", [
+    ("tiny_f32", 1, 8, 1),      # 4 q heads x 8 slot rows = 32 columns of one query tile
+    ("tiny_f32", 1, 30, 1),     # 120 columns: both 16-column blocks of every wave
+    ("tiny_f32", 1, 40, 1),     # 160 columns: too many to pack, one tile per q head
+    ("reads512", 2, 4, 16),     # bf16, 2 q heads per kv head
+])
+def test_slot_read_gqa_packed_heads(torch_cuda, name, n_kv, n_slots, batch):
+    """Gathered slot queries with grouped kv heads at head_dim 64: when the q heads
+    of a kv head fit one query tile together, one workgroup serves them all
+    (column c is head c / rows, row c % rows); otherwise each q head has its own."""
+    inp = make_inputs(config(name, n_kv_heads=n_kv, n_slots=n_slots), batch=batch,
+                      prompt_override=("fixed", 100))
+    dt = inp["dims"].dtype
+    g = _read(inp)
+    ref = oracle.slot_read(inp)
+    frac = _check_slots(g, ref, inp, dt, f"gqa {name} kv{n_kv} S{n_slots}")
+    assert frac > 0.5
