@@ -214,3 +214,18 @@ def test_step_bf16_partial_row_block(torch_cuda):
     torch_cuda.cuda.synchronize()
     refs = oracle.denoise_step(inp, need_logits=True)
     _check_step(inp, out, refs, "bf16", label="ragged 2x200")
+
+
+@pytest.mark.parametrize("name,n_kv,B", [("tiny_f32", 1, 1), ("tiny_f32", 2, 2), ("ragged32", 2, 3)])
+def test_step_gqa_head_dim_64(torch_cuda, name, n_kv, B):
+    """Grouped kv heads at head_dim 64 (4 q heads over 1 or 2 kv heads), every
+    canvas position queried, in fp32 and bf16 (ragged prompts for bf16)."""
+    import torch
+    prompt = ("uniform", 0, 300) if name == "ragged32" else ("fixed", 128)
+    inp = make_inputs(config(name, n_kv_heads=n_kv), batch=B, prompt_override=prompt)
+    dev = _problem(inp)
+    out = dev.step(debug=True)
+    torch.cuda.synchronize()
+    assert int(out["flags"].item()) == 0
+    refs = oracle.denoise_step(inp, need_logits=True)
+    _check_step(inp, out, refs, inp["dims"].dtype, label=f"gqa {name} kv{n_kv} B{B}")
