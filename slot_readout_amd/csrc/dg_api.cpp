@@ -865,8 +865,9 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     sa.off_draw = 1;
     DG_TRY_HIP(dg::launch_slot_spec_build(sa, sa.draw_ids, rs_draw, st), "read canvas launch");
     // The draws differ from canvas b only at the slot positions: k, v of
-    // canvas b are projected once, copied into its draws, and the draws' slot
-    // rows are projected with the q of every slot row.
+    // canvas b are projected once and written into its draws as well, then the
+    // draws' slot rows are projected (over those copies) with the q of every
+    // slot row.
     dg::QkvArgs qa{};
     qa.ids = canvas_ids;
     qa.embed = w->embed;
@@ -887,10 +888,10 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     qa.col1 = qa.nq + 2 * qa.nkv;
     qa.kv_row = sa.kv_row_base;
     qa.part = proj_part;
+    qa.kv_copies = G - 1;   // the draws' copies of canvas b's k, v
     DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "k/v projection launch");
-    DG_TRY_HIP(dg::launch_kv_replicate(k, v, batch, G, d.canvas, qa.nkv, (int)tsize(d), st),
-               "k/v copy launch");
     dg::QkvArgs qg = qa;
+    qg.kv_copies = 0;
     qg.ids = sa.qids;
     qg.M = (int64_t)batch * G * n_slots;
     qg.C = n_slots;

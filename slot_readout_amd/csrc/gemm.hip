@@ -405,11 +405,14 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(QkvArgs a) {
   else { base = static_cast<T *>(a.v); ld = a.nkv; c = col - a.nq - a.nkv; }
   const int64_t orow = col >= a.nq && a.kv_row ? (int64_t)a.kv_row[row] : row;
   if (orow < 0) return;
-  T *o = base + orow * ld + c;
-  o[0] = from_f<T>(s.x * sc);
-  o[1] = from_f<T>(s.y * sc);
-  o[2] = from_f<T>(s.z * sc);
-  o[3] = from_f<T>(s.w * sc);
+  const int ncp = col >= a.nq ? a.kv_copies : 0;
+  for (int cp = 0; cp <= ncp; ++cp) {
+    T *o = base + (orow + (int64_t)cp * a.C) * ld + c;
+    o[0] = from_f<T>(s.x * sc);
+    o[1] = from_f<T>(s.y * sc);
+    o[2] = from_f<T>(s.z * sc);
+    o[3] = from_f<T>(s.w * sc);
+  }
 }
 
 // Split-K reduce of the output projection: h = x + sum of partials, with x
@@ -507,7 +510,11 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
         const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
         if (row >= a.M) continue;
         const int64_t orow = remap ? (int64_t)a.kv_row[row] : row;
-        if (orow >= 0) base[orow * ld + c] = from_f<T>(acc[i][j][r] * sc);
+        if (orow < 0) continue;
+        const T val = from_f<T>(acc[i][j][r] * sc);
+        base[orow * ld + c] = val;
+        if (col >= nq)
+          for (int cp = 1; cp <= a.kv_copies; ++cp) base[(orow + (int64_t)cp * a.C) * ld + c] = val;
       }
   }
 }

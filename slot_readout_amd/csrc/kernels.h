@@ -27,6 +27,9 @@ struct QkvArgs {
   // split-K partials [proj_ksplit][M][col1 - col0] fp32, or null (no split)
   float *part;
   int ksplit, kchunk;      // set by the launcher
+  // each k, v row written is also written kv_copies more times, C, 2C, ...
+  // rows further on (the canvases that follow, holding copies of it)
+  int kv_copies;
 };
 
 struct OprojArgs {
@@ -245,9 +248,5 @@ hipError_t launch_staged_gather(const StagedArgs &a, hipStream_t st);
 hipError_t launch_staged_scatter(const StagedArgs &a, hipStream_t st);
 // pinned = canvas with each stage slot read without error holding its best label
 hipError_t launch_staged_pin(const StagedArgs &a, hipStream_t st);
-
-// copies k and v of canvas g*G (every position) into canvases g*G + 1 .. g*G + G-1
-hipError_t launch_kv_replicate(void *k, void *v, int groups, int G, int C, int nkv, int elem_bytes,
-                               hipStream_t st);
 
 }  // namespace dg

@@ -310,29 +310,6 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
       a.kv_row_base[(int64_t)b * a.C + i] = (int32_t)((int64_t)cb * a.C + i);
 }
 
-// k, v of canvas g*G into canvases g*G + 1 .. g*G + G-1 (16-byte chunks)
-__global__ __launch_bounds__(256) void kv_replicate_kernel(uint4 *k, uint4 *v, int G,
-                                                           int64_t chunks) {
-  const int g = blockIdx.y, j = blockIdx.z + 1;
-  const uint4 *ks = k + (int64_t)g * G * chunks, *vs = v + (int64_t)g * G * chunks;
-  uint4 *kd = k + ((int64_t)g * G + j) * chunks, *vd = v + ((int64_t)g * G + j) * chunks;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
-  }
-}
-
-hipError_t launch_kv_replicate(void *k, void *v, int groups, int G, int C, int nkv, int elem_bytes,
-                               hipStream_t st) {
-  if (groups <= 0 || G <= 1) return hipSuccess;
-  const int64_t bytes = (int64_t)C * nkv * elem_bytes;
-  if (bytes % 16) return hipErrorInvalidValue;
-  const int64_t chunks = bytes / 16;
-  const unsigned bx = (unsigned)(cdiv64(chunks, 256) < 64 ? cdiv64(chunks, 256) : 64);
-  hipLaunchKernelGGL(kv_replicate_kernel, dim3(bx, (unsigned)groups, (unsigned)(G - 1)), dim3(256), 0,
-                     st, static_cast<uint4 *>(k), static_cast<uint4 *>(v), G, chunks);
-  return hipGetLastError();
-}
 
 hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st) {
   const int64_t n = (int64_t)a.B * (a.n_draws + 1);
