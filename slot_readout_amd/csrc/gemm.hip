@@ -331,9 +331,12 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
 }
 
 // Self-conditioning GEMM: d tiles of 256 and about one workgroup per CU.
-// Keeping each vocabulary range's tiles on one XCD (kScGroup) cuts the p~
-// re-reads that reach HBM by ~40% but leaves CUs idle at d = 2816 (11 tiles
-// per range), and measured slower (555-618 us against 481 us), so it is off.
+// Keeping whole vocabulary ranges on one XCD (kScGroup, register-staged
+// kernel) cuts the p~ re-reads that reach HBM by ~40% but leaves CUs idle at
+// d = 2816 (11 tiles per range), and measured slower (555-618 us against
+// 481 us), so it is off.  The direct-to-LDS kernel instead deals consecutive
+// (range, tile) items to each XCD, which keeps a range's tiles on one or two
+// XCDs with every CU busy.
 constexpr int kScTileD = 256;
 constexpr bool kScGroup = false;
 
@@ -1003,8 +1006,14 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void scgemm_dma_kernel(ScArgs a) {
   char *st[NS] = {s0, s1, s2, s3};
   const int ntn = a.d / BN;
   const int nt = ntn * (int)cdiv64(a.M, BM);
-  if ((int)blockIdx.x >= a.ksplit * nt) return;
-  const int z = blockIdx.x / nt, t = blockIdx.x % nt;
+  // Work item (vocabulary range z, output tile t), in that order, and XCD x
+  // (workgroups are dealt to the 8 XCDs round-robin) takes the consecutive items
+  // [x * per, (x + 1) * per): the tiles of one range share its p~ in one L2
+  // instead of fetching it on every XCD, and no CU is left idle.
+  const int total = a.ksplit * nt, per = (total + 7) / 8;
+  const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (item >= total) return;
+  const int z = item / nt, t = item % nt;
   const int n0 = (t % ntn) * BN;
   const int64_t m0 = (int64_t)(t / ntn) * BM;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
@@ -1249,7 +1258,9 @@ hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {
     // vocabulary tiles a split can span: its 64-entry steps, rounded up, plus one
     const int64_t tiles = (int64_t)(a.vocab / 64 + a.ksplit - 1) / a.ksplit * 64 / VTILE + 2;
     if (a.ptilde_blocked && a.embed_t_tiled && a.d % 256 == 0 && tiles <= kScDmaTiles)
-      hipLaunchKernelGGL((scgemm_dma_kernel<4, 2>), grid, dim3(8 * WAVE), 0, st, a);
+      hipLaunchKernelGGL((scgemm_dma_kernel<4, 2>),
+                         dim3((unsigned)(8 * cdiv64(a.ksplit * cdiv64(a.d, 256) * cdiv64(a.M, 256), 8))),
+                         dim3(8 * WAVE), 0, st, a);
     else if (a.ptilde_blocked && a.embed_t_tiled)
       hipLaunchKernelGGL((scgemm_kernel<bf16, 256, kScTileD, 4, 2, 1, 64, true, true>), grid, dim3(8 * WAVE), 0, st, a);
     else if (a.ptilde_blocked)
