@@ -606,7 +606,7 @@ static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               "query tile sizes");
 
 void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
-               int max_len, int *nsplit, int *chunk) {
+               int max_len, int *nsplit, int *chunk, int *nsplit_bound) {
   const int nq = attn_query_tile(head_dim);
   const int nk = head_dim == 512 ? 32 : 64;
   const int64_t base = attn_packed(qn, gathered, Hq, Hkv, head_dim)
@@ -624,6 +624,9 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
     if (ns > maxs) ns = (int)maxs;
     if (ns < 1) ns = 1;
   }
+  // ns is non-decreasing in max_len; the rounded count below never exceeds it,
+  // so ns bounds the splits of every prompt up to max_len (workspace sizing)
+  if (nsplit_bound) *nsplit_bound = ns;
   const int ck = (int)(cdiv64(cdiv64(span, ns), nk) * nk);
   ns = (int)cdiv64(span, ck);
   if (ns < 1) ns = 1;

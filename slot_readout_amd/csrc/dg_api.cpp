@@ -102,6 +102,11 @@ dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const
   return DG_OK;
 }
 
+// A window of C - 1 or more already reaches every canvas key, so the kernels
+// take min(W, C - 1): the same keys, and no int overflow in the window bounds
+// for a W near INT_MAX (a natural way to ask for full attention).
+int window_of(const dg_dims &d) { return d.window < d.canvas - 1 ? d.window : d.canvas - 1; }
+
 struct Arena {
   size_t off = 0;
   size_t take(size_t bytes) {
@@ -121,12 +126,16 @@ AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1) {
   AttnPlan p;
   const bool gathered = qn >= 0;
   if (!gathered) qn = d.canvas;
-  dg::attn_plan(nc, d.canvas, qn, gathered, d.n_q_heads, d.n_kv_heads, d.window, d.head_dim,
-                max_prompt, &p.nsplit, &p.chunk);
-  if (p.nsplit > 1) {
+  int bound = 1;
+  dg::attn_plan(nc, d.canvas, qn, gathered, d.n_q_heads, d.n_kv_heads, window_of(d), d.head_dim,
+                max_prompt, &p.nsplit, &p.chunk, &bound);
+  // partials sized by the bound, so that a workspace planned for max_prompt
+  // also holds the partials of every shorter prompt (the rounded split count
+  // is not monotone in the prompt length)
+  if (bound > 1) {
     const size_t R = (size_t)nc * d.n_q_heads * qn;
-    p.part_o = (size_t)p.nsplit * R * d.head_dim * tsize(d);
-    p.part_ml = (size_t)p.nsplit * R * sizeof(float2);
+    p.part_o = (size_t)bound * R * d.head_dim * tsize(d);
+    p.part_ml = (size_t)bound * R * sizeof(float2);
   }
   return p;
 }
@@ -227,9 +236,10 @@ bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt) {
 // A read needs the hidden state only at its slot rows: the k/v projection runs
 // over every canvas row (all keys); the q projection, attention and the output
 // projection over the slot rows alone (gathered queries, compact rows).
-SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
+// spec: -1 decides by speculate_draws, 0 / 1 forces the two-pass / one-pass order
+SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int spec = -1) {
   SlotPlan p{};
-  p.spec = speculate_draws(d, B, S, nd, max_prompt);
+  p.spec = spec < 0 ? speculate_draws(d, B, S, nd, max_prompt) : spec != 0;
   const int ncmax = p.spec ? B * (nd + 1) : (nd > 1 ? B * nd : B);
   const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
@@ -277,6 +287,18 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   p.rs_draw = a.take(nrows * sizeof(float));
   p.total = a.off;
   return p;
+}
+
+// Workspace bytes that hold a read of any prompt length up to max_prompt.
+// The one-pass order needs more than the two-pass one, and is chosen for
+// shorter prompts (the draws' forward pass grows with the prompt), so a read
+// of a shorter prompt may take the one-pass order where max_prompt's does
+// not: both are then covered.  Each order's size is non-decreasing in the
+// prompt length.
+size_t slot_ws_bound(const dg_dims &d, int B, int S, int max_prompt, int nd) {
+  size_t t = plan_slot(d, B, S, max_prompt, nd).total;
+  if (speculate_draws(d, B, S, nd, 0)) t = std::max(t, plan_slot(d, B, S, max_prompt, nd, 1).total);
+  return t;
 }
 
 // records the caller's stage events (if any) around each stage of a call
@@ -395,7 +417,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.C = d.canvas;
   aa.Hq = d.n_q_heads;
   aa.Hkv = d.n_kv_heads;
-  aa.W = d.window;
+  aa.W = window_of(d);
   aa.max_len = kv->max_len;
   aa.nsplit = ap.nsplit;
   aa.chunk = ap.chunk;
@@ -539,7 +561,7 @@ const char *dg_status_string(dg_status s) {
   switch (s) {
     case DG_OK: return "ok";
     case DG_ERR_INVALID_ARG: return "invalid argument";
-    case DG_ERR_TOO_MANY_LABELS: return "too many labels (at most 26 alternatives)";
+    case DG_ERR_TOO_MANY_LABELS: return "too many labels (more than the 26 single-token labels A..Z)";
     case DG_ERR_UNSUPPORTED: return "unsupported configuration";
     case DG_ERR_WORKSPACE: return "workspace too small";
     case DG_ERR_HIP: return "HIP runtime error";
@@ -554,7 +576,7 @@ const char *dg_version(void) { return "dg 0.1.0 (gfx950)"; }
 dg_status dg_check_label_count(int32_t n) {
   if (n < 1) return fail(DG_ERR_INVALID_ARG, "a question needs at least one alternative (got %d)", n);
   if (n > DG_MAX_LABELS)
-    return fail(DG_ERR_TOO_MANY_LABELS, "at most %d alternatives (got %d)", DG_MAX_LABELS, n);
+    return fail(DG_ERR_TOO_MANY_LABELS, "too many labels: %d > %d", n, DG_MAX_LABELS);
   return ok();
 }
 
@@ -762,7 +784,7 @@ size_t dg_slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slot
   if (check_dims(dims) != DG_OK || batch < 0 || n_slots < 0 || max_prompt < 0 || n_draws < 1 ||
       n_draws > 16)
     return 0;
-  return plan_slot(*dims, batch, n_slots, max_prompt, n_draws).total;
+  return slot_ws_bound(*dims, batch, n_slots, max_prompt, n_draws);
 }
 
 dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
@@ -978,9 +1000,9 @@ StagedPlan plan_staged(const dg_dims &d, int B, int S, int max_prompt, int nd) {
   // a stage reads any number of the slots, and the read's workspace is not
   // monotone in the slot count (speculated draws, split-K partials): take the
   // largest over 1..S
-  p.inner_bytes = plan_slot(d, B, S, max_prompt, nd).total;
+  p.inner_bytes = slot_ws_bound(d, B, S, max_prompt, nd);
   for (int n = 1; n < S; ++n)
-    p.inner_bytes = std::max(p.inner_bytes, plan_slot(d, B, n, max_prompt, nd).total);
+    p.inner_bytes = std::max(p.inner_bytes, slot_ws_bound(d, B, n, max_prompt, nd));
   p.inner = a.take(p.inner_bytes);
   p.total = a.off;
   return p;

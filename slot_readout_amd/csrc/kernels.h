@@ -152,9 +152,12 @@ int attn_query_tile(int head_dim);
 // whether gathered queries pack the G query heads of a kv head into one tile
 bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim);
 // qn queries per canvas; gathered: queries at arbitrary positions (every
-// canvas key is a candidate) instead of consecutive ones
+// canvas key is a candidate) instead of consecutive ones.  nsplit_bound (may
+// be null) receives a split count that is >= nsplit for every prompt length
+// up to max_len and non-decreasing in max_len: partial buffers sized with it
+// fit any shorter prompt.
 void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
-               int max_len, int *nsplit, int *chunk);
+               int max_len, int *nsplit, int *chunk, int *nsplit_bound);
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);

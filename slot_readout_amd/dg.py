@@ -296,6 +296,6 @@ def check_alternatives(question: str, alternatives) -> None:
     n = len(alternatives)
     s = dg_check_label_count(n)
     if s == DG_ERR_TOO_MANY_LABELS:
-        raise ValueError(f"question '{question}': at most {DG_MAX_LABELS} alternatives")
+        raise ValueError(f"too many labels for '{question}': {n} > {DG_MAX_LABELS}")
     if s != DG_OK:
         raise ValueError(f"question '{question}': needs at least one alternative")
