@@ -74,8 +74,15 @@ def embed_input(E, ids, sc_in=None):
     24-ai.news, "Mechanism for deciding completed tokens": the
     self-conditioning vector of the previous step is an additional model
     input; here it is added to the token embedding (absent = 0).
+    An id outside [0, V) names no row; the pages are silent on such input,
+    and the reading taken is that it embeds as a zero row (the library flags
+    it and does the same).
     """
-    x = np.asarray(E, dtype=F64)[np.asarray(ids)]
+    E = np.asarray(E, dtype=F64)
+    ids = np.asarray(ids)
+    ok = (ids >= 0) & (ids < E.shape[0])
+    x = np.zeros(ids.shape + (E.shape[1],), dtype=F64)
+    x[ok] = E[ids[ok]]
     if sc_in is not None:
         x = x + np.asarray(sc_in, dtype=F64)
     return x

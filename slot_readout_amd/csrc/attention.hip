@@ -20,6 +20,8 @@
 // coalesced loads; the V^T fragments come from transposing LDS reads
 // (ds_read_b64_tr_b16).  V carries an extra column of ones, so the same MFMA
 // also accumulates the softmax denominator sum_key p.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -95,7 +97,11 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
   return bad;
 }
 
-template <typename T, int HD>
+// PREC (bf16 only): the probabilities enter the PV product as two bf16 terms,
+// p = hi + lo with hi = bf16(p) and lo = bf16(p - hi) (one more MFMA per V
+// fragment), and O, its split partials and the output are fp32.  The result
+// then carries the rounding of the stored q, k, v only, not that of p and o.
+template <typename T, int HD, bool PREC = false>
 __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
@@ -107,6 +113,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   constexpr int NQ = NW * QB * 16;
   constexpr int VEC = 16 / sizeof(T);
   constexpr bool TR = sizeof(T) == 2;
+  static_assert(!PREC || TR, "split probabilities: bf16 storage");
+  // output / partial type
+  using TO = typename std::conditional<PREC, float, T>::type;
   // bf16 rows of K and V are HD + 16 elements apart: with that stride both the
   // 16-byte K fragment reads and the transposing V reads are free of LDS bank
   // conflicts (measured on gfx950; a 16-byte pad leaves 2-way conflicts)
@@ -416,11 +425,15 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
       for (int t = 0; t < NK / 32; ++t)
 #pragma unroll
         for (int jb = 0; jb < QB; ++jb) {
-          frag pf;
+          frag pf, pl;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             pf[j] = (bf16)sacc[2 * t][jb][j];
             pf[4 + j] = (bf16)sacc[2 * t + 1][jb][j];
+            if constexpr (PREC) {
+              pl[j] = (bf16)(sacc[2 * t][jb][j] - (float)pf[j]);
+              pl[4 + j] = (bf16)(sacc[2 * t + 1][jb][j] - (float)pf[4 + j]);
+            }
           }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
@@ -435,6 +448,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
             __builtin_memcpy(&af, &lo4, 8);
             __builtin_memcpy(reinterpret_cast<char *>(&af) + 8, &hi4, 8);
             oacc[rb][jb] = MF::mma(af, pf, oacc[rb][jb]);
+            if constexpr (PREC) oacc[rb][jb] = MF::mma(af, pl, oacc[rb][jb]);
           }
         }
     } else {
@@ -497,16 +511,16 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
     if (qi >= QN) continue;
     if (a.nsplit == 1) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      T *o = static_cast<T *>(a.o) + (((int64_t)cb * QN + qi) * a.Hq + hq) * HD;
+      TO *o = static_cast<TO *>(a.o) + (((int64_t)cb * QN + qi) * a.Hq + hq) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<T>(oacc[rb][jb][r] * inv);
+        for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<TO>(oacc[rb][jb][r] * inv);
     } else {
       const int64_t row = ((int64_t)cb * a.Hq + hq) * QN + qi;
-      T *po = static_cast<T *>(a.part_o) + ((int64_t)s * R + row) * HD;
+      TO *po = static_cast<TO *>(a.part_o) + ((int64_t)s * R + row) * HD;
 #pragma unroll
-      for (int rb = 0; rb < HD / 16; ++rb) store4v<T>(po + rb * 16 + grp * 4, oacc[rb][jb]);
+      for (int rb = 0; rb < HD / 16; ++rb) store4v<TO>(po + rb * 16 + grp * 4, oacc[rb][jb]);
       if (grp == 0) a.part_ml[(int64_t)s * R + row] = make_float2(mrun[jb], L);
     }
   }
@@ -518,8 +532,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 // partials.  For HD = 64 a split's row is 16 float4 chunks, so the wave reads
 // four splits per load (lane group g = lane / 16 takes splits g, g+4, ...) and
 // the groups are added by a fixed butterfly; wider heads take one split per load.
-template <typename T, int HD>
+template <typename T, int HD, bool PREC = false>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  using TO = typename std::conditional<PREC, float, T>::type;   // partial / output type
   constexpr int C4 = HD / 4;                     // float4 chunks per row
   constexpr int SG = C4 >= 64 ? 1 : 64 / C4;     // splits read side by side
   constexpr int CPL = C4 >= 64 ? C4 / 64 : 1;    // chunks per lane
@@ -542,7 +557,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int64_t nk = plen + (hi - lo);
   const int ns = (int)(cdiv64(nk, a.chunk) < a.nsplit ? cdiv64(nk, a.chunk) : a.nsplit);
   const float2 *ml = a.part_ml + row;
-  const T *po = static_cast<const T *>(a.part_o) + (row * C4 + c0) * 4;
+  const TO *po = static_cast<const TO *>(a.part_o) + (row * C4 + c0) * 4;
   const int64_t sstride = R * C4 * 4;   // elements between splits
 
   float M = -INFINITY;
@@ -562,7 +577,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       L += v.y * w;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float4 o = load4v<T>(po + s * sstride + 256 * c);
+        const float4 o = load4v<TO>(po + s * sstride + 256 * c);
         acc[c].x += w * o.x; acc[c].y += w * o.y; acc[c].z += w * o.z; acc[c].w += w * o.w;
       }
     }
@@ -584,14 +599,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
   if (g != 0) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T *o = static_cast<T *>(a.o) + ((cb * QN + qi) * a.Hq + h) * HD;
+  TO *o = static_cast<TO *>(a.o) + ((cb * QN + qi) * a.Hq + h) * HD;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int d = 4 * (c0 + 64 * c);
-    o[d + 0] = from_f<T>(acc[c].x * inv);
-    o[d + 1] = from_f<T>(acc[c].y * inv);
-    o[d + 2] = from_f<T>(acc[c].z * inv);
-    o[d + 3] = from_f<T>(acc[c].w * inv);
+    o[d + 0] = from_f<TO>(acc[c].x * inv);
+    o[d + 1] = from_f<TO>(acc[c].y * inv);
+    o[d + 2] = from_f<TO>(acc[c].z * inv);
+    o[d + 3] = from_f<TO>(acc[c].w * inv);
   }
 }
 
@@ -634,7 +649,7 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
   *chunk = ck;
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool PREC>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NW = AttnShape<T, HD>::NW;
   constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
@@ -643,18 +658,21 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   AttnArgs b = a;
   b.packed = attn_packed(QN, a.qpos != nullptr, a.Hq, a.Hkv, HD) ? 1 : 0;
   const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, b.packed ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
-  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, dim3(64 * NW), 0, st, b);
+  hipLaunchKernelGGL((attn_kernel<T, HD, PREC>), grid, dim3(64 * NW), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD, PREC>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st) {
-  if (bf && head_dim == 64) return launch_attn_t<bf16, 64>(a, st);
-  if (bf && head_dim == 512) return launch_attn_t<bf16, 512>(a, st);
-  if (!bf && head_dim == 64) return launch_attn_t<float, 64>(a, st);
+  if (a.prec && !bf) return hipErrorInvalidValue;
+  if (bf && head_dim == 64)
+    return a.prec ? launch_attn_t<bf16, 64, true>(a, st) : launch_attn_t<bf16, 64, false>(a, st);
+  if (bf && head_dim == 512)
+    return a.prec ? launch_attn_t<bf16, 512, true>(a, st) : launch_attn_t<bf16, 512, false>(a, st);
+  if (!bf && head_dim == 64) return launch_attn_t<float, 64, false>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -121,8 +121,9 @@ struct AttnPlan {
   size_t part_o = 0, part_ml = 0;
 };
 
-// qn queries per canvas: every position, or qn gathered ones
-AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1) {
+// qn queries per canvas: every position, or qn gathered ones; prec: fp32
+// partials (the split-probability attention of slot reads)
+AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1, bool prec = false) {
   AttnPlan p;
   const bool gathered = qn >= 0;
   if (!gathered) qn = d.canvas;
@@ -134,7 +135,7 @@ AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1) {
   // is not monotone in the prompt length)
   if (bound > 1) {
     const size_t R = (size_t)nc * d.n_q_heads * qn;
-    p.part_o = (size_t)bound * R * d.head_dim * tsize(d);
+    p.part_o = (size_t)bound * R * d.head_dim * (prec ? sizeof(float) : tsize(d));
     p.part_ml = (size_t)bound * R * sizeof(float2);
   }
   return p;
@@ -210,7 +211,7 @@ struct SlotPlan {
   size_t q, k, v, o, part_o, part_ml, proj_part, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
       rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, total;
   AttnPlan first, draws;
-  bool spec;
+  bool spec, prec;
 };
 
 // Whether the draws are computed for every canvas in the first read's pass.
@@ -240,6 +241,10 @@ bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt) {
 SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int spec = -1) {
   SlotPlan p{};
   p.spec = spec < 0 ? speculate_draws(d, B, S, nd, max_prompt) : spec != 0;
+  // bf16 slot rows carry the attention output in fp32 and the hidden state
+  // as bf16 hi | lo halves (see read_prec)
+  const bool prec = d.dtype == DG_BF16;
+  p.prec = prec;
   const int ncmax = p.spec ? B * (nd + 1) : (nd > 1 ? B * nd : B);
   const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
@@ -249,9 +254,9 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   p.q = a.take(nrows * nq * ts);
   p.k = a.take(M * nkv * ts);
   p.v = a.take(M * nkv * ts);
-  p.o = a.take(nrows * nq * ts);
-  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt, S);
-  p.draws = plan_attention(d, ncmax, max_prompt, S);
+  p.o = a.take(nrows * nq * (prec ? sizeof(float) : ts));
+  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt, S, prec);
+  p.draws = plan_attention(d, ncmax, max_prompt, S, prec);
   const size_t po = p.first.part_o > p.draws.part_o ? p.first.part_o : p.draws.part_o;
   const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
   p.part_o = a.take(po);
@@ -267,11 +272,11 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
     for (int64_t m : q_rows) {
       pp = std::max(pp, proj_part_bytes(d, m, nq, d.d_model));
       pp = std::max(pp, proj_part_bytes(d, m, nq + 2 * nkv, d.d_model));
-      pp = std::max(pp, proj_part_bytes(d, m, d.d_model, (int)nq));
+      pp = std::max(pp, proj_part_bytes(d, m, d.d_model, (int)(prec ? 2 * nq : nq)));
     }
     p.proj_part = a.take(pp);
   }
-  p.h = a.take(nrows * d.d_model * ts);
+  p.h = a.take(nrows * d.d_model * ts * (prec ? 2 : 1));
   p.rows = a.take(nrows * sizeof(int32_t));
   p.qpos = a.take(nrows * sizeof(int32_t));
   p.qids = a.take(nrows * sizeof(int32_t));
@@ -344,6 +349,13 @@ struct Gather {
   const int32_t *qpos = nullptr, *qids = nullptr;
   int qn = 0;
   bool qkv_done = false;   // q (compact), k and v are already projected
+  // Precise rows (bf16 reads): attention takes the probabilities as bf16
+  // hi + lo terms and writes o in fp32; the output projection takes o as hi
+  // and lo halves and writes h as bf16 hi | lo halves ([rows, 2d]), which the
+  // LM head sums.  Without it, a slot's logprob carries the bf16 rounding of
+  // p, o and h, an error that grows with |logprob| (about 4e-4 |lp| at the
+  // headline dims); with it, only that of the stored q, k, v remains.
+  bool prec = false;
 };
 
 // S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
@@ -422,6 +434,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.nsplit = ap.nsplit;
   aa.chunk = ap.chunk;
   aa.canvas_per_prompt = canvas_per_prompt;
+  aa.prec = gq.prec ? 1 : 0;
   DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
   DG_MARK(sg, DG_STAGE_ATTENTION, 1);
@@ -440,6 +453,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   oa.vocab = d.vocab;
   oa.C = gq.qpos ? gq.qn : d.canvas;
   oa.part = proj_part;
+  oa.prec = gq.prec ? 1 : 0;
   DG_MARK(sg, DG_STAGE_OPROJ, 0);
   DG_TRY_HIP(dg::launch_oproj(oa, bf, st), "output projection launch");
   DG_MARK(sg, DG_STAGE_OPROJ, 1);
@@ -855,6 +869,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   gq.qpos = sa.qpos;
   gq.qids = sa.qids;
   gq.qn = n_slots;
+  gq.prec = p.prec;
 
   dg::LmheadArgs la{};
   la.head = w->lm_head ? w->lm_head : w->embed;
@@ -872,6 +887,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   la.d = d.d_model;
   la.vocab = d.vocab;
   la.nvt = nvt;
+  la.hl = p.prec ? 1 : 0;
   dg::VocabMergeArgs va{};
   va.stats = la.stats;
   va.nvt = nvt;

@@ -207,6 +207,74 @@ template <typename T, int N> struct RowLoader {
   }
 };
 
+// Rows of a matrix read twice over K: column k of a row of K columns for
+// k < K, and column k - K for K <= k < 2K (the weight side of a product whose
+// other operand is split into hi and lo halves along K).
+template <typename T, int N> struct WrapRowLoader {
+  using Raw = u32x4;
+  const T *p[N];
+  bool live[N];
+  int K;
+  __device__ inline void set(int it, const T *row, bool ok, const T *fallback) {
+    p[it] = ok ? row : fallback;
+    live[it] = ok;
+  }
+  __device__ inline Raw load(int it, int k) const {
+    return *reinterpret_cast<const u32x4 *>(p[it] + (k < K ? k : k - K));
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
+    uint4 v = to_uint4(r);
+    pin(v);
+    return keep_if(v, live[it]);
+  }
+};
+
+// bf16 operand taken from fp32 rows of K columns as two halves along K: for
+// k < K the chunk holds hi = bf16(x[k..k+7]), for K <= k < 2K it holds
+// lo = bf16(x - hi) of columns k - K.  A product over 2K columns against a
+// WrapRowLoader operand then sums hi.w + lo.w = x.w up to 2^-16 of x.
+template <int N> struct F32SplitLoader {
+  struct Raw { u32x4 a, b; int lo; };
+  const float *p[N];
+  bool live[N];
+  int K;
+  __device__ inline void set(int it, const float *row, bool ok, const float *fallback) {
+    p[it] = ok ? row : fallback;
+    live[it] = ok;
+  }
+  __device__ inline Raw load(int it, int k) const {
+    Raw r;
+    r.lo = k >= K;
+    const float *q = p[it] + (k < K ? k : k - K);
+    r.a = *reinterpret_cast<const u32x4 *>(q);
+    r.b = *reinterpret_cast<const u32x4 *>(q + 4);
+    return r;
+  }
+  __device__ inline uint4 finish(int it, const Raw &r) const {
+    uint4 ua = to_uint4(r.a), ub = to_uint4(r.b);
+    pin(ua);
+    pin(ub);
+    const float x[8] = {__uint_as_float(ua.x), __uint_as_float(ua.y), __uint_as_float(ua.z),
+                        __uint_as_float(ua.w), __uint_as_float(ub.x), __uint_as_float(ub.y),
+                        __uint_as_float(ub.z), __uint_as_float(ub.w)};
+    Chunk<bf16> c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bf16 hi = (bf16)x[e];
+      c.v[e] = r.lo ? (bf16)(x[e] - (float)hi) : hi;
+    }
+    return keep_if(c.u, live[it]);
+  }
+};
+
+// h as two bf16 halves of one row: hi = bf16(h) at column c, lo = bf16(h - hi)
+// at column c + d
+__device__ inline void store_split(bf16 *row, int d, int c, float h) {
+  const bf16 hi = (bf16)h;
+  row[c] = hi;
+  row[d + c] = (bf16)(h - (float)hi);
+}
+
 // Rows of a matrix stored in blocks of BR rows x 32 columns (block after block
 // along K): p is the row's first element in the first block, and column k sits
 // k / 32 blocks further.
@@ -434,6 +502,18 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojArgs a) {
   const bool ok = id >= 0 && id < a.vocab;
   const T *E = static_cast<const T *>(a.embed) + (ok ? (int64_t)id * a.d : 0);
   const T *sc = static_cast<const T *>(a.sc_in);
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (a.prec) {   // hi | lo halves of a [M, 2d] row
+      bf16 *h2 = static_cast<bf16 *>(a.h) + row * 2 * a.d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = ok ? to_f(E[c4 + e]) : 0.f;
+        if (sc) x += to_f(sc[row * a.d + c4 + e]);
+        store_split(h2, a.d, c4 + e, acc[e] + x);
+      }
+      return;
+    }
+  }
   T *h = static_cast<T *>(a.h) + row * a.d + c4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -525,9 +605,12 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
 // ---------------------------------------------------------------------------
 // S3: h = x + o Wo^T, x recomputed from the embedding (fp32, unrounded)
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
+// PREC (bf16): o is fp32 and enters as hi and lo bf16 halves over 2K columns
+// against Wo read twice; h is written as hi | lo halves of [M, 2d] rows.
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool PREC = false>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF, BK>;
+  static_assert(!PREC || std::is_same<T, bf16>::value, "split operands: bf16");
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   // the row tiles of one (weight tile, K split) run on one XCD
   int g, mt;
@@ -537,15 +620,23 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
   const int n0 = nt * BN;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
   const int K = a.kdim, d = a.d;
-  const T *o = static_cast<const T *>(a.o);
+  const int KE = PREC ? 2 * K : K;   // columns of the product
   const T *wo = static_cast<const T *>(a.wo);
-  RowLoader<T, G::AI> al;
+  using AL = typename std::conditional<PREC, F32SplitLoader<G::AI>, RowLoader<T, G::AI>>::type;
+  using BL = typename std::conditional<PREC, WrapRowLoader<T, G::BI>, RowLoader<T, G::BI>>::type;
+  using TA = typename std::conditional<PREC, float, T>::type;
+  const TA *o = static_cast<const TA *>(a.o);
+  AL al;
+  BL bl;
+  if constexpr (PREC) {
+    al.K = K;
+    bl.K = K;
+  }
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
     al.set(it, o + row * K, row < a.M, o);
   }
-  RowLoader<T, G::BI> bl;
 #pragma unroll
   for (int it = 0; it < G::BI; ++it) {
     const int n = n0 + G::a_row(it);
@@ -553,7 +644,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
   }
   f32x4 acc[G::TM][G::TN];
   const int kb = ks * a.kchunk;
-  G::run(smem, al, bl, kb, kb + a.kchunk < K ? kb + a.kchunk : K, acc);
+  G::run(smem, al, bl, kb, kb + a.kchunk < KE ? kb + a.kchunk : KE, acc);
   if (a.part) {   // split K: raw partial sums, the reduce adds the residual
     store_partial<G, WGN>(a.part + (int64_t)ks * a.M * d, d, acc, m0, n0, a.M, d);
     return;
@@ -577,7 +668,10 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
         if (col >= d) continue;
         float x = ok ? to_f(E[(int64_t)id * d + col]) : 0.f;
         if (sc) x += to_f(sc[row * d + col]);
-        h[row * d + col] = from_f<T>(acc[i][j][r] + x);
+        if constexpr (PREC)
+          store_split(h + row * 2 * d, d, col, acc[i][j][r] + x);
+        else
+          h[row * d + col] = from_f<T>(acc[i][j][r] + x);
       }
     }
 }
@@ -691,23 +785,49 @@ struct DmaLoop {
 // PF < 0 selects the direct-to-LDS K loop with -PF stages (bf16, BK = 32).
 // TL: the head is read from its copy in BM x 32 blocks (a.head_tiled).
 // F8: the head is read from its e4m3 copy (a.head_fp8, a.head_exp; register K loop)
-template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool TL = false, bool F8 = false>
+// HL: h arrives as bf16 hi | lo halves of [rows, 2d] rows (LmheadArgs.hl);
+// each row takes two MFMA columns, hi in column block j and lo in block
+// j + TN/2 of the same lane, which are added before the epilogue, so the
+// vocabulary tile is streamed once for both halves.
+template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool TL = false, bool F8 = false,
+          bool HL = false>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF < 0 ? 1 : PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
+  static_assert(!HL || (G::TN % 2 == 0 && sizeof(T) == 2), "split rows: bf16, even column blocks");
+  // rows per wave / workgroup and 16-row column blocks per wave after the halves combine
+  constexpr int TNR = HL ? G::TN / 2 : G::TN;
+  constexpr int WNR = HL ? G::WN / 2 : G::WN;
+  constexpr int BNR = HL ? BN / 2 : BN;
   __shared__ float red_m[WGM][BN];
   __shared__ int red_i[WGM][BN];
   __shared__ float red_s[WGM][BN];
   __shared__ float red_t[WGM][BN];
   // group = vocabulary tile; its row tiles share the E tile and run on one XCD
   int vt, rt;
-  if (!xcd_group_tile(a.vocab / BM, (int)cdiv64(a.nrows, BN), &vt, &rt)) return;
+  if (!xcd_group_tile(a.vocab / BM, (int)cdiv64(a.nrows, BNR), &vt, &rt)) return;
   const int v0 = vt * BM;
-  const int64_t n0 = (int64_t)rt * BN;
+  const int64_t n0 = (int64_t)rt * BNR;
   const int d = a.d;
-  if (a.active_rows && !tile_active(a.active_rows, n0, BN, a.nrows, a.rows_per_flag)) return;
+  if (a.active_rows && !tile_active(a.active_rows, n0, BNR, a.nrows, a.rows_per_flag)) return;
   const T *head = static_cast<const T *>(a.head);
   const T *hh = static_cast<const T *>(a.h);
+  // source of tile column r (the B operand): its row of h, and for HL the half;
+  // *ok is false for a column past the rows (or without a source row), which
+  // then reads row 0 and is never stored
+  auto bsrc = [&](int r, bool *ok) -> const T * {
+    int real = r, part = 0;
+    if constexpr (HL) {
+      const int wn_ = r / G::WN, jj = (r % G::WN) / 16;
+      real = wn_ * WNR + (jj % TNR) * 16 + (r % 16);
+      part = jj / TNR;
+    }
+    const int64_t n = n0 + real;
+    int64_t src = -1;
+    if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
+    *ok = src >= 0;
+    return hh + (src >= 0 ? src : 0) * (HL ? 2 * (int64_t)d : (int64_t)d) + part * d;
+  };
   f32x4 acc[G::TM][G::TN];
   if constexpr (PF < 0) {
     // rows past the matrix (or without a source row) read row 0: their
@@ -726,10 +846,8 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
       return TL ? ht + (int64_t)v0 * d + r * 32 : head + (int64_t)(v0 + r) * d;
     };
     auto rowb = [&](int r) {
-      const int64_t n = n0 + r;
-      int64_t src = -1;
-      if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
-      return hh + (src >= 0 ? src : 0) * d;
+      bool ok;
+      return bsrc(r, &ok);
     };
     D::run(st, rowa, rowb, d, TL ? (int64_t)BM * 32 : (int64_t)32, (int64_t)32, acc,
            [](int, typename D::frag(&)[D::TM]) {});
@@ -754,22 +872,27 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     RowLoader<T, G::BI> bl;
 #pragma unroll
     for (int it = 0; it < G::BI; ++it) {
-      const int64_t n = n0 + G::a_row(it);
-      int64_t src = -1;
-      if (n < a.nrows) src = a.row_index ? (int64_t)a.row_index[n] : n;
-      bl.set(it, hh + (src >= 0 ? src : 0) * d, src >= 0, hh);
+      bool ok;
+      const T *p = bsrc(G::a_row(it), &ok);
+      bl.set(it, p, ok, hh);
     }
     G::run(smem, al, bl, 0, d, acc);
+  }
+  if constexpr (HL) {
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TNR; ++j) acc[i][j] += acc[i][j + TNR];
   }
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w / WGN, wn = w % WGN;
   // scale, then pass 1: max and lowest argmax per column (= canvas row)
-  float mx[G::TN];
-  int ix[G::TN];
+  float mx[TNR];
+  int ix[TNR];
 #pragma unroll
-  for (int j = 0; j < G::TN; ++j) {
-    const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
+  for (int j = 0; j < TNR; ++j) {
+    const int64_t n = n0 + wn * WNR + j * 16 + (lane & 15);
     float s = a.logit_scale;
     if (a.row_scale && n < a.nrows) s *= a.row_scale[n];
     float m = -INFINITY;
@@ -798,8 +921,8 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   // label logits of slot rows: the lane holding (label, row) writes it
   if (a.lab_logit) {
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
+    for (int j = 0; j < TNR; ++j) {
+      const int64_t n = n0 + wn * WNR + j * 16 + (lane & 15);
       if (n >= a.nrows) continue;
       const int64_t bs = (n / a.lab_span) * a.lab_S + n % a.lab_S;
       int k = a.lab_n[bs];
@@ -820,15 +943,15 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   }
   if ((lane >> 4) == 0) {
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      red_m[wm][wn * G::WN + j * 16 + lane] = mx[j];
-      red_i[wm][wn * G::WN + j * 16 + lane] = ix[j];
+    for (int j = 0; j < TNR; ++j) {
+      red_m[wm][wn * WNR + j * 16 + lane] = mx[j];
+      red_i[wm][wn * WNR + j * 16 + lane] = ix[j];
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < G::TN; ++j) {
-    const int c = wn * G::WN + j * 16 + (lane & 15);
+  for (int j = 0; j < TNR; ++j) {
+    const int c = wn * WNR + j * 16 + (lane & 15);
     float m = red_m[0][c];
     int id = red_i[0][c];
 #pragma unroll
@@ -844,10 +967,10 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   // for e = e^(l - r ln2) (kept in log2 units: x = l log2 e - r, e = 2^x);
   // p~ = e and logits out
   T *pt = static_cast<T *>(a.ptilde);
-  float ss[G::TN], tt[G::TN];
+  float ss[TNR], tt[TNR];
 #pragma unroll
-  for (int j = 0; j < G::TN; ++j) {
-    const int64_t n = n0 + wn * G::WN + j * 16 + (lane & 15);
+  for (int j = 0; j < TNR; ++j) {
+    const int64_t n = n0 + wn * WNR + j * 16 + (lane & 15);
     const bool live = n < a.nrows;
     const float rj = (float)tile_ref(mx[j]);
     float s = 0.f, t = 0.f;
@@ -885,16 +1008,16 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   }
   if ((lane >> 4) == 0) {
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      red_s[wm][wn * G::WN + j * 16 + lane] = ss[j];
-      red_t[wm][wn * G::WN + j * 16 + lane] = tt[j];
+    for (int j = 0; j < TNR; ++j) {
+      red_s[wm][wn * WNR + j * 16 + lane] = ss[j];
+      red_t[wm][wn * WNR + j * 16 + lane] = tt[j];
     }
   }
   __syncthreads();
   if (wm == 0 && (lane >> 4) == 0) {
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const int c = wn * G::WN + j * 16 + lane;
+    for (int j = 0; j < TNR; ++j) {
+      const int c = wn * WNR + j * 16 + lane;
       const int64_t n = n0 + c;
       if (n >= a.nrows) continue;
       float s = 0.f, t = 0.f;
@@ -1164,18 +1287,26 @@ hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
 static hipError_t launch_oproj_t(const OprojArgs &a, hipStream_t st) {
   const dim3 grid = xcd_grid(cdiv64(a.d, BN) * a.ksplit, cdiv64(a.M, BM));
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (a.prec) {
+      hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN, PF, BK, true>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN, PF, BK>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
+  if (a.prec && !bf) return hipErrorInvalidValue;
   OprojArgs b = a;
-  proj_split(a.M, a.d, a.kdim, bf, &b.ksplit, &b.kchunk);
+  const int ke = a.prec ? 2 * a.kdim : a.kdim;   // split halves double the product's K
+  proj_split(a.M, a.d, ke, bf, &b.ksplit, &b.kchunk);
   if (b.ksplit == 1 || !a.part) {
     b.part = nullptr;
     b.ksplit = 1;
-    b.kchunk = a.kdim;
+    b.kchunk = ke;
   }
   if (bf) {
     if (!b.part && cdiv64(a.M, 128) * cdiv64(a.d, 128) >= 512)
@@ -1196,7 +1327,36 @@ constexpr int64_t kLmFewRows = 64;
 // its register-staged loop, which keeps three workgroups per CU.)
 constexpr int kLmStages = 4;
 
+// one LM-head launch: the grid covers the rows BN (HL: BN / 2) at a time
+template <typename T, int BN, int WGM, int WGN, int PF, int BK, bool TL, bool F8, bool HL>
+static void lmhead_go(const LmheadArgs &a, hipStream_t st) {
+  const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, HL ? BN / 2 : BN));
+  hipLaunchKernelGGL((lmhead_kernel<T, VTILE, BN, WGM, WGN, PF, BK, TL, F8, HL>), grid,
+                     dim3(WGM * WGN * WAVE), 0, st, a);
+}
+
+// Rows given as hi | lo halves (slot reads): the few-row tile takes 64 rows in
+// 128 columns over 8 waves, the large tile 128 rows in 256 columns, each with
+// the loop its plain counterpart uses.
+static hipError_t launch_lmhead_hl(const LmheadArgs &a, hipStream_t st) {
+  const bool few = a.nrows <= kLmFewRows;
+  if (a.head_fp8) {
+    if (few) lmhead_go<bf16, 128, 4, 2, 2, 32, false, true, true>(a, st);
+    else lmhead_go<bf16, 256, 2, 4, 1, 64, false, true, true>(a, st);
+  } else if (few) {
+    if (a.head_tiled) lmhead_go<bf16, 128, 4, 2, 1, 32, true, false, true>(a, st);
+    else lmhead_go<bf16, 128, 4, 2, 1, 32, false, false, true>(a, st);
+  } else if (a.d % 32 == 0) {
+    if (a.head_tiled) lmhead_go<bf16, 256, 2, 4, -kLmStages, 32, true, false, true>(a, st);
+    else lmhead_go<bf16, 256, 2, 4, -kLmStages, 32, false, false, true>(a, st);
+  } else {
+    lmhead_go<bf16, 256, 2, 4, 1, 64, false, false, true>(a, st);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
+  if (a.hl) return bf ? launch_lmhead_hl(a, st) : hipErrorInvalidValue;
   if (bf && a.head_fp8) {
     // e4m3 head: register K loop (the codes are decoded on their way into LDS);
     // with half the bytes per step, the few-row tile keeps two steps in flight

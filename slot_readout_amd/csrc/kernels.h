@@ -44,6 +44,10 @@ struct OprojArgs {
   // split-K partials [proj_ksplit][M][d] fp32, or null (no split)
   float *part;
   int ksplit, kchunk;      // set by the launcher
+  // bf16 only: o is fp32 [M, kdim], taken as bf16 hi and lo halves (the
+  // product runs over 2 kdim columns, Wo read twice), and h is written as bf16
+  // [M, 2d] rows: hi = bf16(h) in columns [0, d), lo = bf16(h - hi) in [d, 2d)
+  int prec;
 };
 
 struct LmheadArgs {
@@ -76,6 +80,9 @@ struct LmheadArgs {
   int d, vocab, nvt;
   // 1 + an id removed from the softmax (its logit is -inf), or 0 for none
   int exclude_id1;
+  // bf16 only: h rows are [*, 2d], bf16 hi = bf16(h) then lo = bf16(h - hi);
+  // the logits are those of hi + lo
+  int hl;
 };
 
 struct ScArgs {
@@ -123,6 +130,9 @@ struct AttnArgs {
   // gathered queries only: one workgroup serves every query head of its kv head
   // (query column c: head kv*G + c / qn, query c % qn); set by the launcher
   int packed;
+  // bf16 only: probabilities enter PV as bf16 hi + lo terms; o and the split
+  // partials are fp32 (o: [nc, qn, Hq, hd] float)
+  int prec;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
 };
 

@@ -19,7 +19,9 @@ def torch_cuda():
     return torch
 
 
-def _step_compare(inp, out, refs, canvases, label, check_sc=True):
+def _step_compare(inp, out, refs, canvases, label, check_sc=True, max_excused=None):
+    """conf, entropy, p.E and argmax of each canvas against the oracle; with
+    max_excused, the fraction of argmax near-ties must stay below it."""
     for i, b in enumerate(canvases):
         ref = refs[i]
         tag = f"{label} canvas {b}"
@@ -27,8 +29,10 @@ def _step_compare(inp, out, refs, canvases, label, check_sc=True):
         assert_float(to_np(out["entropy"][b]), ref["entropy"], "bf16", "entropy", f"{tag} entropy")
         if check_sc:
             assert_row_rel(to_np(out["sc_out"][b]), ref["sc_out"], TOL["bf16"]["sc_out"], f"{tag} sc_out")
-        near = oracle.argmax_near_ties(ref["logits"], TIE_EPS["bf16"]).mask
-        bad = (to_np(out["argmax"][b]) != ref["argmax"]) & ~near
+        nt = oracle.argmax_near_ties(ref["logits"], TIE_EPS["bf16"])
+        if max_excused is not None:
+            assert nt.fraction < max_excused, f"{tag}: {nt.fraction:.2f} of argmax excused"
+        bad = (to_np(out["argmax"][b]) != ref["argmax"]) & ~nt.mask
         assert not bad.any(), f"{tag} argmax at {np.nonzero(bad)[0][:8]}"
 
 
@@ -106,7 +110,7 @@ def test_ragged32_companion_commit(torch_cuda):
     cm = dev.commit(out["conf"], out["entropy"], out["argmax"])
     torch.cuda.synchronize()
     refs = oracle.denoise_step(inp, row_scale=rs, need_sc=False, need_logits=True)
-    _step_compare(inp, out, refs, range(32), "ragged32 companion", check_sc=False)
+    _step_compare(inp, out, refs, range(32), "ragged32 companion", check_sc=False, max_excused=0.5)
     excused = _commit_compare(inp, out, cm, refs, range(32), "ragged32 companion")
     assert excused < 0.5
 
@@ -155,3 +159,67 @@ def test_read_batch_f32_mixed_rereads(torch_cuda):
     _check_slots(g, ref, inp, "f32", "read batch f32 companion")
     du = ref["draws_used"]
     assert (du == 1).mean() > 0.05 and (du == 4).mean() > 0.05
+
+
+def test_headline_step_companion_full(torch_cuda):
+    """The headline step at full size (d 2816, 8/2 x 512 heads, 2048 prompt keys,
+    W 128, V 262,144) with per-row logit multipliers logUniform(0.5, 32): flat
+    rows (H near ln V) and peaked ones, so argmax and the commit order are real
+    decisions.  Compared elementwise: attention output and hidden state of
+    every row, the logits of 16 rows (the 8 flattest and 8 sharpest), conf,
+    entropy, argmax and p.E of every row, then the commit (tau 2.0) with the
+    declared near-tie fraction below one half."""
+    import torch
+    from slot_readout_amd.runtime import DeviceProblem
+    inp = make_inputs(config("bf16_step"))
+    rs = companion_row_scale(inp, (1, 256), 0.5, 32.0)
+    dev = DeviceProblem(inp)
+    out = dev.step(want_sc=True, debug=True, row_scale=torch.from_numpy(rs).cuda())
+    cm = dev.commit(out["conf"], out["entropy"], out["argmax"])
+    torch.cuda.synchronize()
+    ref = oracle.denoise_step(inp, row_scale=rs, need_logits=True)[0]
+    H = ref["entropy"]
+    assert (H < 1).mean() > 0.1 and (H > 6).mean() > 0.1
+    assert_row_rel(to_np(out["attn_out"][0]), ref["attn_out"], TOL["bf16"]["attn_out"], "attn_out")
+    assert_row_rel(to_np(out["hidden_out"][0]), ref["hidden_out"], TOL["bf16"]["hidden_out"], "hidden_out")
+    order = np.argsort(H, kind="stable")
+    rows = np.concatenate([order[:8], order[-8:]])
+    g_l = to_np(out["logits"][0, torch.from_numpy(rows).cuda()])
+    assert_row_rel(g_l, ref["logits"][rows], TOL["bf16"]["logits"], "logits (16 rows)")
+    del g_l
+    out["logits"] = None
+    _step_compare(inp, out, [ref], [0], "headline companion", max_excused=0.5)
+    excused = _commit_compare(inp, out, cm, [ref], [0], "headline companion")
+    assert excused < 0.5
+    assert int(cm["n"][0]) >= 2
+
+
+def test_headline_read_peaked_full(torch_cuda):
+    """The headline read at full size (V 262,144; the draws ride in the first
+    read's pass) with per-slot logit multipliers logUniform(8, 128): label
+    logprobs down to about -110, some slots confident enough to stop at the
+    first read and others re-read with 4 draws (the threshold sits in the
+    widest gap of the first-read entropies).  bf16 at the absolute 1e-2
+    logprob bar."""
+    import torch
+    from slot_readout_amd.runtime import DeviceProblem
+    from tests.test_gpu_slot import _check_slots, _one_pass_draws
+    inp = make_inputs(config("bf16_step"))
+    S = inp["slot_pos"].shape[1]
+    assert _one_pass_draws(inp["dims"], 1, S, inp["n_draws"], int(inp["max_prompt"]))
+    rs = companion_row_scale(inp, (1, S), 8.0, 128.0)
+    inp["entropy_threshold"] = 1e9
+    first = oracle.slot_read(inp, row_scale=rs, n_draws=1)["first_entropy"][0]
+    top = np.sort(first)
+    gaps = np.diff(top)
+    i = int(np.argmax(gaps))
+    assert gaps[i] > 4 * TOL["bf16"]["entropy_abs"], top
+    inp["entropy_threshold"] = float((top[i] + top[i + 1]) / 2)
+    ref = oracle.slot_read(inp, row_scale=rs)
+    du = ref["draws_used"]
+    assert (du == 1).any() and (du == 4).any(), du
+    assert ref["logprobs"].min() < -60
+    dev = DeviceProblem(inp, with_embed_t=False)
+    g = {k: to_np(v) for k, v in dev.slot_read(row_scale=torch.from_numpy(rs).cuda()).items()}
+    torch.cuda.synchronize()
+    _check_slots(g, ref, inp, "bf16", "headline peaked read", max_excused=0.5)

@@ -27,7 +27,10 @@ def _read(inp, row_scale=None, n_draws=None, **kw):
     return {k: to_np(v) for k, v in out.items()}
 
 
-def _check_slots(g, ref, inp, dtype, label=""):
+def _check_slots(g, ref, inp, dtype, label="", max_excused=None):
+    """Every slot output against the oracle's; with max_excused, the fraction
+    of slots whose best label is excused as a declared near-tie must stay
+    below it (companion inputs, where the decisions are meant to be real)."""
     tol = TOL[dtype]
     assert np.array_equal(g["status"], ref["status"]), f"{label} status"
     th = inp["entropy_threshold"]
@@ -47,7 +50,10 @@ def _check_slots(g, ref, inp, dtype, label=""):
                        f"{label} probs[{b},{s}]")
         assert np.all(g["probs"][b, s, k:] == 0) and np.all(g["logprobs"][b, s, k:] == 0)
         assert abs(g["probs"][b, s, :k].sum() - 1) < 1e-5
-    bnear = oracle.best_near_ties(ref["probs"], nl, TIE_EPS[dtype]).mask
+    bnt = oracle.best_near_ties(ref["probs"], nl, TIE_EPS[dtype])
+    bnear = bnt.mask
+    if max_excused is not None:
+        assert bnt.fraction < max_excused, f"{label}: {bnt.fraction:.2f} of best labels excused"
     okb = ok & ~bnear
     assert np.array_equal(g["best"][okb], ref["best"][okb]), f"{label} best"
     bad = ref["status"] != oracle.SLOT_OK
@@ -71,7 +77,7 @@ def test_slot_read_tiny_f32_companion(torch_cuda):
     rs = companion_row_scale(inp, (1, 8), 64.0, 4096.0)
     g = _read(inp, row_scale=rs)
     ref = oracle.slot_read(inp, row_scale=rs)
-    _check_slots(g, ref, inp, "f32", "tiny_f32 companion")
+    _check_slots(g, ref, inp, "f32", "tiny_f32 companion", max_excused=0.5)
     assert (ref["draws_used"] == 1).any() and (ref["draws_used"] == 4).any()
 
 
@@ -157,7 +163,7 @@ def test_slot_read_one_pass_draws_f32(torch_cuda):
     rs = companion_row_scale(inp, (2, 4), 64.0, 2048.0)
     g = _read(inp, row_scale=rs)
     ref = oracle.slot_read(inp, row_scale=rs)
-    _check_slots(g, ref, inp, "f32", "one-pass draws f32")
+    _check_slots(g, ref, inp, "f32", "one-pass draws f32", max_excused=0.5)
     du = ref["draws_used"]
     assert (du == 1).any() and (du == 4).any()
 
@@ -199,7 +205,7 @@ def test_slot_read_many_slots_one_pass(torch_cuda):
     g = _read(inp, row_scale=rs)
     ref = oracle.slot_read(inp, row_scale=rs)
     assert ref["status"][0, 7] == oracle.SLOT_BAD_POS
-    _check_slots(g, ref, inp, "f32", "many slots one pass")
+    _check_slots(g, ref, inp, "f32", "many slots one pass", max_excused=0.5)
 
 
 def test_slot_read_wide_heads_mixed_rereads(torch_cuda):
@@ -249,3 +255,48 @@ def test_slot_read_gqa_packed_heads(torch_cuda, name, n_kv, n_slots, batch):
     ref = oracle.slot_read(inp)
     frac = _check_slots(g, ref, inp, dt, f"gqa {name} kv{n_kv} S{n_slots}")
     assert frac > 0.5
+
+
+def test_slot_read_wide_heads_peaked_rereads(torch_cuda):
+    """Three canvases at d 2816 with 512-wide heads, read in two passes, with
+    per-canvas logit multipliers 1, 24 and 64: flat rows and sharp ones whose
+    label logprobs reach about -90.  The entropy threshold sits in the widest
+    gap between the canvases' largest first-read entropies, so some canvases
+    re-read and some do not.  bf16 storage at the absolute 1e-2 logprob bar:
+    the slot rows carry the attention probabilities, its output and the
+    hidden state as bf16 hi + lo pairs, so only the rounding of the stored
+    q, k, v remains."""
+    cfg = config("bf16_step", vocab=4096, mask_id=4095)
+    inp = make_inputs(cfg, batch=3, prompt_override=("fixed", 200))
+    S = inp["slot_pos"].shape[1]
+    assert not _one_pass_draws(inp["dims"], 3, S, inp["n_draws"], int(inp["max_prompt"]))
+    rs = np.repeat(np.asarray([1.0, 24.0, 64.0], np.float32)[:, None], S, axis=1)
+    inp["entropy_threshold"] = 1e9                # first reads only
+    r0 = oracle.slot_read(inp, row_scale=rs)
+    first, ok = r0["first_entropy"], r0["status"] == oracle.SLOT_OK
+    top = np.sort(np.where(ok, first, -np.inf).max(axis=1))
+    gaps = np.diff(top)
+    i = int(np.argmax(gaps))
+    assert gaps[i] > 4 * TOL["bf16"]["entropy_abs"], top
+    inp["entropy_threshold"] = float((top[i] + top[i + 1]) / 2)
+    ref = oracle.slot_read(inp, row_scale=rs)
+    reread = (ref["draws_used"] > 1).any(axis=1)
+    assert reread.any() and not reread.all(), ref["draws_used"]
+    assert ref["logprobs"][2][:, :4].min() < -80          # sharp rows: large |logprob|
+    g = _read(inp, row_scale=rs)
+    _check_slots(g, ref, inp, "bf16", "wide heads peaked re-reads")
+
+
+@pytest.mark.parametrize("lo,hi", [(16.0, 512.0), (256.0, 1024.0)])
+def test_slot_read_skeleton_bf16_companion(torch_cuda, lo, hi):
+    """Read-batch dims in bf16 with per-slot logit multipliers up to 1024x
+    (label logprobs down to about -100): confident single reads and averaged
+    re-reads, at the absolute 1e-2 logprob bar."""
+    import torch
+    inp = make_inputs(config("reads512"), batch=32, prompt_override=("fixed", 300))
+    rs = companion_row_scale(inp, (32, 4), lo, hi)
+    g = _read(inp, row_scale=rs)
+    ref = oracle.slot_read(inp, row_scale=rs)
+    _check_slots(g, ref, inp, "bf16", f"skeleton bf16 companion {lo}-{hi}", max_excused=0.5)
+    du = ref["draws_used"]
+    assert (du == 1).any() and (du == 4).any()

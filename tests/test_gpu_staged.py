@@ -29,12 +29,11 @@ def _decisive(ref, inp, stage0, dtype):
     return ~(near_th[:, stage0] | near_best[:, stage0]).any(axis=1)
 
 
-# Companion row scales give decisive stage-0 answers; for bf16 their range is
-# capped (16-96 x) so logprobs stay within the workload's magnitude, where the
-# absolute 1e-2 logprob bar applies.
+# Companion row scales (16-512 x) give decisive stage-0 answers, with label
+# logprobs down to about -55, checked at the absolute 1e-2 bar in bf16.
 @pytest.mark.parametrize("name,dtype,over,hi", [
     ("tiny_f32", "f32", dict(batch=4), 512.0),
-    ("reads512", "bf16", dict(batch=16), 96.0),
+    ("reads512", "bf16", dict(batch=16), 512.0),
 ])
 def test_staged_read_matches_oracle(torch_cuda, name, dtype, over, hi):
     import torch

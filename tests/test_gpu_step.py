@@ -119,6 +119,7 @@ def test_step_then_commit_companion(torch_cuda):
     near = oracle.commit_near_ties(ids, ref["conf"], ref["entropy"], inp["dims"].mask_id,
                                    inp["tau"], conf_eps=TIE_EPS["f32"])
     am_near = oracle.argmax_near_ties(ref["logits"], TIE_EPS["f32"]).mask
+    assert oracle.argmax_near_ties(ref["logits"], TIE_EPS["f32"]).fraction < 0.5
     gm = to_np(cm["mask"][0])
     assert np.array_equal(gm[~near], m[~near])
     ok_ids = ~near & ~(am_near & (m == 1))

@@ -36,6 +36,15 @@ def test_embed_gather_is_row_lookup():
     assert np.all(x2 - x == 0.5)
 
 
+def test_embed_out_of_range_ids_are_zero_rows():
+    # ids outside [0, V) (a negative id would otherwise wrap to a real row)
+    V, d = 7, 5
+    E = 100.0 * np.arange(V)[:, None] + np.arange(d)[None, :] + 1.0
+    x = O.embed_input(E, np.array([2, -1, 7, 6]))
+    assert np.array_equal(x[0], E[2]) and np.array_equal(x[3], E[6])
+    assert not x[1].any() and not x[2].any()
+
+
 # ---------------------------------------------------------------- S1/S3 ---
 def test_qkv_projection_selection_matrices():
     # W is [out, in]; a rectangular selection matrix picks input coordinates,
