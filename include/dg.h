@@ -45,7 +45,8 @@
  *     and never synchronise the host.  They are safe to call concurrently from
  *     several threads when each uses its own stream and workspace.
  *   - The library never allocates device memory.  Scratch memory is the
- *     caller-provided workspace, sized by the *_workspace queries.
+ *     caller-provided workspace, sized by the *_workspace queries (except for
+ *     dg_slot_read_noalloc, whose workspace is a static device array).
  *   - Host-visible arguments are checked before anything is launched; a failed
  *     check returns a non-zero dg_status, launches nothing and leaves a message
  *     for dg_last_error().  Index data that lives in device memory (token ids,
@@ -328,6 +329,29 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
                        float *logprobs, float *probs, float *entropy, float *first_entropy,
                        int32_t *best, int32_t *draws_used, int32_t *status,
                        void *workspace, size_t ws_bytes, void *stream);
+
+/* dg_slot_read without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs and errors as dg_slot_read; the
+ * workspace is a static device array of DG_NOALLOC_SCRATCH_BYTES in the
+ * library, one per GPU, held until the process ends, whose address is looked up
+ * on the first call on each device.  The call allocates nothing.
+ *   - DG_ERR_WORKSPACE when dg_slot_read_workspace(dims, batch, n_slots,
+ *     kv->max_len, n_draws) exceeds DG_NOALLOC_SCRATCH_BYTES (the headline
+ *     read, 8 slots at d 2816 / V 262,144, needs about 26 MiB).
+ *   - Every call on a GPU uses that GPU's one array: calls on the same GPU must
+ *     not overlap in time (different streams or threads race on it).  Nothing
+ *     in it needs clearing between calls.
+ *   - Runs on the device current at the call, which must own `stream`. */
+#define DG_NOALLOC_SCRATCH_BYTES (64u << 20)
+dg_status dg_slot_read_noalloc(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                               int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                               const int32_t *slot_pos, const int32_t *label_ids,
+                               const int32_t *n_labels, const int32_t *noise_ids,
+                               float logit_scale, const float *row_scale,
+                               float entropy_threshold, int32_t n_draws,
+                               float *logprobs, float *probs, float *entropy, float *first_entropy,
+                               int32_t *best, int32_t *draws_used, int32_t *status, void *stream);
 
 /* Two-stage structured read (sotaaz, "The server takes at most 26
  * alternatives per question": a question with ask_if is read only when the

@@ -571,6 +571,12 @@ dg_status step_core(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
 
 extern "C" {
 
+// detail message of a failed call made from another source file of the library
+// (not part of the exported interface)
+__attribute__((visibility("hidden"))) dg_status dg_internal_fail(dg_status s, const char *msg) {
+  return fail(s, "%s", msg);
+}
+
 const char *dg_status_string(dg_status s) {
   switch (s) {
     case DG_OK: return "ok";

@@ -17,6 +17,7 @@ DG_FLAG_BAD_TOKEN = 1
 DG_FLAG_BAD_SEQLENS = 2
 DG_SLOT_OK, DG_SLOT_BAD_POS, DG_SLOT_BAD_COUNT, DG_SLOT_BAD_LABEL, DG_SLOT_BAD_NOISE = range(5)
 DG_SLOT_NOT_ASKED = 5
+DG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class DGError(RuntimeError):
@@ -76,6 +77,9 @@ _SIGS = {
     "dg_slot_read": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                             _I32, _P, _I32, _P, _P, _P, _P, _F, _P, _F, _I32,
                             _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_slot_read_noalloc": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
+                                    _I32, _P, _I32, _P, _P, _P, _P, _F, _P, _F, _I32,
+                                    _P, _P, _P, _P, _P, _P, _P, _P]),
     "dg_slot_read_staged_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32, _I32, _I32]),
     "dg_slot_read_staged": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                                    _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _F, _P, _F, _I32,
@@ -220,6 +224,18 @@ def dg_slot_read(dims, weights, kv, batch, canvas_ids, n_slots, slot_pos, label_
         float(logit_scale), _ptr(row_scale), float(entropy_threshold), n_draws, _ptr(logprobs),
         _ptr(probs), _ptr(entropy), _ptr(first_entropy), _ptr(best), _ptr(draws_used),
         _ptr(status), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dg_slot_read_noalloc(dims, weights, kv, batch, canvas_ids, n_slots, slot_pos, label_ids,
+                         n_labels, noise_ids, logit_scale, row_scale, entropy_threshold, n_draws,
+                         logprobs, probs, entropy, first_entropy, best, draws_used, status,
+                         stream=None):
+    _check(lib().dg_slot_read_noalloc(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(kv), batch, _ptr(canvas_ids),
+        n_slots, _ptr(slot_pos), _ptr(label_ids), _ptr(n_labels), _ptr(noise_ids),
+        float(logit_scale), _ptr(row_scale), float(entropy_threshold), n_draws, _ptr(logprobs),
+        _ptr(probs), _ptr(entropy), _ptr(first_entropy), _ptr(best), _ptr(draws_used),
+        _ptr(status), _stream(stream)))
 
 
 def dg_slot_read_staged_workspace(dims, batch, n_slots, max_prompt, n_draws):

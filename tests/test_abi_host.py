@@ -243,3 +243,10 @@ def test_workspace_queries_are_monotone_in_max_prompt(which, dims_kind):
         assert w > 0
         assert w >= prev, f"{which}: workspace({m}) = {w} < workspace of a shorter prompt ({prev})"
         prev = w
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    dg = _lib_or_skip()
+    src = open(HEADER).read()
+    m = re.search(r"#define DG_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == dg.DG_NOALLOC_SCRATCH_BYTES
