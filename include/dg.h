@@ -330,6 +330,30 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
                        int32_t *best, int32_t *draws_used, int32_t *status,
                        void *workspace, size_t ws_bytes, void *stream);
 
+/* The same read in the whole-canvas order: q, attention and the output
+ * projection run over every canvas row of the first read and of the draws,
+ * as the layers below the last one of a multi-layer model need every
+ * position's hidden state for one denoise forward (tau-home "DiffusionGemma
+ * like Jev", section "Refusing JSON token generation": one denoise forward
+ * over the prefilled canvas), and the LM head runs at the slot rows.  With
+ * the single block standing in for the backbone, the slot rows' results
+ * equal dg_slot_read's up to fp32 summation order (dg_slot_read computes q,
+ * attention and the output projection at the slot rows only, which is exact
+ * for a last block).  Arguments, outputs and errors as dg_slot_read; size the
+ * workspace with dg_slot_read_full_canvas_workspace. */
+size_t dg_slot_read_full_canvas_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                                          int32_t max_prompt, int32_t n_draws);
+dg_status dg_slot_read_full_canvas(const dg_dims *dims, const dg_weights *w,
+                                   const dg_prompt_kv *kv, int32_t batch,
+                                   const int32_t *canvas_ids, int32_t n_slots,
+                                   const int32_t *slot_pos, const int32_t *label_ids,
+                                   const int32_t *n_labels, const int32_t *noise_ids,
+                                   float logit_scale, const float *row_scale,
+                                   float entropy_threshold, int32_t n_draws, float *logprobs,
+                                   float *probs, float *entropy, float *first_entropy,
+                                   int32_t *best, int32_t *draws_used, int32_t *status,
+                                   void *workspace, size_t ws_bytes, void *stream);
+
 /* dg_slot_read without a workspace argument, for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses that
  * forbid allocation).  Same arguments, outputs and errors as dg_slot_read; the

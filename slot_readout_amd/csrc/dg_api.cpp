@@ -211,7 +211,7 @@ struct SlotPlan {
   size_t q, k, v, o, part_o, part_ml, proj_part, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
       rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, total;
   AttnPlan first, draws;
-  bool spec, prec;
+  bool spec, prec, full;
 };
 
 // Whether the draws are computed for every canvas in the first read's pass.
@@ -221,14 +221,16 @@ struct SlotPlan {
 // rows (a whole query tile of them), and the output projection of the slot
 // rows.  Both are estimated with sustained rates of about 5 TB/s and
 // 1 PFLOP/s (bf16; 0.1 PFLOP/s fp32).
-bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt) {
+// (full: the whole-canvas order, whose draws run q, attention and the output
+// projection over every canvas row)
+bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt, bool full = false) {
   if (nd <= 1 || B <= 0) return false;
   const double head_s = (double)d.vocab * d.d_model * (double)tsize(d) / 5e12;
   const double hq = (double)d.n_q_heads * d.head_dim, hkv = (double)d.n_kv_heads * d.head_dim;
   const int qt = dg::attn_query_tile(d.head_dim);
-  const double s_att = (double)((S + qt - 1) / qt) * qt;
+  const double s_att = full ? (double)d.canvas : (double)((S + qt - 1) / qt) * qt;
   const double per_canvas = 2.0 * d.d_model * (hq + 2.0 * hkv) * d.canvas +
-                            2.0 * hq * d.d_model * S +
+                            2.0 * hq * d.d_model * (full ? d.canvas : S) +
                             4.0 * hq * ((double)max_prompt + d.canvas) * s_att;
   const double draw_s = (double)B * nd * per_canvas / (d.dtype == DG_BF16 ? 1e15 : 1e14);
   return draw_s < head_s;
@@ -236,11 +238,16 @@ bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt) {
 
 // A read needs the hidden state only at its slot rows: the k/v projection runs
 // over every canvas row (all keys); the q projection, attention and the output
-// projection over the slot rows alone (gathered queries, compact rows).
+// projection over the slot rows alone (gathered queries, compact rows).  The
+// whole-canvas order (full) runs q, attention and the output projection over
+// every canvas row, as the layers below the last one of a deeper model need,
+// and the LM head at the slot rows.
 // spec: -1 decides by speculate_draws, 0 / 1 forces the two-pass / one-pass order
-SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int spec = -1) {
+SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int spec = -1,
+                   bool full = false) {
   SlotPlan p{};
-  p.spec = spec < 0 ? speculate_draws(d, B, S, nd, max_prompt) : spec != 0;
+  p.spec = spec < 0 ? speculate_draws(d, B, S, nd, max_prompt, full) : spec != 0;
+  p.full = full;
   // bf16 slot rows carry the attention output in fp32 and the hidden state
   // as bf16 hi | lo halves (see read_prec)
   const bool prec = d.dtype == DG_BF16;
@@ -250,13 +257,16 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
   const int nvt = d.vocab / dg::VTILE;
   const size_t nrows = (size_t)B * S * (p.spec ? nd + 1 : (nd > 1 ? nd : 1));
+  // rows of q, o and h: the slot rows, or every canvas row (full)
+  const size_t hrows = full ? M : nrows;
   Arena a;
-  p.q = a.take(nrows * nq * ts);
+  p.q = a.take(hrows * nq * ts);
   p.k = a.take(M * nkv * ts);
   p.v = a.take(M * nkv * ts);
-  p.o = a.take(nrows * nq * (prec ? sizeof(float) : ts));
-  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt, S, prec);
-  p.draws = plan_attention(d, ncmax, max_prompt, S, prec);
+  p.o = a.take(hrows * nq * (prec ? sizeof(float) : ts));
+  const int qn = full ? -1 : S;
+  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt, qn, prec);
+  p.draws = plan_attention(d, ncmax, max_prompt, qn, prec);
   const size_t po = p.first.part_o > p.draws.part_o ? p.first.part_o : p.draws.part_o;
   const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
   p.part_o = a.take(po);
@@ -269,6 +279,13 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
     const int64_t kv_rows[] = {B * C, (nd > 1 ? (int64_t)nd : 1) * B * C};
     const int64_t q_rows[] = {Bs, (nd > 1 ? (int64_t)nd : 1) * Bs, (int64_t)(nd + 1) * Bs};
     for (int64_t m : kv_rows) pp = std::max(pp, proj_part_bytes(d, m, 2 * nkv, d.d_model));
+    if (full) {   // q, k, v and the output projection of every canvas row
+      const int64_t f_rows[] = {B * C, (int64_t)ncmax * C};
+      for (int64_t m : f_rows) {
+        pp = std::max(pp, proj_part_bytes(d, m, nq + 2 * nkv, d.d_model));
+        pp = std::max(pp, proj_part_bytes(d, m, d.d_model, (int)(prec ? 2 * nq : nq)));
+      }
+    }
     for (int64_t m : q_rows) {
       pp = std::max(pp, proj_part_bytes(d, m, nq, d.d_model));
       pp = std::max(pp, proj_part_bytes(d, m, nq + 2 * nkv, d.d_model));
@@ -276,12 +293,12 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
     }
     p.proj_part = a.take(pp);
   }
-  p.h = a.take(nrows * d.d_model * ts * (prec ? 2 : 1));
+  p.h = a.take(hrows * d.d_model * ts * (prec ? 2 : 1));
   p.rows = a.take(nrows * sizeof(int32_t));
   p.qpos = a.take(nrows * sizeof(int32_t));
   p.qids = a.take(nrows * sizeof(int32_t));
-  p.kv_row_base = a.take(p.spec ? (size_t)B * d.canvas * sizeof(int32_t) : 0);
-  p.kv_row_slot = a.take(p.spec ? nrows * sizeof(int32_t) : 0);
+  p.kv_row_base = a.take(p.spec && !full ? (size_t)B * d.canvas * sizeof(int32_t) : 0);
+  p.kv_row_slot = a.take(p.spec && !full ? nrows * sizeof(int32_t) : 0);
   p.stats = a.take(nrows * nvt * sizeof(float4));
   p.rowstat = a.take(nrows * sizeof(float2));
   p.lab_logit = a.take(nrows * DG_MAX_LABELS * sizeof(float));
@@ -300,9 +317,10 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
 // of a shorter prompt may take the one-pass order where max_prompt's does
 // not: both are then covered.  Each order's size is non-decreasing in the
 // prompt length.
-size_t slot_ws_bound(const dg_dims &d, int B, int S, int max_prompt, int nd) {
-  size_t t = plan_slot(d, B, S, max_prompt, nd).total;
-  if (speculate_draws(d, B, S, nd, 0)) t = std::max(t, plan_slot(d, B, S, max_prompt, nd, 1).total);
+size_t slot_ws_bound(const dg_dims &d, int B, int S, int max_prompt, int nd, bool full = false) {
+  size_t t = plan_slot(d, B, S, max_prompt, nd, -1, full).total;
+  if (speculate_draws(d, B, S, nd, 0, full))
+    t = std::max(t, plan_slot(d, B, S, max_prompt, nd, 1, full).total);
   return t;
 }
 
@@ -799,21 +817,26 @@ dg_status dg_commit(int32_t batch, int32_t canvas, int32_t mask_id, const int32_
   return ok();
 }
 
-size_t dg_slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
-                              int32_t max_prompt, int32_t n_draws) {
+}  // extern "C"
+
+namespace {
+
+size_t slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots, int32_t max_prompt,
+                           int32_t n_draws, bool full) {
   if (check_dims(dims) != DG_OK || batch < 0 || n_slots < 0 || max_prompt < 0 || n_draws < 1 ||
       n_draws > 16)
     return 0;
-  return slot_ws_bound(*dims, batch, n_slots, max_prompt, n_draws);
+  return slot_ws_bound(*dims, batch, n_slots, max_prompt, n_draws, full);
 }
 
-dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
-                       int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
-                       const int32_t *slot_pos, const int32_t *label_ids, const int32_t *n_labels,
-                       const int32_t *noise_ids, float logit_scale, const float *row_scale,
-                       float entropy_threshold, int32_t n_draws, float *logprobs, float *probs,
-                       float *entropy, float *first_entropy, int32_t *best, int32_t *draws_used,
-                       int32_t *status, void *workspace, size_t ws_bytes, void *stream) {
+// The slot read in the slot-row order (full = false) or the whole-canvas order.
+dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                    int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                    const int32_t *slot_pos, const int32_t *label_ids, const int32_t *n_labels,
+                    const int32_t *noise_ids, float logit_scale, const float *row_scale,
+                    float entropy_threshold, int32_t n_draws, float *logprobs, float *probs,
+                    float *entropy, float *first_entropy, int32_t *best, int32_t *draws_used,
+                    int32_t *status, void *workspace, size_t ws_bytes, void *stream, bool full) {
   dg_status s = dg_slot_read_validate(dims, batch, n_slots, n_draws, entropy_threshold);
   if (s != DG_OK) return s;
   s = check_model(dims, batch, kv ? kv->max_len : 0, w, kv);
@@ -825,7 +848,7 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     return fail(DG_ERR_INVALID_ARG, "slot-read input and output arrays must not be NULL");
   if (n_draws > 1 && !noise_ids) return fail(DG_ERR_INVALID_ARG, "noise_ids is required when n_draws > 1");
   if (!aligned16(workspace)) return fail(DG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  const SlotPlan p = plan_slot(d, batch, n_slots, kv->max_len, n_draws);
+  const SlotPlan p = plan_slot(d, batch, n_slots, kv->max_len, n_draws, -1, full);
   if (!workspace || ws_bytes < p.total)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 ws_bytes, p.total);
@@ -868,13 +891,17 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   sa.draw_ids = at<int32_t>(workspace, p.draw_ids);
   sa.qpos = at<int32_t>(workspace, p.qpos);
   sa.qids = at<int32_t>(workspace, p.qids);
-  sa.kv_row_base = p.spec ? at<int32_t>(workspace, p.kv_row_base) : nullptr;
-  sa.kv_row_slot = p.spec ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
+  const bool kv_copy = p.spec && !full;
+  sa.kv_row_base = kv_copy ? at<int32_t>(workspace, p.kv_row_base) : nullptr;
+  sa.kv_row_slot = kv_copy ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
   sa.mask_id = d.mask_id;
+  sa.full_canvas = full ? 1 : 0;
   Gather gq;
-  gq.qpos = sa.qpos;
-  gq.qids = sa.qids;
-  gq.qn = n_slots;
+  if (!full) {   // whole canvas: no gathered queries (qpos null)
+    gq.qpos = sa.qpos;
+    gq.qids = sa.qids;
+    gq.qn = n_slots;
+  }
   gq.prec = p.prec;
 
   dg::LmheadArgs la{};
@@ -908,6 +935,20 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
     sa.grp_draw = G;
     sa.off_draw = 1;
     DG_TRY_HIP(dg::launch_slot_spec_build(sa, sa.draw_ids, rs_draw, st), "read canvas launch");
+    if (full) {
+      // every row of the B*G canvases through S0..S3, then the slot rows' LM head
+      s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
+                    p.draws, part_o, part_ml, proj_part, h, st, Stages(), gq);
+      if (s != DG_OK) return s;
+      la.nrows = (int64_t)batch * G * n_slots;
+      la.row_scale = rs_draw;
+      la.lab_span = G * n_slots;
+      DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "slot LM head launch");
+      va.nrows = la.nrows;
+      DG_TRY_HIP(dg::launch_vocab_merge(va, st), "slot vocabulary merge launch");
+      DG_TRY_HIP(dg::launch_slot_finish(sa, st), "slot read finish launch");
+      return ok();
+    }
     // The draws differ from canvas b only at the slot positions: k, v of
     // canvas b are projected once and written into its draws as well, then the
     // draws' slot rows are projected (over those copies) with the q of every
@@ -991,6 +1032,49 @@ dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt
   DG_TRY_HIP(dg::launch_vocab_merge(va, st), "draw vocabulary merge launch");
   DG_TRY_HIP(dg::launch_slot_average(sa, st), "draw average launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dg_slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                              int32_t max_prompt, int32_t n_draws) {
+  return slot_read_workspace(dims, batch, n_slots, max_prompt, n_draws, false);
+}
+
+size_t dg_slot_read_full_canvas_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
+                                          int32_t max_prompt, int32_t n_draws) {
+  return slot_read_workspace(dims, batch, n_slots, max_prompt, n_draws, true);
+}
+
+dg_status dg_slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv *kv,
+                       int32_t batch, const int32_t *canvas_ids, int32_t n_slots,
+                       const int32_t *slot_pos, const int32_t *label_ids, const int32_t *n_labels,
+                       const int32_t *noise_ids, float logit_scale, const float *row_scale,
+                       float entropy_threshold, int32_t n_draws, float *logprobs, float *probs,
+                       float *entropy, float *first_entropy, int32_t *best, int32_t *draws_used,
+                       int32_t *status, void *workspace, size_t ws_bytes, void *stream) {
+  return slot_read(dims, w, kv, batch, canvas_ids, n_slots, slot_pos, label_ids, n_labels,
+                   noise_ids, logit_scale, row_scale, entropy_threshold, n_draws, logprobs, probs,
+                   entropy, first_entropy, best, draws_used, status, workspace, ws_bytes, stream,
+                   false);
+}
+
+dg_status dg_slot_read_full_canvas(const dg_dims *dims, const dg_weights *w,
+                                   const dg_prompt_kv *kv, int32_t batch,
+                                   const int32_t *canvas_ids, int32_t n_slots,
+                                   const int32_t *slot_pos, const int32_t *label_ids,
+                                   const int32_t *n_labels, const int32_t *noise_ids,
+                                   float logit_scale, const float *row_scale,
+                                   float entropy_threshold, int32_t n_draws, float *logprobs,
+                                   float *probs, float *entropy, float *first_entropy,
+                                   int32_t *best, int32_t *draws_used, int32_t *status,
+                                   void *workspace, size_t ws_bytes, void *stream) {
+  return slot_read(dims, w, kv, batch, canvas_ids, n_slots, slot_pos, label_ids, n_labels,
+                   noise_ids, logit_scale, row_scale, entropy_threshold, n_draws, logprobs, probs,
+                   entropy, first_entropy, best, draws_used, status, workspace, ws_bytes, stream,
+                   true);
 }
 
 }  // extern "C"

@@ -222,6 +222,9 @@ struct SlotArgs {
   const int32_t *canvas_ids;   // [B, C]
   int32_t *draw_ids;           // [B*nd, C]
   int mask_id;
+  // whole-canvas order: the hidden state has every canvas row, and a slot
+  // row's LM-head row is its canvas row (canvas * C + position)
+  int full_canvas;
 };
 
 hipError_t launch_slot_rows(const SlotArgs &a, hipStream_t st);

@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256) void slot_rows_kernel(SlotArgs a) {
   const int64_t b = bs / a.S;
   const int pos = a.slot_pos[bs];
   const bool in = pos >= 0 && pos < a.C;
-  a.rows[bs] = st == DG_SLOT_OK ? (int32_t)bs : -1;
+  // the LM-head row of the slot: its compact row, or (whole-canvas order) its
+  // canvas row
+  a.rows[bs] = st == DG_SLOT_OK ? (int32_t)(a.full_canvas ? b * a.C + pos : bs) : -1;
   a.qpos[bs] = in ? pos : -1;
   a.qids[bs] = in ? a.canvas_ids[b * a.C + pos] : 0;
 }
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t
   const int64_t b = bd / a.n_draws;
   const int64_t bs = b * a.S + s;
   const bool on = a.canvas_flag[a.B + bs] != 0;
-  a.rows[i] = on ? (int32_t)i : -1;
+  a.rows[i] = on ? (int32_t)(a.full_canvas ? bd * a.C + a.slot_pos[bs] : i) : -1;
   row_active[i] = on ? 1 : 0;
   rs_draw[i] = a.row_scale ? a.row_scale[bs] : 1.f;
   // draw canvases are written only for flagged canvases
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
     const int st = validate_slot(a, bs);
     if (j == 0) a.status[bs] = st;
     const int64_t n = (int64_t)cb * a.S + s;
-    a.rows[n] = st == DG_SLOT_OK ? (int32_t)n : -1;
+    a.rows[n] = st == DG_SLOT_OK ? (int32_t)(a.full_canvas ? (int64_t)cb * a.C + a.slot_pos[bs] : n) : -1;
     rs[n] = a.row_scale ? a.row_scale[bs] : 1.f;
   }
   // slots are written in order, as in the separate draw pass

@@ -77,6 +77,10 @@ _SIGS = {
     "dg_slot_read": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                             _I32, _P, _I32, _P, _P, _P, _P, _F, _P, _F, _I32,
                             _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dg_slot_read_full_canvas_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32, _I32, _I32]),
+    "dg_slot_read_full_canvas": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
+                                        ctypes.POINTER(PromptKV), _I32, _P, _I32, _P, _P, _P, _P,
+                                        _F, _P, _F, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dg_slot_read_noalloc": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                                     _I32, _P, _I32, _P, _P, _P, _P, _F, _P, _F, _I32,
                                     _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -219,6 +223,24 @@ def dg_slot_read(dims, weights, kv, batch, canvas_ids, n_slots, slot_pos, label_
                  entropy, first_entropy, best, draws_used, status, workspace, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dg_slot_read(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(kv), batch, _ptr(canvas_ids),
+        n_slots, _ptr(slot_pos), _ptr(label_ids), _ptr(n_labels), _ptr(noise_ids),
+        float(logit_scale), _ptr(row_scale), float(entropy_threshold), n_draws, _ptr(logprobs),
+        _ptr(probs), _ptr(entropy), _ptr(first_entropy), _ptr(best), _ptr(draws_used),
+        _ptr(status), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dg_slot_read_full_canvas_workspace(dims, batch, n_slots, max_prompt, n_draws):
+    return lib().dg_slot_read_full_canvas_workspace(ctypes.byref(dims), batch, n_slots, max_prompt,
+                                                    n_draws)
+
+
+def dg_slot_read_full_canvas(dims, weights, kv, batch, canvas_ids, n_slots, slot_pos, label_ids,
+                             n_labels, noise_ids, logit_scale, row_scale, entropy_threshold,
+                             n_draws, logprobs, probs, entropy, first_entropy, best, draws_used,
+                             status, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dg_slot_read_full_canvas(
         ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(kv), batch, _ptr(canvas_ids),
         n_slots, _ptr(slot_pos), _ptr(label_ids), _ptr(n_labels), _ptr(noise_ids),
         float(logit_scale), _ptr(row_scale), float(entropy_threshold), n_draws, _ptr(logprobs),

@@ -192,14 +192,18 @@ class DeviceProblem:
                 "draws_used": i(B, S), "status": i(B, S)}
 
     def slot_read(self, row_scale=None, n_draws=None, threshold=None, out=None, stream=None,
-                  label_ids=None, n_labels=None, slot_pos=None, noise_ids=None):
+                  label_ids=None, n_labels=None, slot_pos=None, noise_ids=None,
+                  full_canvas=False):
+        """dg_slot_read (slot-row order), or dg_slot_read_full_canvas."""
         nd = self.inp["n_draws"] if n_draws is None else n_draws
         th = self.inp["entropy_threshold"] if threshold is None else threshold
         if out is None:
             out = self.slot_outputs()
-        ws = self.workspace("slot", dg.dg_slot_read_workspace(self.dims, self.B, self.S,
-                                                               self.max_prompt, nd))
-        dg.dg_slot_read(self.dims, self.weights, self.kv, self.B, self.canvas_ids, self.S,
+        wsf = dg.dg_slot_read_full_canvas_workspace if full_canvas else dg.dg_slot_read_workspace
+        call = dg.dg_slot_read_full_canvas if full_canvas else dg.dg_slot_read
+        ws = self.workspace("slot_full" if full_canvas else "slot",
+                            wsf(self.dims, self.B, self.S, self.max_prompt, nd))
+        call(self.dims, self.weights, self.kv, self.B, self.canvas_ids, self.S,
                         self.slot_pos if slot_pos is None else slot_pos,
                         self.label_ids if label_ids is None else label_ids,
                         self.n_labels if n_labels is None else n_labels,

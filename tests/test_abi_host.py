@@ -221,7 +221,7 @@ def _headline(dg, **kw):
     return dg.make_dims(**base)
 
 
-@pytest.mark.parametrize("which", ["step", "loop", "read", "staged"])
+@pytest.mark.parametrize("which", ["step", "loop", "read", "read_full", "staged"])
 @pytest.mark.parametrize("dims_kind", ["headline", "tiny"])
 def test_workspace_queries_are_monotone_in_max_prompt(which, dims_kind):
     """A workspace sized for max_prompt = M must hold a call whose prompts are
@@ -235,6 +235,7 @@ def test_workspace_queries_are_monotone_in_max_prompt(which, dims_kind):
     q = {"step": lambda m: dg.dg_denoise_step_workspace(d, B, m),
          "loop": lambda m: dg.dg_denoise_loop_workspace(d, B, m),
          "read": lambda m: dg.dg_slot_read_workspace(d, B, 8, m, 4),
+         "read_full": lambda m: dg.dg_slot_read_full_canvas_workspace(d, B, 8, m, 4),
          "staged": lambda m: dg.dg_slot_read_staged_workspace(d, B, 8, m, 4)}[which]
     lens = list(range(0, 4200, 7)) + list(range(4200, 120000, 997))
     prev = 0

@@ -194,7 +194,8 @@ def test_headline_step_companion_full(torch_cuda):
     assert int(cm["n"][0]) >= 2
 
 
-def test_headline_read_peaked_full(torch_cuda):
+@pytest.mark.parametrize("full_canvas", [False, True])
+def test_headline_read_peaked_full(torch_cuda, full_canvas):
     """The headline read at full size (V 262,144; the draws ride in the first
     read's pass) with per-slot logit multipliers logUniform(8, 128): label
     logprobs down to about -110, some slots confident enough to stop at the
@@ -220,6 +221,8 @@ def test_headline_read_peaked_full(torch_cuda):
     assert (du == 1).any() and (du == 4).any(), du
     assert ref["logprobs"].min() < -60
     dev = DeviceProblem(inp, with_embed_t=False)
-    g = {k: to_np(v) for k, v in dev.slot_read(row_scale=torch.from_numpy(rs).cuda()).items()}
+    g = {k: to_np(v) for k, v in dev.slot_read(row_scale=torch.from_numpy(rs).cuda(),
+                                                full_canvas=full_canvas).items()}
     torch.cuda.synchronize()
-    _check_slots(g, ref, inp, "bf16", "headline peaked read", max_excused=0.5)
+    _check_slots(g, ref, inp, "bf16", f"headline peaked read (full canvas {full_canvas})",
+                 max_excused=0.5)

@@ -18,6 +18,7 @@ def torch_cuda():
 
 
 def _read(inp, row_scale=None, n_draws=None, **kw):
+    """dg_slot_read (or, with full_canvas=True, dg_slot_read_full_canvas)."""
     import torch
     from slot_readout_amd.runtime import DeviceProblem
     dev = DeviceProblem(inp, with_embed_t=False)
@@ -300,3 +301,25 @@ def test_slot_read_skeleton_bf16_companion(torch_cuda, lo, hi):
     _check_slots(g, ref, inp, "bf16", f"skeleton bf16 companion {lo}-{hi}", max_excused=0.5)
     du = ref["draws_used"]
     assert (du == 1).any() and (du == 4).any()
+
+
+@pytest.mark.parametrize("name,over,B,prompt,scales", [
+    ("tiny_f32", {}, 1, ("fixed", 128), (64.0, 4096.0)),                 # fp32, two passes
+    ("reads512", {}, 6, ("fixed", 200), (16.0, 512.0)),                  # bf16, two passes
+    ("reads512", dict(vocab=262144, mask_id=262143), 2, ("fixed", 64), (16.0, 512.0)),  # one pass
+    ("bf16_step", dict(vocab=4096, mask_id=4095), 2, ("fixed", 150), (8.0, 128.0)),    # hd 512
+])
+def test_slot_read_full_canvas(torch_cuda, name, over, B, prompt, scales):
+    """The whole-canvas order (q, attention and the output projection over every
+    canvas row, LM head at the slot rows) against the oracle, and against the
+    slot-row order up to summation order."""
+    inp = make_inputs(config(name, **over), batch=B, prompt_override=prompt)
+    dt = inp["dims"].dtype
+    rs = companion_row_scale(inp, inp["slot_pos"].shape, *scales)
+    g = _read(inp, row_scale=rs, full_canvas=True)
+    ref = oracle.slot_read(inp, row_scale=rs)
+    _check_slots(g, ref, inp, dt, f"full canvas {name}", max_excused=0.5)
+    g2 = _read(inp, row_scale=rs)
+    ok = (ref["status"] == oracle.SLOT_OK) & (g["draws_used"] == g2["draws_used"])
+    tol = 2e-4 if dt == "f32" else 1e-2
+    assert np.abs(g["logprobs"][ok] - g2["logprobs"][ok]).max() <= tol
