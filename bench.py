@@ -1,15 +1,24 @@
-"""Throughput of one full pass of the hot path on one MI355X.
+"""Throughput of the hot path on one MI355X.
 
 A step = dg_denoise_step (attention, LM head, fused softmax/entropy, p.E
 self-conditioning) + dg_commit + dg_slot_read (8 slots x 4 labels, first read
 plus averaged noise draws) over one bf16 canvas of 256 tokens with a 2048-token
 cached prompt: d_model 2816, 8 query / 2 KV heads x 512, window +-128, vocab
 262,144.  Inputs are seeded and synthetic and already in HBM when timing
-starts.  The K timed steps carry one HIP event pair each and no other
-instrumentation; K further steps with per-stage HIP events give the stage
-breakdown and the roofline kernel's launch duration.  Prints one JSON line.
+starts.  Each of the K timed steps carries one HIP event pair and nothing
+else (value = K steps / their total time; median and p95 of the per-step
+times beside it); K further steps with per-stage HIP events give the stage
+breakdown and the dominant kernel's launch duration for the roofline.
+
+After the headline steps the same process measures the other workloads, each
+with its own roofline: the read in the whole-canvas order, the 110,707-token
+cold long read, the ragged batch of 32 canvases and the 512-canvas structured
+read batch; then the generation loop, prefill, two-stage read and FP8-head
+legs, the achievable copy / matmul ceilings, and the CPU oracle on a sample.
+Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload NAME] [--no-legs]
 """
 import argparse
 import ctypes
@@ -24,7 +33,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 WORKLOAD = "bf16_step"
+LEG_STEPS = 100                # timed steps of each secondary workload
+
+# Kernels whose operands reach LDS through direct-to-LDS loads: their FETCH_SIZE
+# readings are not scaled by the plain-copy calibration (which uses ordinary
+# vector loads), so no measured traffic is reported for them.
+DMA_KERNELS = ("lmhead", "selfcond")
 
 
 def _hip():
@@ -65,16 +81,24 @@ class Events:
             self.hip.hipEventDestroy(self.arr[i])
 
 
-def attention_work(inp):
-    """Algorithmic bytes and flops of the attention stage (all canvases)."""
+def attention_work(inp, queries=None, canvases=None):
+    """Algorithmic bytes and flops of one attention launch: every prompt key and
+    value once, the canvas k and v, and q and o of the queries (every canvas
+    position, or `queries` per canvas); flops of QK^T and PV over the visible
+    keys.  canvases: canvases per prompt (a read's draws share their prompt)."""
     dm = inp["dims"]
     C, Hq, Hkv, hd, W = dm.canvas, dm.n_q_heads, dm.n_kv_heads, dm.head_dim, dm.window
     es = 2 if dm.dtype == "bf16" else 4
     lens = inp["prompt_lens"].astype("int64")
+    ncv = len(lens) * (canvases or 1)
     kv_bytes = int(lens.sum()) * Hkv * hd * 2 * es
-    canvas_bytes = len(lens) * C * (2 * Hq + 2 * Hkv) * hd * es      # q, o, canvas k, v
-    win = sum(min(C, i + W + 1) - max(0, i - W) for i in range(C))    # visible canvas keys
-    flops = 4.0 * Hq * hd * (C * float(lens.sum()) + len(lens) * win)
+    nq = C if queries is None else queries
+    canvas_bytes = ncv * (2 * nq * Hq + 2 * C * Hkv) * hd * es
+    if queries is None:
+        win = sum(min(C, i + W + 1) - max(0, i - W) for i in range(C))   # visible canvas keys
+        flops = 4.0 * Hq * hd * (C * float(lens.sum()) * (canvases or 1) + ncv * win)
+    else:
+        flops = 4.0 * Hq * hd * nq * (float(lens.sum()) * (canvases or 1) + ncv * min(C, 2 * W + 1))
     return kv_bytes + canvas_bytes, flops, kv_bytes
 
 
@@ -93,6 +117,8 @@ def kernel_source_hash():
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary of the
     workload, if it was taken on the current kernel sources; else None."""
+    if kernel in DMA_KERNELS:
+        return None
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -102,6 +128,17 @@ def measured_traffic(kernel, workload):
         return None
     k = c.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(inp):
@@ -122,10 +159,10 @@ def cpu_baseline(inp):
     total = t3 - t0
     return {
         "value": B * C / total, "unit": "canvas tokens/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"the whole step of the same workload in float64 numpy: denoise step "
-                   f"{t1 - t0:.2f} s + commit {t2 - t1:.3f} s + slot read of {S} slots "
+        "sample": (f"one whole step of the same workload (one canvas) in float64 numpy: denoise "
+                   f"step {t1 - t0:.2f} s + commit {t2 - t1:.3f} s + slot read of {S} slots "
                    f"({int(np.max(rd['draws_used']))} draws) {t3 - t2:.2f} s"),
-        "seconds": round(total, 3),
+        "seconds": round(total, 3), "cpu_model": cpu_model(),
     }
 
 
@@ -154,10 +191,25 @@ def loop_leg(dev, inp, stream, runs=3, check_every=16):
             "tau": inp["tau"]}
 
 
-def prefill_leg(dev, inp, stream, runs=5):
+def timed_median(fn, runs=5):
+    """Median HIP-event time (ms) of `runs` calls of fn after one warm-up call."""
+    import numpy as np
+    import torch
+    ts = []
+    for i in range(runs + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def prefill_leg(dev, inp, stream):
     """dg_prefill_kv of the workload's prompt tokens (seeded ids) into a scratch
-    cache of the same shape, timed with HIP events after the step bench;
-    median of `runs` calls after one warm-up call."""
+    cache of the same shape."""
     import numpy as np
     import torch
     from slot_readout_amd import dg
@@ -169,48 +221,27 @@ def prefill_leg(dev, inp, stream, runs=5):
                            .astype(np.int32)).cuda()
     k = torch.empty((n, dm.n_kv_heads, dm.head_dim), dtype=dev.tdt, device="cuda")
     v = torch.empty_like(k)
-    ts = []
-    for i in range(runs + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dg.dg_prefill_kv(dev.dims, dev.weights, n, ids, k, v, None, stream)
-        e1.record()
-        torch.cuda.synchronize()
-        if i:
-            ts.append(e0.elapsed_time(e1))
-    t = float(np.median(ts))
+    t = timed_median(lambda: dg.dg_prefill_kv(dev.dims, dev.weights, n, ids, k, v, None, stream))
     return {"tokens": n, "ms": round(t, 4), "tokens_per_s": round(n / (t * 1e-3), 1)}
 
 
-def staged_leg(dev, inp, stream, runs=5):
+def staged_leg(dev, inp, stream):
     """dg_slot_read_staged of the workload's slots: the first half in stage 0, the
     second half in stage 1, whose first slot is asked only if stage-0 slot 0
-    answers label 0; median of `runs` calls after one warm-up call."""
-    import numpy as np
-    import torch
+    answers label 0."""
     S = dev.S
     stage = [0] * (S // 2) + [1] * (S - S // 2)
     ask, lab = [-1] * S, [0] * S
     if S >= 2:
         ask[S // 2] = 0
     out = dev.slot_outputs()
-    ts = []
-    for i in range(runs + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dev.slot_read_staged(stage, ask, lab, out=out, stream=stream)
-        e1.record()
-        torch.cuda.synchronize()
-        if i:
-            ts.append(e0.elapsed_time(e1))
-    t = float(np.median(ts))
+    t = timed_median(lambda: dev.slot_read_staged(stage, ask, lab, out=out, stream=stream))
     return {"slots": S, "stages": 2, "ms": round(t, 4), "slot_reads_per_s": round(dev.B * S / (t * 1e-3), 1),
             "reads_per_slot": int(out["draws_used"].max().item()) + 1}
 
 
 def fp8_leg(inp, stream, K=20, W=3):
     """The same step (step + commit + read) with the e4m3 copy of the LM head."""
-    import numpy as np
     import torch
     from slot_readout_amd import dg
     from slot_readout_amd.runtime import DeviceProblem
@@ -239,17 +270,13 @@ def fp8_leg(inp, stream, K=20, W=3):
     ms = e0.elapsed_time(e1) / K
     del dev
     return {"lm_head": "e4m3 codes, per-row power-of-two scales", "ms_per_step": round(ms, 4),
-            "canvas_tokens_per_s": round(dev_tokens(inp) / (ms * 1e-3), 1)}
-
-
-def dev_tokens(inp):
-    return inp["batch"] * inp["dims"].canvas
+            "canvas_tokens_per_s": round(inp["batch"] * dm.canvas / (ms * 1e-3), 1)}
 
 
 def achievable_peaks():
     """Measured ceilings on this GPU, beside the vendor peaks: a 1 GiB device-to-device
     copy (bytes read + written per second) and a bf16 8192^3 matrix product
-    (contiguous operands).  Taken after the timed steps."""
+    (contiguous operands)."""
     import torch
     x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
@@ -276,27 +303,268 @@ def achievable_peaks():
     return out
 
 
+def _pct(xs, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(xs), q)), 4)
+
+
+class Workload:
+    """Device-resident inputs of one workload and its timed step.
+
+    kind: "step" (dg_denoise_step + dg_commit [+ dg_slot_read]) or "read"
+    (dg_slot_read only).  full_canvas selects the read's whole-canvas order."""
+
+    DESC = {
+        "bf16_step": ("one canvas of 256 tokens, 2048-token cached prompt, d_model 2816, 8q/2kv "
+                      "heads x 512, window +-128, vocab 262144, commit tau 2.0, slot read 8 slots x "
+                      "4 labels (4 noise draws)"),
+        "long_read": ("one canvas of 256 tokens over a 110,707-token cached prompt read cold, "
+                      "d_model 256, 4 heads x 64, window +-128, vocab 2048; step + commit"),
+        "ragged32": ("32 canvases of 256 tokens, prompts U{512..8192}, mask fractions U(0.1, 0.9), "
+                     "d_model 256, 4 heads x 64, window +-16, vocab 2048; step + commit"),
+        "reads512": ("512 canvases of 256 tokens, 1024-token prompts, a fixed skeleton with 4 slots, "
+                     "k ~ U{2..26} labels, re-read above entropy 0.1 with 4 noise draws, d_model 256, "
+                     "4 heads x 64, window +-16, vocab 2048; slot read"),
+    }
+
+    def __init__(self, name, hip, stream, lm_fp8=False, full_canvas=False, with_read=None):
+        from slot_readout_amd import dg
+        from slot_readout_amd.runtime import DeviceProblem
+        from synth import config, make_inputs
+        import torch
+        self.name = name
+        self.kind = "read" if name == "reads512" else "step"
+        self.with_read = (name == "bf16_step") if with_read is None else with_read
+        self.full_canvas = full_canvas
+        self.cold = name == "long_read"
+        self.hip, self.stream = hip, stream
+        self.inp = make_inputs(config(name))
+        self.dev = DeviceProblem(self.inp, device="cuda:0", with_lm_fp8=lm_fp8,
+                                 with_embed_t=self.kind == "step")
+        dev = self.dev
+        self.so = dev.step_outputs(want_sc=True) if self.kind == "step" else None
+        self.co = dev.commit_outputs() if self.kind == "step" else None
+        self.ro = dev.slot_outputs()
+        self.ws_step = (dev.workspace("step", dg.dg_denoise_step_workspace(dev.dims, dev.B, dev.max_prompt))
+                        if self.kind == "step" else None)
+        self.flush = None
+        if self.cold:
+            # a read sweep of 1 GiB evicts L2 and the 256 MB MALL without leaving
+            # dirty lines behind, whose write-back would compete with the timed reads
+            self.flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda:0")
+        torch.cuda.synchronize()
+
+    def step(self, dbg=None, mark=lambda j: None):
+        from slot_readout_amd import dg
+        dev, inp, st = self.dev, self.inp, self.stream
+        dm = inp["dims"]
+        mark(0)
+        if self.kind == "step":
+            so, co = self.so, self.co
+            dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, dev.B, dev.canvas_ids, None,
+                               inp["logit_scale"], None, so["conf"], so["entropy"], so["argmax"],
+                               so["sc_out"], dbg, so["flags"], self.ws_step, st)
+            mark(1)
+            dg.dg_commit(dev.B, dev.C, dm.mask_id, dev.canvas_ids, so["conf"], so["entropy"],
+                         so["argmax"], inp["tau"], co["mask"], co["out_ids"], co["n"], st)
+            mark(2)
+            if self.with_read:
+                dev.slot_read(out=self.ro, stream=st, full_canvas=self.full_canvas)
+        else:
+            mark(1)
+            mark(2)
+            dev.slot_read(out=self.ro, stream=st, full_canvas=self.full_canvas)
+        mark(3)
+
+    def run(self, K, W, instrument=True):
+        """W untimed steps, K timed steps (one event pair each), then, with
+        instrument, K steps with per-stage events.  Returns the timing dict."""
+        import numpy as np
+        import torch
+        from slot_readout_amd import dg
+        hip, st = self.hip, self.stream
+        n_st = 2 * dg.DG_N_STAGES
+        span = Events(hip, 2 * K)
+        for _ in range(W):
+            if self.flush is not None:
+                torch.amax(self.flush)
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            if self.flush is not None:
+                torch.amax(self.flush)
+            span.record(2 * k, st)
+            self.step()
+            span.record(2 * k + 1, st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [span.ms(2 * k, 2 * k + 1) for k in range(K)]
+        if self.flush is not None:   # cache flushes sit between the steps: sum the steps
+            total_ms = float(np.sum(per))
+        else:
+            total_ms = span.ms(0, 2 * K - 1)
+        out = {"ms_per_step": total_ms / K, "ms_median": _pct(per, 50), "ms_p95": _pct(per, 95),
+               "wall_s": wall, "steps": K}
+        span.destroy()
+        if instrument:
+            marks = Events(hip, 4 * K)
+            stage_ev = Events(hip, n_st * K)
+            for k in range(K):
+                if self.flush is not None:
+                    torch.amax(self.flush)
+                dbg = dg.make_debug(stage_events=stage_ev.sub(k * n_st)) if self.kind == "step" else None
+                self.step(dbg, lambda j, k=k: marks.record(4 * k + j, st))
+            torch.cuda.synchronize()
+            out["step_ms"] = float(np.mean([marks.ms(4 * k, 4 * k + 1) for k in range(K)]))
+            out["commit_ms"] = float(np.mean([marks.ms(4 * k + 1, 4 * k + 2) for k in range(K)]))
+            out["read_ms"] = float(np.mean([marks.ms(4 * k + 2, 4 * k + 3) for k in range(K)]))
+            if self.kind == "step":
+                out["stages"] = {name: float(np.mean([stage_ev.ms(k * n_st + 2 * i, k * n_st + 2 * i + 1)
+                                                      for k in range(K)]))
+                                 for i, name in enumerate(dg.DG_STAGES)}
+            marks.destroy()
+            stage_ev.destroy()
+        return out
+
+    def release(self):
+        import torch
+        self.dev = self.so = self.co = self.ro = self.flush = None
+        torch.cuda.empty_cache()
+
+
+def kernel_work(w, lm_fp8=False):
+    """(algorithmic bytes, flops) per launch of the step's main kernels."""
+    inp, dm = w.inp, w.inp["dims"]
+    B, C, V, d = inp["batch"], dm.canvas, dm.vocab, dm.d_model
+    M, nvt = B * C, V // 256
+    head_bytes = V * d + V * 4 if lm_fp8 else V * d * 2      # e4m3 codes + exponents
+    lm = (head_bytes + M * d * 2 + M * V * 2 + M * nvt * 16, 2.0 * M * V * d)
+    sc = (d * V * 2 + M * V * 2 + M * nvt * 4 + M * d * 2, 2.0 * M * V * d)
+    at = attention_work(inp)
+    return {"lmhead": lm, "selfcond": sc, "attention": at[:2]}
+
+
+KERNEL_NAMES = {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
+                "selfcond": "scgemm_dma_kernel + sc_reduce4_kernel (S6)",
+                "attention": "attn_kernel + attn_merge_kernel (S2)"}
+
+
+def roofline_of(w, t, dominant=None, lm_fp8=False):
+    """The dominant kernel's roofline from the instrumented stage times, and
+    every stage's rate."""
+    work = kernel_work(w, lm_fp8)
+    st = t["stages"]
+    dom = dominant or max(work, key=lambda k: st[k])
+    nbytes, flops = work[dom]
+    ms = st[dom]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    attn_bound = "hbm"
+    roof = {"kernel": KERNEL_NAMES[dom], "bound": attn_bound, "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(dom, w.name),
+            "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(ms, 4),
+            "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    if dom in DMA_KERNELS:
+        roof["traffic_note"] = ("null: the kernel stages its operands with direct-to-LDS loads, for "
+                                "which the plain-copy calibration of FETCH_SIZE does not hold")
+    stages = {k: {"ms": round(st[k], 4), "GB/s": round(b / (st[k] * 1e-3) / 1e9, 1),
+                  "TFLOP/s": round(f / (st[k] * 1e-3) / 1e12, 1)} for k, (b, f) in work.items()}
+    return roof, stages
+
+
+def leg_step_workload(name, hip, stream, K, W):
+    """A step + commit workload with attention as its roofline kernel."""
+    w = Workload(name, hip, stream)
+    t = w.run(K, W)
+    roof, stages = roofline_of(w, t, dominant="attention")
+    B, C = w.inp["batch"], w.inp["dims"].canvas
+    _, _, kv_bytes = attention_work(w.inp)
+    out = {"workload": name + ": " + Workload.DESC[name], "metric": "canvas tokens/s",
+           "value": round(B * C / (t["ms_per_step"] * 1e-3), 1),
+           "ms_per_step": round(t["ms_per_step"], 4), "ms_median": t["ms_median"], "ms_p95": t["ms_p95"],
+           "steps": K, "cold_cache": w.cold,
+           "breakdown_ms": {"denoise_step": round(t["step_ms"], 4), "commit": round(t["commit_ms"], 4),
+                            "stages": {k: round(v, 4) for k, v in t["stages"].items()}},
+           "roofline": roof, "stage_roofline": stages,
+           "prompt_kv_bytes": int(kv_bytes)}
+    if name == "long_read":
+        out["prefill"] = prefill_leg(w.dev, w.inp, stream)
+    w.release()
+    return out
+
+
+def leg_reads512(hip, stream, K, W):
+    """The 512-canvas structured read batch: slot reads per second.  The roofline
+    is that of the whole read call (its kernels are not instrumented one by one;
+    the per-kernel split is in the committed rocprofv3 summary): the prompt KV
+    read once per attention pass (the first read and the batched draws) against
+    HBM, and the call's flops against the bf16 MFMA peak."""
+    w = Workload("reads512", hip, stream)
+    t = w.run(K, W)
+    inp = w.inp
+    B, S, nd = inp["batch"], inp["slot_pos"].shape[1], inp["n_draws"]
+    du = w.ro["draws_used"]
+    reread = int((du > 1).any(dim=1).sum().item())
+    a1_bytes, a1_flops, kv = attention_work(inp, queries=S)
+    passes_bytes = a1_bytes + (attention_work(inp, queries=S, canvases=nd)[0] if reread else 0)
+    dm = inp["dims"]
+    hq, hkv = dm.n_q_heads * dm.head_dim, dm.n_kv_heads * dm.head_dim
+    ncv = B * (1 + (nd if reread else 0))
+    proj_flops = 2.0 * dm.d_model * (2 * hkv) * dm.canvas * ncv + 4.0 * dm.d_model * hq * S * ncv
+    head_flops = 2.0 * dm.vocab * dm.d_model * S * ncv
+    flops = a1_flops * (1 + (nd if reread else 0)) + proj_flops + head_flops
+    ms = t["ms_per_step"]
+    gbs = passes_bytes / (ms * 1e-3) / 1e9
+    tfl = flops / (ms * 1e-3) / 1e12
+    out = {"workload": "reads512: " + Workload.DESC["reads512"], "metric": "slot reads/s",
+           "value": round(B * S / (ms * 1e-3), 1), "ms_per_read_call": round(ms, 4),
+           "ms_median": t["ms_median"], "ms_p95": t["ms_p95"], "steps": K,
+           "canvases_reread": reread,
+           "roofline": {"kernel": "dg_slot_read call (all kernels)", "bound": "hbm",
+                        "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "algorithmic_bytes_per_call": int(passes_bytes),
+                        "mfma_tflops": round(tfl, 1), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4)}}
+    w.release()
+    return out
+
+
+def leg_read_full_canvas(hip, stream, K, W):
+    """The headline step with its read in the whole-canvas order."""
+    w = Workload("bf16_step", hip, stream, full_canvas=True)
+    t = w.run(K, W)
+    B, C, S = w.inp["batch"], w.inp["dims"].canvas, w.dev.S
+    out = {"ms_per_step": round(t["ms_per_step"], 4), "ms_median": t["ms_median"], "ms_p95": t["ms_p95"],
+           "canvas_tokens_per_s": round(B * C / (t["ms_per_step"] * 1e-3), 1),
+           "read_ms": round(t["read_ms"], 4),
+           "slot_reads_per_s_of_read": round(B * S / (t["read_ms"] * 1e-3), 1)}
+    w.release()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lm-fp8", action="store_true",
                     help="LM head from its e4m3 copy (weight-only FP8, bf16 activations)")
-    ap.add_argument("--no-loop", action="store_true",
-                    help="skip the multi-step generation loop leg (measured after the timed steps)")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="the headline workload only (no secondary workloads or legs)")
     ap.add_argument("--workload", default=WORKLOAD,
-                    choices=["bf16_step", "long_read", "ragged32"],
-                    help="bf16_step (default) times step + commit + slot read; long_read and "
-                         "ragged32 time step + commit and report the attention stage")
+                    choices=["bf16_step", "long_read", "ragged32", "reads512"],
+                    help="profile one workload alone: bf16_step (default; step + commit + slot "
+                         "read, then every leg), long_read and ragged32 (step + commit), "
+                         "reads512 (slot read)")
+    ap.add_argument("--full-canvas", action="store_true",
+                    help="the read in the whole-canvas order (dg_slot_read_full_canvas)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device twice: a plain "
                          "copy of known size that scales the HBM byte counters of a "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE run")
-    ap.add_argument("--cold", action="store_true",
-                    help="evict the caches (read 1 GiB) before every timed step; the default "
-                         "for long_read, whose prompt KV would otherwise sit in the 256 MB MALL")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the hot path runs on a single GPU "
@@ -304,81 +572,26 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from slot_readout_amd import dg
-    from slot_readout_amd.runtime import DeviceProblem
-    from synth import config, make_inputs
 
     dg.lib()   # fails loudly without the HIP library
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    workload = args.workload
-    cold = args.cold or workload == "long_read"
-    with_read = workload == "bf16_step"
-    cfg = config(workload)
-    t_in = time.perf_counter()
-    inp = make_inputs(cfg)
-    dev = DeviceProblem(inp, device="cuda:0", with_lm_fp8=args.lm_fp8)
-    dm = inp["dims"]
-    B, C, S, V, d = dev.B, dev.C, dev.S, dm.vocab, dm.d_model
     stream = torch.cuda.current_stream().cuda_stream
-    so = dev.step_outputs(want_sc=True)
-    co = dev.commit_outputs()
-    ro = dev.slot_outputs()
     hip = _hip()
     K, W = args.steps, args.warmup
-    n_st = 2 * dg.DG_N_STAGES
-    # The metric's K steps carry one event pair each and nothing else; a second
-    # pass of K steps records the per-stage events (each record adds about 3 us,
-    # so they are kept out of the metric) for the breakdown and the roofline.
-    span = Events(hip, 2 * K)
-    marks = Events(hip, 4 * K)
-    stage_ev = Events(hip, n_st * K)
-    dbg_per_step = [dg.make_debug(stage_events=stage_ev.sub(k * n_st)) for k in range(K)]
-    ws_step = dev.workspace("step", dg.dg_denoise_step_workspace(dev.dims, B, dev.max_prompt))
+    legs = not args.no_legs and args.workload == WORKLOAD
 
-    flush = None
-    if cold:
-        # a read sweep of 1 GiB evicts L2 and the 256 MB MALL without leaving dirty
-        # lines behind, whose write-back would otherwise compete with the timed reads
-        flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda:0")
-        torch.cuda.synchronize()
+    if args.workload == "reads512":
+        line = leg_reads512(hip, stream, K, W)
+        print(json.dumps(line), flush=True)
+        return
 
-    def one_step(k=None, instrumented=False):
-        """k: the step's slot in the event blocks (None: warm-up)."""
-        mark = (lambda j: marks.record(4 * k + j, stream)) if instrumented and k is not None else (lambda j: None)
-        dbg = dbg_per_step[k] if instrumented and k is not None else None
-        if flush is not None:
-            torch.amax(flush)
-        if k is not None and not instrumented:
-            span.record(2 * k, stream)
-        mark(0)
-        dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, B, dev.canvas_ids, None,
-                           inp["logit_scale"], None, so["conf"], so["entropy"], so["argmax"],
-                           so["sc_out"], dbg, so["flags"], ws_step, stream)
-        mark(1)
-        dg.dg_commit(B, C, dm.mask_id, dev.canvas_ids, so["conf"], so["entropy"], so["argmax"],
-                     inp["tau"], co["mask"], co["out_ids"], co["n"], stream)
-        mark(2)
-        if with_read:
-            dev.slot_read(out=ro, stream=stream)
-        mark(3)
-        if k is not None and not instrumented:
-            span.record(2 * k + 1, stream)
-
-    for _ in range(W):
-        one_step()
-    torch.cuda.synchronize()
+    t_in = time.perf_counter()
+    w = Workload(args.workload, hip, stream, lm_fp8=args.lm_fp8, full_canvas=args.full_canvas)
     setup_s = time.perf_counter() - t_in
-    t0 = time.perf_counter()
-    for k in range(K):
-        one_step(k)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for k in range(K):   # instrumented pass, outside the metric
-        one_step(k, instrumented=True)
-    torch.cuda.synchronize()
+    t = w.run(K, W)
     if args.copy_calibration:   # outside the timed region
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -386,102 +599,64 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    if cold:   # cache flushes sit between the steps: sum the steps themselves
-        ms_per_step = float(np.mean([span.ms(2 * k, 2 * k + 1) for k in range(K)]))
-    else:
-        ms_per_step = span.ms(0, 2 * K - 1) / K
-    step_ms = float(np.mean([marks.ms(4 * k, 4 * k + 1) for k in range(K)]))
-    commit_ms = float(np.mean([marks.ms(4 * k + 1, 4 * k + 2) for k in range(K)]))
-    read_ms = float(np.mean([marks.ms(4 * k + 2, 4 * k + 3) for k in range(K)]))
-    stages = {}
-    for i, name in enumerate(dg.DG_STAGES):
-        stages[name] = float(np.mean([stage_ev.ms(k * n_st + 2 * i, k * n_st + 2 * i + 1)
-                                      for k in range(K)]))
-    M = B * C
-    nvt = V // 256
-    # algorithmic work per launch of the two vocabulary-sized kernels
-    head_bytes = V * d + V * 4 if args.lm_fp8 else V * d * 2      # e4m3 codes + exponents
-    lm_bytes = head_bytes + M * d * 2 + M * V * 2 + M * nvt * 16
-    lm_flops = 2.0 * M * V * d
-    sc_bytes = d * V * 2 + M * V * 2 + M * nvt * 4 + M * d * 2
-    sc_flops = 2.0 * M * V * d
-    at_bytes, at_flops, kv_bytes = attention_work(inp)
-    cand = {"lmhead": (stages["lmhead"], lm_bytes, lm_flops),
-            "selfcond": (stages["selfcond"], sc_bytes, sc_flops),
-            "attention": (stages["attention"], at_bytes, at_flops)}
-    names = {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
-             "selfcond": "scgemm_dma_kernel + sc_reduce_kernel (S6)",
-             "attention": "attn_kernel + attn_merge_kernel (S2)"}
-    dom = max(cand, key=lambda k: cand[k][0])
-    t_ms, nbytes, flops = cand[dom]
-    achieved_gbs = nbytes / (t_ms * 1e-3) / 1e9
-    roofline = {"kernel": names[dom],
-                "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, workload),
-                "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(t_ms, 4),
-                "mfma_tflops": round(flops / (t_ms * 1e-3) / 1e12, 1),
-                "mfma_frac": round(flops / (t_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    stage_roof = {}
-    for name, (tm, nb, fl) in cand.items():
-        stage_roof[name] = {"ms": round(tm, 4), "GB/s": round(nb / (tm * 1e-3) / 1e9, 1),
-                            "TFLOP/s": round(fl / (tm * 1e-3) / 1e12, 1)}
-
-    value = M / (ms_per_step * 1e-3)
-    wl_desc = {
-        "bf16_step": (f"bf16_step: one canvas of 256 tokens, 2048-token cached prompt, d_model 2816, "
-                      f"8q/2kv heads x 512, window +-128, vocab 262144, commit tau 2.0, slot read "
-                      f"8 slots x 4 labels (4 noise draws)"),
-        "long_read": ("long_read: one canvas of 256 tokens over a 110,707-token cached prompt read "
-                      "cold, d_model 256, 4 heads x 64, window +-128, vocab 2048; step + commit"),
-        "ragged32": ("ragged32: 32 canvases of 256 tokens, prompts U{512..8192}, d_model 256, "
-                     "4 heads x 64, window +-16, vocab 2048; step + commit"),
-    }[workload]
+    inp, dev = w.inp, w.dev
+    B, C, S = dev.B, dev.C, dev.S
+    roof, stage_roof = roofline_of(w, t, lm_fp8=args.lm_fp8)
+    if args.lm_fp8:   # counters were taken with the bf16 head
+        roof["traffic"] = None
+    ms = t["ms_per_step"]
+    _, _, kv_bytes = attention_work(inp)
     line = {
         "metric": "canvas tokens/s per denoise step + slot reads/s; % of MFMA/HBM roofline",
-        "value": round(value, 1), "unit": "canvas tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
+        "value": round(B * C / (ms * 1e-3), 1), "unit": "canvas tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 4),
+        "ms_median": t["ms_median"], "ms_p95": t["ms_p95"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; weights N(0,0.02), prompt K/V N(0,1))",
-        "config": {"workload": wl_desc, "batch": B, "canvas": C,
-                   "prompt": int(inp["max_prompt"]), "slots": S if with_read else 0,
-                   "cold_cache": bool(cold),
+        "config": {"workload": args.workload + ": " + Workload.DESC[args.workload], "batch": B,
+                   "canvas": C, "prompt": int(inp["max_prompt"]), "slots": S if w.with_read else 0,
+                   "cold_cache": bool(w.cold),
+                   "read_order": "whole canvas" if args.full_canvas else "slot rows",
                    "lm_head": "e4m3 codes, per-row power-of-two scales (weight-only FP8)"
                    if args.lm_fp8 else "bf16"},
-        "slot_reads_per_s": round(B * S / (ms_per_step * 1e-3), 1) if with_read else None,
+        "slot_reads_per_s": round(B * S / (ms * 1e-3), 1) if w.with_read else None,
         "breakdown_ms": {"pass": "K further steps with per-stage HIP events, after the timed steps",
-                         "denoise_step": round(step_ms, 4), "commit": round(commit_ms, 4),
-                         "slot_read": round(read_ms, 4),
-                         "stages": {k: round(v, 4) for k, v in stages.items()}},
-        "roofline": roofline,
+                         "denoise_step": round(t["step_ms"], 4), "commit": round(t["commit_ms"], 4),
+                         "slot_read": round(t["read_ms"], 4),
+                         "stages": {k: round(v, 4) for k, v in t["stages"].items()}},
+        "roofline": roof,
         "stage_roofline": stage_roof,
-        "attention_kv_read": {"kv_bytes": int(kv_bytes), "ms": round(stages["attention"], 4),
-                              "GB/s": round(at_bytes / (stages["attention"] * 1e-3) / 1e9, 1),
-                              "hbm_frac": round(at_bytes / (stages["attention"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "host_wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
+        "attention_kv_read": {"kv_bytes": int(kv_bytes), "ms": round(t["stages"]["attention"], 4),
+                              "hbm_frac": stage_roof["attention"]["GB/s"] / HBM_PEAK_GBS},
+        "host_wall_s": round(t["wall_s"], 3), "setup_s": round(setup_s, 1),
     }
-    marks.destroy()
-    span.destroy()
-    if args.lm_fp8:   # counters were taken with the bf16 head
-        line["roofline"]["traffic"] = None
+    if w.with_read:
+        line["read_only"] = {"ms": round(t["read_ms"], 4),
+                             "slot_reads_per_s": round(B * S / (t["read_ms"] * 1e-3), 1)}
     peaks = achievable_peaks()
-    roof = line["roofline"]
     roof["achievable"] = dict(peaks, frac_of_copy=round(roof["achieved"] / peaks["copy_GBs"], 4),
                               mfma_frac_of_matmul=round(roof["mfma_tflops"] / peaks["matmul_bf16_TFLOPs"], 4))
-    if not args.no_loop and workload == WORKLOAD:
+    if legs:
         line["loop"] = loop_leg(dev, inp, stream)
-    if workload in ("bf16_step", "long_read"):
         line["prefill"] = prefill_leg(dev, inp, stream)
-    if workload == WORKLOAD:
         line["staged_read"] = staged_leg(dev, inp, stream)
+    elif args.workload == "long_read":
+        line["prefill"] = prefill_leg(dev, inp, stream)
+    cpu = None
+    if legs and not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp)
+    w.release()
+    if legs:
+        nl = min(K, LEG_STEPS)
+        line["read_full_canvas"] = leg_read_full_canvas(hip, stream, nl, W)
         if not args.lm_fp8:
             line["fp8_head_step"] = fp8_leg(inp, stream)
-    stage_ev.destroy()
-    if not args.no_cpu_baseline and workload == WORKLOAD:
-        line["cpu_baseline"] = cpu_baseline(inp)
-    else:
-        line["cpu_baseline"] = None
+        line["workloads"] = {
+            "long_read": leg_step_workload("long_read", hip, stream, nl, W),
+            "ragged32": leg_step_workload("ragged32", hip, stream, nl, W),
+            "reads512": leg_reads512(hip, stream, nl, W),
+        }
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
