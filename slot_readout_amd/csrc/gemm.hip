@@ -574,31 +574,45 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
     store_partial<G, WGN>(a.part + (int64_t)ks * a.M * nc, nc, acc, m0, n0 - a.col0, a.M, nc);
     return;
   }
-  T *q = static_cast<T *>(a.q), *k = static_cast<T *>(a.k), *v = static_cast<T *>(a.v);
+  // Epilogue through LDS: the tile, scaled and rounded to T, goes to LDS in the
+  // MFMA layout, then each thread stores whole 16-byte row chunks, so a wave
+  // writes full 128-byte lines of q, k and v (the MFMA layout alone would give
+  // 32-byte pieces of four rows per store).  A chunk of VEC columns never
+  // straddles q, k and v (their widths are multiples of 64).
+  constexpr int OP = BN + G::VEC;   // LDS pitch of the output tile, elements
+  static_assert(BM * OP * (int)sizeof(T) <= G::LDS_BYTES, "output tile must fit the K loop's LDS");
+  T *ot = reinterpret_cast<T *>(smem);
+  __syncthreads();   // every wave is done with the K loop's LDS
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
-    const int col = n0 + wn * G::WN + j * 16 + (lane & 15);
-    if (col >= ntot) continue;
-    T *base;
-    int ld, c;
-    float sc = 1.f;
-    if (col < nq) { base = q; ld = nq; c = col; sc = a.q_scale; }
-    else if (col < nq + nk) { base = k; ld = nk; c = col - nq; }
-    else { base = v; ld = nk; c = col - nq - nk; }
-    const bool remap = col >= nq && a.kv_row;
+    const int cl = wn * G::WN + j * 16 + (lane & 15);
+    const float sc = n0 + cl < nq ? a.q_scale : 1.f;
 #pragma unroll
     for (int i = 0; i < G::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
-        if (row >= a.M) continue;
-        const int64_t orow = remap ? (int64_t)a.kv_row[row] : row;
-        if (orow < 0) continue;
-        const T val = from_f<T>(acc[i][j][r] * sc);
-        base[orow * ld + c] = val;
-        if (col >= nq)
-          for (int cp = 1; cp <= a.kv_copies; ++cp) base[(orow + (int64_t)cp * a.C) * ld + c] = val;
-      }
+      for (int r = 0; r < 4; ++r) ot[(wm * G::WM + i * 16 + 4 * (lane >> 4) + r) * OP + cl] =
+          from_f<T>(acc[i][j][r] * sc);
+  }
+  __syncthreads();
+  T *q = static_cast<T *>(a.q), *k = static_cast<T *>(a.k), *v = static_cast<T *>(a.v);
+  constexpr int CPW = BN / G::VEC;   // 16-byte chunks per tile row
+  for (int ch = threadIdx.x; ch < BM * CPW; ch += G::NT) {
+    const int rl = ch / CPW, cc = ch % CPW;
+    const int64_t row = m0 + rl;
+    const int col = n0 + cc * G::VEC;
+    if (row >= a.M || col >= ntot) continue;
+    T *base;
+    int ld, c;
+    if (col < nq) { base = q; ld = nq; c = col; }
+    else if (col < nq + nk) { base = k; ld = nk; c = col - nq; }
+    else { base = v; ld = nk; c = col - nq - nk; }
+    const int64_t orow = col >= nq && a.kv_row ? (int64_t)a.kv_row[row] : row;
+    if (orow < 0) continue;
+    const uint4 val = *reinterpret_cast<const uint4 *>(ot + rl * OP + cc * G::VEC);
+    *reinterpret_cast<uint4 *>(base + orow * ld + c) = val;
+    if (col >= nq)
+      for (int cp = 1; cp <= a.kv_copies; ++cp)
+        *reinterpret_cast<uint4 *>(base + (orow + (int64_t)cp * a.C) * ld + c) = val;
   }
 }
 
