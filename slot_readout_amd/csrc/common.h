@@ -126,4 +126,27 @@ static inline dim3 xcd_grid(int64_t ngroups, int64_t nt) {
   return dim3((unsigned)(8 * cdiv64(ngroups, 8) * nt));
 }
 
+// xcd_group_tile with each group's nt tiles cut into `chunks` runs of
+// ceil(nt / chunks) tiles, each run dealt as a group of its own: its tiles
+// still share the group's operand on one XCD.  With few groups (a tall
+// projection with a handful of weight tiles) whole groups would leave XCDs
+// idle; the runs spread the work over all eight.  Launch
+// xcd_grid(ngroups * chunks, ceil(nt / chunks)).
+__device__ inline bool xcd_group_tile_split(int ngroups, int nt, int chunks, int *g, int *t) {
+  const int per = (nt + chunks - 1) / chunks;
+  int gg, tt;
+  if (!xcd_group_tile(ngroups * chunks, per, &gg, &tt)) return false;
+  *g = gg % ngroups;
+  *t = (gg / ngroups) * per + tt;
+  return *t < nt;
+}
+// runs per group: none below 16 groups (two per XCD or more keep the
+// weight-tile sharing), else enough for at least 32 groups in all, at most
+// one run per tile
+static inline int xcd_chunks(int64_t ngroups, int64_t nt) {
+  if (ngroups >= 16 || nt <= 1) return 1;
+  const int64_t c = cdiv64(32, ngroups);
+  return (int)(c < nt ? c : nt);
+}
+
 }  // namespace dg

@@ -532,7 +532,8 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   // the row tiles of one (weight tile, K split) run on one XCD
   int g, mt;
-  if (!xcd_group_tile((int)cdiv64(a.col1 - a.col0, BN) * a.ksplit, (int)cdiv64(a.M, BM), &g, &mt))
+  if (!xcd_group_tile_split((int)cdiv64(a.col1 - a.col0, BN) * a.ksplit, (int)cdiv64(a.M, BM),
+                            a.rchunks, &g, &mt))
     return;
   const int nt = g / a.ksplit, ks = g % a.ksplit;
   const int64_t m0 = (int64_t)mt * BM;
@@ -628,7 +629,8 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void oproj_kernel(OprojArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   // the row tiles of one (weight tile, K split) run on one XCD
   int g, mt;
-  if (!xcd_group_tile((int)cdiv64(a.d, BN) * a.ksplit, (int)cdiv64(a.M, BM), &g, &mt)) return;
+  if (!xcd_group_tile_split((int)cdiv64(a.d, BN) * a.ksplit, (int)cdiv64(a.M, BM), a.rchunks, &g, &mt))
+    return;
   const int nt = g / a.ksplit, ks = g % a.ksplit;
   const int64_t m0 = (int64_t)mt * BM;
   const int n0 = nt * BN;
@@ -1239,8 +1241,11 @@ __global__ __launch_bounds__(256) void sc_reduce4_kernel(const float *part, cons
 // host launchers
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
-static hipError_t launch_qkv_t(const QkvArgs &a, hipStream_t st) {
-  const dim3 grid = xcd_grid(cdiv64(a.col1 - a.col0, BN) * a.ksplit, cdiv64(a.M, BM));
+static hipError_t launch_qkv_t(const QkvArgs &a0, hipStream_t st) {
+  QkvArgs a = a0;
+  const int64_t ng = cdiv64(a.col1 - a.col0, BN) * a.ksplit, nt = cdiv64(a.M, BM);
+  a.rchunks = xcd_chunks(ng, nt);
+  const dim3 grid = xcd_grid(ng * a.rchunks, cdiv64(nt, a.rchunks));
   if (a.sc_in)
     hipLaunchKernelGGL((qkv_kernel<T, BM, BN, WGM, WGN, PF, BK, true>), grid, dim3(WGM * WGN * WAVE), 0, st, a);
   else
@@ -1299,8 +1304,11 @@ hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK>
-static hipError_t launch_oproj_t(const OprojArgs &a, hipStream_t st) {
-  const dim3 grid = xcd_grid(cdiv64(a.d, BN) * a.ksplit, cdiv64(a.M, BM));
+static hipError_t launch_oproj_t(const OprojArgs &a0, hipStream_t st) {
+  OprojArgs a = a0;
+  const int64_t ng = cdiv64(a.d, BN) * a.ksplit, nt = cdiv64(a.M, BM);
+  a.rchunks = xcd_chunks(ng, nt);
+  const dim3 grid = xcd_grid(ng * a.rchunks, cdiv64(nt, a.rchunks));
   if constexpr (std::is_same<T, bf16>::value) {
     if (a.prec) {
       hipLaunchKernelGGL((oproj_kernel<T, BM, BN, WGM, WGN, PF, BK, true>), grid, dim3(WGM * WGN * WAVE), 0, st, a);

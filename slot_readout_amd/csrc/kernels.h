@@ -30,6 +30,7 @@ struct QkvArgs {
   // each k, v row written is also written kv_copies more times, C, 2C, ...
   // rows further on (the canvases that follow, holding copies of it)
   int kv_copies;
+  int rchunks;             // runs of row tiles per weight tile (set by the launcher)
 };
 
 struct OprojArgs {
@@ -48,6 +49,7 @@ struct OprojArgs {
   // product runs over 2 kdim columns, Wo read twice), and h is written as bf16
   // [M, 2d] rows: hi = bf16(h) in columns [0, d), lo = bf16(h - hi) in [d, 2d)
   int prec;
+  int rchunks;             // runs of row tiles per weight tile (set by the launcher)
 };
 
 struct LmheadArgs {
