@@ -188,7 +188,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   }
   const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
   const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
-  const int64_t cbase = (int64_t)cb * C * kv_stride + (int64_t)g * HD;
+  const int64_t cbase = (int64_t)cb * (a.kv_cmul > 1 ? a.kv_cmul : 1) * C * kv_stride + (int64_t)g * HD;
   const T *kc = static_cast<const T *>(a.k) + cbase;
   const T *vc = static_cast<const T *>(a.v) + cbase;
 

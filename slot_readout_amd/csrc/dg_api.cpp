@@ -298,7 +298,8 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   p.qpos = a.take(nrows * sizeof(int32_t));
   p.qids = a.take(nrows * sizeof(int32_t));
   p.kv_row_base = a.take(p.spec && !full ? (size_t)B * d.canvas * sizeof(int32_t) : 0);
-  p.kv_row_slot = a.take(p.spec && !full ? nrows * sizeof(int32_t) : 0);
+  // one-pass: draw slot rows' k, v rows; two-pass: those of the draw pass
+  p.kv_row_slot = a.take(!full && nd > 1 ? nrows * sizeof(int32_t) : 0);
   p.stats = a.take(nrows * nvt * sizeof(float4));
   p.rowstat = a.take(nrows * sizeof(float2));
   p.lab_logit = a.take(nrows * DG_MAX_LABELS * sizeof(float));
@@ -374,6 +375,9 @@ struct Gather {
   // p, o and h, an error that grows with |logprob| (about 4e-4 |lp| at the
   // headline dims); with it, only that of the stored q, k, v remains.
   bool prec = false;
+  // canvas c's k, v are written to / read from canvas slot c * kv_cmul (the
+  // two-pass read keeps each canvas's k, v where its first draw will be)
+  int kv_cmul = 1;
 };
 
 // S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
@@ -406,6 +410,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   qa.col0 = 0;
   qa.col1 = qa.nq + 2 * qa.nkv;
   qa.kv_row = nullptr;
+  qa.kv_cmul = gq.kv_cmul;
   qa.part = proj_part;
   DG_MARK(sg, DG_STAGE_QKV, 0);
   if (gq.qpos && !gq.qkv_done) {
@@ -453,6 +458,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.chunk = ap.chunk;
   aa.canvas_per_prompt = canvas_per_prompt;
   aa.prec = gq.prec ? 1 : 0;
+  aa.kv_cmul = gq.kv_cmul;
   DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
   DG_MARK(sg, DG_STAGE_ATTENTION, 1);
@@ -893,7 +899,7 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
   sa.qids = at<int32_t>(workspace, p.qids);
   const bool kv_copy = p.spec && !full;
   sa.kv_row_base = kv_copy ? at<int32_t>(workspace, p.kv_row_base) : nullptr;
-  sa.kv_row_slot = kv_copy ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
+  sa.kv_row_slot = !full && n_draws > 1 ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
   sa.mask_id = d.mask_id;
   sa.full_canvas = full ? 1 : 0;
   Gather gq;
@@ -998,13 +1004,19 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
     return ok();
   }
 
-  // first read over the prefilled canvases
+  // first read over the prefilled canvases.  With draws to come (slot-row
+  // order), canvas b's k, v go to canvas slot b * n_draws, where its first draw
+  // will be; a re-read copies them to its other draws and projects only the
+  // draws' slot rows.
   sa.grp_first = 1;
   sa.grp_draw = n_draws;
   sa.off_draw = 0;
+  const bool draw_copies = !full && n_draws > 1;
+  Gather g1 = gq;
+  if (draw_copies) g1.kv_cmul = n_draws;
   DG_TRY_HIP(dg::launch_slot_rows(sa, st), "slot row launch");
   s = run_block(d, w, kv, batch, 1, canvas_ids, nullptr, nullptr, nullptr, q, k, v, o, p.first,
-                part_o, part_ml, proj_part, h, st, Stages(), gq);
+                part_o, part_ml, proj_part, h, st, Stages(), g1);
   if (s != DG_OK) return s;
   la.nrows = (int64_t)batch * n_slots;
   la.row_scale = row_scale;
@@ -1019,8 +1031,39 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
   DG_TRY_HIP(dg::launch_slot_build_draws(sa, st), "draw canvas launch");
   int32_t *row_active = at<int32_t>(workspace, p.row_active);
   DG_TRY_HIP(dg::launch_slot_draw_rows2(sa, row_active, rs_draw, st), "draw row launch");
+  Gather gd = gq;
+  if (draw_copies) {
+    // the draws differ from canvas b only at the slot positions: copy b's k, v
+    // into its other draws, then project q, k, v of the draws' slot rows, whose
+    // k, v land at their positions in the draw canvases
+    const size_t nkv = (size_t)d.n_kv_heads * d.head_dim;
+    DG_TRY_HIP(dg::launch_slot_copy_kv(sa, k, v, (int64_t)(nkv * tsize(d)), st), "draw k/v copy launch");
+    dg::QkvArgs qd{};
+    qd.ids = sa.qids;
+    qd.embed = w->embed;
+    qd.wq = w->wq;
+    qd.wk = w->wk;
+    qd.wv = w->wv;
+    qd.q = q;
+    qd.k = k;
+    qd.v = v;
+    qd.active = sa.draw_active;
+    qd.M = (int64_t)batch * n_draws * n_slots;
+    qd.d = d.d_model;
+    qd.nq = d.n_q_heads * d.head_dim;
+    qd.nkv = (int)nkv;
+    qd.vocab = d.vocab;
+    qd.C = n_slots;            // rows per draw canvas (its active flag)
+    qd.q_scale = q_scale_of(d);
+    qd.col0 = 0;
+    qd.col1 = qd.nq + 2 * qd.nkv;
+    qd.kv_row = sa.kv_row_slot;
+    qd.part = proj_part;
+    DG_TRY_HIP(dg::launch_qkv(qd, bf, st), "draw slot-row projection launch");
+    gd.qkv_done = true;
+  }
   s = run_block(d, w, kv, batch * n_draws, n_draws, sa.draw_ids, nullptr, sa.draw_active, nullptr,
-                q, k, v, o, p.draws, part_o, part_ml, proj_part, h, st, Stages(), gq);
+                q, k, v, o, p.draws, part_o, part_ml, proj_part, h, st, Stages(), gd);
   if (s != DG_OK) return s;
   la.nrows = (int64_t)batch * n_draws * n_slots;
   la.active_rows = row_active;

@@ -474,7 +474,9 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(QkvArgs a) {
   if (col < a.nq) { base = static_cast<T *>(a.q); ld = a.nq; c = col; sc = a.q_scale; }
   else if (col < a.nq + a.nkv) { base = static_cast<T *>(a.k); ld = a.nkv; c = col - a.nq; }
   else { base = static_cast<T *>(a.v); ld = a.nkv; c = col - a.nq - a.nkv; }
-  const int64_t orow = col >= a.nq && a.kv_row ? (int64_t)a.kv_row[row] : row;
+  int64_t orow = row;
+  if (col >= a.nq && a.kv_row) orow = a.kv_row[row];
+  else if (col >= a.nq && a.kv_cmul > 1) orow = (row / a.C) * a.kv_cmul * a.C + row % a.C;
   if (orow < 0) return;
   const int ncp = col >= a.nq ? a.kv_copies : 0;
   for (int cp = 0; cp <= ncp; ++cp) {
@@ -607,7 +609,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
     if (col < nq) { base = q; ld = nq; c = col; }
     else if (col < nq + nk) { base = k; ld = nk; c = col - nq; }
     else { base = v; ld = nk; c = col - nq - nk; }
-    const int64_t orow = col >= nq && a.kv_row ? (int64_t)a.kv_row[row] : row;
+    int64_t orow = row;
+    if (col >= nq && a.kv_row) orow = a.kv_row[row];
+    else if (col >= nq && a.kv_cmul > 1) orow = (row / a.C) * a.kv_cmul * a.C + row % a.C;
     if (orow < 0) continue;
     const uint4 val = *reinterpret_cast<const uint4 *>(ot + rl * OP + cc * G::VEC);
     *reinterpret_cast<uint4 *>(base + orow * ld + c) = val;

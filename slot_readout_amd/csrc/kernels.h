@@ -30,6 +30,10 @@ struct QkvArgs {
   // each k, v row written is also written kv_copies more times, C, 2C, ...
   // rows further on (the canvases that follow, holding copies of it)
   int kv_copies;
+  // with no kv_row map and kv_cmul > 1: input row m of canvas m / C writes
+  // k, v row (m / C) * kv_cmul * C + m % C (canvas c's k, v land in canvas slot
+  // c * kv_cmul, the first of kv_cmul canvases that will hold copies of it)
+  int kv_cmul;
   int rchunks;             // runs of row tiles per weight tile (set by the launcher)
 };
 
@@ -135,6 +139,8 @@ struct AttnArgs {
   // bf16 only: probabilities enter PV as bf16 hi + lo terms; o and the split
   // partials are fp32 (o: [nc, qn, Hq, hd] float)
   int prec;
+  // canvas cb's keys and values are canvas cb * kv_cmul of k and v (0 or 1: cb)
+  int kv_cmul;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
 };
 
@@ -235,6 +241,11 @@ hipError_t launch_slot_build_draws(const SlotArgs &a, hipStream_t st);
 hipError_t launch_slot_draw_rows2(const SlotArgs &a, int32_t *row_active, float *rs_draw,
                                   hipStream_t st);
 hipError_t launch_slot_average(const SlotArgs &a, hipStream_t st);
+// Two-pass draws: for each flagged canvas b, its k and v rows (kv_row_bytes
+// bytes per canvas row, stored at canvas slot b * n_draws) are copied to the
+// canvas slots b * n_draws + 1 .. b * n_draws + n_draws - 1 of its other draws
+hipError_t launch_slot_copy_kv(const SlotArgs &a, void *k, void *v, int64_t kv_row_bytes,
+                               hipStream_t st);
 // one pass over the first read and every draw: ids of the B*(1+nd) canvases,
 // hidden-row indices of their slot rows, and the status of draws with bad noise
 hipError_t launch_slot_spec_build(const SlotArgs &a, int32_t *ids, float *rs, hipStream_t st);

@@ -11,6 +11,8 @@
 // the LM head's weight stream costs more than the draws' forward pass, the
 // draws are instead computed for every canvas in the same pass as the first
 // read and used only where a slot is flagged (same results, one weight stream).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -177,6 +179,26 @@ __global__ __launch_bounds__(256) void slot_draw_rows_kernel(SlotArgs a, int32_t
   const bool in = pos >= 0 && pos < a.C && a.draw_active[bd];
   a.qpos[i] = in ? pos : -1;
   a.qids[i] = in ? a.draw_ids[bd * a.C + pos] : 0;
+  // k, v of the slot row (its noise token) land at its position in the draw
+  // canvas, whose other rows are copies of canvas b's
+  if (a.kv_row_slot) a.kv_row_slot[i] = in ? (int32_t)(bd * a.C + pos) : -1;
+}
+
+// copies of canvas b's k, v rows (at canvas slot b*nd) into its other draws
+// (slots b*nd + 1 .. b*nd + nd - 1), flagged canvases only; 16-byte chunks
+__global__ __launch_bounds__(256) void slot_copy_kv_kernel(SlotArgs a, uint4 *k, uint4 *v,
+                                                           int64_t canvas_chunks) {
+  const int64_t b = blockIdx.y;
+  if (!a.canvas_flag[b]) return;
+  const int64_t src = b * a.n_draws * canvas_chunks;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < canvas_chunks;
+       c += (int64_t)gridDim.x * 256) {
+    const uint4 kk = k[src + c], vv = v[src + c];
+    for (int j = 1; j < a.n_draws; ++j) {
+      k[src + j * canvas_chunks + c] = kk;
+      v[src + j * canvas_chunks + c] = vv;
+    }
+  }
 }
 
 // average of the draws in probability space: r = mean r_d, lp = ln mean e^(lp_d)
@@ -353,6 +375,17 @@ hipError_t launch_slot_draw_rows2(const SlotArgs &a, int32_t *row_active, float 
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(slot_draw_rows_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st, a,
                      row_active, rs_draw);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_copy_kv(const SlotArgs &a, void *k, void *v, int64_t kv_row_bytes,
+                               hipStream_t st) {
+  if (a.B == 0 || a.n_draws < 2) return hipSuccess;
+  if (kv_row_bytes % 16) return hipErrorInvalidValue;
+  const int64_t chunks = (int64_t)a.C * kv_row_bytes / 16;
+  const unsigned gx = (unsigned)std::min<int64_t>(cdiv64(chunks, 256), 16);
+  hipLaunchKernelGGL(slot_copy_kv_kernel, dim3(gx, (unsigned)a.B), dim3(256), 0, st, a,
+                     static_cast<uint4 *>(k), static_cast<uint4 *>(v), chunks);
   return hipGetLastError();
 }
 
