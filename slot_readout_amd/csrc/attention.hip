@@ -76,8 +76,11 @@ template <> __device__ inline float4 load4v<bf16>(const bf16 *p) {
 // [p0, p0 + plen) of the cache, offsets clamped against corrupt cu_seqlens, in
 // which case true is returned), then the canvas keys [lo, hi) that the tile's
 // +-W window can reach (every canvas key for gathered queries).
+// With ncp canvases packed in the tile (gathered queries of canvases that
+// share a prompt), the canvas keys are those of the ncp canvases, one after
+// the other ([0, ncp * C)).
 __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int64_t *p0o,
-                                 int64_t *plen, int *lo, int *hi) {
+                                 int64_t *plen, int *lo, int *hi, int ncp = 1) {
   const int pb = cb / a.canvas_per_prompt;
   int64_t p0 = a.cu[pb], p1 = a.cu[pb + 1];
   bool bad = false;
@@ -89,7 +92,7 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
   *plen = p1 - p0;
   if (a.qpos) {
     *lo = 0;
-    *hi = a.C;
+    *hi = a.C * ncp;
   } else {
     *lo = i0 - a.W > 0 ? i0 - a.W : 0;
     *hi = i0 + nq + a.W < a.C ? i0 + nq + a.W : a.C;   // exclusive
@@ -137,18 +140,22 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   __shared__ __attribute__((aligned(16))) T Vt[2][VSZ];
 
   // group = (canvas, kv head, split); its tiles (the query heads sharing the
-  // kv head x the query tiles) read the same K/V blocks and run on one XCD
+  // kv head x the query tiles) read the same K/V blocks and run on one XCD.
+  // With ncp > 1 a tile holds the gathered queries of ncp consecutive canvases
+  // that share a prompt (a read's draws): the prompt's K/V blocks are staged
+  // once for all of them.
   const int QN = a.qpos ? a.qn : a.C;   // queries per canvas
   const int nqt = (QN + NQ - 1) / NQ;
+  const int ncp = a.cpack > 1 ? a.cpack : 1;
   int grpi, tile;
-  if (!xcd_group_tile(a.nc * a.Hkv * a.nsplit, a.packed ? 1 : (a.Hq / a.Hkv) * nqt, &grpi, &tile))
+  if (!xcd_group_tile(a.nc / ncp * a.Hkv * a.nsplit, a.packed ? 1 : (a.Hq / a.Hkv) * nqt, &grpi, &tile))
     return;
   const int s = grpi % a.nsplit;
-  const int cb = grpi / a.nsplit / a.Hkv;
+  const int cb = grpi / a.nsplit / a.Hkv * ncp;   // the tile's first canvas
   // packed: h is the kv group's first query head and every column names its own
   const int h = (grpi / a.nsplit % a.Hkv) * (a.Hq / a.Hkv) + (a.packed ? 0 : tile / nqt);
   const int qt = a.packed ? 0 : tile % nqt;
-  if (a.active && !a.active[cb]) return;
+  if (a.active && ncp == 1 && !a.active[cb]) return;
   const int G = a.Hq / a.Hkv, g = h / G;
   const int C = a.C, W = a.W;
   const int i0 = qt * NQ;
@@ -157,7 +164,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 
   int64_t p0, plen;
   int lo, hi;
-  const bool bad = tile_keys(a, cb, i0, NQ, &p0, &plen, &lo, &hi);
+  const bool bad = tile_keys(a, cb, i0, NQ, &p0, &plen, &lo, &hi, ncp);
   if (bad && a.flags && threadIdx.x == 0 && s == 0 && qt == 0 && h == 0)
     atomicOr(a.flags, DG_FLAG_BAD_SEQLENS);
   const int64_t nkeys = plen + (hi - lo);
@@ -178,13 +185,16 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   // q rows: canvas positions, or the compact rows of gathered queries
   const T *qbase = static_cast<const T *>(a.q) + (int64_t)cb * (a.qpos ? QN : C) * q_stride +
                    (int64_t)h * HD;
-  // query index and head of each of the lane's columns (packed: c -> (c / QN, c % QN))
-  int cq[QB], chd[QB];
+  // query index, head and canvas (offset from cb) of each of the lane's
+  // columns (packed: c -> canvas c / (G QN), head c / QN % G, query c % QN)
+  int cq[QB], chd[QB], ccv[QB];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int c = i0 + w * QB * 16 + jb * 16 + col;
-    cq[jb] = a.packed ? (c < G * QN ? c % QN : QN) : c;
-    chd[jb] = a.packed ? (c < G * QN ? c / QN : 0) : 0;
+    const bool in = c < ncp * G * QN;
+    cq[jb] = a.packed ? (in ? c % QN : QN) : c;
+    chd[jb] = a.packed ? (in ? c / QN % G : 0) : 0;
+    ccv[jb] = a.packed && in ? c / (G * QN) : 0;
   }
   const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
   const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
@@ -192,16 +202,18 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const T *kc = static_cast<const T *>(a.k) + cbase;
   const T *vc = static_cast<const T *>(a.v) + cbase;
 
-  // canvas position of each query column of the lane; a column past the
-  // canvas (or a gathered query without a position) loads zeros and sees no
-  // canvas key
+  // canvas position of each query column of the lane (packed canvases: in the
+  // concatenation of the tile's canvases, ccv * C + position); a column past
+  // the canvas (or a gathered query without a position, or of an inactive
+  // canvas) loads zeros and sees no canvas key
   int qp[QB];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int qi = cq[jb];
     int p = qi;
-    if (a.qpos) p = qi < QN ? a.qpos[(int64_t)cb * QN + qi] : -1;
-    qp[jb] = p >= 0 && p < C ? p : -(1 << 20);
+    if (a.qpos) p = qi < QN ? a.qpos[(int64_t)(cb + ccv[jb]) * QN + qi] : -1;
+    if (ncp > 1 && a.active && !a.active[cb + ccv[jb]]) p = -1;
+    qp[jb] = p >= 0 && p < C ? ccv[jb] * C + p : -(1 << 20);
   }
   // a wave none of whose columns holds a query (past the canvas end, or past
   // the few gathered queries of a read) only helps stage K and V
@@ -212,7 +224,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   frag qf[QB][KS];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
-    const int qrow = a.qpos ? cq[jb] : qp[jb];
+    const int qrow = a.qpos ? ccv[jb] * QN + cq[jb] : qp[jb];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qp[jb] >= 0)
@@ -374,10 +386,12 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 #pragma unroll
     for (int jb = 0; jb < QB; ++jb) {
       if (!full) {
-        // canvas keys: visible iff |key - qp| <= W, i.e. kl in [qrel - W, qrel + W]
+        // canvas keys: visible iff |key - qp| <= W, i.e. kl in [qrel - W, qrel +
+        // W], and (packed canvases) the key is of the column's own canvas
         const int qrel = qp[jb] - d.k0;
-        const int klo_ok = d.canvas ? qrel - W : -1;
-        const int khi_ok = d.canvas ? min(qrel + W, d.rem - 1) : d.rem - 1;
+        const int cv0 = ccv[jb] * C - d.k0;   // the column's canvas: [cv0, cv0 + C)
+        const int klo_ok = d.canvas ? max(qrel - W, cv0) : -1;
+        const int khi_ok = d.canvas ? min(min(qrel + W, cv0 + C - 1), d.rem - 1) : d.rem - 1;
 #pragma unroll
         for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
@@ -507,17 +521,18 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int qi = cq[jb], hq = h + chd[jb];
+    const int64_t cbq = cb + ccv[jb];   // the column's canvas
     const float L = group4_sum(grp == 0 ? oacc[HD / 16][jb][0] : 0.f);
     if (qi >= QN) continue;
     if (a.nsplit == 1) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      TO *o = static_cast<TO *>(a.o) + (((int64_t)cb * QN + qi) * a.Hq + hq) * HD;
+      TO *o = static_cast<TO *>(a.o) + ((cbq * QN + qi) * a.Hq + hq) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[rb * 16 + grp * 4 + r] = from_f<TO>(oacc[rb][jb][r] * inv);
     } else {
-      const int64_t row = ((int64_t)cb * a.Hq + hq) * QN + qi;
+      const int64_t row = (cbq * a.Hq + hq) * QN + qi;
       TO *po = static_cast<TO *>(a.part_o) + ((int64_t)s * R + row) * HD;
 #pragma unroll
       for (int rb = 0; rb < HD / 16; ++rb) store4v<TO>(po + rb * 16 + grp * 4, oacc[rb][jb]);
@@ -551,9 +566,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int g = SG > 1 ? lane / C4 : 0;
   const int c0 = SG > 1 ? lane % C4 : lane;
+  const int ncp = a.cpack > 1 ? a.cpack : 1;
   int64_t p0, plen;
   int lo, hi;
-  tile_keys(a, (int)cb, qi / NQ * NQ, NQ, &p0, &plen, &lo, &hi);
+  tile_keys(a, (int)(cb / ncp * ncp), qi / NQ * NQ, NQ, &p0, &plen, &lo, &hi, ncp);
   const int64_t nk = plen + (hi - lo);
   const int ns = (int)(cdiv64(nk, a.chunk) < a.nsplit ? cdiv64(nk, a.chunk) : a.nsplit);
   const float2 *ml = a.part_ml + row;
@@ -612,8 +628,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 128; }
 
-bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim) {
-  return gathered && Hq > Hkv && (int64_t)(Hq / Hkv) * qn <= attn_query_tile(head_dim);
+int attn_cpack(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp) {
+  if (!gathered || cpp <= 1) return 1;
+  return (int64_t)cpp * (Hq / Hkv) * qn <= attn_query_tile(head_dim) ? cpp : 1;
+}
+
+bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp) {
+  if (!gathered) return false;
+  if (attn_cpack(qn, gathered, Hq, Hkv, head_dim, cpp) > 1) return true;
+  return Hq > Hkv && (int64_t)(Hq / Hkv) * qn <= attn_query_tile(head_dim);
 }
 static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               AttnShape<float, 64>::NW * AttnShape<float, 64>::QB * 16 == 128 &&
@@ -621,14 +644,16 @@ static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               "query tile sizes");
 
 void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
-               int max_len, int *nsplit, int *chunk, int *nsplit_bound) {
+               int max_len, int cpp, int *nsplit, int *chunk, int *nsplit_bound) {
   const int nq = attn_query_tile(head_dim);
   const int nk = head_dim == 512 ? 32 : 64;
-  const int64_t base = attn_packed(qn, gathered, Hq, Hkv, head_dim)
-                           ? (int64_t)nc * Hkv
+  const int ncp = attn_cpack(qn, gathered, Hq, Hkv, head_dim, cpp);
+  const int64_t base = attn_packed(qn, gathered, Hq, Hkv, head_dim, cpp)
+                           ? (int64_t)nc / ncp * Hkv
                            : (int64_t)nc * Hq * cdiv64(qn, nq);
-  // most keys one query tile can see: the prompt plus its window span
-  const int64_t win = gathered ? C : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
+  // most keys one query tile can see: the prompt plus its window span (every
+  // canvas key of the tile's canvases for gathered queries)
+  const int64_t win = gathered ? (int64_t)C * ncp : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
   const int64_t span = (int64_t)max_len + win;
   // about two workgroups per CU
   const int target = 512;
@@ -656,13 +681,19 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   const int QN = a.qpos ? a.qn : a.C;
   if (QN <= 0) return hipSuccess;
   AttnArgs b = a;
-  b.packed = attn_packed(QN, a.qpos != nullptr, a.Hq, a.Hkv, HD) ? 1 : 0;
-  const dim3 grid = xcd_grid((int64_t)a.nc * a.Hkv * a.nsplit, b.packed ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
+  const bool gathered = a.qpos != nullptr;
+  // canvases packed in one tile must be consecutive in k, v (kv_cmul 1)
+  const int cpp = a.kv_cmul > 1 ? 1 : a.canvas_per_prompt;
+  b.cpack = attn_cpack(QN, gathered, a.Hq, a.Hkv, HD, cpp);
+  b.packed = attn_packed(QN, gathered, a.Hq, a.Hkv, HD, cpp) ? 1 : 0;
+  if (a.nc % b.cpack) return hipErrorInvalidValue;
+  const dim3 grid = xcd_grid((int64_t)a.nc / b.cpack * a.Hkv * a.nsplit,
+                             b.packed ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
   hipLaunchKernelGGL((attn_kernel<T, HD, PREC>), grid, dim3(64 * NW), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD, PREC>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD, PREC>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 

@@ -123,13 +123,16 @@ struct AttnPlan {
 
 // qn queries per canvas: every position, or qn gathered ones; prec: fp32
 // partials (the split-probability attention of slot reads)
-AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1, bool prec = false) {
+// cpp: consecutive canvases sharing a prompt (gathered queries of such
+// canvases may share a tile)
+AttnPlan plan_attention(const dg_dims &d, int nc, int max_prompt, int qn = -1, bool prec = false,
+                        int cpp = 1) {
   AttnPlan p;
   const bool gathered = qn >= 0;
   if (!gathered) qn = d.canvas;
   int bound = 1;
   dg::attn_plan(nc, d.canvas, qn, gathered, d.n_q_heads, d.n_kv_heads, window_of(d), d.head_dim,
-                max_prompt, &p.nsplit, &p.chunk, &bound);
+                max_prompt, cpp, &p.nsplit, &p.chunk, &bound);
   // partials sized by the bound, so that a workspace planned for max_prompt
   // also holds the partials of every shorter prompt (the rounded split count
   // is not monotone in the prompt length)
@@ -265,8 +268,10 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   p.v = a.take(M * nkv * ts);
   p.o = a.take(hrows * nq * (prec ? sizeof(float) : ts));
   const int qn = full ? -1 : S;
-  p.first = plan_attention(d, p.spec ? ncmax : B, max_prompt, qn, prec);
-  p.draws = plan_attention(d, ncmax, max_prompt, qn, prec);
+  // the two-pass first read (one canvas per prompt); the one-pass read or the
+  // draw pass (canvases of one prompt: first read and draws, or the draws)
+  p.first = plan_attention(d, B, max_prompt, qn, prec, 1);
+  p.draws = plan_attention(d, ncmax, max_prompt, qn, prec, p.spec ? nd + 1 : nd);
   const size_t po = p.first.part_o > p.draws.part_o ? p.first.part_o : p.draws.part_o;
   const size_t pm = p.first.part_ml > p.draws.part_ml ? p.first.part_ml : p.draws.part_ml;
   p.part_o = a.take(po);

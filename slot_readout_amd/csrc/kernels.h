@@ -141,6 +141,9 @@ struct AttnArgs {
   int prec;
   // canvas cb's keys and values are canvas cb * kv_cmul of k and v (0 or 1: cb)
   int kv_cmul;
+  // gathered queries of cpack consecutive canvases share a tile (set by the
+  // launcher; they share their prompt)
+  int cpack;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
 };
 
@@ -167,15 +170,19 @@ hipError_t launch_vocab_merge(const VocabMergeArgs &a, hipStream_t st);
 
 // attention: query rows per workgroup, split-KV planning, launch (+ merge)
 int attn_query_tile(int head_dim);
-// whether gathered queries pack the G query heads of a kv head into one tile
-bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim);
+// canvases whose gathered queries share one tile: cpp (the canvases that
+// share a prompt) when all their queries of a kv group fit a query tile, else 1
+int attn_cpack(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp);
+// whether gathered queries pack the G query heads of a kv head (and the
+// cpack canvases) into one tile
+bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp);
 // qn queries per canvas; gathered: queries at arbitrary positions (every
 // canvas key is a candidate) instead of consecutive ones.  nsplit_bound (may
 // be null) receives a split count that is >= nsplit for every prompt length
 // up to max_len and non-decreasing in max_len: partial buffers sized with it
 // fit any shorter prompt.
 void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
-               int max_len, int *nsplit, int *chunk, int *nsplit_bound);
+               int max_len, int cpp, int *nsplit, int *chunk, int *nsplit_bound);
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);

@@ -323,3 +323,20 @@ def test_slot_read_full_canvas(torch_cuda, name, over, B, prompt, scales):
     ok = (ref["status"] == oracle.SLOT_OK) & (g["draws_used"] == g2["draws_used"])
     tol = 2e-4 if dt == "f32" else 1e-2
     assert np.abs(g["logprobs"][ok] - g2["logprobs"][ok]).max() <= tol
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "reads512"])
+def test_slot_read_draws_share_a_tile_at_canvas_edges(torch_cuda, name):
+    """The draws of a canvas read its prompt in one tile (their gathered
+    queries side by side, each draw's own canvas keys behind the prompt's):
+    slots at positions 0, 1, C-2 and C-1, where a window that crossed into the
+    neighbouring draw's keys would show, against the oracle."""
+    inp = make_inputs(config(name, n_slots=4), batch=3, prompt_override=("fixed", 90))
+    C = inp["dims"].canvas
+    for b in range(3):
+        inp["slot_pos"][b] = [0, 1, C - 2, C - 1]
+        inp["canvas_ids"][b, [0, 1, C - 2, C - 1]] = inp["dims"].mask_id
+    ref = oracle.slot_read(inp)
+    assert (ref["draws_used"] == inp["n_draws"]).any()
+    g = _read(inp)
+    _check_slots(g, ref, inp, inp["dims"].dtype, f"draw tile edges {name}")
