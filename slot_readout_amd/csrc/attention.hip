@@ -104,8 +104,13 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
 // p = hi + lo with hi = bf16(p) and lo = bf16(p - hi) (one more MFMA per V
 // fragment), and O, its split partials and the output are fp32.  The result
 // then carries the rounding of the stored q, k, v only, not that of p and o.
-template <typename T, int HD, bool PREC = false>
-__global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnArgs a) {
+// PATCH (a read's draws, a.kpatch set): canvas cb's canvas keys are those of
+// its base canvas cb / canvas_per_prompt, except at the slot positions of the
+// draws (canvases with cb % canvas_per_prompt >= patch_from), whose keys and
+// values are the slot rows cb * qn + s of kpatch / vpatch: the draws differ
+// from their base canvas only there, so no draw canvas's k, v are stored.
+template <typename T, int HD, bool PREC = false, bool PATCH = false>
+__global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T) == 2 ? 4 : 1)) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int QB = AttnShape<T, HD>::QB;
@@ -117,6 +122,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   constexpr int VEC = 16 / sizeof(T);
   constexpr bool TR = sizeof(T) == 2;
   static_assert(!PREC || TR, "split probabilities: bf16 storage");
+  // slot index at each canvas position of the tile's canvases (-1: none)
+  __shared__ short smap[PATCH ? DG_MAX_CANVAS : 1];
   // output / partial type
   using TO = typename std::conditional<PREC, float, T>::type;
   // bf16 rows of K and V are HD + 16 elements apart: with that stride both the
@@ -199,6 +206,19 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
   const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
   const int64_t cbase = (int64_t)cb * (a.kv_cmul > 1 ? a.kv_cmul : 1) * C * kv_stride + (int64_t)g * HD;
+  const int cpp = a.canvas_per_prompt;
+  if constexpr (PATCH) {
+    // the canvases of a tile are draws of one base canvas: they share its slot
+    // positions; in slot order, so a later slot at the same position wins
+    for (int i = threadIdx.x; i < C; i += NT) smap[i] = -1;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int sl = 0; sl < QN; ++sl) {
+        const int p = a.qpos[(int64_t)cb * QN + sl];
+        if (p >= 0 && p < C) smap[p] = (short)sl;
+      }
+    __syncthreads();
+  }
   const T *kc = static_cast<const T *>(a.k) + cbase;
   const T *vc = static_cast<const T *>(a.v) + cbase;
 
@@ -322,7 +342,32 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW)) void attn_kernel(AttnA
   }
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   u32x4 kr[PF][CH], vr[PF][CH];
+  // PATCH: the source of row r of block d (plain loads with per-lane
+  // addresses): prompt rows from the block (blk), canvas rows from the base
+  // canvas (base) or the draw's slot rows (patch).  Rows past the block's keys
+  // read its first row: their scores are masked and their probabilities 0.
+  auto src_row = [&](const Blk &d, int r, const T *blk, const T *base, const T *patch) -> const T * {
+    const int rr = r < d.rem ? r : 0;
+    if (!d.canvas) return blk + (int64_t)rr * kv_stride;
+    const int kk = d.k0 + rr;                  // key of the tile's concatenated canvases
+    const int cj = cb + kk / C, pos = kk % C;  // its canvas and position
+    const int sl = cj % cpp >= a.patch_from ? (int)smap[pos] : -1;
+    return sl >= 0 ? patch + ((int64_t)cj * QN + sl) * kv_stride + (int64_t)g * HD
+                   : base + ((int64_t)(cj / cpp) * C + pos) * kv_stride;
+  };
   auto fetch = [&](const Blk &d, u32x4 (&xk)[CH], u32x4 (&xv)[CH]) {
+    if constexpr (PATCH) {
+      const T *kb0 = static_cast<const T *>(a.k) + (int64_t)g * HD;
+      const T *vb0 = static_cast<const T *>(a.v) + (int64_t)g * HD;
+      const T *kpt = static_cast<const T *>(a.kpatch), *vpt = static_cast<const T *>(a.vpatch);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int kcol = kgo[i] - kkey[i] * (int)kv_stride, vcol = vgo[i] - vkey[i] * (int)kv_stride;
+        xk[i] = *reinterpret_cast<const u32x4 *>(src_row(d, kkey[i], d.kb, kb0, kpt) + kcol);
+        xv[i] = *reinterpret_cast<const u32x4 *>(src_row(d, vkey[i], d.vb, vb0, vpt) + vcol);
+      }
+      return;
+    }
     const int nbytes = d.rem * (int)kv_stride * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(d.kb), (short)0, nbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(d.vb), (short)0, nbytes, 0x00020000);
@@ -674,7 +719,7 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
   *chunk = ck;
 }
 
-template <typename T, int HD, bool PREC>
+template <typename T, int HD, bool PREC, bool PATCH>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NW = AttnShape<T, HD>::NW;
   constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
@@ -689,7 +734,7 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   if (a.nc % b.cpack) return hipErrorInvalidValue;
   const dim3 grid = xcd_grid((int64_t)a.nc / b.cpack * a.Hkv * a.nsplit,
                              b.packed ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
-  hipLaunchKernelGGL((attn_kernel<T, HD, PREC>), grid, dim3(64 * NW), 0, st, b);
+  hipLaunchKernelGGL((attn_kernel<T, HD, PREC, PATCH>), grid, dim3(64 * NW), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
@@ -697,13 +742,23 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool attn_patch_supported(int head_dim, bool bf) { return bf && head_dim == 64; }
+
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st) {
   if (a.prec && !bf) return hipErrorInvalidValue;
-  if (bf && head_dim == 64)
-    return a.prec ? launch_attn_t<bf16, 64, true>(a, st) : launch_attn_t<bf16, 64, false>(a, st);
+  const bool patch = a.kpatch != nullptr;
+  // patched draws: gathered queries of canvases grouped by base canvas, k/v
+  // not duplicated (kv_cmul 1), canvas lengths within the position map
+  if (patch && (!attn_patch_supported(head_dim, bf) || !a.prec || !a.qpos || a.kv_cmul > 1 || a.C > DG_MAX_CANVAS ||
+                !a.vpatch || a.canvas_per_prompt < 1))
+    return hipErrorInvalidValue;
+  if (bf && head_dim == 64) {
+    if (patch) return a.prec ? launch_attn_t<bf16, 64, true, true>(a, st) : hipErrorInvalidValue;
+    return a.prec ? launch_attn_t<bf16, 64, true, false>(a, st) : launch_attn_t<bf16, 64, false, false>(a, st);
+  }
   if (bf && head_dim == 512)
-    return a.prec ? launch_attn_t<bf16, 512, true>(a, st) : launch_attn_t<bf16, 512, false>(a, st);
-  if (!bf && head_dim == 64) return launch_attn_t<float, 64, false>(a, st);
+    return a.prec ? launch_attn_t<bf16, 512, true, false>(a, st) : launch_attn_t<bf16, 512, false, false>(a, st);
+  if (!bf && head_dim == 64) return launch_attn_t<float, 64, false, false>(a, st);
   return hipErrorInvalidValue;
 }
 

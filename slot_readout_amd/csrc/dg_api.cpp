@@ -212,9 +212,9 @@ LoopPlan plan_loop(const dg_dims &d, int B, int max_prompt) {
 
 struct SlotPlan {
   size_t q, k, v, o, part_o, part_ml, proj_part, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
-      rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, total;
+      rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, kpatch, vpatch, total;
   AttnPlan first, draws;
-  bool spec, prec, full;
+  bool spec, prec, full, patch;
 };
 
 // Whether the draws are computed for every canvas in the first read's pass.
@@ -255,8 +255,13 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   // as bf16 hi | lo halves (see read_prec)
   const bool prec = d.dtype == DG_BF16;
   p.prec = prec;
+  // patched draws (slot-row order, head_dim 64 bf16): the draws read their
+  // base canvas's k, v with their own slot rows in place, so only the base
+  // canvases' k, v are stored, plus the draws' slot rows
+  p.patch = !full && nd > 1 && dg::attn_patch_supported(d.head_dim, d.dtype == DG_BF16);
   const int ncmax = p.spec ? B * (nd + 1) : (nd > 1 ? B * nd : B);
   const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
+  const size_t kvrows = p.patch ? (size_t)B * d.canvas : M;   // rows of k, v
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
   const int nvt = d.vocab / dg::VTILE;
   const size_t nrows = (size_t)B * S * (p.spec ? nd + 1 : (nd > 1 ? nd : 1));
@@ -264,8 +269,10 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   const size_t hrows = full ? M : nrows;
   Arena a;
   p.q = a.take(hrows * nq * ts);
-  p.k = a.take(M * nkv * ts);
-  p.v = a.take(M * nkv * ts);
+  p.k = a.take(kvrows * nkv * ts);
+  p.v = a.take(kvrows * nkv * ts);
+  p.kpatch = a.take(p.patch ? nrows * nkv * ts : 0);
+  p.vpatch = a.take(p.patch ? nrows * nkv * ts : 0);
   p.o = a.take(hrows * nq * (prec ? sizeof(float) : ts));
   const int qn = full ? -1 : S;
   // the two-pass first read (one canvas per prompt); the one-pass read or the
@@ -302,9 +309,9 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   p.rows = a.take(nrows * sizeof(int32_t));
   p.qpos = a.take(nrows * sizeof(int32_t));
   p.qids = a.take(nrows * sizeof(int32_t));
-  p.kv_row_base = a.take(p.spec && !full ? (size_t)B * d.canvas * sizeof(int32_t) : 0);
+  p.kv_row_base = a.take(p.spec && !full && !p.patch ? (size_t)B * d.canvas * sizeof(int32_t) : 0);
   // one-pass: draw slot rows' k, v rows; two-pass: those of the draw pass
-  p.kv_row_slot = a.take(!full && nd > 1 ? nrows * sizeof(int32_t) : 0);
+  p.kv_row_slot = a.take(!full && nd > 1 && !p.patch ? nrows * sizeof(int32_t) : 0);
   p.stats = a.take(nrows * nvt * sizeof(float4));
   p.rowstat = a.take(nrows * sizeof(float2));
   p.lab_logit = a.take(nrows * DG_MAX_LABELS * sizeof(float));
@@ -383,6 +390,11 @@ struct Gather {
   // canvas c's k, v are written to / read from canvas slot c * kv_cmul (the
   // two-pass read keeps each canvas's k, v where its first draw will be)
   int kv_cmul = 1;
+  // patched draws: the draws' slot rows of k, v (attention reads the base
+  // canvases' k, v elsewhere), for canvases c with c % canvases_per_prompt >=
+  // patch_from
+  const void *kpatch = nullptr, *vpatch = nullptr;
+  int patch_from = 0;
 };
 
 // S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
@@ -464,6 +476,9 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.canvas_per_prompt = canvas_per_prompt;
   aa.prec = gq.prec ? 1 : 0;
   aa.kv_cmul = gq.kv_cmul;
+  aa.kpatch = gq.kpatch;
+  aa.vpatch = gq.vpatch;
+  aa.patch_from = gq.patch_from;
   DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
   DG_MARK(sg, DG_STAGE_ATTENTION, 1);
@@ -902,9 +917,11 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
   sa.draw_ids = at<int32_t>(workspace, p.draw_ids);
   sa.qpos = at<int32_t>(workspace, p.qpos);
   sa.qids = at<int32_t>(workspace, p.qids);
-  const bool kv_copy = p.spec && !full;
+  const bool kv_copy = p.spec && !full && !p.patch;
   sa.kv_row_base = kv_copy ? at<int32_t>(workspace, p.kv_row_base) : nullptr;
-  sa.kv_row_slot = !full && n_draws > 1 ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
+  sa.kv_row_slot = !full && n_draws > 1 && !p.patch ? at<int32_t>(workspace, p.kv_row_slot) : nullptr;
+  void *kpatch = p.patch ? at<char>(workspace, p.kpatch) : nullptr;
+  void *vpatch = p.patch ? at<char>(workspace, p.vpatch) : nullptr;
   sa.mask_id = d.mask_id;
   sa.full_canvas = full ? 1 : 0;
   Gather gq;
@@ -984,7 +1001,8 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
     qa.col1 = qa.nq + 2 * qa.nkv;
     qa.kv_row = sa.kv_row_base;
     qa.part = proj_part;
-    qa.kv_copies = G - 1;   // the draws' copies of canvas b's k, v
+    // patched draws: canvas b's k, v once (rows b*C), read by every draw
+    qa.kv_copies = p.patch ? 0 : G - 1;   // else the draws' copies of canvas b's k, v
     DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "k/v projection launch");
     dg::QkvArgs qg = qa;
     qg.kv_copies = 0;
@@ -993,9 +1011,19 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
     qg.C = n_slots;
     qg.col0 = 0;
     qg.kv_row = sa.kv_row_slot;
+    if (p.patch) {   // the slot rows' k, v to their compact rows
+      qg.k = kpatch;
+      qg.v = vpatch;
+      qg.kv_row = nullptr;
+    }
     DG_TRY_HIP(dg::launch_qkv(qg, bf, st), "slot-row projection launch");
     Gather gd = gq;
     gd.qkv_done = true;
+    if (p.patch) {   // the first read (j = 0) keeps its base rows
+      gd.kpatch = kpatch;
+      gd.vpatch = vpatch;
+      gd.patch_from = 1;
+    }
     s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
                   p.draws, part_o, part_ml, proj_part, h, st, Stages(), gd);
     if (s != DG_OK) return s;
@@ -1016,7 +1044,7 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
   sa.grp_first = 1;
   sa.grp_draw = n_draws;
   sa.off_draw = 0;
-  const bool draw_copies = !full && n_draws > 1;
+  const bool draw_copies = !full && n_draws > 1 && !p.patch;
   Gather g1 = gq;
   if (draw_copies) g1.kv_cmul = n_draws;
   DG_TRY_HIP(dg::launch_slot_rows(sa, st), "slot row launch");
@@ -1066,6 +1094,34 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
     qd.part = proj_part;
     DG_TRY_HIP(dg::launch_qkv(qd, bf, st), "draw slot-row projection launch");
     gd.qkv_done = true;
+  } else if (p.patch) {
+    // patched draws: the draws read canvas b's k, v (rows b*C) with their own
+    // slot rows, projected here to compact rows
+    dg::QkvArgs qd{};
+    qd.ids = sa.qids;
+    qd.embed = w->embed;
+    qd.wq = w->wq;
+    qd.wk = w->wk;
+    qd.wv = w->wv;
+    qd.q = q;
+    qd.k = kpatch;
+    qd.v = vpatch;
+    qd.active = sa.draw_active;
+    qd.M = (int64_t)batch * n_draws * n_slots;
+    qd.d = d.d_model;
+    qd.nq = d.n_q_heads * d.head_dim;
+    qd.nkv = d.n_kv_heads * d.head_dim;
+    qd.vocab = d.vocab;
+    qd.C = n_slots;            // rows per draw canvas (its active flag)
+    qd.q_scale = q_scale_of(d);
+    qd.col0 = 0;
+    qd.col1 = qd.nq + 2 * qd.nkv;
+    qd.part = proj_part;
+    DG_TRY_HIP(dg::launch_qkv(qd, bf, st), "draw slot-row projection launch");
+    gd.qkv_done = true;
+    gd.kpatch = kpatch;
+    gd.vpatch = vpatch;
+    gd.patch_from = 0;
   }
   s = run_block(d, w, kv, batch * n_draws, n_draws, sa.draw_ids, nullptr, sa.draw_active, nullptr,
                 q, k, v, o, p.draws, part_o, part_ml, proj_part, h, st, Stages(), gd);

@@ -144,6 +144,14 @@ struct AttnArgs {
   // gathered queries of cpack consecutive canvases share a tile (set by the
   // launcher; they share their prompt)
   int cpack;
+  // Draws read from their base canvas (see attn_patch_supported):
+  // with kpatch set, canvas cb's canvas keys are those of canvas
+  // cb / canvas_per_prompt of k, v, except, for canvases with
+  // cb % canvas_per_prompt >= patch_from, at the positions qpos[cb*qn + s]
+  // (shared by the canvases of a base), where they are row cb*qn + s of
+  // kpatch / vpatch ([nc*qn, Hkv*hd]).
+  const void *kpatch, *vpatch;
+  int patch_from;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
 };
 
@@ -184,6 +192,9 @@ bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp);
 void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
                int max_len, int cpp, int *nsplit, int *chunk, int *nsplit_bound);
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
+// whether draws can read their base canvas's k, v with patched slot rows
+// (the bf16 read's precise attention at head_dim 64)
+bool attn_patch_supported(int head_dim, bool bf);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
 // Multi-step loop bookkeeping (one workgroup per canvas).  loop_init: commit

@@ -87,7 +87,7 @@ def test_noalloc_read_rejects_reads_beyond_the_scratch(torch_cuda):
     import torch
     from slot_readout_amd import dg
     from slot_readout_amd.runtime import DeviceProblem
-    inp = make_inputs(config("reads512"), batch=128, prompt_override=("fixed", 16))
+    inp = make_inputs(config("reads512"), batch=256, prompt_override=("fixed", 16))
     dev = DeviceProblem(inp, with_embed_t=False)
     need = dg.dg_slot_read_workspace(dev.dims, dev.B, dev.S, dev.max_prompt, inp["n_draws"])
     assert need > dg.DG_NOALLOC_SCRATCH_BYTES
