@@ -10,5 +10,5 @@ from .dg_oracle import (  # noqa: F401
     commit, denoise_loop, label_read, slot_read_canvas, slot_read, slot_read_staged, NearTies, argmax_near_ties,
     commit_near_ties, best_near_ties, SLOT_OK, SLOT_BAD_POS, SLOT_BAD_COUNT,
     SLOT_BAD_LABEL, SLOT_BAD_NOISE, SLOT_NOT_ASKED, MAX_LABELS, E4M3_MAX, e4m3_row_exponent, e4m3_encode,
-    e4m3_decode, quantize_head_e4m3, dequantize_head_e4m3,
+    e4m3_decode, quantize_rows_e4m3, quantize_head_e4m3, dequantize_head_e4m3, fp8_activations,
 )

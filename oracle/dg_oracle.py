@@ -197,7 +197,7 @@ def lm_logits(h, head, scale, chunk=32768):
 
 
 # --------------------------------------------------------------------------
-# FP8 (e4m3) copy of the LM head: weight-only FP8, bf16 activations
+# FP8 (e4m3) rows: the LM head's copy and, optionally, the hidden rows
 # --------------------------------------------------------------------------
 E4M3_MAX = 448.0   # largest finite e4m3 value (OCP 8-bit float, 4 exponent bits, bias 7)
 
@@ -208,30 +208,31 @@ def e4m3_row_exponent(amax):
     With amax = m 2^E, 1 <= m < 2, and 448 = 1.75 2^8: e = E - 8, plus 1 when
     m > 1.75.  Exact (no division).
     """
-    amax = np.asarray(amax, dtype=np.float32)
+    amax = np.asarray(amax, dtype=np.float64)
     f, x = np.frexp(amax)                  # amax = f 2^x, 0.5 <= f < 1
-    m = 2.0 * f.astype(np.float64)         # 1 <= m < 2, E = x - 1
+    m = 2.0 * f                            # 1 <= m < 2, E = x - 1
     e = (x - 1) - 8 + (m > 1.75)
     return np.where(amax > 0, e, 0).astype(np.int64)
 
 
 def e4m3_encode(q):
     """Round-to-nearest-even to e4m3 codes (uint8) of values |q| <= 448, taken
-    in float32: subnormals (|q| < 2^-6) are multiples of 2^-9, normals have a
-    3-bit mantissa; a mantissa that rounds up to 8 carries into the exponent
-    (for subnormals that carry is the code of 2^-6 itself)."""
-    q = np.asarray(q, dtype=np.float32)
+    in float64 (exact for float32 and bf16 inputs): subnormals (|q| < 2^-6) are
+    multiples of 2^-9, normals have a 3-bit mantissa; a mantissa that rounds up
+    to 8 carries into the exponent (for subnormals that carry is the code of
+    2^-6 itself)."""
+    q = np.asarray(q, dtype=np.float64)
     a = np.abs(q)
     sign = (np.signbit(q)).astype(np.uint8) << 7
     code = np.zeros(a.shape, dtype=np.int64)
-    sub = a < np.float32(2.0 ** -6)
-    code[sub] = np.rint(a[sub] * np.float32(512.0)).astype(np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] * 512.0).astype(np.int64)
     nrm = ~sub
     if nrm.any():
         _, x = np.frexp(a[nrm])
         E = x - 1                                           # a = (1 + f) 2^E
-        frac = (a[nrm] / np.ldexp(np.float32(1.0), E).astype(np.float32)) - np.float32(1.0)
-        m3 = np.rint(frac * np.float32(8.0)).astype(np.int64)
+        frac = a[nrm] / np.ldexp(1.0, E) - 1.0              # exact
+        m3 = np.rint(frac * 8.0).astype(np.int64)
         carry = m3 == 8
         E = E + carry
         m3 = np.where(carry, 0, m3)
@@ -250,19 +251,35 @@ def e4m3_decode(codes):
     return s * val
 
 
-def quantize_head_e4m3(head):
-    """Per vocabulary row: exponent e (e4m3_row_exponent of the row's largest
-    magnitude) and codes of head / 2^e.  The head is read as stored (bf16 values
-    are exact in float32).  Returns (codes uint8 [V, d], exps int64 [V])."""
-    h = np.asarray(head, dtype=np.float32)
-    e = e4m3_row_exponent(np.abs(h).max(axis=1))
-    q = h * np.ldexp(np.float32(1.0), -e).astype(np.float32)[:, None]   # exact: power of two
+def quantize_rows_e4m3(rows):
+    """Per row: exponent e (e4m3_row_exponent of the row's largest magnitude)
+    and the codes of row / 2^e, all in float64 (the division is exact: a power
+    of two).  Returns (codes uint8 [n, d], exps int64 [n])."""
+    x = np.asarray(rows, dtype=np.float64)
+    e = e4m3_row_exponent(np.abs(x).max(axis=1))
+    q = x * np.ldexp(1.0, -e)[:, None]
     return e4m3_encode(q), e
 
 
+def quantize_head_e4m3(head):
+    """quantize_rows_e4m3 of the LM head read as stored (bf16 values are exact
+    in float32 and float64).  Returns (codes uint8 [V, d], exps int64 [V])."""
+    return quantize_rows_e4m3(np.asarray(head, dtype=np.float32))
+
+
 def dequantize_head_e4m3(codes, exps):
-    """The head the FP8 LM head computes with: decode(code) 2^e, float64."""
+    """The rows an FP8 operand stands for: decode(code) 2^e, float64."""
     return e4m3_decode(codes) * np.exp2(np.asarray(exps, dtype=np.float64))[:, None]
+
+
+def fp8_activations(h):
+    """The hidden rows as the FP8 LM head sees them with FP8 activations: each
+    row quantised to e4m3 by the head's own rule (its power-of-two exponent,
+    round to nearest even) and decoded.  The pages name FP8 checkpoints
+    (24-ai.news, performance section) without a scale granularity; the reading
+    taken is one power-of-two scale per row for both operands."""
+    codes, e = quantize_rows_e4m3(h)
+    return dequantize_head_e4m3(codes, e)
 
 
 # --------------------------------------------------------------------------
@@ -319,7 +336,7 @@ def self_condition(p, E):
 # --------------------------------------------------------------------------
 def denoise_canvas(E, Wq, Wk, Wv, Wo, Kp, Vp, ids, dims, sc_in=None, lm_head=None,
                    logit_scale=1.0, row_scale=None, rows=None, need_sc=True,
-                   need_logits=False, exclude_id=None):
+                   need_logits=False, exclude_id=None, act_fp8=False):
     """One decoder-mode denoise step over one canvas (24-ai.news, "How is
     diffusion text generation different?": every canvas position is refined
     in parallel in one forward pass).
@@ -327,7 +344,8 @@ def denoise_canvas(E, Wq, Wk, Wv, Wo, Kp, Vp, ids, dims, sc_in=None, lm_head=Non
     ``rows`` restricts S2..S6 to those positions (S0/S1 keys and values are
     always computed for the whole canvas).  ``exclude_id`` removes one id from
     the vocabulary softmax (its logit becomes -inf): the multi-step loop
-    removes the mask id.  Returns a dict of float64 arrays.
+    removes the mask id.  ``act_fp8``: the LM head reads fp8_activations(h)
+    (hidden_out stays h).  Returns a dict of float64 arrays.
     """
     x = embed_input(E, ids, sc_in)
     q, k, v = qkv_project(x, Wq, Wk, Wv, dims.n_q_heads, dims.n_kv_heads, dims.head_dim)
@@ -337,7 +355,7 @@ def denoise_canvas(E, Wq, Wk, Wv, Wo, Kp, Vp, ids, dims, sc_in=None, lm_head=Non
     h = block_output(x[rows], o, Wo)
     s = logit_scale if row_scale is None else logit_scale * np.asarray(row_scale, F64)[rows]
     head = E if lm_head is None else lm_head
-    l = lm_logits(h, head, s)
+    l = lm_logits(fp8_activations(h) if act_fp8 else h, head, s)
     if exclude_id is not None:
         l[:, exclude_id] = -np.inf
     st = vocab_softmax(l)
@@ -352,7 +370,7 @@ def denoise_canvas(E, Wq, Wk, Wv, Wo, Kp, Vp, ids, dims, sc_in=None, lm_head=Non
 
 
 def denoise_step(inp, sc_in=None, row_scale=None, rows=None, canvases=None,
-                 need_sc=True, need_logits=False):
+                 need_sc=True, need_logits=False, act_fp8=False):
     """Run :func:`denoise_canvas` for each canvas of an input dict.
 
     Returns a list (one entry per canvas in ``canvases``).
@@ -370,7 +388,7 @@ def denoise_step(inp, sc_in=None, row_scale=None, rows=None, canvases=None,
             sc_in=None if sc_in is None else sc_in[b], lm_head=inp.get("lm_head"),
             logit_scale=inp["logit_scale"],
             row_scale=None if row_scale is None else row_scale[b],
-            rows=rows, need_sc=need_sc, need_logits=need_logits))
+            rows=rows, need_sc=need_sc, need_logits=need_logits, act_fp8=act_fp8))
     return res
 
 

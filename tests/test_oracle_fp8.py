@@ -67,3 +67,65 @@ def test_quantized_head_is_within_half_a_step_of_the_head():
     # each row's largest magnitude lands in the top binade: 256 <= |q| <= 448
     qmax = np.abs(q).max(axis=1)[np.arange(64) != 3]
     assert ((qmax > 224) & (qmax <= 448)).all()
+
+
+# ------------------------------------------------- FP8 activations --------
+def test_rows_are_quantised_in_float64_not_float32():
+    # 1.0625 + 2^-40 lies just above the tie between 1.0 and 1.125: the nearest
+    # code is 1.125.  Through float32 the value would become the tie itself and
+    # round to the even code 1.0.
+    x = np.array([[1.0625 + 2.0 ** -40, 448.0]])
+    codes, e = oracle.quantize_rows_e4m3(x)
+    assert e[0] == 0 and codes[0, 0] == 0x39 and codes[0, 1] == 0x7E
+    # an amax a hair above 448 needs the next exponent (float32 would round it to 448)
+    codes, e = oracle.quantize_rows_e4m3(np.array([[448.0 * (1 + 2.0 ** -40), 1.0]]))
+    assert e[0] == 1 and codes[0, 0] == 0x76   # 224 * (1 + tiny) -> 224 = 1.75 * 2^7
+
+
+def test_fp8_activations_on_the_grid_are_unchanged():
+    # rows whose entries are e4m3 values times the row's power of two come back
+    # exactly, so the FP8-activation logits equal the plain ones
+    rng = np.random.default_rng(12)
+    grid = oracle.e4m3_decode(np.arange(0x40, 0x7F))          # 2 .. 448, normal codes
+    h = rng.choice(grid, size=(6, 40)) * rng.choice([-1.0, 1.0], size=(6, 40))
+    h[:, 0] = 448.0                                            # fixes each row's exponent at 0
+    h *= np.exp2(np.arange(-3, 3))[:, None]                    # then 2^-3 .. 2^2
+    np.testing.assert_array_equal(oracle.fp8_activations(h), h)
+    head = rng.normal(size=(30, 40))
+    np.testing.assert_array_equal(oracle.lm_logits(oracle.fp8_activations(h), head, 2.0),
+                                  oracle.lm_logits(h, head, 2.0))
+
+
+def test_fp8_activations_scale_with_powers_of_two_and_stay_within_half_a_step():
+    rng = np.random.default_rng(13)
+    h = rng.normal(size=(8, 64)) * np.exp2(rng.integers(-12, 6, size=(8, 1)))
+    h[2] = 0.0
+    q = oracle.fp8_activations(h)
+    # a power-of-two scale of a row moves its exponent only: the same codes
+    np.testing.assert_array_equal(oracle.fp8_activations(h * 2.0 ** 7), q * 2.0 ** 7)
+    np.testing.assert_array_equal(oracle.fp8_activations(-h), -q)
+    assert not q[2].any()
+    # within half a step: 2^-4 relative for normals of the scaled row, 2^-10 * 2^e below
+    codes, e = oracle.quantize_rows_e4m3(h)
+    s = np.exp2(e.astype(np.float64))[:, None]
+    err = np.abs(q - h) / s
+    normal = np.abs(h / s) >= 2.0 ** -6
+    assert (err[normal] <= 2.0 ** -4 * np.abs(h / s)[normal]).all()
+    assert (err[~normal] <= 2.0 ** -10).all()
+    # and the nearest grid point (brute force over every code, per row)
+    grid = oracle.e4m3_decode(np.array([c for c in range(256) if (c & 0x7F) != 0x7F]))
+    for r in range(8):
+        best = grid[np.abs(grid[None, :] - (h[r] / s[r])[:, None]).argmin(axis=1)] * s[r]
+        np.testing.assert_array_equal(np.abs(q[r] - h[r]), np.abs(best - h[r]))
+
+
+def test_denoise_canvas_act_fp8_reads_quantised_rows():
+    # the FP8-activation step differs from the plain one only in the LM head input
+    from synth import config, make_inputs
+    inp = make_inputs(config("tiny_f32"), prompt_override=("fixed", 16))
+    plain = oracle.denoise_step(inp, need_logits=True)[0]
+    act = oracle.denoise_step(inp, need_logits=True, act_fp8=True)[0]
+    np.testing.assert_array_equal(act["hidden_out"], plain["hidden_out"])
+    want = oracle.lm_logits(oracle.fp8_activations(plain["hidden_out"]), inp["embed"], inp["logit_scale"])
+    np.testing.assert_allclose(act["logits"], want, rtol=0, atol=0)
+    assert np.abs(act["logits"] - plain["logits"]).max() > 0
