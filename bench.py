@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 WORKLOAD = "bf16_step"
 LEG_STEPS = 100                # timed steps of each secondary workload
@@ -240,37 +241,27 @@ def staged_leg(dev, inp, stream):
             "reads_per_slot": int(out["draws_used"].max().item()) + 1}
 
 
-def fp8_leg(inp, stream, K=20, W=3):
-    """The same step (step + commit + read) with the e4m3 copy of the LM head."""
-    import torch
-    from slot_readout_amd import dg
-    from slot_readout_amd.runtime import DeviceProblem
-    dev = DeviceProblem(inp, device="cuda:0", with_lm_fp8=True)
-    dm = inp["dims"]
-    so, co, ro = dev.step_outputs(want_sc=True), dev.commit_outputs(), dev.slot_outputs()
-    ws = dev.workspace("step", dg.dg_denoise_step_workspace(dev.dims, dev.B, dev.max_prompt))
-
-    def step():
-        dg.dg_denoise_step(dev.dims, dev.weights, dev.kv, dev.B, dev.canvas_ids, None,
-                           inp["logit_scale"], None, so["conf"], so["entropy"], so["argmax"],
-                           so["sc_out"], None, so["flags"], ws, stream)
-        dg.dg_commit(dev.B, dev.C, dm.mask_id, dev.canvas_ids, so["conf"], so["entropy"],
-                     so["argmax"], inp["tau"], co["mask"], co["out_ids"], co["n"], stream)
-        dev.slot_read(out=ro, stream=stream)
-
-    for _ in range(W):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / K
-    del dev
-    return {"lm_head": "e4m3 codes, per-row power-of-two scales", "ms_per_step": round(ms, 4),
-            "canvas_tokens_per_s": round(inp["batch"] * dm.canvas / (ms * 1e-3), 1)}
+def fp8_leg(hip, stream, K, W):
+    """The headline step (step + commit + read) with the e4m3 copy of the LM head,
+    weight-only (bf16 activations) and with FP8 activations (both operands e4m3
+    on the FP8 matrix cores): step time, and the LM head's own time and rate
+    against the FP8 and bf16 peaks."""
+    out = {"lm_head": "e4m3 codes, per-row power-of-two scales"}
+    for key, act in (("weight_only", False), ("fp8_activations", True)):
+        w = Workload(WORKLOAD, hip, stream, lm_fp8=True, lm_fp8_act=act)
+        t = w.run(K, W)
+        nbytes, flops = kernel_work(w, lm_fp8=True, act=act)["lmhead"]
+        lm_ms = t["stages"]["lmhead"]
+        tf = flops / (lm_ms * 1e-3) / 1e12
+        out[key] = {"ms_per_step": round(t["ms_per_step"], 4), "ms_median": t["ms_median"],
+                    "canvas_tokens_per_s": round(w.dev.B * w.dev.C / (t["ms_per_step"] * 1e-3), 1),
+                    "lmhead_ms": round(lm_ms, 4), "lmhead_TFLOPs": round(tf, 1),
+                    "lmhead_frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                    "lmhead_frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "lmhead_GBs": round(nbytes / (lm_ms * 1e-3) / 1e9, 1),
+                    "quantise_note": "activation quantisation is inside the lmhead stage" if act else None}
+        w.release()
+    return out
 
 
 def achievable_peaks():
@@ -327,7 +318,8 @@ class Workload:
                      "4 heads x 64, window +-16, vocab 2048; slot read"),
     }
 
-    def __init__(self, name, hip, stream, lm_fp8=False, full_canvas=False, with_read=None):
+    def __init__(self, name, hip, stream, lm_fp8=False, full_canvas=False, with_read=None,
+                 lm_fp8_act=False):
         from slot_readout_amd import dg
         from slot_readout_amd.runtime import DeviceProblem
         from synth import config, make_inputs
@@ -339,7 +331,7 @@ class Workload:
         self.cold = name == "long_read"
         self.hip, self.stream = hip, stream
         self.inp = make_inputs(config(name))
-        self.dev = DeviceProblem(self.inp, device="cuda:0", with_lm_fp8=lm_fp8,
+        self.dev = DeviceProblem(self.inp, device="cuda:0", with_lm_fp8=lm_fp8, lm_fp8_act=lm_fp8_act,
                                  with_embed_t=self.kind == "step")
         dev = self.dev
         self.so = dev.step_outputs(want_sc=True) if self.kind == "step" else None
@@ -433,13 +425,14 @@ class Workload:
         torch.cuda.empty_cache()
 
 
-def kernel_work(w, lm_fp8=False):
+def kernel_work(w, lm_fp8=False, act=False):
     """(algorithmic bytes, flops) per launch of the step's main kernels."""
     inp, dm = w.inp, w.inp["dims"]
     B, C, V, d = inp["batch"], dm.canvas, dm.vocab, dm.d_model
     M, nvt = B * C, V // 256
     head_bytes = V * d + V * 4 if lm_fp8 else V * d * 2      # e4m3 codes + exponents
-    lm = (head_bytes + M * d * 2 + M * V * 2 + M * nvt * 16, 2.0 * M * V * d)
+    h_bytes = M * d + M * 4 if act else M * d * 2             # e4m3 rows + exponents
+    lm = (head_bytes + h_bytes + M * V * 2 + M * nvt * 16, 2.0 * M * V * d)
     sc = (d * V * 2 + M * V * 2 + M * nvt * 4 + M * d * 2, 2.0 * M * V * d)
     at = attention_work(inp)
     return {"lmhead": lm, "selfcond": sc, "attention": at[:2]}
@@ -450,10 +443,10 @@ KERNEL_NAMES = {"lmhead": "lmhead_kernel (S4+S5 tile statistics)",
                 "attention": "attn_kernel + attn_merge_kernel (S2)"}
 
 
-def roofline_of(w, t, dominant=None, lm_fp8=False):
+def roofline_of(w, t, dominant=None, lm_fp8=False, act=False):
     """The dominant kernel's roofline from the instrumented stage times, and
     every stage's rate."""
-    work = kernel_work(w, lm_fp8)
+    work = kernel_work(w, lm_fp8, act)
     st = t["stages"]
     dom = dominant or max(work, key=lambda k: st[k])
     nbytes, flops = work[dom]
@@ -552,6 +545,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lm-fp8", action="store_true",
                     help="LM head from its e4m3 copy (weight-only FP8, bf16 activations)")
+    ap.add_argument("--lm-fp8-act", action="store_true",
+                    help="with --lm-fp8: FP8 activations too (per-row e4m3 h, FP8 matrix cores)")
     ap.add_argument("--no-legs", action="store_true",
                     help="the headline workload only (no secondary workloads or legs)")
     ap.add_argument("--workload", default=WORKLOAD,
@@ -589,7 +584,9 @@ def main():
         return
 
     t_in = time.perf_counter()
-    w = Workload(args.workload, hip, stream, lm_fp8=args.lm_fp8, full_canvas=args.full_canvas)
+    args.lm_fp8 = args.lm_fp8 or args.lm_fp8_act
+    w = Workload(args.workload, hip, stream, lm_fp8=args.lm_fp8, full_canvas=args.full_canvas,
+                 lm_fp8_act=args.lm_fp8_act)
     setup_s = time.perf_counter() - t_in
     t = w.run(K, W)
     if args.copy_calibration:   # outside the timed region
@@ -601,7 +598,7 @@ def main():
         del src, dst
     inp, dev = w.inp, w.dev
     B, C, S = dev.B, dev.C, dev.S
-    roof, stage_roof = roofline_of(w, t, lm_fp8=args.lm_fp8)
+    roof, stage_roof = roofline_of(w, t, lm_fp8=args.lm_fp8, act=args.lm_fp8_act)
     if args.lm_fp8:   # counters were taken with the bf16 head
         roof["traffic"] = None
     ms = t["ms_per_step"]
@@ -617,7 +614,9 @@ def main():
                    "canvas": C, "prompt": int(inp["max_prompt"]), "slots": S if w.with_read else 0,
                    "cold_cache": bool(w.cold),
                    "read_order": "whole canvas" if args.full_canvas else "slot rows",
-                   "lm_head": "e4m3 codes, per-row power-of-two scales (weight-only FP8)"
+                   "lm_head": ("e4m3 head and e4m3 activations, per-row power-of-two scales"
+                               if args.lm_fp8_act else
+                               "e4m3 codes, per-row power-of-two scales (weight-only FP8)")
                    if args.lm_fp8 else "bf16"},
         "slot_reads_per_s": round(B * S / (ms * 1e-3), 1) if w.with_read else None,
         "breakdown_ms": {"pass": "K further steps with per-stage HIP events, after the timed steps",
@@ -650,7 +649,7 @@ def main():
         nl = min(K, LEG_STEPS)
         line["read_full_canvas"] = leg_read_full_canvas(hip, stream, nl, W)
         if not args.lm_fp8:
-            line["fp8_head_step"] = fp8_leg(inp, stream)
+            line["fp8_head_step"] = fp8_leg(hip, stream, nl, W)
         line["workloads"] = {
             "long_read": leg_step_workload("long_read", hip, stream, nl, W),
             "ragged32": leg_step_workload("ragged32", hip, stream, nl, W),

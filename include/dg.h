@@ -118,13 +118,21 @@ typedef struct {
  *            when set, every LM-head pass (denoise step, slot read, loop) uses this
  *            head instead of lm_head / embed, with bf16 activations and fp32
  *            accumulation (weight-only FP8: half the bytes per vocabulary pass).
- *            The embedding and p.E keep the bf16 embed. */
+ *            The embedding and p.E keep the bf16 embed.
+ *   lm_fp8_act  nonzero, with lm_fp8 set: the denoise step (and the loop) also
+ *            quantise each hidden row h[n] to e4m3 by the same rule as the head's
+ *            rows (its own power-of-two exponent e_n, the smallest with max |h[n]|
+ *            <= 448 * 2^e_n) and run the LM head on the FP8 matrix cores, both
+ *            operands e4m3, fp32 accumulation, logits scaled by 2^(e_v + e_n).
+ *            Needs d_model a multiple of 128 (DG_ERR_UNSUPPORTED otherwise).  Slot
+ *            reads keep bf16 activations.  0 (the default) is weight-only FP8. */
 typedef struct {
     const void *embed, *embed_t, *lm_head, *wq, *wk, *wv, *wo;
     const void *lm_tiled;
     const void *embed_t_tiled;
     const void *lm_fp8;
     const int32_t *lm_fp8_exp;
+    int32_t lm_fp8_act;
 } dg_weights;
 
 /* Cached prompt (encoder-mode) keys and values of every sequence, packed.

@@ -99,6 +99,11 @@ dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const
     return fail(DG_ERR_UNSUPPORTED, "the e4m3 LM head (weights.lm_fp8) needs bf16 storage");
   if (!w->lm_fp8 != !w->lm_fp8_exp)
     return fail(DG_ERR_INVALID_ARG, "weights.lm_fp8 and lm_fp8_exp go together");
+  if (w->lm_fp8_act && !w->lm_fp8)
+    return fail(DG_ERR_INVALID_ARG, "weights.lm_fp8_act needs the e4m3 head (lm_fp8)");
+  if (w->lm_fp8_act && d->d_model % 128)
+    return fail(DG_ERR_UNSUPPORTED, "FP8 activations need d_model a multiple of 128 (got %d)",
+                d->d_model);
   return DG_OK;
 }
 
@@ -151,7 +156,8 @@ size_t proj_part_bytes(const dg_dims &d, int64_t M, int64_t ncols, int K) {
 }
 
 struct StepPlan {
-  size_t q, k, v, o, part_o, part_ml, proj_part, h, stats, ptilde, shift, inv_z, sc_part, total;
+  size_t q, k, v, o, part_o, part_ml, proj_part, h, hq, hexp, stats, ptilde, shift, inv_z, sc_part,
+      total;
   AttnPlan attn;
   int ksplit;
 };
@@ -173,6 +179,9 @@ StepPlan plan_step(const dg_dims &d, int B, int max_prompt) {
   p.proj_part = a.take(std::max(proj_part_bytes(d, M, nq + 2 * nkv, d.d_model),
                                 proj_part_bytes(d, M, d.d_model, (int)nq)));
   p.h = a.take(M * d.d_model * ts);
+  // e4m3 codes and exponents of h (FP8 activations; bf16 only)
+  p.hq = a.take(bf ? M * d.d_model : 0);
+  p.hexp = a.take(bf ? M * sizeof(int32_t) : 0);
   p.stats = a.take(M * nvt * sizeof(float4));
   // bf16 p~ is stored in blocks of 256 rows: whole row blocks are allocated
   p.ptilde = a.take((bf ? (M + 255) / 256 * 256 : M) * d.vocab * ts);
@@ -571,6 +580,15 @@ dg_status step_core(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   la.vocab = d.vocab;
   la.nvt = nvt;
   DG_MARK(sg, DG_STAGE_LMHEAD, 0);
+  if (bf && w->lm_fp8 && w->lm_fp8_act) {
+    // per-row e4m3 activations (rows of inactive canvases are quantised too:
+    // their tiles are skipped by the LM head)
+    la.h_fp8 = at<uint8_t>(workspace, p.hq);
+    la.h_exp = at<int32_t>(workspace, p.hexp);
+    DG_TRY_HIP(dg::launch_quantize_e4m3(h, at<uint8_t>(workspace, p.hq), at<int32_t>(workspace, p.hexp),
+                                        (int)M, d.d_model, st),
+               "activation quantisation launch");
+  }
   DG_TRY_HIP(dg::launch_lmhead(la, bf, st), "LM head launch");
   DG_MARK(sg, DG_STAGE_LMHEAD, 1);
 

@@ -797,6 +797,111 @@ struct DmaLoop {
 };
 
 // ---------------------------------------------------------------------------
+// FP8 (e4m3) K loop with direct-to-LDS staging for the LM head with FP8
+// activations: both operands are e4m3 codes (one byte each), K steps of 128
+// codes in NS stages (NS - 1 steps of loads in flight), and the 16x16x128
+// f8f6f4 MFMA (fp32 accumulation), which takes 32 codes of a row per lane:
+// lane l holds row l % 16 and a 32-code group of k chosen by l / 16, the same
+// group for both operands (any consistent assignment of k to lanes gives the
+// same sum).  Rows are 128 bytes in LDS; chunk c of row r sits at chunk
+// c ^ (r & 7), so the 16-byte fragment reads of eight consecutive rows hit
+// eight distinct bank groups.  Each wave instruction of global_load_lds_dwordx4
+// moves 8 rows x 128 bytes; a lane fetches the chunk that belongs in its slot.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WGM, int WGN, int NS>
+struct DmaLoopF8 {
+  static constexpr int BK = 128, NW = WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;
+  static constexpr int QA = BM / 8, NQ = (BM + BN) / 8, QW = NQ / NW;   // 8-row groups
+  static constexpr int STAGE = (BM + BN) * BK;                          // bytes
+  static_assert(NQ % NW == 0, "8-row groups must divide among the waves");
+  static_assert(NS >= 2 && (NS - 2) * QW < 64, "stage count");
+  typedef int v8i __attribute__((ext_vector_type(8)));
+
+  // rowa(r) / rowb(r): first code of row r of the A / B tile (always a
+  // dereferenceable row); K (codes per row) must be a multiple of BK
+  template <class RA, class RB>
+  __device__ static void run(char *(&st)[NS], const RA &rowa, const RB &rowb, int K,
+                             f32x4 (&acc)[TM][TN]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WGN, wn = w % WGN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+    const int nk = K / BK;
+    if (nk <= 0) return;
+    // lane l fills slot (row l / 8, chunk l % 8) of each 8-row group it loads
+    const int r8 = lane >> 3, lc = (lane & 7) ^ r8;
+    const uint8_t *gp[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      const int q = w * QW + i;
+      gp[i] = (q < QA ? rowa(8 * q + r8) : rowb(8 * (q - QA) + r8)) + 16 * lc;
+    }
+    auto dma = [&](int kt, char *s) {
+#pragma unroll
+      for (int i = 0; i < QW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            gp[i] + (int64_t)kt * BK,
+            (__attribute__((address_space(3))) void *)(s + (w * QW + i) * 1024), 16, 0, 0);
+    };
+    // fragment of tile row `row`: logical chunks 2g and 2g + 1, g = lane / 16
+    const int g = lane >> 4;
+    auto frag_at = [&](const char *s, int row) {
+      const int sw = row & 7;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(s + row * BK + (((2 * g) ^ sw) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4 *>(s + row * BK + (((2 * g + 1) ^ sw) << 4));
+      v8i f;
+      f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+      f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+      return f;
+    };
+    auto compute = [&](const char *s) {
+      v8i b[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = frag_at(s, BM + wn * WN + j * 16 + (lane & 15));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const v8i a = frag_at(s, wm * WM + i * 16 + (lane & 15));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          // formats 0 / 0: e4m3 for both operands; block scales 127 (2^0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acc[i][j], 0, 0, 0,
+                                                                        127, 0, 127);
+      }
+    };
+    // vmcnt(n) with the other counters left alone (gfx9 encoding): the loads
+    // of the NS - 2 younger steps may still be in flight
+    constexpr int WN_ = (NS - 2) * QW;
+    constexpr int WAIT = (WN_ & 15) | ((WN_ >> 4) << 14) | (7 << 4) | (15 << 8);
+    // step kt lives in stage kt % NS: wait for this wave's loads of it, then the
+    // barrier (every wave's loads landed, every wave done with step kt - 1's
+    // stage), then the loads of step kt + NS - 1 into that stage (past the
+    // last step they repeat it, never read, so every step issues the same
+    // number of loads), then the MFMAs
+    auto step = [&](int kt, int j) {
+      __builtin_amdgcn_s_waitcnt(WAIT);
+      __builtin_amdgcn_s_barrier();
+      dma(kt + NS - 1 < nk ? kt + NS - 1 : nk - 1, st[(j + NS - 1) % NS]);
+      compute(st[j]);
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) dma(s < nk ? s : nk - 1, st[s]);
+    int k0 = 0;
+    for (; k0 + NS <= nk; k0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) step(k0 + j, j);
+    }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (k0 + j < nk) step(k0 + j, j);
+    // the last (repeated) loads land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  }
+};
+
+// ---------------------------------------------------------------------------
 // S4+S5 (tile part): logits of a VTILE-wide vocabulary tile for BN rows, with
 // per-(row, tile) softmax statistics.  Computed as C^T: MFMA rows are
 // vocabulary entries, MFMA columns are canvas rows, so each row's reduction
@@ -809,12 +914,15 @@ struct DmaLoop {
 // each row takes two MFMA columns, hi in column block j and lo in block
 // j + TN/2 of the same lane, which are added before the epilogue, so the
 // vocabulary tile is streamed once for both halves.
+// FA (with F8): the activations are e4m3 codes too (a.h_fp8, per-row
+// exponents a.h_exp), and the product runs on the FP8 MFMA (DmaLoopF8).
 template <typename T, int BM, int BN, int WGM, int WGN, int PF, int BK, bool TL = false, bool F8 = false,
-          bool HL = false>
+          bool HL = false, bool FA = false>
 __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   using G = Gemm<T, BM, BN, WGM, WGN, PF < 0 ? 1 : PF, BK>;
   static_assert(BM == VTILE, "vocabulary tile must match the stats granularity");
   static_assert(!HL || (G::TN % 2 == 0 && sizeof(T) == 2), "split rows: bf16, even column blocks");
+  static_assert(!FA || (F8 && !HL && !TL), "FP8 activations go with the e4m3 head");
   // rows per wave / workgroup and 16-row column blocks per wave after the halves combine
   constexpr int TNR = HL ? G::TN / 2 : G::TN;
   constexpr int WNR = HL ? G::WN / 2 : G::WN;
@@ -849,7 +957,25 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     return hh + (src >= 0 ? src : 0) * (HL ? 2 * (int64_t)d : (int64_t)d) + part * d;
   };
   f32x4 acc[G::TM][G::TN];
-  if constexpr (PF < 0) {
+  if constexpr (FA) {
+    // three stages where they fit in LDS beside the statistics arrays, else two
+    constexpr int NSF = (BM + BN) * 128 * 3 <= 144 * 1024 ? 3 : 2;
+    using D = DmaLoopF8<BM, BN, WGM, WGN, NSF>;
+    static_assert(D::TM == G::TM && D::TN == G::TN, "tile shape");
+    __shared__ __attribute__((aligned(1024))) char f0[D::STAGE], f1[D::STAGE],
+        f2[NSF > 2 ? D::STAGE : 16];
+    char *st[NSF];
+    st[0] = f0;
+    st[1] = f1;
+    if constexpr (NSF > 2) st[2] = f2;
+    auto rowa = [&](int r) { return a.head_fp8 + (int64_t)(v0 + r) * d; };
+    auto rowb = [&](int r) {
+      bool ok;
+      const T *p = bsrc(r, &ok);   // its row index, through the bf16 row pointer
+      return a.h_fp8 + (p - hh) / d * (int64_t)d;
+    };
+    D::run(st, rowa, rowb, d, acc);
+  } else if constexpr (PF < 0) {
     // rows past the matrix (or without a source row) read row 0: their
     // columns are never stored and columns do not mix
     constexpr int NS = -PF;
@@ -915,6 +1041,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     const int64_t n = n0 + wn * WNR + j * 16 + (lane & 15);
     float s = a.logit_scale;
     if (a.row_scale && n < a.nrows) s *= a.row_scale[n];
+    if constexpr (FA) {   // the row's activation exponent (exact: a power of two)
+      if (n < a.nrows) s = ldexpf(s, a.h_exp[a.row_index ? (a.row_index[n] >= 0 ? a.row_index[n] : 0) : n]);
+    }
     float m = -INFINITY;
     int id = 0x7fffffff;
 #pragma unroll
@@ -1354,10 +1483,10 @@ constexpr int64_t kLmFewRows = 64;
 constexpr int kLmStages = 4;
 
 // one LM-head launch: the grid covers the rows BN (HL: BN / 2) at a time
-template <typename T, int BN, int WGM, int WGN, int PF, int BK, bool TL, bool F8, bool HL>
+template <typename T, int BN, int WGM, int WGN, int PF, int BK, bool TL, bool F8, bool HL, bool FA = false>
 static void lmhead_go(const LmheadArgs &a, hipStream_t st) {
   const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, HL ? BN / 2 : BN));
-  hipLaunchKernelGGL((lmhead_kernel<T, VTILE, BN, WGM, WGN, PF, BK, TL, F8, HL>), grid,
+  hipLaunchKernelGGL((lmhead_kernel<T, VTILE, BN, WGM, WGN, PF, BK, TL, F8, HL, FA>), grid,
                      dim3(WGM * WGN * WAVE), 0, st, a);
 }
 
@@ -1383,6 +1512,14 @@ static hipError_t launch_lmhead_hl(const LmheadArgs &a, hipStream_t st) {
 
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
   if (a.hl) return bf ? launch_lmhead_hl(a, st) : hipErrorInvalidValue;
+  if (a.h_fp8) {
+    // e4m3 head and e4m3 activations: the FP8 MFMA on 256 x 256 tiles, two
+    // stages (measured a little faster than 128-row tiles with three stages,
+    // which read each head tile twice and the fragments with less reuse)
+    if (!bf || !a.head_fp8 || !a.h_exp || a.d % 128) return hipErrorInvalidValue;
+    lmhead_go<bf16, 256, 2, 4, 1, 64, false, true, false, true>(a, st);
+    return hipGetLastError();
+  }
   if (bf && a.head_fp8) {
     // e4m3 head: register K loop (the codes are decoded on their way into LDS);
     // with half the bytes per step, the few-row tile keeps two steps in flight

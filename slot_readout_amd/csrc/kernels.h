@@ -89,6 +89,10 @@ struct LmheadArgs {
   // bf16 only: h rows are [*, 2d], bf16 hi = bf16(h) then lo = bf16(h - hi);
   // the logits are those of hi + lo
   int hl;
+  // e4m3 activations (with head_fp8; d a multiple of 128), or null: h row n
+  // = decode(h_fp8[n]) * 2^h_exp[n] (rows as in h, through row_index)
+  const uint8_t *h_fp8;
+  const int32_t *h_exp;
 };
 
 struct ScArgs {

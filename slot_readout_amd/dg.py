@@ -37,7 +37,7 @@ class Dims(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("embed", "embed_t", "lm_head", "wq", "wk", "wv", "wo", "lm_tiled",
-                 "embed_t_tiled", "lm_fp8", "lm_fp8_exp")]
+                 "embed_t_tiled", "lm_fp8", "lm_fp8_exp")] + [("lm_fp8_act", ctypes.c_int32)]
 
 
 class PromptKV(ctypes.Structure):
@@ -153,9 +153,10 @@ def make_dims(d_model, n_q_heads, n_kv_heads, head_dim, vocab, canvas, window, m
 
 
 def make_weights(embed, wq, wk, wv, wo, embed_t=None, lm_head=None, lm_tiled=None,
-                 embed_t_tiled=None, lm_fp8=None, lm_fp8_exp=None):
+                 embed_t_tiled=None, lm_fp8=None, lm_fp8_exp=None, lm_fp8_act=False):
     return Weights(_ptr(embed), _ptr(embed_t), _ptr(lm_head), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
-                   _ptr(lm_tiled), _ptr(embed_t_tiled), _ptr(lm_fp8), _ptr(lm_fp8_exp))
+                   _ptr(lm_tiled), _ptr(embed_t_tiled), _ptr(lm_fp8), _ptr(lm_fp8_exp),
+                   int(bool(lm_fp8_act)))
 
 
 def make_prompt_kv(k, v, cu_seqlens, max_len, total_len):

@@ -24,7 +24,7 @@ class DeviceProblem:
     """A workload's weights, prompt KV and canvases resident in device memory."""
 
     def __init__(self, inp, device="cuda", with_embed_t=True, with_lm_tiled=True,
-                 with_embed_t_tiled=True, with_lm_fp8=False):
+                 with_embed_t_tiled=True, with_lm_fp8=False, lm_fp8_act=False):
         dm = inp["dims"]
         self.inp = inp
         self.device = device
@@ -58,7 +58,8 @@ class DeviceProblem:
                 and self.d % 256 == 0):
             self.embed_t_tiled = torch.empty((self.V * self.d,), dtype=T, device=device)
             dg.dg_prepare_embed_t_tiled(self.dims, self.embed_t, self.embed_t_tiled)
-        # opt-in e4m3 copy of the LM head (bf16 only): every LM-head pass uses it
+        # opt-in e4m3 copy of the LM head (bf16 only): every LM-head pass uses it;
+        # lm_fp8_act: the step also quantises h per row and runs the FP8 MFMA
         self.lm_fp8 = self.lm_fp8_exp = None
         if with_lm_fp8:
             head = self.lm_head if self.lm_head is not None else self.embed
@@ -85,7 +86,8 @@ class DeviceProblem:
                                        embed_t=self.embed_t, lm_head=self.lm_head,
                                        lm_tiled=self.lm_tiled,
                                        embed_t_tiled=self.embed_t_tiled,
-                                       lm_fp8=self.lm_fp8, lm_fp8_exp=self.lm_fp8_exp)
+                                       lm_fp8=self.lm_fp8, lm_fp8_exp=self.lm_fp8_exp,
+                                       lm_fp8_act=lm_fp8_act and with_lm_fp8)
         self.kv = dg.make_prompt_kv(self.prompt_k, self.prompt_v, self.cu, self.max_prompt,
                                     total)
         self._ws = {}

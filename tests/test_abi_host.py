@@ -101,6 +101,26 @@ def test_validation_rejects_bad_pointers_and_sizes():
     assert dg.dg_denoise_step_validate(d, 1, 0, _weights(dg), kv0) == dg.DG_OK
 
 
+def test_validation_of_the_fp8_head_options():
+    dg = _lib_or_skip()
+    d = _dims(dg)
+    ok = dg.make_weights(256, 256, 256, 256, 256, lm_fp8=1024, lm_fp8_exp=2048)
+    assert dg.dg_denoise_step_validate(d, 1, 128, ok, _kv(dg)) == dg.DG_OK
+    act = dg.make_weights(256, 256, 256, 256, 256, lm_fp8=1024, lm_fp8_exp=2048, lm_fp8_act=True)
+    assert dg.dg_denoise_step_validate(d, 1, 128, act, _kv(dg)) == dg.DG_OK
+    # codes without exponents, activations without the e4m3 head
+    w = dg.make_weights(256, 256, 256, 256, 256, lm_fp8=1024)
+    assert dg.dg_denoise_step_validate(d, 1, 128, w, _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    w = dg.make_weights(256, 256, 256, 256, 256, lm_fp8_act=True)
+    assert dg.dg_denoise_step_validate(d, 1, 128, w, _kv(dg)) == dg.DG_ERR_INVALID_ARG
+    assert "lm_fp8_act" in dg.dg_last_error()
+    # FP8 activations step K by 128; fp32 storage has no e4m3 head
+    d192 = _dims(dg, d_model=192)
+    assert dg.dg_denoise_step_validate(d192, 1, 128, ok, _kv(dg)) == dg.DG_OK
+    assert dg.dg_denoise_step_validate(d192, 1, 128, act, _kv(dg)) == dg.DG_ERR_UNSUPPORTED
+    assert dg.dg_denoise_step_validate(_dims(dg, dtype="f32"), 1, 128, ok, _kv(dg)) == dg.DG_ERR_UNSUPPORTED
+
+
 def test_slot_read_and_commit_validation():
     dg = _lib_or_skip()
     d = _dims(dg)
