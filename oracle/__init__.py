@@ -5,7 +5,8 @@ bench's CPU-baseline leg may import or call this package.  The HIP library
 never calls it and shares no code with it.
 """
 from .dg_oracle import (  # noqa: F401
-    embed_input, qkv_project, prefill_kv, window_attention, block_output, lm_logits,
+    embed_input, qkv_project, prefill_kv, causal_attention, encode_prompt, window_attention,
+    block_output, lm_logits,
     vocab_softmax, self_condition, denoise_canvas, denoise_step, commit_canvas,
     commit, denoise_loop, label_read, slot_read_canvas, slot_read, slot_read_staged, NearTies, argmax_near_ties,
     commit_near_ties, best_near_ties, SLOT_OK, SLOT_BAD_POS, SLOT_BAD_COUNT,

@@ -123,6 +123,55 @@ def prefill_kv(E, Wk, Wv, ids, n_kv_heads, head_dim):
     return k.reshape(n, n_kv_heads, head_dim), v.reshape(n, n_kv_heads, head_dim)
 
 
+def causal_attention(q, k, v, rows=None):
+    """Causal self-attention over one prompt sequence (encoder mode).
+
+    thakicloud, "What is DiffusionGemma": the encoder mode runs the model over
+    the prompt and fills the KV cache that decoder mode reads; encoder-mode
+    attention is the ordinary left-to-right (causal) kind.  Query t sees keys
+    s <= t of its own sequence.  q: [P, Hq, hd], k, v: [P, Hkv, hd] (GQA head
+    h reads kv head h // (Hq / Hkv)); ``rows`` selects the query positions
+    (default all).  Returns o: [len(rows), Hq, hd].
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    P, Hq, hd = q.shape
+    G = Hq // k.shape[1]
+    rows = np.arange(P) if rows is None else np.asarray(rows)
+    out = np.empty((len(rows), Hq, hd))
+    scale = 1.0 / math.sqrt(hd)
+    visible = np.arange(P)[None, :] <= rows[:, None]                  # [R, P]
+    for h in range(Hq):
+        g = h // G
+        s = (q[rows, h, :] @ k[:, g, :].T) * scale
+        s = np.where(visible, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)
+        out[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ v[:, g, :]
+    return out
+
+
+def encode_prompt(E, Wq, Wk, Wv, Wo, ids, dims, rows=None):
+    """Encoder-mode forward of the one-block surrogate over one prompt.
+
+    The block's key and value projections of the prompt embeddings are the
+    cache entries (prefill_kv); its queries attend causally (causal_attention)
+    and the block output h = x + o Wo^T is the encoder's hidden state, which a
+    following block would read.  Ids outside [0, V) embed as zero rows.
+    ``rows`` restricts attention and output to those positions.  Returns a
+    dict of float64 arrays: k, v [P, Hkv, hd]; attn_out [R, Hq*hd]; hidden_out
+    [R, d].
+    """
+    x = embed_input(E, ids)
+    q, k, v = qkv_project(x, Wq, Wk, Wv, dims.n_q_heads, dims.n_kv_heads, dims.head_dim)
+    P = x.shape[0]
+    rows = np.arange(P) if rows is None else np.asarray(rows)
+    o = causal_attention(q, k, v, rows)
+    return {"k": k, "v": v, "attn_out": o.reshape(len(rows), -1),
+            "hidden_out": block_output(x[rows], o, Wo), "rows": rows}
+
+
 def block_output(x, o, Wo):
     """h = x + concat_heads(o) Wo^T  (residual around the attention block)."""
     n = o.shape[0]
