@@ -210,7 +210,8 @@ def timed_median(fn, runs=5):
 
 def prefill_leg(dev, inp, stream):
     """dg_prefill_kv of the workload's prompt tokens (seeded ids) into a scratch
-    cache of the same shape."""
+    cache of the same shape, then the encoder-mode forward over the same
+    prompts (dg_prefill_encode: cache rows, causal attention, block output)."""
     import numpy as np
     import torch
     from slot_readout_amd import dg
@@ -223,7 +224,22 @@ def prefill_leg(dev, inp, stream):
     k = torch.empty((n, dm.n_kv_heads, dm.head_dim), dtype=dev.tdt, device="cuda")
     v = torch.empty_like(k)
     t = timed_median(lambda: dg.dg_prefill_kv(dev.dims, dev.weights, n, ids, k, v, None, stream))
-    return {"tokens": n, "ms": round(t, 4), "tokens_per_s": round(n / (t * 1e-3), 1)}
+    out = {"tokens": n, "ms": round(t, 4), "tokens_per_s": round(n / (t * 1e-3), 1)}
+    # encoder-mode forward: causal attention over each prompt
+    cu = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).cuda()
+    B, max_len = len(inp["cu_seqlens"]) - 1, int(inp["max_prompt"])
+    hid = torch.empty((n, dm.d_model), dtype=dev.tdt, device="cuda")
+    ws = torch.empty(max(dg.dg_prefill_encode_workspace(dev.dims, B, max_len), 256), dtype=torch.uint8,
+                     device="cuda")
+    te = timed_median(lambda: dg.dg_prefill_encode(dev.dims, dev.weights, B, cu, max_len, n, ids, k, v,
+                                                   hid, None, None, ws, stream))
+    lens = inp["prompt_lens"].astype(np.float64)
+    causal_flops = 4.0 * dm.n_q_heads * dm.head_dim * float((lens * (lens + 1) / 2).sum())
+    out["encode"] = {"ms": round(te, 4), "tokens_per_s": round(n / (te * 1e-3), 1),
+                     "causal_attention_TFLOPs_of_call": round(causal_flops / (te * 1e-3) / 1e12, 1),
+                     "note": "whole call (projections, causal attention, output projection); "
+                             "TFLOP/s counts the causal attention's flops only"}
+    return out
 
 
 def staged_leg(dev, inp, stream):

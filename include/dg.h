@@ -303,6 +303,42 @@ dg_status dg_commit(int32_t batch, int32_t canvas, int32_t mask_id,
 size_t dg_slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
                               int32_t max_prompt, int32_t n_draws);
 
+/* Encoder-mode forward over the prompts: the encoder mode runs the model over
+ * the prompt with left-to-right (causal) attention and fills the KV cache that
+ * the decoder-mode denoise step reads (thakicloud, "What is DiffusionGemma").
+ * With one block standing in for the backbone:
+ *   k_out, v_out  the cache rows, exactly as dg_prefill_kv writes them (every
+ *                 row of [0, total_len), k_t = E[id_t] Wk^T, v_t = E[id_t] Wv^T);
+ *   attn_out      [total_len, n_q_heads*head_dim] T or NULL: for token t of
+ *                 sequence b, softmax(q_t . k_s / sqrt(head_dim)) v_s over the
+ *                 tokens s <= t of its own sequence (GQA as in the step), with
+ *                 q_t = E[id_t] Wq^T;
+ *   hidden_out    [total_len, d_model] T or NULL: the block output
+ *                 E[id_t] + attn_t Wo^T, the encoder's hidden state that a
+ *                 following block would read.
+ * Sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (device int32
+ * [batch+1], non-decreasing, <= total_len; offsets outside that are clamped as
+ * the step clamps them and set DG_FLAG_BAD_SEQLENS), at most max_len tokens
+ * each (host; a longer sequence is cut to its first max_len tokens).  Rows of
+ * attn_out / hidden_out outside every sequence are left untouched; rows that
+ * clamped sequences share hold the result of one of them.
+ *   prompt_ids    [total_len] int32, device; ids outside [0, vocab) embed as zero
+ *                 rows and set DG_FLAG_BAD_TOKEN
+ *   dev_flags     device int32 or NULL: cleared, then set as described
+ * The prompts run in chunks of `canvas` tokens, each chunk attending to the
+ * cache rows of its sequence before it and causally within itself.  With
+ * hidden_out and attn_out both NULL the call equals dg_prefill_kv over
+ * total_len rows (no workspace needed).  Workspace: dg_prefill_encode_workspace
+ * bytes (monotone in batch and max_len).  Allocates nothing; asynchronous on
+ * stream.  Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE,
+ * DG_ERR_HIP. */
+size_t dg_prefill_encode_workspace(const dg_dims *dims, int32_t batch, int32_t max_len);
+dg_status dg_prefill_encode(const dg_dims *dims, const dg_weights *w, int32_t batch,
+                            const int32_t *cu_seqlens, int32_t max_len, int64_t total_len,
+                            const int32_t *prompt_ids, void *k_out, void *v_out,
+                            void *hidden_out, void *attn_out, int32_t *dev_flags,
+                            void *workspace, size_t ws_bytes, void *stream);
+
 /* Structured read of `n_slots` slots in each of `batch` caller-prefilled canvases.
  * The canvas is never modified and nothing is committed.
  *   canvas_ids   [batch, canvas] int32   prefilled skeleton (slots usually mask_id)

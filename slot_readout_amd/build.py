@@ -15,7 +15,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libdg.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gemm.hip", "attention.hip", "vocab_commit.hip", "slot.hip", "noalloc.hip", "dg_api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "vocab_commit.hip", "slot.hip", "encode.hip", "noalloc.hip",
+           "dg_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -79,8 +79,20 @@ template <> __device__ inline float4 load4v<bf16>(const bf16 *p) {
 // With ncp canvases packed in the tile (gathered queries of canvases that
 // share a prompt), the canvas keys are those of the ncp canvases, one after
 // the other ([0, ncp * C)).
+// Encoder-mode chunks (a.chunks): the keys of the sequence before the chunk,
+// then the chunk's own keys up to the tile's last query (none for a tile past
+// the chunk's end).
 __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int64_t *p0o,
                                  int64_t *plen, int *lo, int *hi, int ncp = 1) {
+  if (a.chunks) {
+    const int4 c = a.chunks[cb];
+    const bool past = i0 >= c.z;
+    *p0o = c.x;
+    *plen = past ? 0 : c.y;
+    *lo = 0;
+    *hi = past ? 0 : (i0 + nq < c.z ? i0 + nq : c.z);
+    return false;
+  }
   const int pb = cb / a.canvas_per_prompt;
   int64_t p0 = a.cu[pb], p1 = a.cu[pb + 1];
   bool bad = false;
@@ -164,7 +176,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   const int qt = a.packed ? 0 : tile % nqt;
   if (a.active && ncp == 1 && !a.active[cb]) return;
   const int G = a.Hq / a.Hkv, g = h / G;
-  const int C = a.C, W = a.W;
+  const int C = a.C, W = a.chunks ? a.C - 1 : a.W;
+  const int Wup = a.chunks ? 0 : W;   // reach of the window after the query
   const int i0 = qt * NQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -233,6 +246,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
     int p = qi;
     if (a.qpos) p = qi < QN ? a.qpos[(int64_t)(cb + ccv[jb]) * QN + qi] : -1;
     if (ncp > 1 && a.active && !a.active[cb + ccv[jb]]) p = -1;
+    if (a.chunks && p >= a.chunks[cb].z) p = -1;   // past the chunk's tokens
     qp[jb] = p >= 0 && p < C ? ccv[jb] * C + p : -(1 << 20);
   }
   // a wave none of whose columns holds a query (past the canvas end, or past
@@ -435,8 +449,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
         // W], and (packed canvases) the key is of the column's own canvas
         const int qrel = qp[jb] - d.k0;
         const int cv0 = ccv[jb] * C - d.k0;   // the column's canvas: [cv0, cv0 + C)
+        // (encoder-mode chunks: keys at or before the query, W = C - 1)
         const int klo_ok = d.canvas ? max(qrel - W, cv0) : -1;
-        const int khi_ok = d.canvas ? min(min(qrel + W, cv0 + C - 1), d.rem - 1) : d.rem - 1;
+        const int khi_ok = d.canvas ? min(min(qrel + Wup, cv0 + C - 1), d.rem - 1) : d.rem - 1;
 #pragma unroll
         for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
@@ -751,6 +766,9 @@ hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_
   // not duplicated (kv_cmul 1), canvas lengths within the position map
   if (patch && (!attn_patch_supported(head_dim, bf) || !a.prec || !a.qpos || a.kv_cmul > 1 || a.C > DG_MAX_CANVAS ||
                 !a.vpatch || a.canvas_per_prompt < 1))
+    return hipErrorInvalidValue;
+  // encoder-mode chunks: every position of each chunk, one canvas per tile
+  if (a.chunks && (a.qpos || patch || a.kv_cmul > 1 || a.canvas_per_prompt != 1))
     return hipErrorInvalidValue;
   if (bf && head_dim == 64) {
     if (patch) return a.prec ? launch_attn_t<bf16, 64, true, true>(a, st) : hipErrorInvalidValue;

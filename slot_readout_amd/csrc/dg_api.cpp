@@ -404,6 +404,8 @@ struct Gather {
   // patch_from
   const void *kpatch = nullptr, *vpatch = nullptr;
   int patch_from = 0;
+  // encoder mode: the canvases are causal prompt chunks (AttnArgs::chunks)
+  const int4 *chunks = nullptr;
 };
 
 // S0..S3 of one pass over nc canvases: q,k,v -> attention -> h
@@ -488,6 +490,7 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.kpatch = gq.kpatch;
   aa.vpatch = gq.vpatch;
   aa.patch_from = gq.patch_from;
+  aa.chunks = gq.chunks;
   DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
   DG_MARK(sg, DG_STAGE_ATTENTION, 1);
@@ -627,6 +630,76 @@ dg_status step_core(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   }
   DG_MARK(sg, DG_STAGE_SELFCOND, 1);
   return DG_OK;
+}
+
+
+// k, v cache rows of n_tokens prompt tokens (the block's projections of E[id])
+dg_status prefill_rows(const dg_dims &d, const dg_weights *w, int64_t n_tokens,
+                       const int32_t *prompt_ids, void *k_out, void *v_out, int32_t *dev_flags,
+                       hipStream_t st) {
+  dg::QkvArgs qa{};
+  qa.ids = prompt_ids;
+  qa.embed = w->embed;
+  qa.wq = w->wk;   // no q column is computed; any valid matrix pointer
+  qa.wk = w->wk;
+  qa.wv = w->wv;
+  qa.k = k_out;
+  qa.v = v_out;
+  qa.flags = dev_flags;
+  qa.M = n_tokens;
+  qa.d = d.d_model;
+  qa.nq = d.n_q_heads * d.head_dim;
+  qa.nkv = d.n_kv_heads * d.head_dim;
+  qa.vocab = d.vocab;
+  qa.C = d.canvas;
+  qa.q_scale = 1.f;
+  qa.col0 = qa.nq;                 // the k and v columns of [q | k | v]
+  qa.col1 = qa.nq + 2 * qa.nkv;
+  DG_TRY_HIP(dg::launch_qkv(qa, d.dtype == DG_BF16, st), "prefill projection launch");
+  return DG_OK;
+}
+
+// Workspace of the encoder-mode forward: B sequences of at most max_len tokens
+// in J = ceil(max_len / C) chunks of C rows each.
+struct EncodePlan {
+  size_t q, k, v, o, h, part_o, part_ml, proj_part, ids, chunks, active, total;
+  AttnPlan attn;
+  int J;
+};
+
+EncodePlan plan_encode(const dg_dims &d, int B, int max_len) {
+  EncodePlan p{};
+  p.J = (int)((max_len + d.canvas - 1) / d.canvas);
+  const int64_t NC = (int64_t)B * p.J, M = NC * d.canvas;
+  if (NC == 0) return p;   // nothing to run: no workspace
+  const size_t ts = tsize(d);
+  const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
+  Arena a;
+  p.q = a.take(M * nq * ts);
+  p.k = a.take(M * nkv * ts);
+  p.v = a.take(M * nkv * ts);
+  p.o = a.take(M * nq * ts);
+  p.h = a.take(M * d.d_model * ts);
+  p.attn = plan_attention(d, (int)NC, max_len);
+  // split partials: the most that any shorter max_len needs (more chunks can
+  // mean fewer splits), so that the size only grows with max_len
+  size_t po = 0, pml = 0, pp = 0;
+  for (int j = 1; j <= p.J; ++j) {
+    const int64_t nc = (int64_t)B * j, m = nc * d.canvas;
+    const AttnPlan ap = plan_attention(d, (int)nc, std::min(max_len, j * d.canvas));
+    po = std::max(po, ap.part_o);
+    pml = std::max(pml, ap.part_ml);
+    pp = std::max(pp, std::max(proj_part_bytes(d, m, nq + 2 * nkv, d.d_model),
+                               proj_part_bytes(d, m, d.d_model, (int)nq)));
+  }
+  p.part_o = a.take(po);
+  p.part_ml = a.take(pml);
+  p.proj_part = a.take(pp);
+  p.ids = a.take(M * sizeof(int32_t));
+  p.chunks = a.take(NC * sizeof(int4));
+  p.active = a.take(NC * sizeof(int32_t));
+  p.total = a.off;
+  return p;
 }
 
 }  // namespace
@@ -796,6 +869,7 @@ dg_status dg_denoise_loop(const dg_dims *dims, const dg_weights *w, const dg_pro
   return ok();
 }
 
+
 dg_status dg_prefill_kv(const dg_dims *dims, const dg_weights *w, int64_t n_tokens,
                         const int32_t *prompt_ids, void *k_out, void *v_out,
                         int32_t *dev_flags, void *stream) {
@@ -810,28 +884,87 @@ dg_status dg_prefill_kv(const dg_dims *dims, const dg_weights *w, int64_t n_toke
   if (!aligned16(w->embed) || !aligned16(w->wk) || !aligned16(w->wv) || !aligned16(k_out) ||
       !aligned16(v_out))
     return fail(DG_ERR_INVALID_ARG, "weights and the k/v outputs must be 16-byte aligned");
-  const dg_dims &d = *dims;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
-  dg::QkvArgs qa{};
-  qa.ids = prompt_ids;
-  qa.embed = w->embed;
-  qa.wq = w->wk;   // no q column is computed; any valid matrix pointer
-  qa.wk = w->wk;
-  qa.wv = w->wv;
-  qa.k = k_out;
-  qa.v = v_out;
-  qa.flags = dev_flags;
-  qa.M = n_tokens;
-  qa.d = d.d_model;
-  qa.nq = d.n_q_heads * d.head_dim;
-  qa.nkv = d.n_kv_heads * d.head_dim;
-  qa.vocab = d.vocab;
-  qa.C = d.canvas;
-  qa.q_scale = 1.f;
-  qa.col0 = qa.nq;                 // the k and v columns of [q | k | v]
-  qa.col1 = qa.nq + 2 * qa.nkv;
-  DG_TRY_HIP(dg::launch_qkv(qa, d.dtype == DG_BF16, st), "prefill projection launch");
+  s = prefill_rows(*dims, w, n_tokens, prompt_ids, k_out, v_out, dev_flags, st);
+  return s != DG_OK ? s : ok();
+}
+
+size_t dg_prefill_encode_workspace(const dg_dims *dims, int32_t batch, int32_t max_len) {
+  if (check_dims(dims) != DG_OK || batch < 0 || max_len < 0) return 0;
+  return plan_encode(*dims, batch, max_len).total;
+}
+
+dg_status dg_prefill_encode(const dg_dims *dims, const dg_weights *w, int32_t batch,
+                            const int32_t *cu_seqlens, int32_t max_len, int64_t total_len,
+                            const int32_t *prompt_ids, void *k_out, void *v_out, void *hidden_out,
+                            void *attn_out, int32_t *dev_flags, void *workspace, size_t ws_bytes,
+                            void *stream) {
+  dg_status s = check_dims(dims);
+  if (s != DG_OK) return s;
+  if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (max_len < 0 || total_len < 0)
+    return fail(DG_ERR_INVALID_ARG, "max_len and total_len must be >= 0");
+  const bool fwd = hidden_out || attn_out;
+  if (!w || !w->embed || !w->wk || !w->wv || (fwd && (!w->wq || !w->wo)))
+    return fail(DG_ERR_INVALID_ARG,
+                "the encoder needs weights.embed, wk and wv (and wq, wo for hidden_out / attn_out)");
+  if (total_len > 0 && (!prompt_ids || !k_out || !v_out))
+    return fail(DG_ERR_INVALID_ARG, "prompt_ids, k_out and v_out are required");
+  if (fwd && batch > 0 && !cu_seqlens) return fail(DG_ERR_INVALID_ARG, "cu_seqlens is required");
+  const void *ptrs[] = {w->embed, w->wq, w->wk, w->wv, w->wo, k_out, v_out, hidden_out, attn_out, workspace};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(DG_ERR_INVALID_ARG, "weights, outputs and workspace must be 16-byte aligned");
+  const dg_dims &d = *dims;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool run = fwd && batch > 0 && max_len > 0 && total_len > 0;
+  const EncodePlan p = plan_encode(d, run ? batch : 0, run ? max_len : 0);
+  if (run && (!workspace || ws_bytes < p.total))
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                ws_bytes, p.total);
+  if (dev_flags) DG_TRY_HIP(dg::launch_clear_i32(dev_flags, 1, st), "flag clear launch");
+  if (total_len > 0) {
+    s = prefill_rows(d, w, total_len, prompt_ids, k_out, v_out, dev_flags, st);
+    if (s != DG_OK) return s;
+  }
+  if (!run) return ok();
+  dg::EncodeArgs ea{};
+  ea.cu = cu_seqlens;
+  ea.prompt_ids = prompt_ids;
+  ea.flags = dev_flags;
+  ea.ids_pad = at<int32_t>(workspace, p.ids);
+  ea.chunks = at<int4>(workspace, p.chunks);
+  ea.active = at<int32_t>(workspace, p.active);
+  ea.h_pad = at<char>(workspace, p.h);
+  ea.o_pad = at<char>(workspace, p.o);
+  ea.hidden_out = hidden_out;
+  ea.attn_out = attn_out;
+  ea.total_len = total_len;
+  ea.h_row_bytes = (int64_t)d.d_model * tsize(d);
+  ea.o_row_bytes = (int64_t)d.n_q_heads * d.head_dim * tsize(d);
+  ea.B = batch;
+  ea.J = p.J;
+  ea.C = d.canvas;
+  ea.max_len = max_len;
+  DG_TRY_HIP(dg::launch_encode_plan(ea, st), "encoder chunk plan launch");
+  const dg_prompt_kv kv{k_out, v_out, cu_seqlens, max_len, total_len};
+  Gather g;
+  g.chunks = ea.chunks;
+  const int nc = batch * p.J;
+  s = run_block(d, w, &kv, nc, 1, ea.ids_pad, nullptr, ea.active, dev_flags, at<char>(workspace, p.q),
+                at<char>(workspace, p.k), at<char>(workspace, p.v), at<char>(workspace, p.o), p.attn,
+                at<char>(workspace, p.part_o), at<float2>(workspace, p.part_ml),
+                at<float>(workspace, p.proj_part), at<char>(workspace, p.h), st, Stages(), g);
+  if (s != DG_OK) return s;
+  if (hidden_out || attn_out) {
+    if (!hidden_out) {   // attention rows only: the scatter copies hidden rows first
+      ea.hidden_out = attn_out;
+      ea.h_pad = ea.o_pad;
+      ea.h_row_bytes = ea.o_row_bytes;
+      ea.attn_out = nullptr;
+    }
+    DG_TRY_HIP(dg::launch_encode_scatter(ea, st), "encoder output copy launch");
+  }
   return ok();
 }
 

@@ -156,7 +156,28 @@ struct AttnArgs {
   // kpatch / vpatch ([nc*qn, Hkv*hd]).
   const void *kpatch, *vpatch;
   int patch_from;
+  // Encoder mode (causal attention over prompts cut into chunks of C tokens),
+  // or null: canvas cb is a chunk, and chunks[cb] = {x: first cache row of its
+  // sequence, y: tokens of the sequence before the chunk (its prompt keys are
+  // rows [x, x + y) of kp, vp), z: tokens in the chunk (<= C; queries and
+  // canvas keys at positions >= z are absent), w: unused}.  A canvas key is
+  // visible to the queries at or after it (no window).
+  const int4 *chunks;
   // q arrives pre-scaled by log2(e) / sqrt(hd): q.k is the score in log2 units
+};
+
+// Encoder-mode layout (encode.hip): B sequences cut into J chunks of C tokens
+struct EncodeArgs {
+  const int32_t *cu;           // [B + 1] sequence offsets in the cache rows
+  const int32_t *prompt_ids;   // [total_len]
+  int32_t *flags;
+  int32_t *ids_pad;            // [B * J, C] token ids of each chunk (0 past its end)
+  int4 *chunks;                // [B * J] AttnArgs::chunks
+  int32_t *active;             // [B * J] 1 for a chunk holding tokens
+  const void *h_pad, *o_pad;   // [B * J, C, *] rows of the chunks
+  void *hidden_out, *attn_out; // [total_len, *] token rows (attn_out may be null)
+  int64_t total_len, h_row_bytes, o_row_bytes;
+  int B, J, C, max_len;
 };
 
 struct CommitArgs {
@@ -220,6 +241,8 @@ hipError_t launch_quantize_e4m3(const void *head, uint8_t *codes, int32_t *exps,
 hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, bool bf,
                             hipStream_t st);
 hipError_t launch_clear_i32(int32_t *p, int64_t n, hipStream_t st);
+hipError_t launch_encode_plan(const EncodeArgs &a, hipStream_t st);
+hipError_t launch_encode_scatter(const EncodeArgs &a, hipStream_t st);
 
 // slot read pieces
 struct SlotArgs {

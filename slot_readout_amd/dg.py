@@ -69,6 +69,9 @@ _SIGS = {
     "dg_commit": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _F, _P, _P, _P, _P]),
     "dg_prefill_kv": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.c_int64, _P, _P,
                              _P, _P, _P]),
+    "dg_prefill_encode_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32]),
+    "dg_prefill_encode": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), _I32, _P, _I32,
+                                 ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dg_denoise_loop_workspace": (_SZ, [ctypes.POINTER(Dims), _I32, _I32]),
     "dg_denoise_loop": (_I32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(PromptKV),
                                _I32, _P, _P, _F, _P, _F, _I32, _I32, _P, _P,
@@ -195,6 +198,19 @@ def dg_prefill_kv(dims, weights, n_tokens, prompt_ids, k_out, v_out, dev_flags=N
     _check(lib().dg_prefill_kv(ctypes.byref(dims), ctypes.byref(weights), int(n_tokens),
                                _ptr(prompt_ids), _ptr(k_out), _ptr(v_out), _ptr(dev_flags),
                                _stream(stream)))
+
+
+def dg_prefill_encode_workspace(dims, batch, max_len):
+    return lib().dg_prefill_encode_workspace(ctypes.byref(dims), batch, max_len)
+
+
+def dg_prefill_encode(dims, weights, batch, cu_seqlens, max_len, total_len, prompt_ids, k_out, v_out,
+                      hidden_out=None, attn_out=None, dev_flags=None, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dg_prefill_encode(ctypes.byref(dims), ctypes.byref(weights), int(batch),
+                                   _ptr(cu_seqlens), int(max_len), int(total_len), _ptr(prompt_ids),
+                                   _ptr(k_out), _ptr(v_out), _ptr(hidden_out), _ptr(attn_out),
+                                   _ptr(dev_flags), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dg_denoise_loop_workspace(dims, batch, max_prompt):

@@ -132,6 +132,26 @@ class DeviceProblem:
                            out["argmax"], out["sc_out"], dbg, out["flags"], ws, stream)
         return out
 
+    # ------------------------------------------------------------- encoder --
+    def encode(self, prompt_ids, cu, max_len, total_len, want_hidden=True, want_attn=True,
+               stream=None):
+        """dg_prefill_encode of packed prompts (device int32 ids and offsets):
+        returns k, v (cache rows), hidden, attn (or None) and the flag word."""
+        dm = self.inp["dims"]
+        n = max(int(total_len), 1)
+        out = {"k": torch.empty((n, dm.n_kv_heads, dm.head_dim), dtype=self.tdt, device=self.device),
+               "flags": torch.zeros(1, dtype=torch.int32, device=self.device)}
+        out["v"] = torch.empty_like(out["k"])
+        out["hidden"] = (torch.empty((n, self.d), dtype=self.tdt, device=self.device)
+                         if want_hidden else None)
+        out["attn"] = (torch.empty((n, dm.n_q_heads * dm.head_dim), dtype=self.tdt, device=self.device)
+                       if want_attn else None)
+        B = int(cu.numel()) - 1
+        ws = self.workspace("encode", dg.dg_prefill_encode_workspace(self.dims, B, int(max_len)))
+        dg.dg_prefill_encode(self.dims, self.weights, B, cu, int(max_len), int(total_len), prompt_ids,
+                             out["k"], out["v"], out["hidden"], out["attn"], out["flags"], ws, stream)
+        return out
+
     # -------------------------------------------------------------- commit --
     def commit_outputs(self):
         B, C = self.B, self.C

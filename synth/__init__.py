@@ -6,7 +6,7 @@ the HIP path consume what it returns, so the two sides always see identical
 inputs.
 """
 from .configs import CONFIGS, Dims, config
-from .generate import make_inputs, round_bf16, companion_row_scale
+from .generate import make_inputs, round_bf16, companion_row_scale, prompt_batch
 
 __all__ = ["CONFIGS", "Dims", "config", "make_inputs", "round_bf16",
-           "companion_row_scale"]
+           "companion_row_scale", "prompt_batch"]

@@ -158,3 +158,14 @@ def companion_row_scale(inp: dict, shape, lo: float = 16.0, hi: float = 512.0) -
     total = np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape))
     # the multipliers scale on top of the workload's own logit scale
     return (total / inp["logit_scale"]).astype(np.float32)
+
+
+def prompt_batch(vocab: int, lengths, seed: int):
+    """Packed prompt token ids for the encoder-mode forward: sequence b holds
+    lengths[b] ids uniform over [0, V-2] (the mask id V-1 never appears), the
+    sequences back to back.  Returns (ids int32 [sum lengths], cu int32 [B+1])."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    ids = rng.integers(0, vocab - 1, size=int(cu[-1])).astype(np.int32)
+    return ids, cu

@@ -241,7 +241,7 @@ def _headline(dg, **kw):
     return dg.make_dims(**base)
 
 
-@pytest.mark.parametrize("which", ["step", "loop", "read", "read_full", "staged"])
+@pytest.mark.parametrize("which", ["step", "loop", "read", "read_full", "staged", "encode"])
 @pytest.mark.parametrize("dims_kind", ["headline", "tiny"])
 def test_workspace_queries_are_monotone_in_max_prompt(which, dims_kind):
     """A workspace sized for max_prompt = M must hold a call whose prompts are
@@ -256,12 +256,13 @@ def test_workspace_queries_are_monotone_in_max_prompt(which, dims_kind):
          "loop": lambda m: dg.dg_denoise_loop_workspace(d, B, m),
          "read": lambda m: dg.dg_slot_read_workspace(d, B, 8, m, 4),
          "read_full": lambda m: dg.dg_slot_read_full_canvas_workspace(d, B, 8, m, 4),
-         "staged": lambda m: dg.dg_slot_read_staged_workspace(d, B, 8, m, 4)}[which]
+         "staged": lambda m: dg.dg_slot_read_staged_workspace(d, B, 8, m, 4),
+         "encode": lambda m: dg.dg_prefill_encode_workspace(d, B, m)}[which]
     lens = list(range(0, 4200, 7)) + list(range(4200, 120000, 997))
     prev = 0
     for m in lens:
         w = q(m)
-        assert w > 0
+        assert w > 0 or (which == "encode" and m == 0)   # no prompt: nothing to encode
         assert w >= prev, f"{which}: workspace({m}) = {w} < workspace of a shorter prompt ({prev})"
         prev = w
 
@@ -271,3 +272,32 @@ def test_noalloc_scratch_size_matches_the_header():
     src = open(HEADER).read()
     m = re.search(r"#define DG_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == dg.DG_NOALLOC_SCRATCH_BYTES
+
+
+def test_encode_rejects_bad_arguments_before_any_launch():
+    """dg_prefill_encode's checks run on the host before anything is launched."""
+    dg = _lib_or_skip()
+    d = _dims(dg)
+    full = dg.make_weights(256, 256, 256, 256, 256)
+    assert dg.dg_prefill_encode_workspace(d, 2, 0) == 0
+    assert dg.dg_prefill_encode_workspace(d, 0, 700) == 0
+    ws = dg.dg_prefill_encode_workspace(d, 2, 700)
+    assert ws > dg.dg_prefill_encode_workspace(d, 2, 256) > 0
+    L = dg.lib()
+
+    def call(dims=d, w=full, batch=2, cu=1024, max_len=700, total=900, ids=2048, k=4096, v=8192,
+             hidden=16384, attn=None, wsp=32768, wsb=ws):
+        return L.dg_prefill_encode(dims, w, batch, cu, max_len, total, ids, k, v, hidden, attn, None,
+                                   wsp, wsb, None)
+    assert call(batch=-1) == dg.DG_ERR_INVALID_ARG
+    assert call(max_len=-1) == dg.DG_ERR_INVALID_ARG
+    assert call(total=-5) == dg.DG_ERR_INVALID_ARG
+    assert call(cu=None) == dg.DG_ERR_INVALID_ARG
+    assert call(ids=None) == dg.DG_ERR_INVALID_ARG
+    assert call(k=None) == dg.DG_ERR_INVALID_ARG
+    assert call(hidden=16388) == dg.DG_ERR_INVALID_ARG            # misaligned output
+    assert call(w=dg.make_weights(256, 256, 256, 256, 0)) == dg.DG_ERR_INVALID_ARG   # no wo
+    assert "wq, wo" in dg.dg_last_error()
+    assert call(wsb=ws - 1) == dg.DG_ERR_WORKSPACE
+    assert call(wsp=None) == dg.DG_ERR_WORKSPACE
+    assert call(dims=_dims(dg, head_dim=128)) == dg.DG_ERR_UNSUPPORTED
