@@ -16,7 +16,7 @@ OUT = os.path.join(PKG, "libdg.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["gemm.hip", "attention.hip", "vocab_commit.hip", "slot.hip", "encode.hip", "noalloc.hip",
-           "dg_api.cpp"]
+           "plan.cpp", "dg_api.cpp"]
 ARCH = "gfx950"
 
 

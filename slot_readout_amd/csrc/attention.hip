@@ -686,53 +686,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
-int attn_query_tile(int head_dim) { return head_dim == 512 ? 64 : 128; }
-
-int attn_cpack(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp) {
-  if (!gathered || cpp <= 1) return 1;
-  return (int64_t)cpp * (Hq / Hkv) * qn <= attn_query_tile(head_dim) ? cpp : 1;
-}
-
-bool attn_packed(int qn, bool gathered, int Hq, int Hkv, int head_dim, int cpp) {
-  if (!gathered) return false;
-  if (attn_cpack(qn, gathered, Hq, Hkv, head_dim, cpp) > 1) return true;
-  return Hq > Hkv && (int64_t)(Hq / Hkv) * qn <= attn_query_tile(head_dim);
-}
 static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               AttnShape<float, 64>::NW * AttnShape<float, 64>::QB * 16 == 128 &&
               AttnShape<bf16, 512>::NW * AttnShape<bf16, 512>::QB * 16 == 64,
               "query tile sizes");
-
-void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int head_dim,
-               int max_len, int cpp, int *nsplit, int *chunk, int *nsplit_bound) {
-  const int nq = attn_query_tile(head_dim);
-  const int nk = head_dim == 512 ? 32 : 64;
-  const int ncp = attn_cpack(qn, gathered, Hq, Hkv, head_dim, cpp);
-  const int64_t base = attn_packed(qn, gathered, Hq, Hkv, head_dim, cpp)
-                           ? (int64_t)nc / ncp * Hkv
-                           : (int64_t)nc * Hq * cdiv64(qn, nq);
-  // most keys one query tile can see: the prompt plus its window span (every
-  // canvas key of the tile's canvases for gathered queries)
-  const int64_t win = gathered ? (int64_t)C * ncp : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
-  const int64_t span = (int64_t)max_len + win;
-  // about two workgroups per CU
-  const int target = 512;
-  int ns = 1;
-  if (base < target) {
-    ns = (int)cdiv64(target, base);
-    const int64_t maxs = cdiv64(span, 4 * nk);   // keep at least ~4 key blocks per split
-    if (ns > maxs) ns = (int)maxs;
-    if (ns < 1) ns = 1;
-  }
-  // ns is non-decreasing in max_len; the rounded count below never exceeds it,
-  // so ns bounds the splits of every prompt up to max_len (workspace sizing)
-  if (nsplit_bound) *nsplit_bound = ns;
-  const int ck = (int)(cdiv64(cdiv64(span, ns), nk) * nk);
-  ns = (int)cdiv64(span, ck);
-  if (ns < 1) ns = 1;
-  *nsplit = ns;
-  *chunk = ck;
-}
 
 template <typename T, int HD, bool PREC, bool PATCH>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
@@ -756,8 +713,6 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((attn_merge_kernel<T, HD, PREC>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, b);
   return hipGetLastError();
 }
-
-bool attn_patch_supported(int head_dim, bool bf) { return bf && head_dim == 64; }
 
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st) {
   if (a.prec && !bf) return hipErrorInvalidValue;

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "dg.h"
@@ -73,12 +74,33 @@ dg_status check_dims(const dg_dims *d) {
   return DG_OK;
 }
 
+// Size limits shared by the calls and their workspace queries: canvas rows
+// (batch * canvas, times the canvases per batch entry of a read) and slot rows
+// are addressed as int32, and prompt lengths leave room for the attention
+// plan's key spans.
+constexpr int64_t kMaxRows = INT32_MAX;
+constexpr int32_t kMaxPrompt = 1 << 30;
+
+bool sizes_fit(const dg_dims &d, int64_t canvases, int32_t max_prompt, int64_t slot_rows = 0) {
+  return canvases * d.canvas <= kMaxRows && slot_rows <= kMaxRows && max_prompt <= kMaxPrompt;
+}
+
+dg_status check_sizes(const dg_dims &d, int64_t canvases, int32_t max_prompt, int64_t slot_rows = 0) {
+  if (sizes_fit(d, canvases, max_prompt, slot_rows)) return DG_OK;
+  return fail(DG_ERR_INVALID_ARG,
+              "sizes out of range: %lld canvases of %d rows, %lld slot rows (at most 2^31 - 1 rows), "
+              "max_prompt %d (at most 2^30)",
+              (long long)canvases, d.canvas, (long long)slot_rows, max_prompt);
+}
+
 dg_status check_model(const dg_dims *d, int32_t batch, int32_t max_prompt, const dg_weights *w,
                       const dg_prompt_kv *kv) {
   dg_status s = check_dims(d);
   if (s != DG_OK) return s;
   if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
   if (max_prompt < 0) return fail(DG_ERR_INVALID_ARG, "max_prompt %d < 0", max_prompt);
+  s = check_sizes(*d, batch, max_prompt);
+  if (s != DG_OK) return s;
   if (!w) return fail(DG_ERR_INVALID_ARG, "weights is NULL");
   if (!w->embed || !w->wq || !w->wk || !w->wv || !w->wo)
     return fail(DG_ERR_INVALID_ARG, "embed, wq, wk, wv and wo are required");
@@ -665,13 +687,19 @@ struct EncodePlan {
   size_t q, k, v, o, h, part_o, part_ml, proj_part, ids, chunks, active, total;
   AttnPlan attn;
   int J;
+  bool too_big;   // more chunk rows than int32 addresses (no plan)
 };
 
 EncodePlan plan_encode(const dg_dims &d, int B, int max_len) {
   EncodePlan p{};
-  p.J = (int)((max_len + d.canvas - 1) / d.canvas);
-  const int64_t NC = (int64_t)B * p.J, M = NC * d.canvas;
+  const int64_t J = ((int64_t)max_len + d.canvas - 1) / d.canvas;
+  const int64_t NC = (int64_t)B * J, M = NC * d.canvas;
+  p.J = (int)J;
   if (NC == 0) return p;   // nothing to run: no workspace
+  if (M > INT32_MAX) {     // the chunk rows are addressed as int32
+    p.too_big = true;
+    return p;
+  }
   const size_t ts = tsize(d);
   const size_t nq = (size_t)d.n_q_heads * d.head_dim, nkv = (size_t)d.n_kv_heads * d.head_dim;
   Arena a;
@@ -683,8 +711,10 @@ EncodePlan plan_encode(const dg_dims &d, int B, int max_len) {
   p.attn = plan_attention(d, (int)NC, max_len);
   // split partials: the most that any shorter max_len needs (more chunks can
   // mean fewer splits), so that the size only grows with max_len
+  // (past 1024 chunks per sequence there are enough tiles that neither the
+  // attention nor the projections split)
   size_t po = 0, pml = 0, pp = 0;
-  for (int j = 1; j <= p.J; ++j) {
+  for (int j = 1; j <= p.J; j = (j < 1024 || j == p.J) ? j + 1 : p.J) {
     const int64_t nc = (int64_t)B * j, m = nc * d.canvas;
     const AttnPlan ap = plan_attention(d, (int)nc, std::min(max_len, j * d.canvas));
     po = std::max(po, ap.part_o);
@@ -713,7 +743,11 @@ __attribute__((visibility("hidden"))) dg_status dg_internal_fail(dg_status s, co
 }
 
 const char *dg_status_string(dg_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the value as one (a C++ load of an
+  // enum outside its enumerators' range is undefined)
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case DG_OK: return "ok";
     case DG_ERR_INVALID_ARG: return "invalid argument";
     case DG_ERR_TOO_MANY_LABELS: return "too many labels (more than the 26 single-token labels A..Z)";
@@ -749,6 +783,9 @@ dg_status dg_slot_read_validate(const dg_dims *dims, int32_t batch, int32_t n_sl
   if (n_slots < 0) return fail(DG_ERR_INVALID_ARG, "n_slots %d < 0", n_slots);
   if (n_draws < 1 || n_draws > 16) return fail(DG_ERR_INVALID_ARG, "n_draws %d outside [1, 16]", n_draws);
   if (!(entropy_threshold >= 0.f)) return fail(DG_ERR_INVALID_ARG, "entropy_threshold must be >= 0");
+  // a read holds up to 1 + n_draws canvases per batch entry
+  s = check_sizes(*dims, (int64_t)batch * (n_draws + 1), 0, (int64_t)batch * n_slots * (n_draws + 1));
+  if (s != DG_OK) return s;
   return ok();
 }
 
@@ -756,11 +793,14 @@ dg_status dg_commit_validate(int32_t batch, int32_t canvas) {
   if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
   if (canvas < 1 || canvas > DG_MAX_CANVAS)
     return fail(DG_ERR_INVALID_ARG, "canvas %d outside [1, %d]", canvas, DG_MAX_CANVAS);
+  if ((int64_t)batch * canvas > kMaxRows)
+    return fail(DG_ERR_INVALID_ARG, "batch %d x canvas %d exceeds 2^31 - 1 rows", batch, canvas);
   return ok();
 }
 
 size_t dg_denoise_step_workspace(const dg_dims *dims, int32_t batch, int32_t max_prompt) {
-  if (check_dims(dims) != DG_OK || batch < 0 || max_prompt < 0) return 0;
+  if (check_dims(dims) != DG_OK || batch < 0 || max_prompt < 0 || !sizes_fit(*dims, batch, max_prompt))
+    return 0;
   return plan_step(*dims, batch, max_prompt).total;
 }
 
@@ -785,7 +825,8 @@ dg_status dg_denoise_step(const dg_dims *dims, const dg_weights *w, const dg_pro
 }
 
 size_t dg_denoise_loop_workspace(const dg_dims *dims, int32_t batch, int32_t max_prompt) {
-  if (check_dims(dims) != DG_OK || batch < 0 || max_prompt < 0) return 0;
+  if (check_dims(dims) != DG_OK || batch < 0 || max_prompt < 0 || !sizes_fit(*dims, batch, max_prompt))
+    return 0;
   return plan_loop(*dims, batch, max_prompt).total;
 }
 
@@ -891,8 +932,9 @@ dg_status dg_prefill_kv(const dg_dims *dims, const dg_weights *w, int64_t n_toke
 }
 
 size_t dg_prefill_encode_workspace(const dg_dims *dims, int32_t batch, int32_t max_len) {
-  if (check_dims(dims) != DG_OK || batch < 0 || max_len < 0) return 0;
-  return plan_encode(*dims, batch, max_len).total;
+  if (check_dims(dims) != DG_OK || batch < 0 || max_len < 0 || max_len > kMaxPrompt) return 0;
+  const EncodePlan p = plan_encode(*dims, batch, max_len);
+  return p.too_big ? 0 : p.total;
 }
 
 dg_status dg_prefill_encode(const dg_dims *dims, const dg_weights *w, int32_t batch,
@@ -905,6 +947,7 @@ dg_status dg_prefill_encode(const dg_dims *dims, const dg_weights *w, int32_t ba
   if (batch < 0) return fail(DG_ERR_INVALID_ARG, "batch %d < 0", batch);
   if (max_len < 0 || total_len < 0)
     return fail(DG_ERR_INVALID_ARG, "max_len and total_len must be >= 0");
+  if (max_len > kMaxPrompt) return fail(DG_ERR_INVALID_ARG, "max_len %d exceeds 2^30", max_len);
   const bool fwd = hidden_out || attn_out;
   if (!w || !w->embed || !w->wk || !w->wv || (fwd && (!w->wq || !w->wo)))
     return fail(DG_ERR_INVALID_ARG,
@@ -919,6 +962,9 @@ dg_status dg_prefill_encode(const dg_dims *dims, const dg_weights *w, int32_t ba
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool run = fwd && batch > 0 && max_len > 0 && total_len > 0;
   const EncodePlan p = plan_encode(d, run ? batch : 0, run ? max_len : 0);
+  if (p.too_big)
+    return fail(DG_ERR_INVALID_ARG, "batch %d x %d chunks of %d tokens exceed 2^31 - 1 rows", batch, p.J,
+                d.canvas);
   if (run && (!workspace || ws_bytes < p.total))
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 ws_bytes, p.total);
@@ -1001,7 +1047,8 @@ namespace {
 size_t slot_read_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots, int32_t max_prompt,
                            int32_t n_draws, bool full) {
   if (check_dims(dims) != DG_OK || batch < 0 || n_slots < 0 || max_prompt < 0 || n_draws < 1 ||
-      n_draws > 16)
+      n_draws > 16 ||
+      !sizes_fit(*dims, (int64_t)batch * (n_draws + 1), max_prompt, (int64_t)batch * n_slots * (n_draws + 1)))
     return 0;
   return slot_ws_bound(*dims, batch, n_slots, max_prompt, n_draws, full);
 }
@@ -1374,7 +1421,8 @@ extern "C" {
 
 size_t dg_slot_read_staged_workspace(const dg_dims *dims, int32_t batch, int32_t n_slots,
                                      int32_t max_prompt, int32_t n_draws) {
-  if (dg_slot_read_validate(dims, batch, n_slots, n_draws, 0.1f) != DG_OK || max_prompt < 0)
+  if (dg_slot_read_validate(dims, batch, n_slots, n_draws, 0.1f) != DG_OK || max_prompt < 0 ||
+      max_prompt > kMaxPrompt)
     return 0;
   return plan_staged(*dims, batch, n_slots, max_prompt, n_draws).total;
 }

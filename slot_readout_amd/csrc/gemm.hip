@@ -404,10 +404,8 @@ __device__ inline bool tile_active(const int32_t *active, int64_t m0, int64_t ro
 // d = 2816 (11 tiles per range), and measured slower (555-618 us against
 // 481 us), so it is off.  The direct-to-LDS kernel instead deals consecutive
 // (range, tile) items to each XCD, which keeps a range's tiles on one or two
-// XCDs with every CU busy.
-constexpr int kScTileD = 256;
-constexpr bool kScGroup = false;
-
+// XCDs with every CU busy.  (kScTileD and kScGroup sit in kernels.h, beside
+// the split planning that reads them.)
 
 // Split-K partial of one tile: element (row, col) of the tile's accumulators to
 // dst[row * ld + col] for row < M, col < ncols (fp32, no epilogue)
@@ -1386,33 +1384,6 @@ static hipError_t launch_qkv_t(const QkvArgs &a0, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Projections at small M are weight-streaming and latency-bound: 64 x 64 tiles
-// with a 4-stage prefetch, and below 256 tiles the K range is split so that
-// about 512 workgroups stream the weights (the bf16 path; K splits of at least
-// 512).  Partials are summed by a separate reduce in split order.  Measured at
-// d 2816: the read's projections of 40 slot rows take 15-17.5 instead of 19-27
-// us; splitting the step's 384-tile q,k,v projection in two, or its output
-// projection in five, was no faster (each extra launch costs about 4 us).
-static void proj_split(int64_t M, int64_t ncols, int K, bool bf, int *ks, int *kchunk) {
-  *ks = 1;
-  *kchunk = K;
-  if (!bf || M <= 0 || ncols <= 0 || K <= 0) return;
-  const int64_t tiles = cdiv64(M, 64) * cdiv64(ncols, 64);
-  if (tiles >= 256) return;
-  int64_t s = 512 / tiles;
-  if (s > K / 512) s = K / 512;
-  if (s < 2) return;
-  const int64_t steps = cdiv64(K, 64), per = cdiv64(steps, s);
-  *ks = (int)cdiv64(steps, per);
-  *kchunk = (int)(per * 64);
-}
-
-int proj_ksplit(int64_t M, int64_t ncols, int K, bool bf) {
-  int ks, kc;
-  proj_split(M, ncols, K, bf, &ks, &kc);
-  return ks;
-}
-
 hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
   const int64_t ntot = a.col1 - a.col0;
   if (a.M <= 0 || ntot <= 0) return hipSuccess;
@@ -1551,27 +1522,6 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
     hipLaunchKernelGGL((lmhead_kernel<float, VTILE, 64, 4, 1, 1, 16>), grid, dim3(4 * WAVE), 0, st, a);
   }
   return hipGetLastError();
-}
-
-// Vocabulary ranges of the self-conditioning GEMM: about one workgroup per CU
-// (with XCD grouping: as many whole ranges per XCD as fit its 32 CUs).
-int sc_ksplit(int64_t M, int d, int vocab, bool bf) {
-  const int64_t tiles = bf ? cdiv64(M, 256) * cdiv64(d, kScTileD) : cdiv64(M, 64) * cdiv64(d, 64);
-  const int nk = vocab / (bf ? 64 : 16);
-  const int64_t per_xcd = 32 / tiles;
-  int64_t ks = kScGroup ? (per_xcd >= 1 ? 8 * per_xcd : 8) : 256 / tiles;
-  if (ks > nk) ks = nk;
-  if (ks > 64) ks = 64;
-  // bf16: once about 128 workgroups run, each split spans at least 512
-  // vocabulary entries (16 K steps of the direct-to-LDS loop), so short loops
-  // do not trade their work for fp32 partial-sum traffic (ragged batch of 32
-  // canvases: 8 -> 4 splits, 39 -> 35 us)
-  if (bf) {
-    const int64_t cap = std::max<int64_t>(vocab / 512, cdiv64(128, tiles));
-    if (ks > cap) ks = cap;
-  }
-  if (ks < 1) ks = 1;
-  return (int)ks;
 }
 
 hipError_t launch_scgemm(const ScArgs &a, bool bf, hipStream_t st) {

@@ -9,6 +9,10 @@ namespace dg {
 
 // Vocabulary tile of the LM-head statistics (and of the p~ rescale factors).
 constexpr int VTILE = 256;
+// Self-conditioning GEMM: d columns per workgroup (bf16), and whether a
+// vocabulary range's workgroups are kept on one XCD
+constexpr int kScTileD = 256;
+constexpr bool kScGroup = false;
 
 struct QkvArgs {
   const int32_t *ids;      // [M] token ids
@@ -194,6 +198,8 @@ struct CommitArgs {
 // K splits of a projection of M rows x ncols outputs over K (1: none); the
 // partial buffer of a split launch holds ksplit * M * ncols floats
 int proj_ksplit(int64_t M, int64_t ncols, int K, bool bf);
+// K split of a projection: ks splits of kchunk columns each (ks = 1: none)
+void proj_split(int64_t M, int64_t ncols, int K, bool bf, int *ks, int *kchunk);
 hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st);
 hipError_t launch_oproj(const OprojArgs &a, bool bf, hipStream_t st);
 hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st);

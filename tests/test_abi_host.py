@@ -301,3 +301,16 @@ def test_encode_rejects_bad_arguments_before_any_launch():
     assert call(wsb=ws - 1) == dg.DG_ERR_WORKSPACE
     assert call(wsp=None) == dg.DG_ERR_WORKSPACE
     assert call(dims=_dims(dg, head_dim=128)) == dg.DG_ERR_UNSUPPORTED
+
+
+def test_status_string_of_any_int():
+    """A C caller may pass any int as a status: values outside the enumerators
+    name no status."""
+    dg = _lib_or_skip()
+    L = dg.lib()
+    f = L.dg_status_string
+    f.restype = __import__("ctypes").c_char_p
+    f.argtypes = [__import__("ctypes").c_int]
+    assert f(0) == b"ok"
+    for bad in (-2, -1, 6, 99, 2 ** 31 - 1):
+        assert f(bad) == b"unknown status"
