@@ -655,7 +655,7 @@ def main():
         line["loop"] = loop_leg(dev, inp, stream)
         line["prefill"] = prefill_leg(dev, inp, stream)
         line["staged_read"] = staged_leg(dev, inp, stream)
-    elif args.workload == "long_read":
+    elif args.workload == "long_read" and not args.no_legs:
         line["prefill"] = prefill_leg(dev, inp, stream)
     cpu = None
     if legs and not args.no_cpu_baseline:

@@ -145,6 +145,14 @@ def _one_pass_draws(dims, B, S, nd, max_prompt):
     ts = 2 if dims.dtype == "bf16" else 4
     head_s = dims.vocab * dims.d_model * ts / 5e12
     hq, hkv = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    if dims.dtype == "bf16" and dims.head_dim == 64:
+        # patched draws: their slot rows' projections and attention, against the
+        # LM-head stream plus a second stream of the prompts' k, v
+        per_draw = (2 * dims.d_model * (hq + 2 * hkv) * S + 2 * hq * dims.d_model * S
+                    + 4 * hq * (max_prompt + dims.canvas) * S)
+        draw_s = B * nd * per_draw / 1e15
+        kv_s = B * max_prompt * 2 * hkv * ts / 5e12
+        return nd > 1 and draw_s < head_s + kv_s
     qt = 64 if dims.head_dim == 512 else 128
     s_att = -(-S // qt) * qt
     per_canvas = (2 * dims.d_model * (hq + 2 * hkv) * dims.canvas + 2 * hq * dims.d_model * S
@@ -340,3 +348,19 @@ def test_slot_read_draws_share_a_tile_at_canvas_edges(torch_cuda, name):
     assert (ref["draws_used"] == inp["n_draws"]).any()
     g = _read(inp)
     _check_slots(g, ref, inp, inp["dims"].dtype, f"draw tile edges {name}")
+
+
+def test_slot_read_patched_draws_two_pass(torch_cuda):
+    """Read-batch dims in bf16 with 150 slots per canvas and a 64-token prompt:
+    the draws' slot rows outweigh a second pass, so the two-pass order runs with
+    patched draws (the draws read their base canvas's k, v with their own slot
+    rows in place), two gathered query tiles per canvas, against the oracle."""
+    inp = make_inputs(config("reads512", n_slots=150), batch=2, prompt_override=("fixed", 64))
+    S = inp["slot_pos"].shape[1]
+    assert not _one_pass_draws(inp["dims"], 2, S, inp["n_draws"], int(inp["max_prompt"]))
+    rs = companion_row_scale(inp, (2, S), 4.0, 256.0)
+    g = _read(inp, row_scale=rs)
+    ref = oracle.slot_read(inp, row_scale=rs)
+    _check_slots(g, ref, inp, "bf16", "patched draws two-pass", max_excused=0.5)
+    du = ref["draws_used"]
+    assert (du == 1).any() and (du == inp["n_draws"]).any()
