@@ -1501,9 +1501,11 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
       const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 256));
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 256, 2, 4, 1, 64, false, true>), grid, dim3(8 * WAVE), 0, st, a);
     }
-  } else if (bf && a.nrows <= kLmFewRows) {
+  } else if (bf && (a.nrows <= kLmFewRows || (int64_t)(a.vocab / VTILE) * cdiv64(a.nrows, 256) < 64)) {
     // few rows (slot reads): a 64-row tile keeps the MFMA work proportional to
-    // the rows and three workgroups per CU keep the vocabulary stream busy
+    // the rows and three workgroups per CU keep the vocabulary stream busy.
+    // Also when 256-row tiles would leave most CUs idle (a small vocabulary: one
+    // canvas at V 2,048 is 8 tiles; 64-row tiles give 32, 22 -> 18 us)
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
     if (a.head_tiled)
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32, true>), grid, dim3(4 * WAVE), 0, st, a);
