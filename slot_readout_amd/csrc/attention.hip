@@ -19,7 +19,11 @@
 // registers.  For bf16, K and V are both staged row-major in LDS from
 // coalesced loads; the V^T fragments come from transposing LDS reads
 // (ds_read_b64_tr_b16).  V carries an extra column of ones, so the same MFMA
-// also accumulates the softmax denominator sum_key p.
+// also accumulates the softmax denominator sum_key p (for bf16 that block of
+// V^T is a constant fragment held in registers, not read from LDS).
+// The waves raise their priority while they issue MFMAs: a wave that is ready
+// to issue them goes ahead of the softmax work of the other waves on its SIMD,
+// so the matrix cores idle less (long read at head_dim 64: 60 -> 55 us).
 #include <type_traits>
 
 #include "common.h"
@@ -152,7 +156,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   __shared__ __attribute__((aligned(16))) T Ks[2][NK * KP];
   // V plus one extra 16-wide block whose first element is 1: the PV MFMA then
   // also yields sum_key p (the softmax denominator).  bf16: V row-major [NK][VKP]
-  // read through transposing LDS reads; fp32: V^T [RB*16][VP] staged element-wise.
+  // read through transposing LDS reads (the extra block is a register constant;
+  // its 16 columns in LDS only pad the rows); fp32: V^T [RB*16][VP] staged
+  // element-wise, with the extra block.
   constexpr int RB = HD / 16 + 1;
   constexpr int VKP = HD + 16;
   constexpr int VSZ = TR ? NK * VKP : RB * 16 * VP;
@@ -288,15 +294,17 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   float mrun[QB];
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) mrun[jb] = -INFINITY;
+  // the block of V^T past the head: row HD is all ones, the rest zeros.  bf16:
+  // lane (col, grp) of a fragment holds row HD + col, so the fragment is a
+  // constant; fp32: staged once in both LDS buffers
+  frag ones_frag{};
+  if constexpr (TR) {
 #pragma unroll
-  for (int bf = 0; bf < 2; ++bf) {
-    if constexpr (TR) {
-      for (int i = threadIdx.x; i < NK * 16; i += NT)
-        Vt[bf][(i / 16) * VKP + HD + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
-    } else {
-      for (int i = threadIdx.x; i < 16 * VP; i += NT)
-        Vt[bf][HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
-    }
+    for (int e = 0; e < MF::KPL; ++e) ones_frag[e] = from_f<T>(col == 0 ? 1.f : 0.f);
+  } else {
+#pragma unroll
+    for (int bf = 0; bf < 2; ++bf)
+      for (int i = threadIdx.x; i < 16 * VP; i += NT) Vt[bf][HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
   }
 
   // block b: prompt blocks first, then canvas-window blocks; b >= nb names an
@@ -422,18 +430,35 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
     mref[jb] = 0.f;
     negm[jb] = zero4();
   }
+  // head_dim 64 (without split probabilities): every K fragment of the block is
+  // read before the first score MFMA, so the block waits for LDS once
+  constexpr bool KPRE = HD == 64 && !PREC;
+  // MFMA-phase priority (head_dim 64 bf16; at head_dim 512 and in fp32 the
+  // priority changes cost the scheduler's freedom and registers spill)
+  constexpr bool PRIO = HD == 64 && TR;
   auto compute = [&](const Blk &d, int bf) {
     f32x4 sacc[NK / 16][QB];
+    auto kfrag = [&](int ks, int kb2) {
+      return *reinterpret_cast<const frag *>(Ks[bf] + (kb2 * 16 + col) * KP + ks * MF::KI + grp * MF::KPL);
+    };
+    frag kf[KPRE ? KS : 1][KPRE ? NK / 16 : 1];
+    if constexpr (KPRE) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb2 = 0; kb2 < NK / 16; ++kb2) kf[ks][kb2] = kfrag(ks, kb2);
+    }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2) {
-        const frag af = *reinterpret_cast<const frag *>(Ks[bf] + (kb2 * 16 + col) * KP + ks * MF::KI +
-                                                         grp * MF::KPL);
+        const frag af = KPRE ? kf[KPRE ? ks : 0][KPRE ? kb2 : 0] : kfrag(ks, kb2);
 #pragma unroll
         for (int jb = 0; jb < QB; ++jb)
           sacc[kb2][jb] = MF::mma(af, qf[jb][ks], ks == 0 ? (INIT_NEG ? negm[jb] : zero4()) : sacc[kb2][jb]);
       }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     if constexpr (!INIT_NEG) {
 #pragma unroll
       for (int kb2 = 0; kb2 < NK / 16; ++kb2)
@@ -452,12 +477,15 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
         // (encoder-mode chunks: keys at or before the query, W = C - 1)
         const int klo_ok = d.canvas ? max(qrel - W, cv0) : -1;
         const int khi_ok = d.canvas ? min(min(qrel + Wup, cv0 + C - 1), d.rem - 1) : d.rem - 1;
+        // key kl = kb2 * 16 + grp * 4 + r, compared as kb2 * 16 + r against the
+        // bounds less grp * 4: the offsets are inline constants, not registers
+        const int glo = klo_ok - grp * 4, ghi = khi_ok - grp * 4;
 #pragma unroll
         for (int kb2 = 0; kb2 < NK / 16; ++kb2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int kl = kb2 * 16 + grp * 4 + r;
-            const bool ok = kl >= klo_ok && kl <= khi_ok;
+            const int kc = kb2 * 16 + r;
+            const bool ok = kc >= glo && kc <= ghi;
             sacc[kb2][jb][r] = ok ? sacc[kb2][jb][r] : -INFINITY;
           }
       }
@@ -494,6 +522,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
         for (int r = 0; r < 4; ++r) sacc[kb2][jb][r] = __builtin_amdgcn_exp2f(sacc[kb2][jb][r]);
     }
 
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     if constexpr (MF::KPL == 8) {
 #pragma unroll
       for (int t = 0; t < NK / 32; ++t)
@@ -515,12 +544,14 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
             // 32t+16+4grp+0..3 for d = rb*16 + col.  A transposing read where
             // source lane s of the group points at V[key0 + s/4][d0 + 4(s%4)]
             // returns V[key0 + 0..3][d0 + lane%16] in each lane.
-            const T *src0 = Vt[bf] + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
-            const v4s lo4 = ds_read_tr16(src0);
-            const v4s hi4 = ds_read_tr16(src0 + 16 * VKP);
-            frag af;
-            __builtin_memcpy(&af, &lo4, 8);
-            __builtin_memcpy(reinterpret_cast<char *>(&af) + 8, &hi4, 8);
+            frag af = ones_frag;
+            if (rb < HD / 16) {
+              const T *src0 = Vt[bf] + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
+              const v4s lo4 = ds_read_tr16(src0);
+              const v4s hi4 = ds_read_tr16(src0 + 16 * VKP);
+              __builtin_memcpy(&af, &lo4, 8);
+              __builtin_memcpy(reinterpret_cast<char *>(&af) + 8, &hi4, 8);
+            }
             oacc[rb][jb] = MF::mma(af, pf, oacc[rb][jb]);
             if constexpr (PREC) oacc[rb][jb] = MF::mma(af, pl, oacc[rb][jb]);
           }
@@ -537,6 +568,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
             for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = MF::mma(af, sacc[kb2][jb][r], oacc[rb][jb]);
           }
     }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // Pipeline: block b is computed from LDS buffer b % 2 while block b+1 is
