@@ -48,6 +48,12 @@ __device__ inline v4s ds_read_tr16(const void *p) {
       (__attribute__((address_space(3))) v4s *)(p));
 }
 
+// one 16-byte chunk per lane from global memory straight into LDS: lane l
+// writes bytes [16 l, 16 l + 16) after dst (dst must be wave-uniform)
+__device__ inline void lds_row16(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
 __device__ inline void pin4(uint4 &v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
@@ -153,7 +159,10 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   static_assert(NK * CPK % NT == 0, "block/thread mismatch");
   // K and V tiles are double-buffered: block b lives in buffer b % 2, so the
   // next block can be staged while the current one is read, one barrier apart
-  __shared__ __attribute__((aligned(16))) T Ks[2][NK * KP];
+  // (each buffer its own array: the compiler then sees that reads of one buffer
+  // do not depend on direct-to-LDS loads into the other)
+  __shared__ __attribute__((aligned(16))) T Ks0[NK * KP], Ks1[NK * KP];
+  auto Ks = [&](int bf) -> T * { return bf ? Ks1 : Ks0; };
   // V plus one extra 16-wide block whose first element is 1: the PV MFMA then
   // also yields sum_key p (the softmax denominator).  bf16: V row-major [NK][VKP]
   // read through transposing LDS reads (the extra block is a register constant;
@@ -162,7 +171,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   constexpr int RB = HD / 16 + 1;
   constexpr int VKP = HD + 16;
   constexpr int VSZ = TR ? NK * VKP : RB * 16 * VP;
-  __shared__ __attribute__((aligned(16))) T Vt[2][VSZ];
+  __shared__ __attribute__((aligned(16))) T Vt0[VSZ], Vt1[VSZ];
+  auto Vt = [&](int bf) -> T * { return bf ? Vt1 : Vt0; };
 
   // group = (canvas, kv head, split); its tiles (the query heads sharing the
   // kv head x the query tiles) read the same K/V blocks and run on one XCD.
@@ -304,7 +314,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   } else {
 #pragma unroll
     for (int bf = 0; bf < 2; ++bf)
-      for (int i = threadIdx.x; i < 16 * VP; i += NT) Vt[bf][HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
+      for (int i = threadIdx.x; i < 16 * VP; i += NT) Vt(bf)[HD * VP + i] = from_f<T>(i < VP ? 1.f : 0.f);
   }
 
   // block b: prompt blocks first, then canvas-window blocks; b >= nb names an
@@ -363,7 +373,11 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
     }
   }
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 kr[PF][CH], vr[PF][CH];
+  // head_dim 512 (bf16): a key row of K or V is 1 KB, one direct-to-LDS wave
+  // instruction (64 lanes x 16 bytes), so the blocks are staged straight into
+  // LDS and no registers hold them
+  constexpr bool DMA = TR && HD == 512 && !PATCH;
+  u32x4 kr[DMA ? 1 : PF][DMA ? 1 : CH], vr[DMA ? 1 : PF][DMA ? 1 : CH];
   // PATCH: the source of row r of block d (plain loads with per-lane
   // addresses): prompt rows from the block (blk), canvas rows from the base
   // canvas (base) or the draw's slot rows (patch).  Rows past the block's keys
@@ -405,14 +419,14 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
       uint4 kx{xk[i].x, xk[i].y, xk[i].z, xk[i].w}, vx{xv[i].x, xv[i].y, xv[i].z, xv[i].w};
       pin4(kx);
       pin4(vx);
-      *reinterpret_cast<uint4 *>(Ks[bf] + klo[i]) = kx;
+      *reinterpret_cast<uint4 *>(Ks(bf) + klo[i]) = kx;
       if constexpr (TR) {
-        *reinterpret_cast<uint4 *>(Vt[bf] + vlo[i]) = vx;
+        *reinterpret_cast<uint4 *>(Vt(bf) + vlo[i]) = vx;
       } else {
         Chunk<T> vch;
         vch.u = vx;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) Vt[bf][vlo[i] + e * VP] = vch.v[e];
+        for (int e = 0; e < VEC; ++e) Vt(bf)[vlo[i] + e * VP] = vch.v[e];
       }
     }
   };
@@ -439,7 +453,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   auto compute = [&](const Blk &d, int bf) {
     f32x4 sacc[NK / 16][QB];
     auto kfrag = [&](int ks, int kb2) {
-      return *reinterpret_cast<const frag *>(Ks[bf] + (kb2 * 16 + col) * KP + ks * MF::KI + grp * MF::KPL);
+      return *reinterpret_cast<const frag *>(Ks(bf) + (kb2 * 16 + col) * KP + ks * MF::KI + grp * MF::KPL);
     };
     frag kf[KPRE ? KS : 1][KPRE ? NK / 16 : 1];
     if constexpr (KPRE) {
@@ -546,7 +560,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
             // returns V[key0 + 0..3][d0 + lane%16] in each lane.
             frag af = ones_frag;
             if (rb < HD / 16) {
-              const T *src0 = Vt[bf] + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
+              const T *src0 = Vt(bf) + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
               const v4s lo4 = ds_read_tr16(src0);
               const v4s hi4 = ds_read_tr16(src0 + 16 * VKP);
               __builtin_memcpy(&af, &lo4, 8);
@@ -563,7 +577,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const frag af = Vt[bf][(rb * 16 + col) * VP + kb2 * 16 + grp * 4 + r];
+            const frag af = Vt(bf)[(rb * 16 + col) * VP + kb2 * 16 + grp * 4 + r];
 #pragma unroll
             for (int jb = 0; jb < QB; ++jb) oacc[rb][jb] = MF::mma(af, sacc[kb2][jb][r], oacc[rb][jb]);
           }
@@ -579,6 +593,42 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   // unconditionally (past the end, with the empty block), so the loads retire
   // in issue order and each stage waits only for its own slot.
   constexpr int U = PF % 2 == 0 ? PF : 2 * PF;
+  if constexpr (DMA) {
+    static_assert(HD * (int)sizeof(T) == 16 * 64 && NK % NW == 0, "one wave instruction per key row");
+    // wave wu stages key rows wu, wu + NW, ... of K and V; rows past the block's
+    // keys read its first row (their scores are masked, their p is 0)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    auto dma = [&](const Blk &d, int bf) {
+#pragma unroll
+      for (int i = 0; i < NK / NW; ++i) {
+        const int r = wu + i * NW;
+        const int64_t rr = r < d.rem ? r : 0;
+        lds_row16(d.kb + rr * kv_stride + lane * VEC, Ks(bf) + r * KP);
+        lds_row16(d.vb + rr * kv_stride + lane * VEC, Vt(bf) + r * VKP);
+      }
+    };
+    // vmcnt(0), the other counters left alone (gfx9 encoding)
+    constexpr int WAIT0 = (7 << 4) | (15 << 8);
+    // block b is read from buffer b % 2 while block b+1 lands in the other one,
+    // which every wave finished reading before the barrier that ended block b-1
+    if (nb > 0) {
+      dma(desc(0), 0);
+      __builtin_amdgcn_s_waitcnt(WAIT0);
+      __syncthreads();
+    }
+    for (int b = 0; b < nb; b += 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (b + j < nb) {
+          if (b + j + 1 < nb) dma(desc(b + j + 1), (j + 1) % 2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (live) compute(desc(b + j), j);
+          __builtin_amdgcn_s_waitcnt(WAIT0);
+          __syncthreads();
+        }
+      }
+    }
+  } else {
   if (nb > 0) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) fetch(desc(j), kr[j], vr[j]);
@@ -607,6 +657,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
       if (b0 + j + 1 < nb) stage(kr[sl], vr[sl], (j + 1) % 2);
       __syncthreads();
     }
+  }
   }
 
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
