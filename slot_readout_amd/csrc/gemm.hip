@@ -1034,6 +1034,13 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
   // scale, then pass 1: max and lowest argmax per column (= canvas row)
   float mx[TNR];
   int ix[TNR];
+  // first vocabulary row of the wave's block.  The excluded id, if any, is
+  // entry (iex, rex) of lane group gex in at most one wave: a uniform test and
+  // uniform indices, instead of a comparison per value
+  const int vw0 = v0 + wm * G::WM;
+  const int exr = a.exclude_id1 - 1 - vw0;
+  const bool ex_here = a.exclude_id1 > 0 && exr >= 0 && exr < G::WM;
+  const int iex = exr >> 4, gex = (exr >> 2) & 3, rex = exr & 3;
 #pragma unroll
   for (int j = 0; j < TNR; ++j) {
     const int64_t n = n0 + wn * WNR + j * 16 + (lane & 15);
@@ -1048,12 +1055,23 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     for (int i = 0; i < G::TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4) + r;
         float sv = s;
-        if constexpr (F8) sv = ldexpf(s, a.head_exp[v]);   // exact: a power of two
-        const float l = v + 1 == a.exclude_id1 ? -INFINITY : acc[i][j][r] * sv;
-        acc[i][j][r] = l;
-        if (l > m) { m = l; id = v; }
+        if constexpr (F8) sv = ldexpf(s, a.head_exp[vw0 + i * 16 + 4 * (lane >> 4) + r]);   // exact: a power of two
+        acc[i][j][r] *= sv;
+      }
+    if (ex_here && (lane >> 4) == gex) {
+#pragma unroll
+      for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (i == iex && r == rex) acc[i][j][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l = acc[i][j][r];
+        if (l > m) { m = l; id = vw0 + i * 16 + 4 * (lane >> 4) + r; }
       }
     // across the four lane groups: larger value, then lower id
 #pragma unroll
@@ -1120,10 +1138,18 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
     const int64_t n = n0 + wn * WNR + j * 16 + (lane & 15);
     const bool live = n < a.nrows;
     const float rj = (float)tile_ref(mx[j]);
+    // the row's p~ and logits at vocabulary vw0 + 4 (lane >> 4), the lane's
+    // first entry; entry vw0 + i*16 + 4 (lane >> 4) is then a constant offset
+    // away: i*16 in a row-major row, and in the 256 x 32 blocked layout (vw0 is
+    // a multiple of 32) (i >> 1) blocks of 8192 plus (i & 1)*16
+    T *pj = nullptr;
+    if (pt && live)
+      pj = pt + (a.ptilde_blocked ? ((n >> 8) * (a.vocab >> 5) + (vw0 >> 5)) * 8192 + (n & 255) * 32
+                                  : n * a.vocab + vw0) + 4 * (lane >> 4);
+    float *lj = a.logits && live ? a.logits + n * a.vocab + vw0 + 4 * (lane >> 4) : nullptr;
     float s = 0.f, t = 0.f;
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
-      const int vb = v0 + wm * G::WM + i * 16 + 4 * (lane >> 4);
       f32x4 e4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1136,15 +1162,9 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void lmhead_kernel(LmheadArgs a) {
         t += e * x;
         e4[r] = e;
       }
-      // four consecutive vocabulary entries of one row: one 8- (bf16) or 16-byte
-      // store (row-major, or inside one 256 x 32 block)
-      if (pt && live) {
-        const int64_t off = a.ptilde_blocked
-                                ? ((n >> 8) * (a.vocab >> 5) + (vb >> 5)) * 8192 + (n & 255) * 32 + (vb & 31)
-                                : n * a.vocab + vb;
-        store4<T>(pt + off, e4);
-      }
-      if (a.logits && live) *reinterpret_cast<f32x4 *>(a.logits + n * a.vocab + vb) = acc[i][j];
+      // four consecutive vocabulary entries of one row: one 8- (bf16) or 16-byte store
+      if (pj) store4<T>(pj + (a.ptilde_blocked ? (i >> 1) * 8192 + (i & 1) * 16 : i * 16), e4);
+      if (lj) *reinterpret_cast<f32x4 *>(lj + i * 16) = acc[i][j];
     }
     s += __shfl_xor(s, 16);
     t += __shfl_xor(t, 16);
