@@ -59,6 +59,8 @@ __device__ inline void pin4(uint4 &v) {
 }
 
 constexpr float kLazy = 8.f;
+// owners in the key table of a patched tile
+constexpr int kKeyShared = 0xFE, kKeyNone = 0xFF;
 
 // Split partials of O are kept in the storage type: fp32, or bf16 whose
 // rounding (2^-9 relative) matches that of the final bf16 output.
@@ -89,11 +91,17 @@ template <> __device__ inline float4 load4v<bf16>(const bf16 *p) {
 // With ncp canvases packed in the tile (gathered queries of canvases that
 // share a prompt), the canvas keys are those of the ncp canvases, one after
 // the other ([0, ncp * C)).
+// Patched draws (a.kpatch, gathered queries): the tile's canvases share their
+// base canvas and their query positions, so the canvas keys are the base
+// canvas's rows at positions [*alo, *alo + *na) -- the union of the windows of
+// the tile's queries -- then the ncp * qn slot rows of the tile's canvases in
+// kpatch ([0, *na + ncp * qn)).
 // Encoder-mode chunks (a.chunks): the keys of the sequence before the chunk,
 // then the chunk's own keys up to the tile's last query (none for a tile past
 // the chunk's end).
 __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int64_t *p0o,
-                                 int64_t *plen, int *lo, int *hi, int ncp = 1) {
+                                 int64_t *plen, int *lo, int *hi, int ncp = 1, int *alo = nullptr,
+                                 int *na = nullptr) {
   if (a.chunks) {
     const int4 c = a.chunks[cb];
     const bool past = i0 >= c.z;
@@ -112,7 +120,23 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
   if (p1 - p0 > a.max_len) { p1 = p0 + a.max_len; bad = true; }
   *p0o = p0;
   *plen = p1 - p0;
-  if (a.qpos) {
+  if (a.qpos && a.kpatch) {
+    int mn = a.C, mx = -1;
+    for (int sl = 0; sl < a.qn; ++sl) {
+      const int p = a.qpos[(int64_t)cb * a.qn + sl];
+      if (p >= 0 && p < a.C) {
+        mn = p < mn ? p : mn;
+        mx = p > mx ? p : mx;
+      }
+    }
+    // (the host clamps W to C - 1, so mx + W + 1 does not overflow)
+    const int l0 = mx < 0 ? 0 : (mn - a.W > 0 ? mn - a.W : 0);
+    const int l1 = mx < 0 ? 0 : (mx + a.W + 1 < a.C ? mx + a.W + 1 : a.C);
+    if (alo) *alo = l0;
+    if (na) *na = l1 - l0;
+    *lo = 0;
+    *hi = (l1 - l0) + ncp * a.qn;
+  } else if (a.qpos) {
     *lo = 0;
     *hi = a.C * ncp;
   } else {
@@ -144,8 +168,13 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   constexpr int VEC = 16 / sizeof(T);
   constexpr bool TR = sizeof(T) == 2;
   static_assert(!PREC || TR, "split probabilities: bf16 storage");
-  // slot index at each canvas position of the tile's canvases (-1: none)
+  // slot index at each canvas position of the tile's canvases (-1: none), and
+  // the table of the tile's canvas keys (see tile_keys): position | owner << 16
+  // | slot-position flag << 24, owner kKeyShared for a base row (seen by every
+  // canvas of the tile, except by a draw at one of its slot positions), a canvas
+  // j of the tile for its slot row, or kKeyNone
   __shared__ short smap[PATCH ? DG_MAX_CANVAS : 1];
+  __shared__ int kinfo[PATCH ? 2 * DG_MAX_CANVAS : 1];
   // output / partial type
   using TO = typename std::conditional<PREC, float, T>::type;
   // bf16 rows of K and V are HD + 16 elements apart: with that stride both the
@@ -199,8 +228,8 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   const int col = lane & 15, grp = lane >> 4;
 
   int64_t p0, plen;
-  int lo, hi;
-  const bool bad = tile_keys(a, cb, i0, NQ, &p0, &plen, &lo, &hi, ncp);
+  int lo, hi, alo = 0, na = 0;
+  const bool bad = tile_keys(a, cb, i0, NQ, &p0, &plen, &lo, &hi, ncp, &alo, &na);
   if (bad && a.flags && threadIdx.x == 0 && s == 0 && qt == 0 && h == 0)
     atomicOr(a.flags, DG_FLAG_BAD_SEQLENS);
   const int64_t nkeys = plen + (hi - lo);
@@ -246,6 +275,18 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
         const int p = a.qpos[(int64_t)cb * QN + sl];
         if (p >= 0 && p < C) smap[p] = (short)sl;
       }
+    __syncthreads();
+    for (int kk = threadIdx.x; kk < na; kk += NT) {
+      const int p = alo + kk;
+      kinfo[kk] = p | (kKeyShared << 16) | (smap[p] >= 0 ? 1 << 24 : 0);
+    }
+    for (int kb = threadIdx.x; kb < ncp * QN; kb += NT) {
+      const int j = kb / QN, sl = kb % QN;
+      const int p = a.qpos[(int64_t)(cb + j) * QN + sl];
+      // the slot row of a draw at its position, unless a later slot there wins
+      const bool own = p >= 0 && p < C && (cb + j) % cpp >= a.patch_from && smap[p] == sl;
+      kinfo[na + kb] = own ? p | (j << 16) : kKeyNone << 16;
+    }
     __syncthreads();
   }
   const T *kc = static_cast<const T *>(a.k) + cbase;
@@ -385,11 +426,9 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   auto src_row = [&](const Blk &d, int r, const T *blk, const T *base, const T *patch) -> const T * {
     const int rr = r < d.rem ? r : 0;
     if (!d.canvas) return blk + (int64_t)rr * kv_stride;
-    const int kk = d.k0 + rr;                  // key of the tile's concatenated canvases
-    const int cj = cb + kk / C, pos = kk % C;  // its canvas and position
-    const int sl = cj % cpp >= a.patch_from ? (int)smap[pos] : -1;
-    return sl >= 0 ? patch + ((int64_t)cj * QN + sl) * kv_stride + (int64_t)g * HD
-                   : base + ((int64_t)(cj / cpp) * C + pos) * kv_stride;
+    const int kk = d.k0 + rr;   // canvas key of the tile: a base row, then the slot rows
+    return kk < na ? base + ((int64_t)(cb / cpp) * C + alo + kk) * kv_stride
+                   : patch + ((int64_t)cb * QN + (kk - na)) * kv_stride + (int64_t)g * HD;
   };
   auto fetch = [&](const Blk &d, u32x4 (&xk)[CH], u32x4 (&xv)[CH]) {
     if constexpr (PATCH) {
@@ -483,7 +522,23 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
     const bool full = !d.canvas && d.rem == NK;   // uniform: no key of the block is masked
 #pragma unroll
     for (int jb = 0; jb < QB; ++jb) {
-      if (!full) {
+      if (PATCH && d.canvas) {
+        // a base row is seen within the window, except by a draw at one of its
+        // slot positions; a slot row only by its own canvas, within the window
+        const int pq = qp[jb] - ccv[jb] * C;   // the query's position (negative: none)
+        const bool cpat = (cb + ccv[jb]) % cpp >= a.patch_from;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NK / 16; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kl = kb2 * 16 + grp * 4 + r;
+            const int info = kinfo[d.k0 + (kl < d.rem ? kl : 0)];
+            const int own = (info >> 16) & 0xFF, dp = (info & 0xFFFF) - pq;
+            const bool ok = kl < d.rem && qp[jb] >= 0 && dp >= -W && dp <= W &&
+                            (own == kKeyShared ? !(cpat && (info >> 24)) : own == ccv[jb]);
+            sacc[kb2][jb][r] = ok ? sacc[kb2][jb][r] : -INFINITY;
+          }
+      } else if (!full) {
         // canvas keys: visible iff |key - qp| <= W, i.e. kl in [qrel - W, qrel +
         // W], and (packed canvases) the key is of the column's own canvas
         const int qrel = qp[jb] - d.k0;
@@ -802,7 +857,7 @@ hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_
   const bool patch = a.kpatch != nullptr;
   // patched draws: gathered queries of canvases grouped by base canvas, k/v
   // not duplicated (kv_cmul 1), canvas lengths within the position map
-  if (patch && (!attn_patch_supported(head_dim, bf) || !a.prec || !a.qpos || a.kv_cmul > 1 || a.C > DG_MAX_CANVAS ||
+  if (patch && (!attn_patch_supported(head_dim, bf, a.qn) || !a.prec || !a.qpos || a.kv_cmul > 1 || a.C > DG_MAX_CANVAS ||
                 !a.vpatch || a.canvas_per_prompt < 1))
     return hipErrorInvalidValue;
   // encoder-mode chunks: every position of each chunk, one canvas per tile

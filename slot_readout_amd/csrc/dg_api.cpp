@@ -269,7 +269,7 @@ bool speculate_draws(const dg_dims &d, int B, int S, int nd, int max_prompt, boo
   if (nd <= 1 || B <= 0) return false;
   const double head_s = (double)d.vocab * d.d_model * (double)tsize(d) / 5e12;
   const double hq = (double)d.n_q_heads * d.head_dim, hkv = (double)d.n_kv_heads * d.head_dim;
-  if (!full && dg::attn_patch_supported(d.head_dim, d.dtype == DG_BF16)) {
+  if (!full && dg::attn_patch_supported(d.head_dim, d.dtype == DG_BF16, S)) {
     const double per_draw = 2.0 * d.d_model * (hq + 2.0 * hkv) * S + 2.0 * hq * d.d_model * S +
                             4.0 * hq * ((double)max_prompt + d.canvas) * S;
     const double draw_s = (double)B * nd * per_draw / 1e15;
@@ -304,7 +304,7 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   // patched draws (slot-row order, head_dim 64 bf16): the draws read their
   // base canvas's k, v with their own slot rows in place, so only the base
   // canvases' k, v are stored, plus the draws' slot rows
-  p.patch = !full && nd > 1 && dg::attn_patch_supported(d.head_dim, d.dtype == DG_BF16);
+  p.patch = !full && nd > 1 && dg::attn_patch_supported(d.head_dim, d.dtype == DG_BF16, S);
   const int ncmax = p.spec ? B * (nd + 1) : (nd > 1 ? B * nd : B);
   const size_t M = (size_t)ncmax * d.canvas, ts = tsize(d);
   const size_t kvrows = p.patch ? (size_t)B * d.canvas : M;   // rows of k, v

@@ -225,7 +225,7 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
 hipError_t launch_attention(const AttnArgs &a, int head_dim, bool bf, hipStream_t st);
 // whether draws can read their base canvas's k, v with patched slot rows
 // (the bf16 read's precise attention at head_dim 64)
-bool attn_patch_supported(int head_dim, bool bf);
+bool attn_patch_supported(int head_dim, bool bf, int n_slots);
 
 hipError_t launch_commit(const CommitArgs &a, hipStream_t st);
 // Multi-step loop bookkeeping (one workgroup per canvas).  loop_init: commit

@@ -79,7 +79,9 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
                            : (int64_t)nc * Hq * cdiv64(qn, nq);
   // most keys one query tile can see: the prompt plus its window span (every
   // canvas key of the tile's canvases for gathered queries)
-  const int64_t win = gathered ? (int64_t)C * ncp : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
+  // (patched tiles: at most C base rows and ncp * qn slot rows)
+  const int64_t win = gathered ? std::max<int64_t>((int64_t)C * ncp, (int64_t)C + (int64_t)ncp * qn)
+                               : (nq + 2 * (int64_t)W < C ? nq + 2 * (int64_t)W : C);
   const int64_t span = (int64_t)max_len + win;
   // about two workgroups per CU at head_dim 64; at head_dim 512 one (its 135 KB
   // of LDS leaves room for one), so each CU runs a single workgroup with twice
@@ -103,6 +105,10 @@ void attn_plan(int nc, int C, int qn, bool gathered, int Hq, int Hkv, int W, int
   *chunk = ck;
 }
 
-bool attn_patch_supported(int head_dim, bool bf) { return bf && head_dim == 64; }
+// (a patched tile keeps its canvas keys -- at most C base rows and cpack * qn
+// slot rows, qn <= C -- in a table of 2 DG_MAX_CANVAS entries)
+bool attn_patch_supported(int head_dim, bool bf, int n_slots) {
+  return bf && head_dim == 64 && n_slots >= 0 && n_slots <= DG_MAX_CANVAS;
+}
 
 }  // namespace dg

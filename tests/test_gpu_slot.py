@@ -145,7 +145,7 @@ def _one_pass_draws(dims, B, S, nd, max_prompt):
     ts = 2 if dims.dtype == "bf16" else 4
     head_s = dims.vocab * dims.d_model * ts / 5e12
     hq, hkv = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
-    if dims.dtype == "bf16" and dims.head_dim == 64:
+    if dims.dtype == "bf16" and dims.head_dim == 64 and S <= 1024:
         # patched draws: their slot rows' projections and attention, against the
         # LM-head stream plus a second stream of the prompts' k, v
         per_draw = (2 * dims.d_model * (hq + 2 * hkv) * S + 2 * hq * dims.d_model * S
