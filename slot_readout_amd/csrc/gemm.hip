@@ -1525,9 +1525,16 @@ hipError_t launch_lmhead(const LmheadArgs &a, bool bf, hipStream_t st) {
     // few rows (slot reads): a 64-row tile keeps the MFMA work proportional to
     // the rows and three workgroups per CU keep the vocabulary stream busy.
     // Also when 256-row tiles would leave most CUs idle (a small vocabulary: one
-    // canvas at V 2,048 is 8 tiles; 64-row tiles give 32, 22 -> 18 us)
+    // canvas at V 2,048 is 8 tiles; 64-row tiles give 32, 22 -> 18 us); there
+    // the K loop is short and latency-bound, and the direct-to-LDS loop with
+    // four stages keeps three steps in flight (18 -> 15 us)
     const dim3 grid = xcd_grid(a.vocab / VTILE, cdiv64(a.nrows, 64));
-    if (a.head_tiled)
+    if (a.nrows > kLmFewRows && a.d % 32 == 0) {
+      if (a.head_tiled)
+        hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, -4, 32, true>), grid, dim3(4 * WAVE), 0, st, a);
+      else
+        hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, -4, 32>), grid, dim3(4 * WAVE), 0, st, a);
+    } else if (a.head_tiled)
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32, true>), grid, dim3(4 * WAVE), 0, st, a);
     else
       hipLaunchKernelGGL((lmhead_kernel<bf16, VTILE, 64, 4, 1, 1, 32>), grid, dim3(4 * WAVE), 0, st, a);
