@@ -92,10 +92,11 @@ template <> __device__ inline float4 load4v<bf16>(const bf16 *p) {
 // share a prompt), the canvas keys are those of the ncp canvases, one after
 // the other ([0, ncp * C)).
 // Patched draws (a.kpatch, gathered queries): the tile's canvases share their
-// base canvas and their query positions, so the canvas keys are the base
-// canvas's rows at positions [*alo, *alo + *na) -- the union of the windows of
-// the tile's queries -- then the ncp * qn slot rows of the tile's canvases in
-// kpatch ([0, *na + ncp * qn)).
+// base canvas and their query positions, so the canvas keys are *na rows of
+// the base canvas -- the listed union of the windows of its queries
+// (a.win_cnt), else every position of [*alo, *alo + *na) from the lowest window
+// start to the highest window end -- then the ncp * qn slot rows of the tile's
+// canvases in kpatch ([0, *na + ncp * qn)).
 // Encoder-mode chunks (a.chunks): the keys of the sequence before the chunk,
 // then the chunk's own keys up to the tile's last query (none for a tile past
 // the chunk's end).
@@ -120,7 +121,13 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
   if (p1 - p0 > a.max_len) { p1 = p0 + a.max_len; bad = true; }
   *p0o = p0;
   *plen = p1 - p0;
-  if (a.qpos && a.kpatch) {
+  if (a.qpos && a.kpatch && a.win_cnt) {
+    const int n = a.win_cnt[cb / a.canvas_per_prompt];
+    if (alo) *alo = 0;
+    if (na) *na = n;
+    *lo = 0;
+    *hi = n + ncp * a.qn;
+  } else if (a.qpos && a.kpatch) {
     int mn = a.C, mx = -1;
     for (int sl = 0; sl < a.qn; ++sl) {
       const int p = a.qpos[(int64_t)cb * a.qn + sl];
@@ -277,7 +284,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
       }
     __syncthreads();
     for (int kk = threadIdx.x; kk < na; kk += NT) {
-      const int p = alo + kk;
+      const int p = a.win_pos ? a.win_pos[(int64_t)(cb / cpp) * C + kk] : alo + kk;
       kinfo[kk] = p | (kKeyShared << 16) | (smap[p] >= 0 ? 1 << 24 : 0);
     }
     for (int kb = threadIdx.x; kb < ncp * QN; kb += NT) {
@@ -427,7 +434,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
     const int rr = r < d.rem ? r : 0;
     if (!d.canvas) return blk + (int64_t)rr * kv_stride;
     const int kk = d.k0 + rr;   // canvas key of the tile: a base row, then the slot rows
-    return kk < na ? base + ((int64_t)(cb / cpp) * C + alo + kk) * kv_stride
+    return kk < na ? base + ((int64_t)(cb / cpp) * C + (kinfo[kk] & 0xFFFF)) * kv_stride
                    : patch + ((int64_t)cb * QN + (kk - na)) * kv_stride + (int64_t)g * HD;
   };
   auto fetch = [&](const Blk &d, u32x4 (&xk)[CH], u32x4 (&xv)[CH]) {

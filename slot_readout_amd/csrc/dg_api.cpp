@@ -243,7 +243,8 @@ LoopPlan plan_loop(const dg_dims &d, int B, int max_prompt) {
 
 struct SlotPlan {
   size_t q, k, v, o, part_o, part_ml, proj_part, h, rows, qpos, qids, kv_row_base, kv_row_slot, stats,
-      rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, kpatch, vpatch, total;
+      rowstat, lab_logit, flags, draw_active, draw_ids, row_active, rs_draw, kpatch, vpatch, win_pos,
+      win_cnt, win_ids, win_rows, win_total, total;
   AttnPlan first, draws;
   bool spec, prec, full, patch;
 };
@@ -366,6 +367,14 @@ SlotPlan plan_slot(const dg_dims &d, int B, int S, int max_prompt, int nd, int s
   p.draw_ids = a.take(nd > 1 ? (size_t)ncmax * d.canvas * sizeof(int32_t) : 0);
   p.row_active = a.take(nrows * sizeof(int32_t));
   p.rs_draw = a.take(nrows * sizeof(float));
+  // one-pass patched reads: the rows within the slots' windows (see SlotArgs)
+  const bool win = p.spec && p.patch;
+  const size_t bc = win ? (size_t)B * d.canvas * sizeof(int32_t) : 0;
+  p.win_pos = a.take(bc);
+  p.win_cnt = a.take(win ? (size_t)B * sizeof(int32_t) : 0);
+  p.win_ids = a.take(bc);
+  p.win_rows = a.take(bc);
+  p.win_total = a.take(win ? sizeof(int32_t) : 0);
   p.total = a.off;
   return p;
 }
@@ -441,6 +450,8 @@ struct Gather {
   // patch_from
   const void *kpatch = nullptr, *vpatch = nullptr;
   int patch_from = 0;
+  // patched tiles read only these base rows (AttnArgs::win_pos), or null
+  const int32_t *win_pos = nullptr, *win_cnt = nullptr;
   // encoder mode: the canvases are causal prompt chunks (AttnArgs::chunks)
   const int4 *chunks = nullptr;
 };
@@ -527,6 +538,8 @@ dg_status run_block(const dg_dims &d, const dg_weights *w, const dg_prompt_kv *k
   aa.kpatch = gq.kpatch;
   aa.vpatch = gq.vpatch;
   aa.patch_from = gq.patch_from;
+  aa.win_pos = gq.win_pos;
+  aa.win_cnt = gq.win_cnt;
   aa.chunks = gq.chunks;
   DG_MARK(sg, DG_STAGE_ATTENTION, 0);
   DG_TRY_HIP(dg::launch_attention(aa, d.head_dim, bf, st), "attention launch");
@@ -1175,6 +1188,18 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
     sa.grp_first = G;
     sa.grp_draw = G;
     sa.off_draw = 1;
+    // patched draws: a base canvas's k, v are read only within its slots'
+    // windows, so only those rows are projected (a list built with the canvases)
+    const bool win = p.patch && !full;
+    if (win) {
+      sa.W = window_of(d);
+      sa.win_pos = at<int32_t>(workspace, p.win_pos);
+      sa.win_cnt = at<int32_t>(workspace, p.win_cnt);
+      sa.win_ids = at<int32_t>(workspace, p.win_ids);
+      sa.win_rows = at<int32_t>(workspace, p.win_rows);
+      sa.win_total = at<int32_t>(workspace, p.win_total);
+      DG_TRY_HIP(dg::launch_clear_i32(sa.win_total, 1, st), "window row count clear launch");
+    }
     DG_TRY_HIP(dg::launch_slot_spec_build(sa, sa.draw_ids, rs_draw, st), "read canvas launch");
     if (full) {
       // every row of the B*G canvases through S0..S3, then the slot rows' LM head
@@ -1216,9 +1241,15 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
     qa.part = proj_part;
     // patched draws: canvas b's k, v once (rows b*C), read by every draw
     qa.kv_copies = p.patch ? 0 : G - 1;   // else the draws' copies of canvas b's k, v
+    if (win) {   // the listed rows only (their count is on the device)
+      qa.ids = sa.win_ids;
+      qa.kv_row = sa.win_rows;
+      qa.m_dev = sa.win_total;
+    }
     DG_TRY_HIP(dg::launch_qkv(qa, bf, st), "k/v projection launch");
     dg::QkvArgs qg = qa;
     qg.kv_copies = 0;
+    qg.m_dev = nullptr;
     qg.ids = sa.qids;
     qg.M = (int64_t)batch * G * n_slots;
     qg.C = n_slots;
@@ -1236,6 +1267,10 @@ dg_status slot_read(const dg_dims *dims, const dg_weights *w, const dg_prompt_kv
       gd.kpatch = kpatch;
       gd.vpatch = vpatch;
       gd.patch_from = 1;
+      if (win) {
+        gd.win_pos = sa.win_pos;
+        gd.win_cnt = sa.win_cnt;
+      }
     }
     s = run_block(d, w, kv, batch * G, G, sa.draw_ids, nullptr, nullptr, nullptr, q, k, v, o,
                   p.draws, part_o, part_ml, proj_part, h, st, Stages(), gd);

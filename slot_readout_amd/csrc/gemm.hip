@@ -539,6 +539,13 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
   const int64_t m0 = (int64_t)mt * BM;
   const int n0 = a.col0 + nt * BN;
   if (!tile_active(a.active, m0, BM, a.M, a.C)) return;
+  // rows past a count on the device (at most M) are skipped
+  int64_t M = a.M;
+  if (a.m_dev) {
+    const int64_t md = *a.m_dev;
+    M = md < M ? md : M;
+  }
+  if (m0 >= M) return;
   const T *E = static_cast<const T *>(a.embed);
   const T *sc = static_cast<const T *>(a.sc_in);
   const int nq = a.nq, nk = a.nkv, ntot = a.col1, d = a.d;
@@ -546,7 +553,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
 #pragma unroll
   for (int it = 0; it < G::AI; ++it) {
     const int64_t row = m0 + G::a_row(it);
-    const bool in = row < a.M;
+    const bool in = row < M;
     const int id = in ? a.ids[row] : 0;
     const bool ok = in && id >= 0 && id < a.vocab;
     if (in && !ok && a.flags && G::a_kc(it) == 0) atomicOr(a.flags, DG_FLAG_BAD_TOKEN);
@@ -601,7 +608,7 @@ __global__ __launch_bounds__(WGM *WGN *WAVE) void qkv_kernel(QkvArgs a) {
     const int rl = ch / CPW, cc = ch % CPW;
     const int64_t row = m0 + rl;
     const int col = n0 + cc * G::VEC;
-    if (row >= a.M || col >= ntot) continue;
+    if (row >= M || col >= ntot) continue;
     T *base;
     int ld, c;
     if (col < nq) { base = q; ld = nq; c = col; }
@@ -1410,7 +1417,7 @@ hipError_t launch_qkv(const QkvArgs &a, bool bf, hipStream_t st) {
   if (a.col0 < 0 || a.col1 > a.nq + 2 * a.nkv) return hipErrorInvalidValue;
   QkvArgs b = a;
   proj_split(a.M, ntot, a.d, bf, &b.ksplit, &b.kchunk);
-  if (b.ksplit == 1 || !a.part) {
+  if (b.ksplit == 1 || !a.part || a.m_dev) {
     b.part = nullptr;
     b.ksplit = 1;
     b.kchunk = a.d;

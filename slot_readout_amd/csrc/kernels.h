@@ -34,6 +34,8 @@ struct QkvArgs {
   // each k, v row written is also written kv_copies more times, C, 2C, ...
   // rows further on (the canvases that follow, holding copies of it)
   int kv_copies;
+  // rows past *m_dev (a count on the device, at most M) are skipped, or null
+  const int32_t *m_dev;
   // with no kv_row map and kv_cmul > 1: input row m of canvas m / C writes
   // k, v row (m / C) * kv_cmul * C + m % C (canvas c's k, v land in canvas slot
   // c * kv_cmul, the first of kv_cmul canvases that will hold copies of it)
@@ -160,6 +162,11 @@ struct AttnArgs {
   // kpatch / vpatch ([nc*qn, Hkv*hd]).
   const void *kpatch, *vpatch;
   int patch_from;
+  // patched tiles: with win_cnt set, the base canvas c's rows a tile reads are
+  // its win_cnt[c] positions win_pos[c*C + k] (ascending: the union of the
+  // windows of its queries); else every position from the lowest window start
+  // to the highest window end
+  const int32_t *win_pos, *win_cnt;
   // Encoder mode (causal attention over prompts cut into chunks of C tokens),
   // or null: canvas cb is a chunk, and chunks[cb] = {x: first cache row of its
   // sequence, y: tokens of the sequence before the chunk (its prompt keys are
@@ -284,6 +291,13 @@ struct SlotArgs {
   // whole-canvas order: the hidden state has every canvas row, and a slot
   // row's LM-head row is its canvas row (canvas * C + position)
   int full_canvas;
+  // one-pass patched reads (win_pos set): the union of the windows (+-W) of
+  // base canvas b's slots, as win_cnt[b] ascending positions win_pos[b*C + k],
+  // and the same rows of every base canvas in one list for the k/v projection
+  // (win_ids: token ids, win_rows: canvas rows b*C + position; win_total counts
+  // them, zeroed before the build)
+  int W;
+  int32_t *win_pos, *win_cnt, *win_ids, *win_rows, *win_total;
 };
 
 hipError_t launch_slot_rows(const SlotArgs &a, hipStream_t st);

@@ -332,6 +332,42 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
   if (j == 0 && a.kv_row_base)
     for (int i = threadIdx.x; i < a.C; i += 256)
       a.kv_row_base[(int64_t)b * a.C + i] = (int32_t)((int64_t)cb * a.C + i);
+  if (j == 0 && a.win_pos) {
+    // the positions within +-W of any of canvas b's in-range slots, ascending
+    // (a ballot and the per-wave counts place them), then the same rows in the
+    // projection's list at a range taken from the running total
+    __shared__ int wsum[4];
+    __shared__ int wbase;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int total = 0;
+    for (int c0 = 0; c0 < a.C; c0 += 256) {
+      const int p = c0 + threadIdx.x;
+      bool in = false;
+      if (p < a.C)
+        for (int s = 0; s < a.S && !in; ++s) {
+          const int q = a.slot_pos[(int64_t)b * a.S + s];
+          in = q >= 0 && q < a.C && p - q <= a.W && q - p <= a.W;
+        }
+      const uint64_t m = __ballot(in);
+      if (lane == 0) wsum[wv] = __popcll(m);
+      __syncthreads();
+      int off = total;
+      for (int i = 0; i < wv; ++i) off += wsum[i];
+      if (in) a.win_pos[(int64_t)b * a.C + off + __popcll(m & ((1ull << lane) - 1))] = p;
+      total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      a.win_cnt[b] = total;
+      wbase = atomicAdd(a.win_total, total);
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < total; k += 256) {
+      const int p = a.win_pos[(int64_t)b * a.C + k];
+      a.win_ids[wbase + k] = a.canvas_ids[(int64_t)b * a.C + p];
+      a.win_rows[wbase + k] = (int32_t)((int64_t)b * a.C + p);
+    }
+  }
 }
 
 
