@@ -521,7 +521,20 @@ def leg_reads512(hip, stream, K, W):
     dm = inp["dims"]
     hq, hkv = dm.n_q_heads * dm.head_dim, dm.n_kv_heads * dm.head_dim
     ncv = B * (1 + (nd if reread else 0))
-    proj_flops = 2.0 * dm.d_model * (2 * hkv) * dm.canvas * ncv + 4.0 * dm.d_model * hq * S * ncv
+    # k, v are needed only at the canvas rows within +-W of a slot (once per
+    # base canvas: the draws differ from it only at the slots); q and the output
+    # projection at the slot rows of every canvas read
+    import numpy as np
+    sp = inp["slot_pos"]
+    sp = sp.cpu().numpy() if hasattr(sp, "cpu") else np.asarray(sp)
+    wnd = min(dm.window, dm.canvas - 1)
+    pos = np.arange(dm.canvas)
+    near = np.zeros((B, dm.canvas), dtype=bool)
+    for s_ in range(S):
+        q = sp[:, s_:s_ + 1]
+        near |= (q >= 0) & (q < dm.canvas) & (np.abs(pos[None, :] - q) <= wnd)
+    kv_rows = int(near.sum())
+    proj_flops = 2.0 * dm.d_model * (2 * hkv) * kv_rows + 4.0 * dm.d_model * hq * S * ncv
     head_flops = 2.0 * dm.vocab * dm.d_model * S * ncv
     flops = a1_flops * (1 + (nd if reread else 0)) + proj_flops + head_flops
     ms = t["ms_per_step"]
@@ -534,7 +547,7 @@ def leg_reads512(hip, stream, K, W):
            "roofline": {"kernel": "dg_slot_read call (all kernels)", "bound": "hbm",
                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                        "algorithmic_bytes_per_call": int(passes_bytes),
+                        "algorithmic_bytes_per_call": int(passes_bytes), "kv_rows": kv_rows,
                         "mfma_tflops": round(tfl, 1), "mfma_frac": round(tfl / BF16_PEAK_TFLOPS, 4)}}
     w.release()
     return out
