@@ -507,9 +507,12 @@ def leg_step_workload(name, hip, stream, K, W):
 def leg_reads512(hip, stream, K, W):
     """The 512-canvas structured read batch: slot reads per second.  The roofline
     is that of the whole read call (its kernels are not instrumented one by one;
-    the per-kernel split is in the committed rocprofv3 summary): the prompt KV
-    read once per attention pass (the first read and the batched draws) against
-    HBM, and the call's flops against the bf16 MFMA peak."""
+    the per-kernel split is in the committed rocprofv3 summary) against HBM: the
+    least traffic the call's work needs -- every prompt key and value once (the
+    draws of a canvas differ from it only at the slots, so one pass over the
+    prompt serves the first read and the draws), the base canvases' k and v at
+    the rows within +-W of a slot, and the slot rows' q, o and the draws' slot
+    k, v -- and the call's flops against the bf16 MFMA peak."""
     w = Workload("reads512", hip, stream)
     t = w.run(K, W)
     inp = w.inp
@@ -517,9 +520,9 @@ def leg_reads512(hip, stream, K, W):
     du = w.ro["draws_used"]
     reread = int((du > 1).any(dim=1).sum().item())
     a1_bytes, a1_flops, kv = attention_work(inp, queries=S)
-    passes_bytes = a1_bytes + (attention_work(inp, queries=S, canvases=nd)[0] if reread else 0)
     dm = inp["dims"]
     hq, hkv = dm.n_q_heads * dm.head_dim, dm.n_kv_heads * dm.head_dim
+    es = 2 if dm.dtype == "bf16" else 4
     ncv = B * (1 + (nd if reread else 0))
     # k, v are needed only at the canvas rows within +-W of a slot (once per
     # base canvas: the draws differ from it only at the slots); q and the output
@@ -534,6 +537,8 @@ def leg_reads512(hip, stream, K, W):
         q = sp[:, s_:s_ + 1]
         near |= (q >= 0) & (q < dm.canvas) & (np.abs(pos[None, :] - q) <= wnd)
     kv_rows = int(near.sum())
+    passes_bytes = (kv + kv_rows * 2 * hkv * es + ncv * S * 2 * hq * es
+                    + (B * nd * S * 2 * hkv * es if reread else 0))
     proj_flops = 2.0 * dm.d_model * (2 * hkv) * kv_rows + 4.0 * dm.d_model * hq * S * ncv
     head_flops = 2.0 * dm.vocab * dm.d_model * S * ncv
     flops = a1_flops * (1 + (nd if reread else 0)) + proj_flops + head_flops
