@@ -188,6 +188,33 @@ def test_slot_read_one_pass_draws_bf16(torch_cuda):
     _check_slots(g, ref, inp, "bf16", "one-pass draws bf16")
 
 
+@pytest.mark.parametrize("window", [0, 5, 255, 400])
+def test_slot_read_one_pass_window_rows(torch_cuda, window):
+    """One-pass patched draws project and attend only the base rows within +-W
+    of one of the canvas's slots, listed per canvas on the device: W = 0 (the
+    slot positions alone), a small window, W = C - 1 and W > C (every row).
+    Three canvases with different slot sets (one slot out of range; two slots
+    at one position; slots at both canvas ends), so the canvases' lists differ
+    in length, against the oracle."""
+    inp = make_inputs(config("reads512", vocab=262144, mask_id=262143, window=window), batch=3,
+                      prompt_override=("fixed", 96))
+    dims = inp["dims"]
+    C = dims.canvas
+    assert inp["slot_pos"].shape[1] == 4
+    inp["slot_pos"][0] = [10, 200, C + 5, 11]
+    inp["slot_pos"][1] = [50, 50, 120, 121]
+    inp["slot_pos"][2] = [0, 1, C - 2, C - 1]
+    for b in range(3):
+        for p in inp["slot_pos"][b]:
+            if 0 <= p < C:
+                inp["canvas_ids"][b, p] = dims.mask_id
+    assert _one_pass_draws(dims, 3, 4, inp["n_draws"], int(inp["max_prompt"]))
+    ref = oracle.slot_read(inp)
+    assert ref["status"][0, 2] == oracle.SLOT_BAD_POS
+    g = _read(inp)
+    _check_slots(g, ref, inp, "bf16", f"one-pass window rows W={window}")
+
+
 def test_slot_read_many_slots_two_pass(torch_cuda):
     """150 slots on one canvas: more slot rows than one gathered query tile holds
     (128 at head_dim 64), and the 22 slots past the 128 masked positions all sit
