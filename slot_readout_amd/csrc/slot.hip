@@ -333,21 +333,40 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
     for (int i = threadIdx.x; i < a.C; i += 256)
       a.kv_row_base[(int64_t)b * a.C + i] = (int32_t)((int64_t)cb * a.C + i);
   if (j == 0 && a.win_pos) {
-    // the positions within +-W of any of canvas b's in-range slots, ascending
-    // (a ballot and the per-wave counts place them), then the same rows in the
-    // projection's list at a range taken from the running total
-    __shared__ int wsum[4];
+    // the positions within +-W of any of canvas b's in-range slots, ascending,
+    // then the same rows in the projection's list at a range taken from the
+    // running total.  Each slot adds +1 at its window's first position and -1
+    // past its last; a position is in a window where the running sum of these
+    // marks is positive (a scan per 256 positions), and a ballot with the
+    // per-wave counts places it.
+    __shared__ int cover[DG_MAX_CANVAS + 1];
+    __shared__ int wsum[4], wtot[4];
     __shared__ int wbase;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int total = 0;
+    for (int i = threadIdx.x; i <= a.C; i += 256) cover[i] = 0;
+    __syncthreads();
+    for (int s = threadIdx.x; s < a.S; s += 256) {
+      const int q = a.slot_pos[(int64_t)b * a.S + s];
+      if (q >= 0 && q < a.C) {   // (W <= C - 1, so q + W does not overflow)
+        atomicAdd(&cover[q - a.W > 0 ? q - a.W : 0], 1);
+        atomicAdd(&cover[(q + a.W < a.C - 1 ? q + a.W : a.C - 1) + 1], -1);
+      }
+    }
+    __syncthreads();
+    int total = 0, run = 0;   // run: the marks before the chunk
     for (int c0 = 0; c0 < a.C; c0 += 256) {
       const int p = c0 + threadIdx.x;
-      bool in = false;
-      if (p < a.C)
-        for (int s = 0; s < a.S && !in; ++s) {
-          const int q = a.slot_pos[(int64_t)b * a.S + s];
-          in = q >= 0 && q < a.C && p - q <= a.W && q - p <= a.W;
-        }
+      int x = p < a.C ? cover[p] : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wtot[wv] = x;
+      __syncthreads();
+      int pre = run;
+      for (int i = 0; i < wv; ++i) pre += wtot[i];
+      const bool in = p < a.C && pre + x > 0;
       const uint64_t m = __ballot(in);
       if (lane == 0) wsum[wv] = __popcll(m);
       __syncthreads();
@@ -355,6 +374,7 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
       for (int i = 0; i < wv; ++i) off += wsum[i];
       if (in) a.win_pos[(int64_t)b * a.C + off + __popcll(m & ((1ull << lane) - 1))] = p;
       total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      run += wtot[0] + wtot[1] + wtot[2] + wtot[3];
       __syncthreads();
     }
     if (threadIdx.x == 0) {

@@ -188,31 +188,37 @@ def test_slot_read_one_pass_draws_bf16(torch_cuda):
     _check_slots(g, ref, inp, "bf16", "one-pass draws bf16")
 
 
-@pytest.mark.parametrize("window", [0, 5, 255, 400])
-def test_slot_read_one_pass_window_rows(torch_cuda, window):
+@pytest.mark.parametrize("window,n_slots", [(0, 4), (5, 4), (255, 4), (400, 4), (5, 40), (0, 120)])
+def test_slot_read_one_pass_window_rows(torch_cuda, window, n_slots):
     """One-pass patched draws project and attend only the base rows within +-W
     of one of the canvas's slots, listed per canvas on the device: W = 0 (the
-    slot positions alone), a small window, W = C - 1 and W > C (every row).
-    Three canvases with different slot sets (one slot out of range; two slots
-    at one position; slots at both canvas ends), so the canvases' lists differ
-    in length, against the oracle."""
-    inp = make_inputs(config("reads512", vocab=262144, mask_id=262143, window=window), batch=3,
-                      prompt_override=("fixed", 96))
+    slot positions alone), a small window, W = C - 1 and W > C (every row), and
+    40 or 120 slots per canvas.  Three canvases with different slot sets (a slot
+    out of range, two slots at one position, slots at both canvas ends), so the
+    canvases' lists differ in length, against the oracle."""
+    inp = make_inputs(config("reads512", vocab=262144, mask_id=262143, window=window, n_slots=n_slots),
+                      batch=3, prompt_override=("fixed", 96))
     dims = inp["dims"]
     C = dims.canvas
-    assert inp["slot_pos"].shape[1] == 4
-    inp["slot_pos"][0] = [10, 200, C + 5, 11]
-    inp["slot_pos"][1] = [50, 50, 120, 121]
-    inp["slot_pos"][2] = [0, 1, C - 2, C - 1]
+    sp = inp["slot_pos"]
+    assert sp.shape[1] == n_slots
+    if n_slots == 4:
+        sp[0] = [10, 200, C + 5, 11]
+        sp[1] = [50, 50, 120, 121]
+        sp[2] = [0, 1, C - 2, C - 1]
+    else:
+        sp[0, 2] = C + 5
+        sp[1, 1] = sp[1, 0]
+        sp[2, 0], sp[2, -1] = 0, C - 1
     for b in range(3):
-        for p in inp["slot_pos"][b]:
+        for p in sp[b]:
             if 0 <= p < C:
                 inp["canvas_ids"][b, p] = dims.mask_id
-    assert _one_pass_draws(dims, 3, 4, inp["n_draws"], int(inp["max_prompt"]))
+    assert _one_pass_draws(dims, 3, n_slots, inp["n_draws"], int(inp["max_prompt"]))
     ref = oracle.slot_read(inp)
     assert ref["status"][0, 2] == oracle.SLOT_BAD_POS
     g = _read(inp)
-    _check_slots(g, ref, inp, "bf16", f"one-pass window rows W={window}")
+    _check_slots(g, ref, inp, "bf16", f"one-pass window rows W={window} S={n_slots}")
 
 
 def test_slot_read_many_slots_two_pass(torch_cuda):
