@@ -752,6 +752,56 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
 // partials.  For HD = 64 a split's row is 16 float4 chunks, so the wave reads
 // four splits per load (lane group g = lane / 16 takes splits g, g+4, ...) and
 // the groups are added by a fixed butterfly; wider heads take one split per load.
+// The same merge for few splits at head_dim 64: a 16-lane group per output row
+// (its 16 float4 chunks), four rows per wave, each group over all the splits of
+// its row in order.  One wave per row would leave most of its lanes idle and
+// pay a wave's fixed cost per 64 outputs.
+template <typename T, bool PREC = false>
+__global__ __launch_bounds__(256) void attn_merge_rows_kernel(AttnArgs a) {
+  using TO = typename std::conditional<PREC, float, T>::type;   // partial / output type
+  constexpr int HD = 64, C4 = HD / 4;
+  constexpr int NQ = AttnShape<T, HD>::NW * AttnShape<T, HD>::QB * 16;
+  const int QN = a.qpos ? a.qn : a.C;
+  const int64_t R = (int64_t)a.nc * a.Hq * QN;
+  const int lane = threadIdx.x & 63;
+  const int c0 = lane % C4;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= R) return;
+  const int qi = (int)(row % QN);
+  const int64_t ch = row / QN;
+  const int h = (int)(ch % a.Hq);
+  const int64_t cb = ch / a.Hq;
+  if (a.active && !a.active[cb]) return;
+  const int ncp = a.cpack > 1 ? a.cpack : 1;
+  int64_t p0, plen;
+  int lo, hi;
+  tile_keys(a, (int)(cb / ncp * ncp), qi / NQ * NQ, NQ, &p0, &plen, &lo, &hi, ncp);
+  const int64_t nk = plen + (hi - lo);
+  const int ns = (int)(cdiv64(nk, a.chunk) < a.nsplit ? cdiv64(nk, a.chunk) : a.nsplit);
+  const float2 *ml = a.part_ml + row;
+  const TO *po = static_cast<const TO *>(a.part_o) + (row * C4 + c0) * 4;
+  const int64_t sstride = R * C4 * 4;   // elements between splits
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[(int64_t)s * R].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY)
+    for (int s = 0; s < ns; ++s) {
+      const float2 v = ml[(int64_t)s * R];
+      // raw v_exp_f32: the argument is <= 0 or -inf
+      const float w = __builtin_amdgcn_exp2f(v.x - M);
+      L += v.y * w;
+      const float4 o = load4v<TO>(po + s * sstride);
+      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+    }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  TO *o = static_cast<TO *>(a.o) + ((cb * QN + qi) * a.Hq + h) * HD + 4 * c0;
+  o[0] = from_f<TO>(acc.x * inv);
+  o[1] = from_f<TO>(acc.y * inv);
+  o[2] = from_f<TO>(acc.z * inv);
+  o[3] = from_f<TO>(acc.w * inv);
+}
+
 template <typename T, int HD, bool PREC = false>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   using TO = typename std::conditional<PREC, float, T>::type;   // partial / output type
@@ -836,6 +886,9 @@ static_assert(AttnShape<bf16, 64>::NW * AttnShape<bf16, 64>::QB * 16 == 128 &&
               AttnShape<bf16, 512>::NW * AttnShape<bf16, 512>::QB * 16 == 64,
               "query tile sizes");
 
+// splits up to which the head_dim-64 merge takes a lane group per row
+constexpr int kMergeRowsSplits = 8;
+
 template <typename T, int HD, bool PREC, bool PATCH>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   constexpr int NW = AttnShape<T, HD>::NW;
@@ -855,7 +908,10 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD, PREC>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, b);
+  if (HD == 64 && a.nsplit <= kMergeRowsSplits)
+    hipLaunchKernelGGL((attn_merge_rows_kernel<T, PREC>), dim3((unsigned)cdiv64(R, 16)), dim3(256), 0, st, b);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<T, HD, PREC>), dim3((unsigned)cdiv64(R, 4)), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 
