@@ -221,6 +221,23 @@ def test_slot_read_one_pass_window_rows(torch_cuda, window, n_slots):
     _check_slots(g, ref, inp, "bf16", f"one-pass window rows W={window} S={n_slots}")
 
 
+@pytest.mark.parametrize("name,B", [("reads512", 52), ("tiny_f32", 34)])
+def test_slot_read_label_logits_of_many_rows(torch_cuda, name, B):
+    """A read whose LM head has 1,024 rows or more takes its label logits from
+    a dot product per (row, label) instead of the vocabulary tiles: 52
+    read-batch canvases in one pass (1,040 rows, bf16 split rows, up to 26
+    labels), and 34 tiny fp32 canvases whose draws all run in a second pass
+    (1,088 rows), against the oracle."""
+    inp = make_inputs(config(name), batch=B, prompt_override=("fixed", 64) if name == "reads512" else None)
+    S = inp["slot_pos"].shape[1]
+    ref = oracle.slot_read(inp)
+    flagged = int((ref["draws_used"] > 1).any(axis=1).sum())
+    rows = B * (1 + inp["n_draws"]) * S if name == "reads512" else flagged * inp["n_draws"] * S
+    assert rows >= 1024
+    g = _read(inp)
+    _check_slots(g, ref, inp, inp["dims"].dtype, f"label logits of many rows {name}")
+
+
 def test_slot_read_many_slots_two_pass(torch_cuda):
     """150 slots on one canvas: more slot rows than one gathered query tile holds
     (128 at head_dim 64), and the 22 slots past the 128 masked positions all sit
