@@ -23,11 +23,17 @@ __device__ inline int validate_slot(const SlotArgs &a, int64_t bs) {
   const int k = a.n_labels[bs];
   if (pos < 0 || pos >= a.C) return DG_SLOT_BAD_POS;
   if (k < 1 || k > DG_MAX_LABELS) return DG_SLOT_BAD_COUNT;
-  for (int j = 0; j < k; ++j) {
-    const int lab = a.label_ids[bs * DG_MAX_LABELS + j];
-    if (lab < 0 || lab >= a.V) return DG_SLOT_BAD_LABEL;
-  }
-  return DG_SLOT_OK;
+  // every label is loaded before any is tested (no exit per label, so the
+  // loads are in flight together instead of one after another)
+  const int32_t *labs = a.label_ids + bs * DG_MAX_LABELS;
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < DG_MAX_LABELS; ++j)
+    if (j < k) {
+      const int lab = labs[j];
+      bad |= lab < 0 || lab >= a.V;
+    }
+  return bad ? DG_SLOT_BAD_LABEL : DG_SLOT_OK;
 }
 
 // rows of the first pass: slot (b, s) is row bs = b*S + s, at position pos of canvas b
@@ -142,20 +148,30 @@ __global__ __launch_bounds__(256) void slot_build_draws_kernel(SlotArgs a) {
   if (!act) return;
   int32_t *dst = a.draw_ids + (int64_t)bd * a.C;
   const int32_t *src = a.canvas_ids + (int64_t)b * a.C;
-  for (int i = threadIdx.x; i < a.C; i += 256) dst[i] = src[i];
+  __shared__ int last[DG_MAX_CANVAS];
+  for (int i = threadIdx.x; i < a.C; i += 256) {
+    dst[i] = src[i];
+    last[i] = -1;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int s = 0; s < a.S; ++s) {
-      const int64_t bs = (int64_t)b * a.S + s;
-      const int pos = a.slot_pos[bs];
-      if (pos < 0 || pos >= a.C) continue;
-      int nid = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
-      if (nid < 0 || nid >= a.V) {
-        nid = a.mask_id;
-        if (a.status[bs] == DG_SLOT_OK) a.status[bs] = DG_SLOT_BAD_NOISE;
-      }
-      dst[pos] = nid;
+  // where two slots share a position the later one wins, as when the slots
+  // are written in order (the highest slot index at each position, by LDS
+  // atomics, then each winner writes)
+  for (int s = threadIdx.x; s < a.S; s += 256) {
+    const int pos = a.slot_pos[(int64_t)b * a.S + s];
+    if (pos >= 0 && pos < a.C) atomicMax(&last[pos], s);
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.S; s += 256) {
+    const int64_t bs = (int64_t)b * a.S + s;
+    const int pos = a.slot_pos[bs];
+    if (pos < 0 || pos >= a.C) continue;
+    int nid = a.noise_ids[((int64_t)d * a.B + b) * a.S + s];
+    if (nid < 0 || nid >= a.V) {
+      nid = a.mask_id;
+      if (a.status[bs] == DG_SLOT_OK) a.status[bs] = DG_SLOT_BAD_NOISE;
     }
+    if (last[pos] == s) dst[pos] = nid;
   }
 }
 
@@ -307,12 +323,22 @@ __global__ __launch_bounds__(256) void slot_spec_build_kernel(SlotArgs a, int32_
     a.rows[n] = st == DG_SLOT_OK ? (int32_t)(a.full_canvas ? (int64_t)cb * a.C + a.slot_pos[bs] : n) : -1;
     rs[n] = a.row_scale ? a.row_scale[bs] : 1.f;
   }
-  // slots are written in order, as in the separate draw pass
-  if (j > 0 && threadIdx.x == 0) {
-    for (int s = 0; s < a.S; ++s) {
-      const int64_t bs = (int64_t)b * a.S + s;
-      const int pos = a.slot_pos[bs];
-      if (pos < 0 || pos >= a.C) continue;
+  // the draw's noise ids at the slot positions; where two slots share a
+  // position the later one wins, as when the slots are written in order (the
+  // highest slot index at each position is found with LDS atomics, then each
+  // winner writes)
+  if (j > 0) {
+    __shared__ int last[DG_MAX_CANVAS];
+    for (int i = threadIdx.x; i < a.C; i += 256) last[i] = -1;
+    __syncthreads();
+    for (int s = threadIdx.x; s < a.S; s += 256) {
+      const int pos = a.slot_pos[(int64_t)b * a.S + s];
+      if (pos >= 0 && pos < a.C) atomicMax(&last[pos], s);
+    }
+    __syncthreads();
+    for (int s = threadIdx.x; s < a.S; s += 256) {
+      const int pos = a.slot_pos[(int64_t)b * a.S + s];
+      if (pos < 0 || pos >= a.C || last[pos] != s) continue;
       int nid = a.noise_ids[((int64_t)(j - 1) * a.B + b) * a.S + s];
       if (nid < 0 || nid >= a.V) nid = a.mask_id;
       dst[pos] = nid;
