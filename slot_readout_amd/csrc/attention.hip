@@ -162,8 +162,12 @@ __device__ inline bool tile_keys(const AttnArgs &a, int cb, int i0, int nq, int6
 // draws (canvases with cb % canvas_per_prompt >= patch_from), whose keys and
 // values are the slot rows cb * qn + s of kpatch / vpatch: the draws differ
 // from their base canvas only there, so no draw canvas's k, v are stored.
-template <typename T, int HD, bool PREC = false, bool PATCH = false>
-__global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T) == 2 ? 4 : 1)) void attn_kernel(AttnArgs a) {
+// HK > 1 (patched tiles, bf16, head_dim 64): the workgroup serves all HK kv
+// heads of its canvases: K/V rows are staged whole (HK heads side by side) and
+// each wave takes the columns of one kv head (NQ / HK columns per head), so the
+// gathered queries of every head compute on one staging of the keys.
+template <typename T, int HD, bool PREC = false, bool PATCH = false, int HK = 1>
+__global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HK > 1 ? 2 : (HD == 64 && sizeof(T) == 2 ? 4 : 1))) void attn_kernel(AttnArgs a) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int QB = AttnShape<T, HD>::QB;
@@ -187,10 +191,12 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   // bf16 rows of K and V are HD + 16 elements apart: with that stride both the
   // 16-byte K fragment reads and the transposing V reads are free of LDS bank
   // conflicts (measured on gfx950; a 16-byte pad leaves 2-way conflicts)
-  constexpr int KP = TR ? HD + 16 : HD + VEC;
+  static_assert(HK == 1 || (PATCH && TR && HD == 64), "packed kv heads: patched bf16 tiles at head_dim 64");
+  constexpr int RW = HK * HD;                   // elements of a staged key row
+  constexpr int KP = TR ? RW + 16 : RW + VEC;
   constexpr int VP = NK + VEC;
   constexpr int KS = HD / MF::KI;
-  constexpr int CPK = HD / VEC;                 // 16-byte chunks per key row
+  constexpr int CPK = RW / VEC;                 // 16-byte chunks per key row
   constexpr int CH = NK * CPK / NT;             // chunks of K (and of V) per thread per block
   static_assert(NK * CPK % NT == 0, "block/thread mismatch");
   // K and V tiles are double-buffered: block b lives in buffer b % 2, so the
@@ -205,7 +211,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   // its 16 columns in LDS only pad the rows); fp32: V^T [RB*16][VP] staged
   // element-wise, with the extra block.
   constexpr int RB = HD / 16 + 1;
-  constexpr int VKP = HD + 16;
+  constexpr int VKP = RW + 16;
   constexpr int VSZ = TR ? NK * VKP : RB * 16 * VP;
   __shared__ __attribute__((aligned(16))) T Vt0[VSZ], Vt1[VSZ];
   auto Vt = [&](int bf) -> T * { return bf ? Vt1 : Vt0; };
@@ -219,12 +225,14 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   const int nqt = (QN + NQ - 1) / NQ;
   const int ncp = a.cpack > 1 ? a.cpack : 1;
   int grpi, tile;
-  if (!xcd_group_tile(a.nc / ncp * a.Hkv * a.nsplit, a.packed ? 1 : (a.Hq / a.Hkv) * nqt, &grpi, &tile))
+  const int hkg = HK > 1 ? 1 : a.Hkv;   // kv-head groups per canvas group
+  if (!xcd_group_tile(a.nc / ncp * hkg * a.nsplit, (HK > 1 || a.packed) ? 1 : (a.Hq / a.Hkv) * nqt, &grpi, &tile))
     return;
   const int s = grpi % a.nsplit;
-  const int cb = grpi / a.nsplit / a.Hkv * ncp;   // the tile's first canvas
+  const int cb = grpi / a.nsplit / hkg * ncp;   // the tile's first canvas
   // packed: h is the kv group's first query head and every column names its own
-  const int h = (grpi / a.nsplit % a.Hkv) * (a.Hq / a.Hkv) + (a.packed ? 0 : tile / nqt);
+  // (HK > 1: h = 0 and the columns name their heads)
+  const int h = HK > 1 ? 0 : (grpi / a.nsplit % a.Hkv) * (a.Hq / a.Hkv) + (a.packed ? 0 : tile / nqt);
   const int qt = a.packed ? 0 : tile % nqt;
   if (a.active && ncp == 1 && !a.active[cb]) return;
   const int G = a.Hq / a.Hkv, g = h / G;
@@ -263,11 +271,24 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
 #pragma unroll
   for (int jb = 0; jb < QB; ++jb) {
     const int c = i0 + w * QB * 16 + jb * 16 + col;
-    const bool in = c < ncp * G * QN;
-    cq[jb] = a.packed ? (in ? c % QN : QN) : c;
-    chd[jb] = a.packed ? (in ? c / QN % G : 0) : 0;
-    ccv[jb] = a.packed && in ? c / (G * QN) : 0;
+    if constexpr (HK > 1) {
+      // column c: kv head c / (NQ / HK), then the packed order within the head
+      constexpr int CPH = NQ / HK;
+      const int lc = c % CPH;
+      const bool in = lc < ncp * G * QN;
+      cq[jb] = in ? lc % QN : QN;
+      chd[jb] = in ? c / CPH * G + lc / QN % G : 0;
+      ccv[jb] = in ? lc / (G * QN) : 0;
+    } else {
+      const bool in = c < ncp * G * QN;
+      cq[jb] = a.packed ? (in ? c % QN : QN) : c;
+      chd[jb] = a.packed ? (in ? c / QN % G : 0) : 0;
+      ccv[jb] = a.packed && in ? c / (G * QN) : 0;
+    }
   }
+  // offset of the wave's kv head in a staged row (HK > 1)
+  static_assert(HK == 1 || (NQ / HK) % (QB * 16) == 0, "a wave's columns within one kv head");
+  const int gofs = HK > 1 ? (w * QB * 16) / (NQ / HK) * HD : 0;
   const T *kp = static_cast<const T *>(a.kp) + (int64_t)g * HD;
   const T *vp = static_cast<const T *>(a.vp) + (int64_t)g * HD;
   const int64_t cbase = (int64_t)cb * (a.kv_cmul > 1 ? a.kv_cmul : 1) * C * kv_stride + (int64_t)g * HD;
@@ -499,7 +520,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
   auto compute = [&](const Blk &d, int bf) {
     f32x4 sacc[NK / 16][QB];
     auto kfrag = [&](int ks, int kb2) {
-      return *reinterpret_cast<const frag *>(Ks(bf) + (kb2 * 16 + col) * KP + ks * MF::KI + grp * MF::KPL);
+      return *reinterpret_cast<const frag *>(Ks(bf) + (kb2 * 16 + col) * KP + gofs + ks * MF::KI + grp * MF::KPL);
     };
     frag kf[KPRE ? KS : 1][KPRE ? NK / 16 : 1];
     if constexpr (KPRE) {
@@ -622,7 +643,7 @@ __global__ __launch_bounds__((64 * AttnShape<T, HD>::NW), (HD == 64 && sizeof(T)
             // returns V[key0 + 0..3][d0 + lane%16] in each lane.
             frag af = ones_frag;
             if (rb < HD / 16) {
-              const T *src0 = Vt(bf) + (t * 32 + grp * 4 + (col >> 2)) * VKP + rb * 16 + 4 * (col & 3);
+              const T *src0 = Vt(bf) + (t * 32 + grp * 4 + (col >> 2)) * VKP + gofs + rb * 16 + 4 * (col & 3);
               const v4s lo4 = ds_read_tr16(src0);
               const v4s hi4 = ds_read_tr16(src0 + 16 * VKP);
               __builtin_memcpy(&af, &lo4, 8);
@@ -891,6 +912,7 @@ constexpr int kMergeRowsSplits = 8;
 
 template <typename T, int HD, bool PREC, bool PATCH>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
+  constexpr int HKP = 4;   // kv heads a patched tile can serve together
   constexpr int NW = AttnShape<T, HD>::NW;
   constexpr int NQ = NW * AttnShape<T, HD>::QB * 16;
   const int QN = a.qpos ? a.qn : a.C;
@@ -902,9 +924,19 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   b.cpack = attn_cpack(QN, gathered, a.Hq, a.Hkv, HD, cpp);
   b.packed = attn_packed(QN, gathered, a.Hq, a.Hkv, HD, cpp) ? 1 : 0;
   if (a.nc % b.cpack) return hipErrorInvalidValue;
-  const dim3 grid = xcd_grid((int64_t)a.nc / b.cpack * a.Hkv * a.nsplit,
-                             b.packed ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
-  hipLaunchKernelGGL((attn_kernel<T, HD, PREC, PATCH>), grid, dim3(64 * NW), 0, st, b);
+  // patched tiles of 4 kv heads whose gathered queries fit a quarter tile each:
+  // one workgroup for the four
+  bool hk = false;
+  if constexpr (PATCH && HD == 64 && sizeof(T) == 2)
+    hk = a.Hkv == HKP && b.packed && (int64_t)(a.Hq / a.Hkv) * b.cpack * QN <= NQ / HKP;
+  const dim3 grid = xcd_grid((int64_t)a.nc / b.cpack * (hk ? 1 : a.Hkv) * a.nsplit,
+                             (hk || b.packed) ? 1 : (a.Hq / a.Hkv) * cdiv64(QN, NQ));
+  if constexpr (PATCH && HD == 64 && sizeof(T) == 2) {
+    if (hk) hipLaunchKernelGGL((attn_kernel<T, HD, PREC, PATCH, HKP>), grid, dim3(64 * NW), 0, st, b);
+    else hipLaunchKernelGGL((attn_kernel<T, HD, PREC, PATCH>), grid, dim3(64 * NW), 0, st, b);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<T, HD, PREC, PATCH>), grid, dim3(64 * NW), 0, st, b);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t R = (int64_t)a.nc * a.Hq * QN;
