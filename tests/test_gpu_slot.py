@@ -316,6 +316,22 @@ def test_slot_read_gqa_packed_heads(torch_cuda, name, n_kv, n_slots, batch):
     assert frac > 0.5
 
 
+@pytest.mark.parametrize("n_q,n_slots", [(4, 4), (8, 2)])
+def test_slot_read_patched_four_kv_heads(torch_cuda, n_q, n_slots):
+    """One-pass patched reads with four kv heads whose queries fit a quarter of
+    a tile each, which one workgroup serves together (each wave on one kv
+    head's slice of the staged rows): 4 q heads x 4 slots (MHA) and 8 q heads x
+    2 slots (two q heads per kv head), 16 canvases, against the oracle."""
+    inp = make_inputs(config("reads512", n_q_heads=n_q, n_kv_heads=4, n_slots=n_slots), batch=16,
+                      prompt_override=("fixed", 100))
+    dims = inp["dims"]
+    assert _one_pass_draws(dims, 16, n_slots, inp["n_draws"], int(inp["max_prompt"]))
+    assert (n_q // 4) * (1 + inp["n_draws"]) * n_slots <= 32
+    g = _read(inp)
+    ref = oracle.slot_read(inp)
+    _check_slots(g, ref, inp, "bf16", f"patched four kv heads q{n_q} S{n_slots}")
+
+
 def test_slot_read_wide_heads_peaked_rereads(torch_cuda):
     """Three canvases at d 2816 with 512-wide heads, read in two passes, with
     per-canvas logit multipliers 1, 24 and 64: flat rows and sharp ones whose
